@@ -1,0 +1,133 @@
+"""Byte layout of the compressed cache and its byte accounting.
+
+TEST INFRASTRUCTURE (see the package docstring).  The pages fix the bit
+budgets but not the packing; the layout below is this implementation's
+definition, written here independently of the HIP library so that packed bytes
+can be compared bit for bit.
+
+Per (sequence, KV head) slot of ``capacity`` tokens:
+
+* key planes   uint8  [capacity][P_k * d/8], P_k = key_mse_bits + key_qjl.
+  Plane p < key_mse_bits holds bit p of every coordinate's Lloyd-Max index;
+  plane key_mse_bits holds the QJL sign bits (1 = non-negative).  Inside a
+  plane, coordinate i is bit i % 8 of byte i // 8 (LSB first).
+* key norm, key residual norm   [capacity] fp32 or fp16.
+* value planes uint32 [capacity/32][value_bits][d]: word (blk, p, c) holds, in
+  bit t, bit p of the code of token 32*blk + t at channel c.
+* value meta (min/max values)   fp16 [capacity][d/group][2] = (scale, min).
+* value norm (MSE values)       [capacity] fp32 or fp16.
+
+``memory_bytes`` counts, as in [audit] AUDIT 1: the quantized data, the
+per-layer parameters (Pi, S, codebook tables) and the bf16 ring.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Layout:
+    d: int = 128
+    key_mse_bits: int = 2
+    key_qjl: int = 1
+    value_kind: str = "minmax"  # "minmax" | "mse"
+    value_bits: int = 2
+    value_group: int = 32
+    scalar_dtype: str = "f32"  # "f32" | "f16"
+
+    @property
+    def scalar_bytes(self) -> int:
+        return 4 if self.scalar_dtype == "f32" else 2
+
+    @property
+    def key_planes(self) -> int:
+        return self.key_mse_bits + self.key_qjl
+
+
+def bytes_per_token_head(lay: Layout) -> dict:
+    """Stored bytes for one token of one KV head, by field."""
+    s = lay.scalar_bytes
+    k_bits = lay.key_planes * lay.d // 8
+    k_scal = s * (1 + lay.key_qjl)
+    v_bits = lay.value_bits * lay.d // 8
+    if lay.value_kind == "minmax":
+        v_scal = (lay.d // lay.value_group) * 2 * 2
+    else:
+        v_scal = s
+    return {"k_bits": k_bits, "k_scalars": k_scal, "v_bits": v_bits, "v_scalars": v_scal,
+            "total": k_bits + k_scal + v_bits + v_scal}
+
+
+def codebook_table_bytes(bits: int) -> int:
+    """fp32 centroids (2^b), boundaries (2^b + 1) and decision boundaries (2^b - 1)."""
+    levels = 1 << bits
+    return 4 * (levels + (levels + 1) + (levels - 1))
+
+
+def memory_bytes(lay: Layout, batch: int, h_kv: int, n_tokens: int, what: str,
+                 ring_cap: int = 128) -> int:
+    """what: "data" (quantized tensors only), "params" (Pi and S in fp32 plus
+    the codebook tables), "ring" (bf16 K and V ring of ring_cap tokens)."""
+    if what == "data":
+        return bytes_per_token_head(lay)["total"] * batch * h_kv * n_tokens
+    if what == "params":
+        p = 2 * lay.d * lay.d * 4 + codebook_table_bytes(lay.key_mse_bits)
+        if lay.value_kind == "mse":
+            p += codebook_table_bytes(lay.value_bits)
+        return p
+    if what == "ring":
+        return batch * ring_cap * h_kv * lay.d * 2 * 2
+    raise ValueError(what)
+
+
+def pack_key_planes(idx: np.ndarray, qjl: np.ndarray | None, mse_bits: int) -> np.ndarray:
+    """(T, d) indices and (T, d) sign bits -> (T, P_k * d/8) uint8 planes."""
+    idx = np.asarray(idx, dtype=np.int64)
+    t, d = idx.shape
+    planes = [((idx >> p) & 1).astype(np.uint8) for p in range(mse_bits)]
+    if qjl is not None:
+        planes.append(np.asarray(qjl, dtype=np.uint8) & 1)
+    bits = np.concatenate(planes, axis=1)  # (T, P*d)
+    return np.packbits(bits, axis=1, bitorder="little")
+
+
+def unpack_key_planes(packed: np.ndarray, d: int, mse_bits: int, qjl: bool):
+    """Inverse of pack_key_planes: returns (idx, qjl_bits or None)."""
+    p_k = mse_bits + (1 if qjl else 0)
+    bits = np.unpackbits(np.asarray(packed, dtype=np.uint8), axis=1, bitorder="little")
+    bits = bits[:, : p_k * d].reshape(-1, p_k, d).astype(np.int64)
+    idx = np.zeros((bits.shape[0], d), dtype=np.int64)
+    for p in range(mse_bits):
+        idx |= bits[:, p, :] << p
+    return idx, (bits[:, mse_bits, :].astype(np.uint8) if qjl else None)
+
+
+def pack_value_planes(code: np.ndarray, bits: int, capacity: int | None = None) -> np.ndarray:
+    """(T, d) codes -> (capacity/32, bits, d) uint32 token-transposed planes.
+    Tokens T..capacity-1 are zero."""
+    code = np.asarray(code, dtype=np.int64)
+    t, d = code.shape
+    cap = t if capacity is None else capacity
+    if cap % 32 or cap < t:
+        raise ValueError("capacity must be a multiple of 32 and hold every token")
+    full = np.zeros((cap, d), dtype=np.int64)
+    full[:t] = code
+    blocks = full.reshape(cap // 32, 32, d)  # (blk, t, c)
+    out = np.zeros((cap // 32, bits, d), dtype=np.uint64)
+    for p in range(bits):
+        bit = ((blocks >> p) & 1).astype(np.uint64)  # (blk, t, c)
+        out[:, p, :] = np.sum(bit << np.arange(32, dtype=np.uint64)[None, :, None], axis=1)
+    return out.astype(np.uint32)
+
+
+def unpack_value_planes(words: np.ndarray, n_tokens: int) -> np.ndarray:
+    """(capacity/32, bits, d) uint32 -> (n_tokens, d) codes."""
+    w = np.asarray(words, dtype=np.uint64)
+    nblk, bits, d = w.shape
+    tt = np.arange(32, dtype=np.uint64)
+    code = np.zeros((nblk, 32, d), dtype=np.int64)
+    for p in range(bits):
+        code |= (((w[:, p, None, :] >> tt[None, :, None]) & 1).astype(np.int64)) << p
+    return code.reshape(nblk * 32, d)[:n_tokens]

@@ -1,0 +1,101 @@
+"""Pins of the oracle's packed layout (round trips, bit positions worked by hand)
+and of its byte accounting against the compression figures the pages print."""
+import json
+import os
+
+import numpy as np
+
+import oracle
+from oracle.layout import Layout, bytes_per_token_head, memory_bytes
+
+
+def test_key_planes_round_trip_and_bit_positions():
+    rng = np.random.default_rng(0)
+    for mse_bits in (1, 2, 3, 4):
+        idx = rng.integers(0, 1 << mse_bits, size=(37, 128))
+        qjl = rng.integers(0, 2, size=(37, 128)).astype(np.uint8)
+        packed = oracle.pack_key_planes(idx, qjl, mse_bits)
+        assert packed.shape == (37, (mse_bits + 1) * 16) and packed.dtype == np.uint8
+        i2, q2 = oracle.unpack_key_planes(packed, 128, mse_bits, True)
+        assert np.array_equal(i2, idx) and np.array_equal(q2, qjl)
+    # worked example: 2-bit index 2 (binary 10) at coordinate 9 sets plane 1,
+    # byte 9 // 8 = 1, bit 9 % 8 = 1 -> byte 16 + 1 = 17 holds 0b10; the QJL bit
+    # of coordinate 127 is the top bit of the last byte
+    idx = np.zeros((1, 128), dtype=np.int64)
+    idx[0, 9] = 2
+    qjl = np.zeros((1, 128), dtype=np.uint8)
+    qjl[0, 127] = 1
+    p = oracle.pack_key_planes(idx, qjl, 2)[0]
+    expect = np.zeros(48, dtype=np.uint8)
+    expect[17] = 0b10
+    expect[47] = 0x80
+    assert np.array_equal(p, expect)
+
+
+def test_value_planes_round_trip_and_bit_positions():
+    rng = np.random.default_rng(1)
+    for bits in (1, 2, 3, 4):
+        code = rng.integers(0, 1 << bits, size=(70, 128))
+        words = oracle.pack_value_planes(code, bits, capacity=96)
+        assert words.shape == (3, bits, 128) and words.dtype == np.uint32
+        assert np.array_equal(oracle.unpack_value_planes(words, 70), code)
+        assert np.all(oracle.unpack_value_planes(words, 96)[70:] == 0)
+    # worked example: token 33 (block 1, bit 1), channel 5, code 3 = planes 0 and 1
+    code = np.zeros((64, 128), dtype=np.int64)
+    code[33, 5] = 3
+    w = oracle.pack_value_planes(code, 2)
+    assert w[1, 0, 5] == 2 and w[1, 1, 5] == 2 and np.count_nonzero(w) == 2
+
+
+def _gold(golden_dir):
+    return json.load(open(os.path.join(golden_dir, "byte_counts.json")))
+
+
+def test_audit_data_only_ratio(golden_dir):
+    g = _gold(golden_dir)["audit_data_only"]
+    lay = Layout(**g["layout"])
+    assert bytes_per_token_head(lay)["total"] == g["bytes_per_token_head"]
+    n, h_kv = 4096, 8
+    fp16 = n * h_kv * 128 * 2 * 2
+    ratio = fp16 / memory_bytes(lay, 1, h_kv, n, "data")
+    assert round(ratio, 1) == g["ratio_printed"]
+    assert abs(ratio - 5.12) < 1e-12
+
+
+def test_audit_all_in_ratios(golden_dir):
+    gold = _gold(golden_dir)
+    g = gold["audit_all_in"]
+    lay = Layout(**gold["audit_data_only"]["layout"])
+    h_kv = g["h_kv"]
+    assert 2 * 128 * 128 * 4 == g["pi_plus_s_bytes"]
+    params = memory_bytes(lay, 1, h_kv, 0, "params")
+    assert params - g["pi_plus_s_bytes"] == 4 * (4 + 5 + 3)  # 2-bit MSE codebook tables
+    ring_one_tensor = memory_bytes(lay, 1, h_kv, 0, "ring") // 2  # the audit's ring term
+    got = {}
+    for n_s, printed in g["ratios_printed"].items():
+        n = int(n_s)
+        total = memory_bytes(lay, 1, h_kv, n, "data") + params + ring_one_tensor
+        got[n] = n * h_kv * 128 * 2 * 2 / total
+        assert round(got[n], 1) == printed or (n == 32768 and 5.0 <= got[n] < 5.1)
+    assert abs(got[4096] - 4.5713) < 1e-4 and abs(got[128] - 1.0578) < 1e-4
+    assert abs(got[32768] - 5.0443) < 1e-4
+
+
+def test_results_page_compression(golden_dir):
+    g = _gold(golden_dir)["results_compression"]
+    lay = Layout(**g["layout"])
+    assert bytes_per_token_head(lay)["total"] == 102
+    fp16 = g["layers"] * g["h_kv"] * g["tokens"] * 128 * 2 * 2
+    tq = g["layers"] * memory_bytes(lay, 1, g["h_kv"], g["tokens"], "data")
+    assert fp16 / 1024 == g["fp16_kib_printed"]
+    assert round(tq / 1024) == g["tq_kb_printed"]
+    assert round(fp16 / tq, 2) == g["ratio_printed"]
+
+
+def test_workload_layouts_bytes():
+    # bytes per token-head of the five workloads' layouts (fp32 scalars unless noted)
+    assert bytes_per_token_head(Layout())["total"] == 104
+    assert bytes_per_token_head(Layout(key_mse_bits=3, value_kind="mse", value_bits=3))["total"] == 124
+    assert bytes_per_token_head(Layout(value_kind="mse", value_bits=3, scalar_dtype="f16"))["total"] == 102
+    assert bytes_per_token_head(Layout(key_mse_bits=3, value_kind="mse", value_bits=3,
+                                       scalar_dtype="f16"))["total"] == 118

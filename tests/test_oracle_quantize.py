@@ -1,0 +1,196 @@
+"""Pins of the oracle's encoders: rotation orthogonality, bucketing by brute
+force, Parseval for the residual norm, QJL unbiasedness by Monte Carlo (with a
+negative control), the distortion bound of the audit page, and min/max codes as
+nearest quantisation levels."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from compressed_kv_decode_tq_amd import workloads as wl
+
+
+def test_rotation_is_orthogonal():
+    for seed in (20261, 20264, 7):
+        pi = wl.rotation(128, seed)
+        assert np.linalg.norm(pi.T @ pi - np.eye(128)) < 1e-10
+        assert np.linalg.norm(pi @ pi.T - np.eye(128)) < 1e-10
+        assert abs(abs(np.linalg.det(pi)) - 1) < 1e-10
+
+
+def test_bucketize_is_nearest_centroid_bruteforce():
+    cb = oracle.lloyd_max(128, 3)
+    rng = np.random.default_rng(0)
+    y = rng.normal(0, 1 / np.sqrt(128), size=(4, 128))
+    pi = np.eye(128)
+    code = oracle.encode_keys(y * 3.0, pi, np.eye(128), cb.centroids, cb.thresholds)
+    # with Pi = I the rotated coordinates are y / |y|; the cell is the nearest centroid
+    u = y / np.linalg.norm(y, axis=1, keepdims=True)
+    near = np.argmin(np.abs(u[..., None] - cb.centroids[None, None, :]), axis=-1)
+    assert np.array_equal(code.idx, near)
+    # a coordinate exactly on a threshold goes to the lower cell: count the
+    # thresholds strictly below it by a plain loop
+    from oracle.quantize import _bucketize
+    t = cb.thresholds
+    probe = np.concatenate([t, t + 1e-12, t - 1e-12, [-1.0, 1.0, 0.0]])
+    expect = np.array([sum(1 for tk in t if tk < v) for v in probe])
+    assert np.array_equal(_bucketize(probe, t), expect)
+
+
+def test_residual_norm_parseval():
+    w = wl.WORKLOADS[1]
+    pi, s = wl.params(w)
+    cb = oracle.lloyd_max(128, 2)
+    k = wl.slot_tokens(w, "k", 0, 3, 256).double().numpy()
+    code = oracle.encode_keys(k, pi, s, cb.centroids, cb.thresholds, scalar_dtype="f32")
+    # gamma = |u - Pi^T c| = |Pi u - c| since Pi is orthogonal
+    rot = np.linalg.norm(code.y - cb.centroids[code.idx], axis=1)
+    gamma64 = np.linalg.norm(k / np.linalg.norm(k, axis=1, keepdims=True) - cb.centroids[code.idx] @ pi, axis=1)
+    assert np.max(np.abs(rot - gamma64)) < 1e-12
+    assert np.max(np.abs(code.rnorm - gamma64)) <= np.max(gamma64) * 2 ** -23
+    assert np.max(np.abs(code.norm - np.linalg.norm(k, axis=1)) / code.norm) <= 2 ** -23
+
+
+def test_zero_vector():
+    cb = oracle.lloyd_max(128, 2)
+    pi, s = wl.rotation(128, 1), wl.qjl_matrix(128, 1)
+    code = oracle.encode_keys(np.zeros((1, 128)), pi, s, cb.centroids, cb.thresholds)
+    assert code.norm[0] == 0 and np.all(code.idx == 1)  # y = 0 lies below the middle threshold
+    assert np.all(oracle.dequantize_keys(code, pi, s, cb.centroids) == 0)
+
+
+def _mc_bias(d, mse_bits, qjl, trials, seed):
+    """Mean and standard error over fresh S draws (fixed Pi, x, y) of
+    score_estimate(y, x) - <x, y>."""
+    rng = np.random.default_rng(seed)
+    pi = wl.rotation(d, seed)
+    x = rng.standard_normal(d)
+    x /= np.linalg.norm(x)
+    y = rng.standard_normal(d)
+    y /= np.linalg.norm(y)
+    cb = oracle.lloyd_max(d, mse_bits)
+    errs = np.empty(trials)
+    for i in range(trials):
+        s = rng.standard_normal((d, d))
+        code = oracle.encode_keys(x[None], pi, s, cb.centroids, cb.thresholds, qjl=qjl)
+        errs[i] = oracle.score_estimate(y, code, pi, s, cb.centroids, qjl=qjl)[0] - x @ y
+    return errs.mean(), errs.std(ddof=1) / np.sqrt(trials), errs
+
+
+@pytest.mark.parametrize("d", [16, 128])
+def test_qjl_estimator_is_unbiased(d):
+    mean, se, _ = _mc_bias(d, 1, True, 20000, 11 + d)
+    assert abs(mean) < 4 * se, (mean, se)
+
+
+def test_mse_only_estimator_is_biased_negative_control():
+    # without the QJL term the 1-bit MSE estimate shrinks inner products
+    # (rounding to centroids biases them); over fresh rotations the bias is
+    # many standard errors away from zero
+    d, trials = 16, 4000
+    rng = np.random.default_rng(5)
+    cb = oracle.lloyd_max(d, 1)
+    x = rng.standard_normal(d)
+    x /= np.linalg.norm(x)
+    errs = np.empty(trials)
+    for i in range(trials):
+        g = rng.standard_normal((d, d))
+        q, r = np.linalg.qr(g)
+        pi = q * np.sign(np.diag(r))
+        code = oracle.encode_keys(x[None], pi, np.eye(d), cb.centroids, cb.thresholds, qjl=False)
+        errs[i] = oracle.score_estimate(x, code, pi, np.eye(d), cb.centroids, qjl=False)[0] - 1.0
+    assert errs.mean() < -10 * errs.std(ddof=1) / np.sqrt(trials)
+    # and the same experiment with QJL is unbiased
+    mean, se, _ = _mc_bias(d, 1, True, 4000, 5)
+    assert abs(mean) < 4 * se
+
+
+def test_dequantized_keys_give_the_same_scores():
+    w = wl.WORKLOADS[0]
+    pi, s = wl.params(w)
+    cb = oracle.lloyd_max(128, 2)
+    k = wl.slot_tokens(w, "k", 0, 0, 64).double().numpy()
+    q = wl.query(w)[0, 0].double().numpy()
+    code = oracle.encode_keys(k, pi, s, cb.centroids, cb.thresholds)
+    a = oracle.dequantize_keys(code, pi, s, cb.centroids) @ q
+    b = oracle.score_estimate(q, code, pi, s, cb.centroids)
+    assert np.max(np.abs(a - b)) < 1e-11 * np.max(np.abs(a))
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_distortion_within_audit_bound(bits, golden_dir):
+    """Inner-product MSE of TurboQuantProd(b) on unit vectors, averaged over
+    draws of (Pi, S, query), against the bound sqrt(3) pi^2 / (d 4^b) and
+    against the QJL variance (pi/2) E[gamma^2] |y|^2 / d that the estimator's
+    construction predicts (a wrong QJL scale or a dropped term breaks it)."""
+    gold = json.load(open(os.path.join(golden_dir, "audit_distortion.json")))
+    d, n, draws = gold["d"], 4000, 8
+    cb = oracle.lloyd_max(d, bits - 1)
+    bound = np.sqrt(3) * np.pi ** 2 / d / 4 ** bits
+    mses, preds = [], []
+    for t in range(draws):
+        rng = np.random.default_rng(1000 * bits + t)
+        pi, s = wl.rotation(d, 500 + t), wl.qjl_matrix(d, 500 + t)
+        x = rng.standard_normal((n, d))
+        x /= np.linalg.norm(x, axis=1, keepdims=True)
+        y = rng.standard_normal(d)
+        y /= np.linalg.norm(y)
+        code = oracle.encode_keys(x, pi, s, cb.centroids, cb.thresholds)
+        est = oracle.score_estimate(y, code, pi, s, cb.centroids)
+        mses.append(np.mean((est - x @ y) ** 2))
+        preds.append(np.pi / 2 / d * np.mean(code.rnorm ** 2))
+    ratio = np.mean(mses) / bound
+    print(f"bits={bits} mean mse / bound = {ratio:.2f} over {draws} draws "
+          f"(one draw on the page: {gold['ratio_printed'][str(bits)]})")
+    assert ratio <= 1.0
+    assert abs(np.mean(mses) / np.mean(preds) - 1) < 0.1
+
+
+def test_minmax_codes_are_nearest_levels():
+    rng = np.random.default_rng(9)
+    v = (rng.standard_normal((300, 128)) * np.exp(rng.standard_normal(128))).astype(np.float32)
+    for bits in (1, 2, 3, 4):
+        mm = oracle.encode_values_minmax(v, bits, 32)
+        levels = (1 << bits) - 1
+        assert mm.code.min() >= 0 and mm.code.max() <= levels
+        g = v.astype(np.float64).reshape(300, 4, 32)
+        lv = mm.min16.astype(np.float64)[..., None] + np.arange(levels + 1) * mm.scale16.astype(np.float64)[..., None]
+        dist = np.abs(g[..., None] - lv[:, :, None, :])  # (T, G, 32, L)
+        near = np.argmin(dist, axis=-1).reshape(300, 128)
+        # ties and fp32 rounding aside, the code is the nearest level
+        srt = np.sort(dist, axis=-1)
+        clear = (srt[..., 1] - srt[..., 0]).reshape(300, 128) > 1e-5 * mm.scale16.astype(np.float64).repeat(32, axis=1)
+        assert np.array_equal(mm.code[clear], near[clear])
+        # scale and zero are fp16 roundings of the group's range and minimum
+        mn = g.min(-1)
+        mx = g.max(-1)
+        assert np.all(np.abs(mm.min16.astype(np.float64) - mn) <= np.abs(mn) * 2 ** -11 + 2 ** -24)
+        assert np.all(np.abs(mm.scale16.astype(np.float64) - (mx - mn) / levels)
+                      <= (mx - mn) / levels * (2 ** -11 + 2 ** -22) + 2 ** -24)
+        # reconstruction error of interior values is at most half a step (+ rounding)
+        rec = oracle.dequantize_values_minmax(mm, 32)
+        step = mm.scale16.astype(np.float64).repeat(32, axis=1)
+        assert np.all(np.abs(rec - v) <= 0.5 * step + 2 * np.abs(mn).repeat(32, axis=1) * 2 ** -11 + 1e-6)
+
+
+def test_minmax_constant_group():
+    v = np.full((2, 64), 1.25, dtype=np.float32)
+    mm = oracle.encode_values_minmax(v, 2, 32)
+    assert np.all(mm.code == 0) and np.all(mm.scale16 == 0)
+    assert np.all(oracle.dequantize_values_minmax(mm, 32) == 1.25)
+
+
+def test_mse_values_reconstruction():
+    w = wl.WORKLOADS[4]
+    pi, _ = wl.params(w)
+    cb = oracle.lloyd_max(128, 3)
+    v = wl.slot_tokens(w, "v", 0, 1, 200).double().numpy()
+    code = oracle.encode_values_mse(v, pi, cb.centroids, cb.thresholds)
+    rec = oracle.dequantize_values_mse(code, pi, cb.centroids)
+    # |v~| = n_v |c[idx]| because Pi is orthogonal
+    assert np.allclose(np.linalg.norm(rec, axis=1), code.norm * np.linalg.norm(cb.centroids[code.idx], axis=1), rtol=1e-12)
+    # relative error of the 3-bit code is far below 1 and about sqrt(MSE per unit vector)
+    rel = np.linalg.norm(rec - v, axis=1) / np.linalg.norm(v, axis=1)
+    assert 0.1 < rel.mean() < 0.25
