@@ -1,0 +1,508 @@
+// Encode kernels for gfx950: the rotation y = Pi u and the QJL projection of
+// the residual run as bf16-split MFMA GEMMs (the only dense contractions of the
+// method), the Lloyd-Max bucketing, residual and sign sketch run in registers,
+// and the codes are written as bit planes.
+//
+// Method (page "TurboQuant — Random rotation trước khi quantize, 3-bit KV cache
+// không mất accuracy", section "Ý tưởng cốt lõi"; TurboQuantProd of page
+// "turboquant/audit_claims.py", AUDIT 3):
+//   n = |k|, y = Pi k / n, idx_i = #{t : t < y_i}, r = y - c[idx] (the residual
+//   in rotated space; |r| equals the residual norm in the original space),
+//   sigma = sign(S r_orig) = sign(S Pi^T r).
+//
+// Precision: bf16 inputs are exact in bf16, so Pi k = Pi_hi k + Pi_lo k needs
+// two MFMA passes (Pi split into bf16 hi + lo, error ~2^-17 |Pi|); fp32 inputs
+// add a third pass with k split into hi + lo.  The residual is fp32, so the QJL
+// GEMM uses three passes (S' hi/lo x r hi/lo, dropping lo x lo).  fp32
+// accumulation throughout.
+#include "tq_common.h"
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+constexpr int kLdsStride = kD + 8;  // bf16 elements per LDS row (16 B pad: no bank conflicts)
+constexpr int kEncThreads = 256;    // 4 waves; each wave encodes one 32-token tile at a time
+
+// Derive the bf16 operands from Pi and S (fp32, row-major [128][128]).
+__global__ void prepare_params_kernel(const float* __restrict__ pi, const float* __restrict__ s,
+                                      uint16_t* __restrict__ out) {
+  const int i = blockIdx.x;   // row
+  const int k = threadIdx.x;  // column (contraction index for S')
+  // Pi split
+  const float p = pi[i * kD + k];
+  const uint32_t hi = f2bf(p);
+  const uint32_t lo = f2bf(p - bf2f(hi));
+  out[kOffPiHi / 2 + i * kD + k] = (uint16_t)hi;
+  out[kOffPiLo / 2 + i * kD + k] = (uint16_t)lo;
+  // S' = S Pi^T in double, at the permuted column
+  const int j = sp_column(k);
+  double acc = 0.0;
+  for (int m = 0; m < kD; ++m) acc += (double)s[i * kD + m] * (double)pi[j * kD + m];
+  const float x = (float)acc;
+  const uint32_t shi = f2bf(x);
+  const uint32_t slo = f2bf((float)(acc - (double)bf2f(shi)));
+  out[kOffSpHi / 2 + i * kD + k] = (uint16_t)shi;
+  out[kOffSpLo / 2 + i * kD + k] = (uint16_t)slo;
+}
+
+// Map a tile index to (sequence, head, 32-token destination block).
+__device__ __forceinline__ void tile_coords(const EncodeArgs& a, int tile, int& b, int& h,
+                                            int64_t& blk) {
+  b = 0;
+  while (b + 1 < a.batch && tile >= a.tile_start.v[b + 1]) ++b;
+  const int64_t pos = a.pos.v[b];
+  const int64_t blk0 = pos >> 5;
+  const int64_t nblk = ((pos + a.n_new + 31) >> 5) - blk0;
+  const int64_t r = tile - a.tile_start.v[b];
+  h = (int)(r / nblk);
+  blk = blk0 + r % nblk;
+}
+
+// Valid-token mask of a 32-token destination block (bit t: position 32*blk+t
+// receives a new token in this call).
+__device__ __forceinline__ uint32_t block_mask(int64_t blk, int64_t pos, int64_t n_new) {
+  const int64_t lo = pos - blk * 32, hi = pos + n_new - blk * 32;  // [lo, hi) in block coordinates
+  const int64_t a = lo < 0 ? 0 : lo, e = hi > 32 ? 32 : hi;
+  if (e <= a) return 0u;
+  const uint32_t upto = e >= 32 ? 0xffffffffu : ((1u << e) - 1u);
+  return upto & ~((1u << a) - 1u);
+}
+
+// Store one word of a value bit plane; words of partly covered blocks keep the
+// bits of tokens this call does not write.
+__device__ __forceinline__ void store_plane_word(uint32_t* p, uint32_t w, uint32_t vmask) {
+  if (vmask == 0xffffffffu)
+    *p = w;
+  else
+    *p = (*p & ~vmask) | (w & vmask);
+}
+
+// Rotation-based encode of one 32-token tile per wave.
+//   VALUE = false: TurboQuantProd keys (MSE_BITS-bit Lloyd-Max + QJL if QJL),
+//                  token-major key planes, |k| and |r|.
+//   VALUE = true : TurboQuant-MSE values, token-transposed value planes, |v|.
+template <bool IN_BF16, int MSE_BITS, bool QJL, bool VALUE>
+__global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
+  constexpr int NMAT = QJL ? 4 : 2;
+  constexpr int NP = MSE_BITS + (QJL ? 1 : 0);  // bit planes written per token
+  constexpr int LV = 1 << MSE_BITS;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[NMAT][kD][kLdsStride];
+
+  // Stage Pi_hi, Pi_lo (and S'_hi, S'_lo) once per work-group.
+  for (int idx = threadIdx.x; idx < NMAT * kD * (kD / 8); idx += blockDim.x) {
+    const int m = idx / (kD * kD / 8), rem = idx % (kD * kD / 8);
+    const int row = rem / (kD / 8), c8 = rem % (kD / 8);
+    *reinterpret_cast<u32x4*>(&lds[m][row][c8 * 8]) =
+        *reinterpret_cast<const u32x4*>(a.derived + (size_t)m * kD * kD + row * kD + c8 * 8);
+  }
+  __syncthreads();
+
+  const float* cent = VALUE ? a.v_cent : a.k_cent;
+  const float* thr = VALUE ? a.v_thr : a.k_thr;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+  const int tc = lane & 15;  // token inside a 16-token column tile
+  const int g = lane >> 4;   // lane group: coordinates 8g..8g+7 of each k-step
+  const void* src = VALUE ? a.v : a.k;
+
+  for (int tile = blockIdx.x * nwaves + wave; tile < a.num_tiles; tile += gridDim.x * nwaves) {
+    int b, h;
+    int64_t blk;
+    tile_coords(a, tile, b, h, blk);
+    const int64_t pos = a.pos.v[b];
+    const int64_t slot = (int64_t)b * a.h_kv + h;
+
+    // ---- load the tile: two 16-token column tiles, 32 coordinates per lane
+    u32x4 kin[2][4], klo[2][4];
+    float ss[2];
+    bool valid[2];
+    int64_t dpos[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      dpos[ct] = blk * 32 + 16 * ct + tc;
+      const int64_t t = dpos[ct] - pos;
+      valid[ct] = t >= 0 && t < a.n_new;
+      ss[ct] = 0.f;
+      const int64_t row = ((int64_t)b * a.n_new + (valid[ct] ? t : 0)) * a.h_kv + h;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int c0 = 32 * ks + 8 * g;
+        if (IN_BF16) {
+          u32x4 x = valid[ct] ? *reinterpret_cast<const u32x4*>(
+                                    reinterpret_cast<const uint16_t*>(src) + row * kD + c0)
+                              : u32x4{0u, 0u, 0u, 0u};
+          kin[ct][ks] = x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float lo = bf2f(x[e] & 0xffffu), hi = bf2f(x[e] >> 16);
+            ss[ct] += lo * lo + hi * hi;
+          }
+        } else {
+          const float* fp = reinterpret_cast<const float*>(src) + row * kD + c0;
+          float f[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) f[e] = valid[ct] ? fp[e] : 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t h0 = f2bf(f[2 * e]), h1 = f2bf(f[2 * e + 1]);
+            const uint32_t l0 = f2bf(f[2 * e] - bf2f(h0)), l1 = f2bf(f[2 * e + 1] - bf2f(h1));
+            kin[ct][ks][e] = h0 | (h1 << 16);
+            klo[ct][ks][e] = l0 | (l1 << 16);
+            ss[ct] += f[2 * e] * f[2 * e] + f[2 * e + 1] * f[2 * e + 1];
+          }
+        }
+      }
+    }
+    float nrm[2], inv[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      float s2 = ss[ct];
+      s2 += __shfl_xor(s2, 16);
+      s2 += __shfl_xor(s2, 32);
+      nrm[ct] = sqrtf(s2);
+      inv[ct] = nrm[ct] > 0.f ? 1.0f / nrm[ct] : 0.f;
+    }
+
+    // ---- GEMM 1: Y = Pi K^T (row tile rt = coordinates 16rt..16rt+15); bucketing
+    uint32_t words[NP][2][4];  // [plane][ct][m]: bits of coordinates 32m..32m+31
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) words[p][ct][m] = 0u;
+    u32x4 rhi[2][4], rlo[2][4];
+    float gg[2] = {0.f, 0.f};
+    uint32_t vw[VALUE ? NP : 1][2];  // value planes: words of channels lane and lane+64
+#pragma unroll
+    for (int p = 0; p < (VALUE ? NP : 1); ++p) vw[p][0] = vw[p][1] = 0u;
+
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt) {
+      // keep the scheduler from hoisting every row tile's LDS operands at once
+      __builtin_amdgcn_sched_barrier(0);
+      floatx4 acc[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x4 ahi = *reinterpret_cast<const u32x4*>(&lds[0][16 * rt + tc][32 * ks + 8 * g]);
+        const u32x4 alo = *reinterpret_cast<const u32x4*>(&lds[1][16 * rt + tc][32 * ks + 8 * g]);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          acc[ct] = mfma_bf16(ahi, kin[ct][ks], acc[ct]);
+          acc[ct] = mfma_bf16(alo, kin[ct][ks], acc[ct]);
+          if (!IN_BF16) acc[ct] = mfma_bf16(ahi, klo[ct][ks], acc[ct]);
+        }
+      }
+      int idxs[2][4];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const float y = acc[ct][rr] * inv[ct];
+          int idx = 0;
+          float c = cent[0];
+#pragma unroll
+          for (int k = 0; k < LV - 1; ++k) {
+            const bool gt = y > thr[k];
+            idx += gt ? 1 : 0;
+            c = gt ? cent[k + 1] : c;
+          }
+          idxs[ct][rr] = idx;
+          const int bit = (rt & 1) * 16 + 4 * g + rr;
+          if (!VALUE) {
+#pragma unroll
+            for (int p = 0; p < MSE_BITS; ++p) words[p][ct][rt >> 1] |= (uint32_t)((idx >> p) & 1) << bit;
+          }
+          if (QJL) {
+            const float res = y - c;
+            gg[ct] += res * res;
+            const uint32_t rh = f2bf(res), rl = f2bf(res - bf2f(rh));
+            const int e = (rt & 1) * 4 + rr;  // element of the k-step rt/2 B operand
+            const int sh = (e & 1) * 16;
+            if ((e & 1) == 0) {
+              rhi[ct][rt >> 1][e >> 1] = rh;
+              rlo[ct][rt >> 1][e >> 1] = rl;
+            } else {
+              rhi[ct][rt >> 1][e >> 1] |= rh << sh;
+              rlo[ct][rt >> 1][e >> 1] |= rl << sh;
+            }
+          }
+        }
+      }
+      if (VALUE) {
+        // token-transposed planes: one ballot gives, in bits 16g'..16g'+15, the
+        // bit of channel 16rt + 4g' + rr for the 16 tokens of a column tile
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+#pragma unroll
+          for (int p = 0; p < NP; ++p) {
+            const uint64_t m0 = __ballot((idxs[0][rr] >> p) & 1);
+            const uint64_t m1 = __ballot((idxs[1][rr] >> p) & 1);
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const int ch = 16 * rt + 4 * gq + rr;
+              const uint32_t w = (uint32_t)((m0 >> (16 * gq)) & 0xffffu) |
+                                 ((uint32_t)((m1 >> (16 * gq)) & 0xffffu) << 16);
+              if (lane == (ch & 63)) vw[p][ch >> 6] = w;
+            }
+          }
+        }
+      }
+    }
+
+    if (VALUE) {
+      const uint32_t vmask = block_mask(blk, pos, a.n_new);
+      const int64_t nblk_cap = a.capacity >> 5;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        uint32_t* base = a.v_planes + ((slot * nblk_cap + blk) * NP + p) * kD;
+        store_plane_word(base + lane, vw[p][0], vmask);
+        store_plane_word(base + 64 + lane, vw[p][1], vmask);
+      }
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+        if (valid[ct] && g == 0) store_scalar(a.v_norm, slot * a.capacity + dpos[ct], nrm[ct], a.scalar_f16);
+      continue;
+    }
+
+    float gam[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      float s2 = gg[ct];
+      s2 += __shfl_xor(s2, 16);
+      s2 += __shfl_xor(s2, 32);
+      gam[ct] = sqrtf(s2);
+    }
+
+    // ---- GEMM 2: Z = S' R (QJL projection of the rotated residual), signs
+    if (QJL) {
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt) {
+        __builtin_amdgcn_sched_barrier(0);
+        floatx4 z[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const u32x4 ahi = *reinterpret_cast<const u32x4*>(&lds[2 % NMAT][16 * rt + tc][32 * ks + 8 * g]);
+          const u32x4 alo = *reinterpret_cast<const u32x4*>(&lds[3 % NMAT][16 * rt + tc][32 * ks + 8 * g]);
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) {
+            z[ct] = mfma_bf16(ahi, rhi[ct][ks], z[ct]);
+            z[ct] = mfma_bf16(alo, rhi[ct][ks], z[ct]);
+            z[ct] = mfma_bf16(ahi, rlo[ct][ks], z[ct]);
+          }
+        }
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            words[NP - 1][ct][rt >> 1] |= (z[ct][rr] >= 0.f ? 1u : 0u) << ((rt & 1) * 16 + 4 * g + rr);
+      }
+    }
+
+    // ---- gather plane words: lane group g ends with the word of coordinates 32g..32g+31
+    const size_t rec = (size_t)NP * (kD / 8);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const uint32_t* w = words[p][ct];
+        uint32_t ka = (g & 2) ? w[2] : w[0], kb = (g & 2) ? w[3] : w[1];
+        const uint32_t sa = (g & 2) ? w[0] : w[2], sb = (g & 2) ? w[1] : w[3];
+        ka |= __shfl_xor(sa, 32);
+        kb |= __shfl_xor(sb, 32);
+        const uint32_t send = (g & 1) ? ka : kb;
+        const uint32_t keep = (g & 1) ? kb : ka;
+        const uint32_t fin = keep | __shfl_xor(send, 16);
+        if (valid[ct])
+          *reinterpret_cast<uint32_t*>(a.k_planes + (slot * a.capacity + dpos[ct]) * rec + p * (kD / 8) + 4 * g) = fin;
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      if (valid[ct] && g == 0) {
+        store_scalar(a.k_norm, slot * a.capacity + dpos[ct], nrm[ct], a.scalar_f16);
+        if (QJL) store_scalar(a.k_rnorm, slot * a.capacity + dpos[ct], gam[ct], a.scalar_f16);
+      }
+    }
+  }
+}
+
+// Asymmetric min/max value code, one 32-token tile per wave: lane = (token,
+// half of the channels).  IEEE fp32 arithmetic in a fixed order so the codes
+// are reproducible bit for bit:
+//   delta = fp16(fp32(max - min) / (2^b - 1)), zero = fp16(min)
+//   code  = clamp(rint(fp32(v - zero) * fp32(1 / delta)), 0, 2^b - 1), 0 if delta == 0
+template <bool IN_BF16, int BITS, int GS>
+__global__ __launch_bounds__(256) void encode_minmax_kernel(EncodeArgs a) {
+  constexpr int L = (1 << BITS) - 1;
+  constexpr int NG = 64 / GS;  // groups per lane
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+  const int tok = lane & 31, half = lane >> 5;
+  for (int tile = blockIdx.x * nwaves + wave; tile < a.num_tiles; tile += gridDim.x * nwaves) {
+    int b, h;
+    int64_t blk;
+    tile_coords(a, tile, b, h, blk);
+    const int64_t pos = a.pos.v[b];
+    const int64_t slot = (int64_t)b * a.h_kv + h;
+    const int64_t dp = blk * 32 + tok;
+    const int64_t t = dp - pos;
+    const bool valid = t >= 0 && t < a.n_new;
+    const int64_t row = ((int64_t)b * a.n_new + (valid ? t : 0)) * a.h_kv + h;
+    float x[64];
+    if (IN_BF16) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.v) + row * kD + 64 * half);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const u32x4 w = valid ? p[i] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[8 * i + 2 * e] = bf2f(w[e] & 0xffffu);
+          x[8 * i + 2 * e + 1] = bf2f(w[e] >> 16);
+        }
+      }
+    } else {
+      const floatx4* p = reinterpret_cast<const floatx4*>(reinterpret_cast<const float*>(a.v) + row * kD + 64 * half);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const floatx4 w = valid ? p[i] : floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * i + e] = w[e];
+      }
+    }
+    uint32_t code[64];
+    const int ngroups_row = kD / GS;
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      float mn = x[gi * GS], mx = x[gi * GS];
+#pragma unroll
+      for (int e = 1; e < GS; ++e) {
+        mn = fminf(mn, x[gi * GS + e]);
+        mx = fmaxf(mx, x[gi * GS + e]);
+      }
+      const __half d16 = __float2half_rn(__fdiv_rn(__fsub_rn(mx, mn), (float)L));
+      const __half z16 = __float2half_rn(mn);
+      const float d32 = __half2float(d16), z32 = __half2float(z16);
+      const float invd = d32 != 0.f ? __fdiv_rn(1.0f, d32) : 0.f;
+#pragma unroll
+      for (int e = 0; e < GS; ++e) {
+        float r = rintf(__fmul_rn(__fsub_rn(x[gi * GS + e], z32), invd));
+        r = fminf(fmaxf(r, 0.f), (float)L);
+        code[gi * GS + e] = d32 != 0.f ? (uint32_t)r : 0u;
+      }
+      if (valid) {
+        const int grp = half * NG + gi;
+        uint16_t* m = a.v_meta + ((slot * a.capacity + dp) * ngroups_row + grp) * 2;
+        const uint32_t packed = (uint32_t)__half_as_ushort(d16) | ((uint32_t)__half_as_ushort(z16) << 16);
+        *reinterpret_cast<uint32_t*>(m) = packed;
+      }
+    }
+    // token-transposed planes: ballot over the wave gives tokens 0..31 of
+    // channel e (low half) and of channel 64 + e (high half)
+    uint32_t w[BITS][2];
+#pragma unroll
+    for (int p = 0; p < BITS; ++p) w[p][0] = w[p][1] = 0u;
+#pragma unroll
+    for (int e = 0; e < 64; ++e) {
+#pragma unroll
+      for (int p = 0; p < BITS; ++p) {
+        const uint64_t m = __ballot((code[e] >> p) & 1u);
+        if (lane == e) {
+          w[p][0] = (uint32_t)m;
+          w[p][1] = (uint32_t)(m >> 32);
+        }
+      }
+    }
+    const uint32_t vmask = block_mask(blk, pos, a.n_new);
+    const int64_t nblk_cap = a.capacity >> 5;
+#pragma unroll
+    for (int p = 0; p < BITS; ++p) {
+      uint32_t* base = a.v_planes + ((slot * nblk_cap + blk) * BITS + p) * kD;
+      store_plane_word(base + lane, w[p][0], vmask);
+      store_plane_word(base + 64 + lane, w[p][1], vmask);
+    }
+  }
+}
+
+int encode_grid(int tiles, int waves_per_block) {
+  const int want = (tiles + waves_per_block - 1) / waves_per_block;
+  return want < 1 ? 1 : want;
+}
+
+template <bool BF16, int MB, bool QJL, bool VALUE>
+hipError_t launch_rot(const EncodeArgs& a, hipStream_t st) {
+  int grid = encode_grid(a.num_tiles, kEncThreads / 64);
+  const int cus = device_cu_count();
+  if (grid > cus) grid = cus;  // persistent: the LDS staging is paid once per work-group
+  hipLaunchKernelGGL((encode_rot_kernel<BF16, MB, QJL, VALUE>), dim3(grid), dim3(kEncThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+template <bool BF16, bool QJL, bool VALUE>
+hipError_t dispatch_rot_bits(const EncodeArgs& a, int bits, hipStream_t st) {
+  switch (bits) {
+    case 1: return launch_rot<BF16, 1, QJL, VALUE>(a, st);
+    case 2: return launch_rot<BF16, 2, QJL, VALUE>(a, st);
+    case 3: return launch_rot<BF16, 3, QJL, VALUE>(a, st);
+    case 4: return launch_rot<BF16, 4, QJL, VALUE>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <bool BF16, int BITS>
+hipError_t launch_mm(const EncodeArgs& a, hipStream_t st) {
+  const int grid = encode_grid(a.num_tiles, 4);
+  switch (a.value_group) {
+    case 16: hipLaunchKernelGGL((encode_minmax_kernel<BF16, BITS, 16>), dim3(grid), dim3(256), 0, st, a); break;
+    case 32: hipLaunchKernelGGL((encode_minmax_kernel<BF16, BITS, 32>), dim3(grid), dim3(256), 0, st, a); break;
+    case 64: hipLaunchKernelGGL((encode_minmax_kernel<BF16, BITS, 64>), dim3(grid), dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <bool BF16>
+hipError_t dispatch_mm(const EncodeArgs& a, int bits, hipStream_t st) {
+  switch (bits) {
+    case 1: return launch_mm<BF16, 1>(a, st);
+    case 2: return launch_mm<BF16, 2>(a, st);
+    case 3: return launch_mm<BF16, 3>(a, st);
+    case 4: return launch_mm<BF16, 4>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_prepare_params(const float* pi, const float* s, uint16_t* derived,
+                                 hipStream_t stream) {
+  hipLaunchKernelGGL(prepare_params_kernel, dim3(kD), dim3(kD), 0, stream, pi, s, derived);
+  return hipGetLastError();
+}
+
+hipError_t launch_encode_keys(const EncodeArgs& a, int in_bf16, int mse_bits, int qjl,
+                              hipStream_t stream) {
+  if (a.num_tiles == 0) return hipSuccess;
+  if (in_bf16)
+    return qjl ? dispatch_rot_bits<true, true, false>(a, mse_bits, stream)
+               : dispatch_rot_bits<true, false, false>(a, mse_bits, stream);
+  return qjl ? dispatch_rot_bits<false, true, false>(a, mse_bits, stream)
+             : dispatch_rot_bits<false, false, false>(a, mse_bits, stream);
+}
+
+hipError_t launch_encode_values_mse(const EncodeArgs& a, int in_bf16, int bits, hipStream_t stream) {
+  if (a.num_tiles == 0) return hipSuccess;
+  return in_bf16 ? dispatch_rot_bits<true, false, true>(a, bits, stream)
+                 : dispatch_rot_bits<false, false, true>(a, bits, stream);
+}
+
+hipError_t launch_encode_values_minmax(const EncodeArgs& a, int in_bf16, int bits,
+                                       hipStream_t stream) {
+  if (a.num_tiles == 0) return hipSuccess;
+  return in_bf16 ? dispatch_mm<true>(a, bits, stream) : dispatch_mm<false>(a, bits, stream);
+}
+
+}  // namespace tq

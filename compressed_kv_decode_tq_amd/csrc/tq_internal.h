@@ -1,0 +1,120 @@
+// Internal declarations shared by the host entry points and the HIP kernels of
+// libtq.  Nothing here is part of the C ABI (include/tq.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq.h"
+
+namespace tq {
+
+constexpr int kD = 128;            // head dimension every kernel is built for
+constexpr int kMaxSeqPerLaunch = 64; // per-sequence host values travel in kernel arguments
+constexpr int kMaxGroup = 8;       // query heads per KV head handled by one decode work-group
+constexpr int kMaxRing = 128;      // ring tokens attended per sequence
+
+// Byte offsets of the operands tq_prepare_params derives from Pi and S.  Each is
+// a bf16 [128][128] row-major matrix.
+//   pi_hi/pi_lo : Pi = pi_hi + pi_lo + O(2^-17 |Pi|)
+//   sp_hi/sp_lo : S' = S Pi^T with its columns permuted into the order in which
+//                 the encode kernel holds the rotated residual (see sp_column).
+constexpr size_t kOffPiHi = 0;
+constexpr size_t kOffPiLo = kOffPiHi + kD * kD * 2;
+constexpr size_t kOffSpHi = kOffPiLo + kD * kD * 2;
+constexpr size_t kOffSpLo = kOffSpHi + kD * kD * 2;
+constexpr size_t kDerivedBytes = kOffSpLo + kD * kD * 2;
+
+// Column of S' that the encode kernel's second GEMM meets at contraction index
+// k.  The first GEMM leaves, in lane group g of a 16x16x32 MFMA, the rotated
+// coordinates 16*rt + 4*g + r (row tile rt, accumulator r); the kernel feeds
+// them back as the B operand of k-step ks = rt/2 without moving data, so
+// contraction index k = 32*ks + 8*g + e holds coordinate 16*(2*ks + e/4) + 4*g + e%4.
+__host__ __device__ constexpr int sp_column(int k) {
+  return 16 * (2 * (k / 32) + (k % 8) / 4) + 4 * ((k % 32) / 8) + (k % 4);
+}
+
+// Per-sequence values for one launch (at most kMaxSeqPerLaunch sequences).
+struct SeqValues {
+  int64_t v[kMaxSeqPerLaunch];
+};
+
+struct EncodeArgs {
+  const void* k;         // [batch][n_new][h_kv][d]
+  const void* v;
+  uint8_t* k_planes;
+  void* k_norm;
+  void* k_rnorm;
+  uint32_t* v_planes;
+  uint16_t* v_meta;
+  void* v_norm;
+  const uint16_t* derived;  // bf16 matrices at the kOff* offsets (in elements: /2)
+  int64_t n_new;
+  int64_t capacity;
+  int32_t batch;          // sequences in this launch
+  int32_t h_kv;
+  int32_t scalar_f16;     // 1: scalars stored as fp16
+  int32_t value_group;
+  int32_t num_tiles;      // (sequence, head, 32-token block) tiles of this launch
+  int32_t blocks_per_seq_head_max;
+  float k_cent[16];
+  float k_thr[15];
+  float v_cent[16];
+  float v_thr[15];
+  SeqValues pos;          // first destination position per sequence
+  SeqValues tile_start;   // prefix count of tiles per sequence (tile_start.v[batch] = total)
+};
+
+struct DecodeArgs {
+  const void* q;          // [batch][h_q][d]
+  const uint8_t* k_planes;
+  const void* k_norm;
+  const void* k_rnorm;
+  const uint32_t* v_planes;
+  const uint16_t* v_meta;
+  const void* v_norm;
+  const float* pi;        // fp32 [d][d]
+  const float* s;
+  const uint16_t* ring_k; // bf16 [batch][ring_cap][h_kv][d]
+  const uint16_t* ring_v;
+  float* out;             // [batch][h_q][d]
+  float* qprep;           // workspace: [batch][h_q][2][d] fp32 (Pi q, S q)
+  float* partial;         // workspace: [splits][batch][h_q][d + 2] (m, l, acc)
+  int64_t capacity;
+  int32_t batch;
+  int32_t h_q;
+  int32_t h_kv;
+  int32_t group;          // h_q / h_kv
+  int32_t q_bf16;
+  int32_t scalar_f16;
+  int32_t value_group;
+  int32_t ring_cap;
+  int32_t splits;
+  int32_t split_len;      // tokens per split (multiple of 64)
+  float scale;            // softmax scale tau
+  float k_cent[16];
+  float v_cent[16];
+  SeqValues n_comp;
+  SeqValues n_ring;
+};
+
+// Launchers (defined in the .hip files).  Each returns hipSuccess or the
+// launch error.
+hipError_t launch_prepare_params(const float* pi, const float* s, uint16_t* derived,
+                                 hipStream_t stream);
+hipError_t launch_encode_keys(const EncodeArgs& a, int in_bf16, int mse_bits, int qjl,
+                              hipStream_t stream);
+hipError_t launch_encode_values_mse(const EncodeArgs& a, int in_bf16, int bits,
+                                    hipStream_t stream);
+hipError_t launch_encode_values_minmax(const EncodeArgs& a, int in_bf16, int bits,
+                                       hipStream_t stream);
+hipError_t launch_ring_append(const void* k_new, const void* v_new, int in_bf16, int batch,
+                              int h_kv, uint16_t* ring_k, uint16_t* ring_v, int ring_cap,
+                              const SeqValues& n_ring, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int key_mse_bits, int key_qjl, int value_mse,
+                         int value_bits, hipStream_t stream);
+
+// Decode work split used for the workspace size and the launch.
+void decode_split(int64_t max_tokens, int64_t units, int32_t* splits, int32_t* split_len);
+
+}  // namespace tq

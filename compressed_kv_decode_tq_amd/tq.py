@@ -1,0 +1,283 @@
+"""Thin Python binding of libtq (include/tq.h).
+
+Argument marshalling only: every step of encode and decode runs in the HIP
+kernels of libtq.so.  PyTorch provides device memory and the current stream.
+Functions keep the C names without the ``tq_`` prefix.  A missing or unloadable
+libtq.so raises at first use; there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+import numpy as np
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtq.so")
+
+TQ_OK, TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY, TQ_ERR_WORKSPACE, TQ_ERR_HIP = 0, -1, -2, -3, -4, -5
+TQ_F32, TQ_BF16, TQ_F16 = 0, 1, 2
+TQ_V_MINMAX, TQ_V_MSE = 0, 1
+TQ_BYTES_DATA, TQ_BYTES_PARAMS, TQ_BYTES_RING = 0, 1, 2
+MAX_LEVELS = 16
+
+#: Every symbol include/tq.h declares.
+EXPORTS = ("tq_make_codebook", "tq_memory_bytes", "tq_params_derived_bytes", "tq_prepare_params",
+           "tq_encode_kv", "tq_ring_append", "tq_decode_workspace_bytes", "tq_decode_attn",
+           "tq_last_error", "tq_version")
+
+
+class TqError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libtq error {code}: {msg}")
+        self.code = code
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [("head_dim", ctypes.c_int32), ("key_mse_bits", ctypes.c_int32),
+                ("key_qjl", ctypes.c_int32), ("value_kind", ctypes.c_int32),
+                ("value_bits", ctypes.c_int32), ("value_group", ctypes.c_int32),
+                ("scalar_dtype", ctypes.c_int32)]
+
+
+class _Params(ctypes.Structure):
+    _fields_ = [("pi", ctypes.c_void_p), ("s", ctypes.c_void_p), ("derived", ctypes.c_void_p),
+                ("k_centroids", ctypes.c_float * MAX_LEVELS),
+                ("k_thresholds", ctypes.c_float * (MAX_LEVELS - 1)),
+                ("v_centroids", ctypes.c_float * MAX_LEVELS),
+                ("v_thresholds", ctypes.c_float * (MAX_LEVELS - 1))]
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("k_planes", ctypes.c_void_p), ("k_norm", ctypes.c_void_p),
+                ("k_rnorm", ctypes.c_void_p), ("v_planes", ctypes.c_void_p),
+                ("v_meta", ctypes.c_void_p), ("v_norm", ctypes.c_void_p),
+                ("batch", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("capacity", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libtq.so (built in-tree by compressed_kv_decode_tq_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"{_LIB_PATH} is not built; run python -m compressed_kv_decode_tq_amd.build")
+        L = ctypes.CDLL(_LIB_PATH)
+        i32, i64, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+        P = ctypes.POINTER
+        L.tq_make_codebook.argtypes = [i32, i32, P(ctypes.c_float), P(ctypes.c_float)]
+        L.tq_make_codebook.restype = ctypes.c_int
+        L.tq_memory_bytes.argtypes = [P(_Layout), i32, i32, i64, i32, i32]
+        L.tq_memory_bytes.restype = i64
+        L.tq_params_derived_bytes.argtypes = [i32]
+        L.tq_params_derived_bytes.restype = sz
+        L.tq_prepare_params.argtypes = [i32, vp, vp, vp, sz, vp]
+        L.tq_prepare_params.restype = ctypes.c_int
+        L.tq_encode_kv.argtypes = [P(_Layout), P(_Params), vp, vp, i32, i64, P(i64), P(_Cache), vp]
+        L.tq_encode_kv.restype = ctypes.c_int
+        L.tq_ring_append.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, i32, P(i32), vp]
+        L.tq_ring_append.restype = ctypes.c_int
+        L.tq_decode_workspace_bytes.argtypes = [P(_Layout), i32, i32, i32, i64]
+        L.tq_decode_workspace_bytes.restype = sz
+        L.tq_decode_attn.argtypes = [P(_Layout), P(_Params), vp, i32, i32, P(_Cache), P(i64), vp, vp,
+                                     i32, P(i32), ctypes.c_float, vp, vp, sz, vp]
+        L.tq_decode_attn.restype = ctypes.c_int
+        L.tq_last_error.argtypes = []
+        L.tq_last_error.restype = ctypes.c_char_p
+        L.tq_version.argtypes = []
+        L.tq_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != TQ_OK:
+        raise TqError(rc, lib().tq_last_error().decode())
+
+
+@dataclasses.dataclass(frozen=True)
+class Layout:
+    head_dim: int = 128
+    key_mse_bits: int = 2
+    key_qjl: int = 1
+    value_kind: int = TQ_V_MINMAX
+    value_bits: int = 2
+    value_group: int = 32
+    scalar_dtype: int = TQ_F32
+
+    def c(self) -> _Layout:
+        return _Layout(self.head_dim, self.key_mse_bits, self.key_qjl, self.value_kind,
+                       self.value_bits, self.value_group, self.scalar_dtype)
+
+    @property
+    def key_planes(self) -> int:
+        return self.key_mse_bits + self.key_qjl
+
+    @property
+    def scalar_torch_dtype(self) -> torch.dtype:
+        return torch.float32 if self.scalar_dtype == TQ_F32 else torch.float16
+
+
+def make_codebook(d: int, bits: int):
+    """Lloyd-Max centroids (2^bits) and thresholds (2^bits - 1) as float32 arrays."""
+    c = (ctypes.c_float * (1 << bits))()
+    t = (ctypes.c_float * max(1, (1 << bits) - 1))()
+    _check(lib().tq_make_codebook(d, bits, c, t))
+    return np.frombuffer(c, dtype=np.float32).copy(), np.frombuffer(t, dtype=np.float32)[: (1 << bits) - 1].copy()
+
+
+def memory_bytes(layout: Layout, batch: int, num_kv_heads: int, n_tokens: int, ring_cap: int, what: int) -> int:
+    lay = layout.c()
+    r = lib().tq_memory_bytes(ctypes.byref(lay), batch, num_kv_heads, n_tokens, ring_cap, what)
+    if r < 0:
+        _check(int(r))
+    return int(r)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else int(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return TQ_F32
+    if t.dtype == torch.bfloat16:
+        return TQ_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+class Params:
+    """Per-layer parameters on one device: Pi and S (fp32), the operands
+    tq_prepare_params derives from them, and the codebook tables."""
+
+    def __init__(self, layout: Layout, pi, s, device="cuda", stream=None,
+                 k_codebook=None, v_codebook=None):
+        d = layout.head_dim
+        self.layout = layout
+        self.pi = torch.as_tensor(np.asarray(pi, dtype=np.float32)).to(device).contiguous()
+        self.s = torch.as_tensor(np.asarray(s, dtype=np.float32)).to(device).contiguous()
+        nbytes = lib().tq_params_derived_bytes(d)
+        if nbytes == 0:
+            raise TqError(TQ_ERR_UNSUPPORTED, f"head_dim {d} is not built")
+        self.derived = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _check(lib().tq_prepare_params(d, _ptr(self.pi), _ptr(self.s), _ptr(self.derived), nbytes, _stream(stream)))
+        self.k_centroids, self.k_thresholds = k_codebook or make_codebook(d, layout.key_mse_bits)
+        if layout.value_kind == TQ_V_MSE:
+            self.v_centroids, self.v_thresholds = v_codebook or make_codebook(d, layout.value_bits)
+        else:
+            self.v_centroids = self.v_thresholds = np.zeros(0, dtype=np.float32)
+
+    def c(self) -> _Params:
+        p = _Params()
+        p.pi, p.s, p.derived = _ptr(self.pi), _ptr(self.s), _ptr(self.derived)
+        for i, x in enumerate(self.k_centroids):
+            p.k_centroids[i] = float(x)
+        for i, x in enumerate(self.k_thresholds):
+            p.k_thresholds[i] = float(x)
+        for i, x in enumerate(self.v_centroids):
+            p.v_centroids[i] = float(x)
+        for i, x in enumerate(self.v_thresholds):
+            p.v_thresholds[i] = float(x)
+        return p
+
+
+class Cache:
+    """Device tensors of a compressed cache (layout as in include/tq.h)."""
+
+    def __init__(self, layout: Layout, batch: int, num_kv_heads: int, capacity: int, device="cuda"):
+        if capacity % 32:
+            raise ValueError("capacity must be a multiple of 32")
+        d = layout.head_dim
+        self.layout, self.batch, self.num_kv_heads, self.capacity = layout, batch, num_kv_heads, capacity
+        sd = layout.scalar_torch_dtype
+        shp = (batch, num_kv_heads, capacity)
+        self.k_planes = torch.zeros(*shp, layout.key_planes * d // 8, dtype=torch.uint8, device=device)
+        self.k_norm = torch.zeros(shp, dtype=sd, device=device)
+        self.k_rnorm = torch.zeros(shp, dtype=sd, device=device) if layout.key_qjl else None
+        self.v_planes = torch.zeros(batch, num_kv_heads, capacity // 32, layout.value_bits, d,
+                                    dtype=torch.int32, device=device)
+        if layout.value_kind == TQ_V_MINMAX:
+            self.v_meta = torch.zeros(*shp, d // layout.value_group, 2, dtype=torch.float16, device=device)
+            self.v_norm = None
+        else:
+            self.v_meta = None
+            self.v_norm = torch.zeros(shp, dtype=sd, device=device)
+
+    def c(self) -> _Cache:
+        return _Cache(_ptr(self.k_planes), _ptr(self.k_norm), _ptr(self.k_rnorm), _ptr(self.v_planes),
+                      _ptr(self.v_meta), _ptr(self.v_norm), self.batch, self.num_kv_heads, self.capacity)
+
+
+def encode_kv(params: Params, k: torch.Tensor, v: torch.Tensor, dst_pos, cache: Cache, stream=None):
+    """Encode k, v ([B, n_new, H_kv, d], fp32 or bf16, contiguous, on device)
+    into cache positions dst_pos[b] ... dst_pos[b] + n_new - 1."""
+    if k.shape != v.shape or k.dtype != v.dtype or k.dim() != 4:
+        raise ValueError("k and v must be [B, n_new, H_kv, d] with the same dtype")
+    if not (k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("k and v must be contiguous")
+    if k.shape[0] != cache.batch or k.shape[2] != cache.num_kv_heads:
+        raise ValueError("k/v batch or head count does not match the cache")
+    pos = (ctypes.c_int64 * cache.batch)(*[int(x) for x in dst_pos])
+    lay, prm, cc = params.layout.c(), params.c(), cache.c()
+    _check(lib().tq_encode_kv(ctypes.byref(lay), ctypes.byref(prm), _ptr(k), _ptr(v), _dtype_code(k),
+                              k.shape[1], pos, ctypes.byref(cc), _stream(stream)))
+
+
+def ring_append(k_new: torch.Tensor, v_new: torch.Tensor, ring_k: torch.Tensor, ring_v: torch.Tensor,
+                n_ring, stream=None):
+    """Write one token per sequence (k_new, v_new: [B, 1, H_kv, d]) into the
+    bf16 rings ([B, R, H_kv, d]) at positions n_ring[b]."""
+    b, r, h, d = ring_k.shape
+    if ring_k.dtype != torch.bfloat16 or ring_v.dtype != torch.bfloat16:
+        raise ValueError("rings are bf16")
+    if tuple(k_new.shape) != (b, 1, h, d) or not k_new.is_contiguous() or not v_new.is_contiguous():
+        raise ValueError("k_new/v_new must be contiguous [B, 1, H_kv, d]")
+    nr = (ctypes.c_int32 * b)(*[int(x) for x in n_ring])
+    _check(lib().tq_ring_append(_ptr(k_new), _ptr(v_new), _dtype_code(k_new), b, h, d,
+                                _ptr(ring_k), _ptr(ring_v), r, nr, _stream(stream)))
+
+
+def decode_workspace_bytes(layout: Layout, batch: int, num_q_heads: int, num_kv_heads: int, max_tokens: int) -> int:
+    lay = layout.c()
+    return int(lib().tq_decode_workspace_bytes(ctypes.byref(lay), batch, num_q_heads, num_kv_heads, max_tokens))
+
+
+def decode_attn(params: Params, q: torch.Tensor, cache: Cache, n_compressed, ring_k=None, ring_v=None,
+                n_ring=None, scale: float | None = None, out: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """One decode step: q [B, H_q, d] (fp32 or bf16) -> out [B, H_q, d] fp32."""
+    lay_py = params.layout
+    b, h_q, d = q.shape
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(d))
+    if out is None:
+        out = torch.empty((b, h_q, d), dtype=torch.float32, device=q.device)
+    nc = (ctypes.c_int64 * b)(*[int(x) for x in n_compressed])
+    max_tokens = max(int(x) for x in n_compressed)
+    need = decode_workspace_bytes(lay_py, b, h_q, cache.num_kv_heads, max_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ring_cap = 0 if ring_k is None else ring_k.shape[1]
+    nr = (ctypes.c_int32 * b)(*([int(x) for x in n_ring] if n_ring is not None else [0] * b))
+    lay, prm, cc = lay_py.c(), params.c(), cache.c()
+    _check(lib().tq_decode_attn(ctypes.byref(lay), ctypes.byref(prm), _ptr(q), _dtype_code(q), h_q,
+                                ctypes.byref(cc), nc, _ptr(ring_k), _ptr(ring_v), ring_cap, nr,
+                                float(scale), _ptr(out), _ptr(workspace), workspace.numel(),
+                                _stream(stream)))
+    return out
+
+
+def version() -> str:
+    return lib().tq_version().decode()

@@ -1,0 +1,189 @@
+/*
+ * tq.h — C ABI of the TurboQuant compressed-KV library for AMD MI355X (gfx950).
+ *
+ * What the library computes (sources cited by page title and section):
+ *
+ *  - Encoding of attention keys with the product quantizer TurboQuantProd: a
+ *    fixed random orthogonal rotation Pi of the unit key, one Lloyd-Max scalar
+ *    quantizer shared by every rotated coordinate, and a 1-bit QJL sign sketch
+ *    sign(S r) of the residual r together with |r|  (page "TurboQuant — Random
+ *    rotation trước khi quantize, 3-bit KV cache không mất accuracy",
+ *    section "Ý tưởng cốt lõi"; page "turboquant/audit_claims.py", AUDIT 3 and
+ *    AUDIT 5 for the TurboQuantProd(bits) interface).
+ *  - Encoding of values either with the asymmetric min/max group code of the
+ *    compressed store (page "turboquant/audit_claims.py", AUDIT 1:
+ *    value_bits, value_group_size) or with the same rotated Lloyd-Max code.
+ *  - Single-query decode attention that reads only the compressed cache plus a
+ *    bf16 ring of recent tokens: scores from the rotated query against the
+ *    codebook-indexed keys plus the QJL correction, online softmax, values
+ *    decoded on chip (page "03. Results & Benchmarks", sections "Latency
+ *    Benchmarks" and "Next Steps"; rotate the query at run time: page
+ *    "TurboQuant — ...", section "Tại sao nó hoạt động").
+ *  - Byte accounting of the cache (page "turboquant/audit_claims.py", AUDIT 1).
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless the argument name ends in _host.
+ *    Every buffer is owned by the caller; the library never allocates or
+ *    frees device memory and keeps no state between calls.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Device work is
+ *    enqueued on it asynchronously; a device fault surfaces at the caller's
+ *    next synchronisation.
+ *  - Return value: TQ_OK (0) or a negative TQ_ERR_* code.  Every argument is
+ *    checked on the host before anything is launched, so a call that returns
+ *    an error other than TQ_ERR_HIP has written nothing.  tq_last_error()
+ *    describes the most recent failure of the calling thread.
+ *  - Layout of the compressed cache, per (sequence b, KV head h) slot of
+ *    `capacity` token positions (capacity a multiple of 32):
+ *      k_planes  uint8 [batch][h_kv][capacity][(key_mse_bits+key_qjl)*d/8]
+ *                plane p < key_mse_bits holds bit p of each coordinate's
+ *                Lloyd-Max index, plane key_mse_bits the QJL sign bits
+ *                (1 = non-negative); coordinate i is bit i%8 of byte i/8.
+ *      k_norm    [batch][h_kv][capacity] scalar_dtype   |k|
+ *      k_rnorm   [batch][h_kv][capacity] scalar_dtype   |r| (QJL keys only)
+ *      v_planes  uint32 [batch][h_kv][capacity/32][value_bits][d]: bit t of
+ *                word (blk, p, c) is bit p of the code of token 32*blk+t,
+ *                channel c.
+ *      v_meta    fp16 [batch][h_kv][capacity][d/value_group][2] = (scale, min)
+ *                (min/max values only)
+ *      v_norm    [batch][h_kv][capacity] scalar_dtype   |v| (MSE values only)
+ *  - K/V inputs are [batch][n][h_kv][d] row-major; queries [batch][h_q][d];
+ *    the bf16 ring is [batch][ring_cap][h_kv][d] for K and for V.  Query head
+ *    hq reads KV head hq / (h_q / h_kv).
+ */
+#ifndef TQ_H_
+#define TQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  TQ_OK = 0,
+  TQ_ERR_INVALID = -1,     /* bad pointer, size or combination of arguments     */
+  TQ_ERR_UNSUPPORTED = -2, /* valid but not built (e.g. head_dim other than 128) */
+  TQ_ERR_CAPACITY = -3,    /* a write would land beyond the cache capacity      */
+  TQ_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required        */
+  TQ_ERR_HIP = -5          /* a HIP launch or API call failed                   */
+};
+
+enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 };    /* element types               */
+enum { TQ_V_MINMAX = 0, TQ_V_MSE = 1 };          /* value codes                 */
+enum { TQ_BYTES_DATA = 0, TQ_BYTES_PARAMS = 1, TQ_BYTES_RING = 2 };
+
+#define TQ_MAX_LEVELS 16 /* 2^4: largest codebook */
+
+/* Quantizer layout.  Only head_dim = 128 is built. */
+typedef struct tq_layout {
+  int32_t head_dim;     /* d                                                   */
+  int32_t key_mse_bits; /* 1..4: Lloyd-Max bits per key coordinate (b-1 of a
+                           TurboQuantProd(b) key)                              */
+  int32_t key_qjl;      /* 1: one QJL sign bit per coordinate plus |r|; 0: none */
+  int32_t value_kind;   /* TQ_V_MINMAX | TQ_V_MSE                              */
+  int32_t value_bits;   /* 1..4                                                */
+  int32_t value_group;  /* min/max group of consecutive channels; divides d    */
+  int32_t scalar_dtype; /* TQ_F32 | TQ_F16: storage of |k|, |r| and |v|        */
+} tq_layout;
+
+/* Per-layer parameters.  pi, s and derived are device pointers; the codebook
+ * tables are host values copied into each launch. */
+typedef struct tq_params {
+  const float* pi;      /* [d][d] fp32 row-major orthogonal rotation Pi        */
+  const float* s;       /* [d][d] fp32 row-major QJL projection S              */
+  const void* derived;  /* filled by tq_prepare_params from pi and s           */
+  float k_centroids[TQ_MAX_LEVELS];      /* 2^key_mse_bits, ascending          */
+  float k_thresholds[TQ_MAX_LEVELS - 1]; /* 2^key_mse_bits - 1 decision bounds */
+  float v_centroids[TQ_MAX_LEVELS];      /* MSE values: 2^value_bits levels    */
+  float v_thresholds[TQ_MAX_LEVELS - 1];
+} tq_params;
+
+/* Compressed cache: device planes as described above. */
+typedef struct tq_cache {
+  uint8_t* k_planes;
+  void* k_norm;
+  void* k_rnorm;
+  uint32_t* v_planes;
+  uint16_t* v_meta;
+  void* v_norm;
+  int32_t batch;
+  int32_t num_kv_heads;
+  int64_t capacity;
+} tq_cache;
+
+/* Lloyd-Max codebook for one coordinate of a randomly rotated unit vector in
+ * dimension d: the law with density proportional to (1-x^2)^((d-3)/2) on
+ * [-1,1] (page "TurboQuant — ...", section "Ý tưởng cốt lõi": concentrated
+ * Beta law, one MSE-optimal scalar quantizer).  Solved in double precision,
+ * written as fp32: centroids_host[2^bits] ascending and thresholds_host
+ * [2^bits - 1] midpoints.  Host only.  Errors: TQ_ERR_INVALID for d < 3,
+ * bits outside 1..4 or NULL outputs. */
+int tq_make_codebook(int32_t d, int32_t bits, float* centroids_host, float* thresholds_host);
+
+/* Bytes of the cache (page "turboquant/audit_claims.py", AUDIT 1 accounting).
+ * what = TQ_BYTES_DATA: quantized tensors for n_tokens tokens of every
+ * (sequence, KV head); TQ_BYTES_PARAMS: Pi and S in fp32 plus the fp32
+ * codebook tables (centroids, cell edges, decision thresholds); TQ_BYTES_RING:
+ * the bf16 K and V ring of ring_cap tokens.  Returns the count, or a negative
+ * TQ_ERR_* code. */
+int64_t tq_memory_bytes(const tq_layout* layout, int32_t batch, int32_t num_kv_heads,
+                        int64_t n_tokens, int32_t ring_cap, int32_t what);
+
+/* Size of the buffer tq_prepare_params fills for head dimension d. */
+size_t tq_params_derived_bytes(int32_t d);
+
+/* Derive, on the device, the per-layer operands the kernels use from Pi and
+ * S: bf16 hi/lo splits of Pi and of S Pi^T (the QJL projection expressed on
+ * the rotated residual).  Run once per layer.  derived must hold
+ * tq_params_derived_bytes(d) bytes. */
+int tq_prepare_params(int32_t d, const float* pi, const float* s, void* derived,
+                      size_t derived_bytes, void* stream);
+
+/* Encode n_new tokens of every sequence and KV head into the cache at token
+ * positions dst_pos_host[b] .. dst_pos_host[b] + n_new - 1.  k, v:
+ * [batch][n_new][h_kv][d] in in_dtype (TQ_F32 or TQ_BF16).  Writes the key
+ * planes and norms and the value planes and scalars of those positions only;
+ * other positions of a shared 32-token value block are preserved.  Errors:
+ * TQ_ERR_CAPACITY when a position exceeds capacity; TQ_ERR_INVALID on NULL or
+ * inconsistent pointers. */
+int tq_encode_kv(const tq_layout* layout, const tq_params* params, const void* k,
+                 const void* v, int32_t in_dtype, int64_t n_new, const int64_t* dst_pos_host,
+                 const tq_cache* cache, void* stream);
+
+/* Append one token per sequence to the bf16 ring at position n_ring_host[b]
+ * (which must be < ring_cap), rounding to bf16.  k_new, v_new:
+ * [batch][1][h_kv][d] in in_dtype (TQ_F32 or TQ_BF16). */
+int tq_ring_append(const void* k_new, const void* v_new, int32_t in_dtype, int32_t batch,
+                   int32_t num_kv_heads, int32_t head_dim, void* ring_k, void* ring_v,
+                   int32_t ring_cap, const int32_t* n_ring_host, void* stream);
+
+/* Workspace bytes tq_decode_attn needs for these sizes (max_tokens = the
+ * largest compressed length of any sequence). */
+size_t tq_decode_workspace_bytes(const tq_layout* layout, int32_t batch, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int64_t max_tokens);
+
+/* One decode step: for every sequence b and query head hq, attention of
+ * q[b][hq] over the n_compressed_host[b] compressed tokens of KV head
+ * hq / (h_q / h_kv) and the first n_ring_host[b] ring tokens, with scores
+ * softmax_scale * <q, k>.  out: [batch][h_q][d] fp32.  q_dtype: TQ_F32 or
+ * TQ_BF16.  ring_k/ring_v may be NULL when ring_cap is 0.  A sequence with no
+ * token at all gets a zero output.  Errors: TQ_ERR_WORKSPACE when
+ * workspace_bytes is below tq_decode_workspace_bytes. */
+int tq_decode_attn(const tq_layout* layout, const tq_params* params, const void* q,
+                   int32_t q_dtype, int32_t num_q_heads, const tq_cache* cache,
+                   const int64_t* n_compressed_host, const void* ring_k, const void* ring_v,
+                   int32_t ring_cap, const int32_t* n_ring_host, float softmax_scale, float* out,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Text of the most recent error of the calling thread ("" if none). */
+const char* tq_last_error(void);
+
+/* Library version string. */
+const char* tq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H_ */

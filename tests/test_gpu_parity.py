@@ -1,0 +1,289 @@
+"""GPU parity of the HIP path (through the C ABI) against the float64 oracle.
+
+Encode: packed codes bit-exact except where the oracle's rotated coordinate (or
+QJL projection) lies within 1e-5 of a decision boundary, mismatch counts
+printed; min/max value codes and fp16 scale/zero bit-exact; stored norms within
+fp32 rounding (fp16: one ulp).  Decode: both sides read the same oracle-packed
+cache, each attention output vector within 2e-3 max relative error.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from compressed_kv_decode_tq_amd import tq
+from compressed_kv_decode_tq_amd import workloads as wl
+from tq_testlib import (OUT_RTOL, WINDOW, books, dequant_slot, encode_slot, key_plane_mismatches,
+                        layout_of, max_rel_err, read_key_planes, read_value_planes, say, upload_slot)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    tq.lib()
+
+
+SMALL = {
+    "single": wl.WORKLOADS[0],
+    "gqa4": wl.WORKLOADS[1],
+    "qwen_k3_f16": wl.QWEN_VARIANTS[0].replace(n_tokens=2048),
+    "qwen_k3_f32": wl.QWEN_VARIANTS[2].replace(n_tokens=1024),
+    "qwen": wl.by_name("qwen2.5-1.5b-layer-n4096").replace(n_tokens=1536),
+    "batched_small": wl.WORKLOADS[3].replace(batch=3, n_tokens=640, decode_steps=1),
+    "long_small": wl.WORKLOADS[4].replace(n_tokens=1024, decode_steps=1),
+}
+
+
+def _params(w):
+    pi, s = wl.params(w)
+    return pi, s, tq.Params(layout_of(w), pi, s, device=DEV)
+
+
+def _check_encode_slot(w, bk, cache, b, h, ref, start, n, tag):
+    """Compare the device cache slot (b, h) positions start..start+n-1 with the
+    oracle code `ref`; returns excused counts."""
+    lay = layout_of(w)
+    kp = cache.k_planes[b, h, start:start + n].cpu().numpy()
+    bad, ex_m, ex_q = key_plane_mismatches(w, bk, kp, ref.key)
+    assert bad == 0, f"{tag}: {bad} key bits differ outside the {WINDOW} window"
+    flip = np.any(read_key_planes_mask(w, bk, kp, ref), axis=1)
+    f16 = w.scalar_dtype == "f16"
+    kn = cache.k_norm[b, h, start:start + n].float().cpu().double().numpy()
+    if f16:
+        ulp = np.spacing(ref.key.norm.astype(np.float16)).astype(np.float64)
+        assert np.all(np.abs(kn - ref.key.norm) <= ulp * 1.01), tag
+    else:
+        assert np.max(np.abs(kn - ref.key.norm) / np.maximum(ref.key.norm, 1e-30)) <= 1e-6, tag
+    if w.key_qjl:
+        kr = cache.k_rnorm[b, h, start:start + n].float().cpu().double().numpy()
+        ok = ~flip
+        if f16:
+            ulp = np.spacing(ref.key.rnorm.astype(np.float16)).astype(np.float64)
+            assert np.all(np.abs(kr - ref.key.rnorm)[ok] <= ulp[ok] * 1.01), tag
+        else:
+            rel = np.abs(kr - ref.key.rnorm) / np.maximum(ref.key.rnorm, 1e-30)
+            assert np.all(rel[ok] <= 1e-5), (tag, np.max(rel[ok]))
+    # values
+    blk0 = start // 32
+    nblk = (start + n + 31) // 32 - blk0
+    words = cache.v_planes[b, h, blk0:blk0 + nblk].cpu().numpy()
+    codes = read_value_planes(words, nblk * 32)[start - blk0 * 32: start - blk0 * 32 + n]
+    if w.value_kind == "minmax":
+        assert np.array_equal(codes, ref.val.code), f"{tag}: min/max codes differ"
+        meta = cache.v_meta[b, h, start:start + n].cpu().numpy()
+        assert np.array_equal(meta[..., 0].view(np.uint16), ref.val.scale16.view(np.uint16)), tag
+        assert np.array_equal(meta[..., 1].view(np.uint16), ref.val.min16.view(np.uint16)), tag
+        ex_v = 0
+    else:
+        bad_v = codes != ref.val.idx
+        near = np.min(np.abs(ref.val.y[..., None] - bk.v.thresholds[None, None, :]), axis=-1) < WINDOW
+        assert np.sum(bad_v & ~near) == 0, f"{tag}: MSE value codes differ outside the window"
+        ex_v = int(np.sum(bad_v))
+        vn = cache.v_norm[b, h, start:start + n].float().cpu().double().numpy()
+        if f16:
+            ulp = np.spacing(ref.val.norm.astype(np.float16)).astype(np.float64)
+            assert np.all(np.abs(vn - ref.val.norm) <= ulp * 1.01), tag
+        else:
+            assert np.max(np.abs(vn - ref.val.norm) / np.maximum(ref.val.norm, 1e-30)) <= 1e-6, tag
+    return ex_m, ex_q, ex_v
+
+
+def read_key_planes_mask(w, bk, kp, ref):
+    idx_g, _ = read_key_planes(kp, w.d, w.key_mse_bits, bool(w.key_qjl))
+    return idx_g != ref.key.idx
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_encode_parity(name):
+    w = SMALL[name]
+    say(f"[encode parity] {name}: B={w.batch} H_kv={w.h_kv} N={w.n_tokens} {w.in_dtype}")
+    bk = books(w)
+    pi, s, prm = _params(w)
+    k, v = wl.prefill_kv(w)
+    cap = ((w.n_tokens + 31) // 32) * 32
+    cache = tq.Cache(layout_of(w), w.batch, w.h_kv, cap, device=DEV)
+    tq.encode_kv(prm, k.to(DEV), v.to(DEV), [0] * w.batch, cache)
+    torch.cuda.synchronize()
+    tot = np.zeros(3, dtype=np.int64)
+    for b in range(w.batch):
+        for h in range(w.h_kv):
+            ref = encode_slot(w, bk, pi, s, k[b, :, h].double().numpy(), v[b, :, h].double().numpy())
+            tot += _check_encode_slot(w, bk, cache, b, h, ref, 0, w.n_tokens, f"{name} b{b} h{h}")
+    n_coord = w.batch * w.h_kv * w.n_tokens * w.d
+    say(f"  excused flips: key MSE {tot[0]}, key QJL {tot[1]}, value MSE {tot[2]} of {n_coord} coordinates")
+
+
+@pytest.mark.parametrize("value_kind", ["minmax", "mse"])
+def test_encode_ragged_positions_preserve_neighbours(value_kind):
+    base = SMALL["batched_small"] if value_kind == "minmax" else SMALL["long_small"]
+    w = base.replace(batch=3, h_kv=2, h_q=8, n_tokens=77)
+    say(f"[encode ragged] {value_kind}")
+    bk = books(w)
+    pi, s, prm = _params(w)
+    k, v = wl.prefill_kv(w)
+    cap = 256
+    cache = tq.Cache(layout_of(w), w.batch, w.h_kv, cap, device=DEV)
+    g = torch.Generator(device="cpu").manual_seed(5)
+    for t in (cache.k_planes, cache.v_planes):
+        t.copy_(torch.randint(0, 255 if t.dtype == torch.uint8 else 2 ** 31 - 1, t.shape, generator=g, dtype=t.dtype))
+    before = {n: getattr(cache, n).clone() for n in ("k_planes", "v_planes")}
+    pos = [0, 45, 179]
+    tq.encode_kv(prm, k.to(DEV), v.to(DEV), pos, cache)
+    torch.cuda.synchronize()
+    for b in range(3):
+        p0 = pos[b]
+        # key records outside the written range are untouched
+        kp = cache.k_planes[b].cpu()
+        kb = before["k_planes"][b].cpu()
+        mask = torch.ones(cap, dtype=torch.bool)
+        mask[p0:p0 + 77] = False
+        assert torch.equal(kp[:, mask], kb[:, mask])
+        # value bits of untouched tokens in shared blocks are preserved
+        for h in range(w.h_kv):
+            va = read_value_planes(cache.v_planes[b, h].cpu().numpy(), cap)
+            vbh = read_value_planes(before["v_planes"][b, h].cpu().numpy(), cap)
+            assert np.array_equal(va[mask.numpy()], vbh[mask.numpy()])
+            ref = encode_slot(w, bk, pi, s, k[b, :, h].double().numpy(), v[b, :, h].double().numpy())
+            _check_encode_slot(w, bk, cache, b, h, ref, p0, 77, f"ragged b{b} h{h}")
+
+
+def _oracle_cache(w, bk, pi, s, k, v, n_comp):
+    """Oracle codes per slot and their dequantized K/V."""
+    codes, kd, vd = {}, [], []
+    for b in range(w.batch):
+        kr, vr = [], []
+        for h in range(w.h_kv):
+            n = n_comp[b]
+            sc = encode_slot(w, bk, pi, s, k[b, :n, h].double().numpy(), v[b, :n, h].double().numpy())
+            codes[b, h] = sc
+            a, c = dequant_slot(w, bk, pi, s, sc)
+            kr.append(a)
+            vr.append(c)
+        kd.append(kr)
+        vd.append(vr)
+    return codes, kd, vd
+
+
+def _decode_case(w, n_comp, n_ring, tag, steps_kv=None):
+    say(f"[decode parity] {tag}: B={w.batch} H_q={w.h_q} H_kv={w.h_kv} n={n_comp} ring={n_ring}")
+    bk = books(w)
+    pi, s, prm = _params(w)
+    k, v = wl.prefill_kv(w)
+    cap = max(32, ((max(n_comp) + 31) // 32) * 32)
+    codes, kd, vd = _oracle_cache(w, bk, pi, s, k, v, n_comp)
+    cache = tq.Cache(layout_of(w), w.batch, w.h_kv, cap, device=DEV)
+    for (b, h), sc in codes.items():
+        if n_comp[b] > 0:
+            upload_slot(cache, w, b, h, sc)
+    q = wl.query(w)
+    rk = rv = None
+    if max(n_ring) > 0:
+        g = np.random.default_rng(11)
+        rk = torch.from_numpy(g.standard_normal((w.batch, 128, w.h_kv, w.d))).to(torch.bfloat16)
+        rv = torch.from_numpy(g.standard_normal((w.batch, 128, w.h_kv, w.d))).to(torch.bfloat16)
+    out = tq.decode_attn(prm, q.to(DEV), cache, n_comp, None if rk is None else rk.to(DEV),
+                         None if rv is None else rv.to(DEV), n_ring)
+    torch.cuda.synchronize()
+    ref = oracle.decode_attention(q.double().numpy(), kd, vd,
+                                  None if rk is None else rk.double().numpy(),
+                                  None if rv is None else rv.double().numpy(), n_ring)
+    got = out.cpu().double().numpy()
+    err = max_rel_err(got, ref)
+    say(f"  max rel err {err.max():.2e} (bound {OUT_RTOL})")
+    for b in range(w.batch):
+        if n_comp[b] == 0 and n_ring[b] == 0:
+            assert np.all(got[b] == 0)
+    assert err.max() <= OUT_RTOL
+    return got
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_decode_parity(name):
+    w = SMALL[name]
+    nr = [1] * w.batch if w.ring_cap else [0] * w.batch
+    _decode_case(w, [w.n_tokens] * w.batch, nr, name)
+
+
+def test_decode_ragged_lengths_and_ring_sizes():
+    w = SMALL["batched_small"].replace(batch=5, n_tokens=1000)
+    _decode_case(w, [0, 37, 1000, 513, 64], [5, 0, 128, 127, 1], "ragged minmax")
+    w = SMALL["long_small"].replace(batch=3, n_tokens=700)
+    _decode_case(w, [700, 1, 256], [0, 0, 0], "ragged mse")
+
+
+def test_decode_empty_sequence_gives_zero():
+    w = SMALL["batched_small"].replace(batch=2, n_tokens=64)
+    _decode_case(w, [0, 64], [0, 3], "empty")
+
+
+def test_decode_group_sizes():
+    for g, hk in ((1, 4), (2, 2), (3, 2), (5, 1), (8, 1)):
+        w = SMALL["gqa4"].replace(h_kv=hk, h_q=g * hk, n_tokens=300)
+        _decode_case(w, [300], [1], f"G={g}")
+
+
+def test_decode_split_invariance_and_determinism():
+    """The same slot decoded alone (many splits) and among 40 copies (fewer
+    splits) gives the same output to fp32 rounding; repeated calls are bitwise
+    identical."""
+    w = SMALL["batched_small"].replace(batch=1, h_kv=1, h_q=4, n_tokens=4096)
+    bk = books(w)
+    pi, s, prm = _params(w)
+    k, v = wl.prefill_kv(w)
+    codes, _, _ = _oracle_cache(w, bk, pi, s, k, v, [4096])
+    say("[decode split invariance]")
+    outs = []
+    for copies in (1, 40):
+        cache = tq.Cache(layout_of(w), copies, 1, 4096, device=DEV)
+        for b in range(copies):
+            upload_slot(cache, w, b, 0, codes[0, 0])
+        q = wl.query(w).repeat(copies, 1, 1)
+        o1 = tq.decode_attn(prm, q.to(DEV), cache, [4096] * copies)
+        o2 = tq.decode_attn(prm, q.to(DEV), cache, [4096] * copies)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2)
+        outs.append(o1[0].cpu().double().numpy())
+    assert np.max(max_rel_err(outs[0], outs[1])) < 1e-5
+
+
+@pytest.mark.parametrize("name", ["single", "gqa4", "qwen", "batched_small", "long_small"])
+def test_end_to_end(name):
+    """GPU encode + ring append + GPU decode against oracle encode + oracle decode
+    from the same raw inputs (rare boundary-window code flips included)."""
+    w = SMALL[name]
+    say(f"[end to end] {name}")
+    bk = books(w)
+    pi, s, prm = _params(w)
+    k, v = wl.prefill_kv(w)
+    n = w.n_tokens
+    cap = ((n + 31) // 32) * 32
+    cache = tq.Cache(layout_of(w), w.batch, w.h_kv, cap, device=DEV)
+    tq.encode_kv(prm, k.to(DEV), v.to(DEV), [0] * w.batch, cache)
+    q = wl.query(w)
+    n_ring = [0] * w.batch
+    rk = rv = None
+    if w.step_mode == "ring":
+        kn, vn = wl.step_kv(w, 0)
+        rk = torch.zeros((w.batch, w.ring_cap, w.h_kv, w.d), dtype=torch.bfloat16, device=DEV)
+        rv = torch.zeros_like(rk)
+        tq.ring_append(kn.to(DEV).contiguous(), vn.to(DEV).contiguous(), rk, rv, n_ring)
+        n_ring = [1] * w.batch
+    out = tq.decode_attn(prm, q.to(DEV), cache, [n] * w.batch, rk, rv, n_ring)
+    torch.cuda.synchronize()
+    _, kd, vd = _oracle_cache(w, bk, pi, s, k, v, [n] * w.batch)
+    ring_k = ring_v = None
+    if rk is not None:
+        # the ring holds bf16(k_new): the oracle reads the same rounding of the step token
+        ring_k = np.zeros((w.batch, 1, w.h_kv, w.d))
+        ring_v = np.zeros_like(ring_k)
+        ring_k[:, 0] = kn[:, 0].to(torch.bfloat16).double().numpy()
+        ring_v[:, 0] = vn[:, 0].to(torch.bfloat16).double().numpy()
+        assert torch.equal(rk[:, 0].cpu(), kn[:, 0].to(torch.bfloat16))
+    ref = oracle.decode_attention(q.double().numpy(), kd, vd, ring_k, ring_v, n_ring)
+    err = max_rel_err(out.cpu().double().numpy(), ref)
+    say(f"  max rel err {err.max():.2e}")
+    assert err.max() <= OUT_RTOL

@@ -1,0 +1,148 @@
+"""Shared helpers of the GPU parity tests: oracle-side encoding of whole cache
+slots, upload of oracle-packed caches into device tensors, and the comparison
+rules (boundary windows for codes, relative bounds for outputs)."""
+from __future__ import annotations
+
+import dataclasses
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from compressed_kv_decode_tq_amd import tq
+from compressed_kv_decode_tq_amd import workloads as wl
+
+WINDOW = 1e-5          # codes may differ only where the oracle's coordinate is this close to a boundary
+OUT_RTOL = 2e-3        # max relative error of an attention output vector
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def layout_of(w: wl.Workload) -> tq.Layout:
+    return tq.Layout(head_dim=w.d, key_mse_bits=w.key_mse_bits, key_qjl=w.key_qjl,
+                     value_kind=tq.TQ_V_MINMAX if w.value_kind == "minmax" else tq.TQ_V_MSE,
+                     value_bits=w.value_bits, value_group=w.value_group,
+                     scalar_dtype=tq.TQ_F32 if w.scalar_dtype == "f32" else tq.TQ_F16)
+
+
+def olayout_of(w: wl.Workload) -> oracle.Layout:
+    return oracle.Layout(d=w.d, key_mse_bits=w.key_mse_bits, key_qjl=w.key_qjl,
+                         value_kind=w.value_kind, value_bits=w.value_bits,
+                         value_group=w.value_group, scalar_dtype=w.scalar_dtype)
+
+
+@dataclasses.dataclass
+class OracleBooks:
+    k: oracle.Codebook
+    v: oracle.Codebook | None
+
+
+def books(w: wl.Workload) -> OracleBooks:
+    return OracleBooks(oracle.lloyd_max(w.d, w.key_mse_bits),
+                       oracle.lloyd_max(w.d, w.value_bits) if w.value_kind == "mse" else None)
+
+
+@dataclasses.dataclass
+class SlotCode:
+    """Oracle encoding of the tokens of one (sequence, KV head) slot."""
+    key: oracle.KeyCode
+    val: object  # ValueMinMax | ValueMSE
+
+
+def encode_slot(w: wl.Workload, bk: OracleBooks, pi, s, k: np.ndarray, v: np.ndarray) -> SlotCode:
+    key = oracle.encode_keys(k, pi, s, bk.k.centroids, bk.k.thresholds, w.scalar_dtype, qjl=bool(w.key_qjl))
+    if w.value_kind == "minmax":
+        val = oracle.encode_values_minmax(v, w.value_bits, w.value_group)
+    else:
+        val = oracle.encode_values_mse(v, pi, bk.v.centroids, bk.v.thresholds, w.scalar_dtype)
+    return SlotCode(key, val)
+
+
+def dequant_slot(w: wl.Workload, bk: OracleBooks, pi, s, sc: SlotCode):
+    kd = oracle.dequantize_keys(sc.key, pi, s, bk.k.centroids, qjl=bool(w.key_qjl))
+    if w.value_kind == "minmax":
+        vd = oracle.dequantize_values_minmax(sc.val, w.value_group)
+    else:
+        vd = oracle.dequantize_values_mse(sc.val, pi, bk.v.centroids)
+    return kd, vd
+
+
+def _f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().double().numpy()
+
+
+def upload_slot(cache: tq.Cache, w: wl.Workload, b: int, h: int, sc: SlotCode, start: int = 0):
+    """Write the oracle-packed codes of one slot into the device cache at
+    positions start .. start + T - 1 (start a multiple of 32)."""
+    assert start % 32 == 0
+    t = sc.key.idx.shape[0]
+    dev = cache.k_planes.device
+    kp = oracle.pack_key_planes(sc.key.idx, sc.key.qjl if w.key_qjl else None, w.key_mse_bits)
+    cache.k_planes[b, h, start:start + t] = torch.from_numpy(kp).to(dev)
+    sd = np.float32 if w.scalar_dtype == "f32" else np.float16
+    cache.k_norm[b, h, start:start + t] = torch.from_numpy(sc.key.norm.astype(sd)).to(dev)
+    if w.key_qjl:
+        cache.k_rnorm[b, h, start:start + t] = torch.from_numpy(sc.key.rnorm.astype(sd)).to(dev)
+    if w.value_kind == "minmax":
+        codes = sc.val.code
+        meta = np.stack([sc.val.scale16, sc.val.min16], axis=-1)
+        cache.v_meta[b, h, start:start + t] = torch.from_numpy(meta).to(dev)
+    else:
+        codes = sc.val.idx
+        cache.v_norm[b, h, start:start + t] = torch.from_numpy(sc.val.norm.astype(sd)).to(dev)
+    cap = ((t + 31) // 32) * 32
+    words = oracle.pack_value_planes(codes, w.value_bits, cap).view(np.int32)
+    cache.v_planes[b, h, start // 32:start // 32 + cap // 32] = torch.from_numpy(words).to(dev)
+
+
+def max_rel_err(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Per output vector: |got - ref|_inf / |ref|_inf (last axis)."""
+    num = np.max(np.abs(got - ref), axis=-1)
+    den = np.max(np.abs(ref), axis=-1)
+    return np.where(den > 0, num / np.where(den > 0, den, 1), num)
+
+
+def read_key_planes(planes: np.ndarray, d: int, mse_bits: int, qjl: bool):
+    """Read codes back from key plane bytes [T, P * d/8] (bit i%8 of byte i/8 of
+    plane p is bit p of coordinate i's index; the last plane holds QJL bits)."""
+    bits = np.unpackbits(np.ascontiguousarray(planes, dtype=np.uint8), axis=1, bitorder="little")
+    p_k = mse_bits + (1 if qjl else 0)
+    bits = bits[:, : p_k * d].reshape(-1, p_k, d).astype(np.int64)
+    idx = sum(bits[:, p, :] << p for p in range(mse_bits))
+    return idx, (bits[:, mse_bits, :].astype(np.uint8) if qjl else None)
+
+
+def read_value_planes(words: np.ndarray, n_tokens: int) -> np.ndarray:
+    """Codes [n_tokens, d] from token-transposed words [blocks, bits, d]."""
+    w = np.ascontiguousarray(words).view(np.uint32).astype(np.uint64)
+    nblk, bits, d = w.shape
+    t = np.arange(32, dtype=np.uint64)
+    code = np.zeros((nblk, 32, d), dtype=np.int64)
+    for p in range(bits):
+        code |= ((w[:, p, None, :] >> t[None, :, None]) & 1).astype(np.int64) << p
+    return code.reshape(-1, d)[:n_tokens]
+
+
+def key_plane_mismatches(w: wl.Workload, bk: OracleBooks, gpu_planes: np.ndarray, ref: oracle.KeyCode):
+    """Compare GPU key planes with the oracle's code bit by bit.  Returns
+    (unexcused, excused_mse, excused_qjl): a mismatching MSE bit is excused when
+    the oracle's rotated coordinate lies within WINDOW of a decision boundary; a
+    mismatching QJL bit when |z_i| < WINDOW or the token has an excused MSE flip."""
+    t, d = ref.idx.shape
+    idx_g, qjl_g = read_key_planes(gpu_planes, d, w.key_mse_bits, bool(w.key_qjl))
+    mse_bad = idx_g != ref.idx
+    near = np.min(np.abs(ref.y[..., None] - bk.k.thresholds[None, None, :]), axis=-1) < WINDOW
+    unexcused = int(np.sum(mse_bad & ~near))
+    excused_mse = int(np.sum(mse_bad & near))
+    excused_qjl = 0
+    if w.key_qjl:
+        q_bad = qjl_g != ref.qjl
+        tok_flip = np.any(mse_bad & near, axis=1)
+        ok = (np.abs(ref.z) < WINDOW) | tok_flip[:, None]
+        unexcused += int(np.sum(q_bad & ~ok))
+        excused_qjl = int(np.sum(q_bad & ok))
+    return unexcused, excused_mse, excused_qjl
