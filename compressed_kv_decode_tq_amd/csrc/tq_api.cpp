@@ -15,6 +15,13 @@ int make_codebook(int d, int bits, double* cent, double* thr);  // tq_codebook.c
 namespace {
 
 thread_local char g_err[512] = "";
+thread_local tq::TimedLaunch g_timed[3];  // indexed by TQ_KERNEL_*
+
+tq::TimedLaunch take_timed(int kernel) {
+  tq::TimedLaunch t = g_timed[kernel];
+  g_timed[kernel] = tq::TimedLaunch{};
+  return t;
+}
 
 int fail(int code, const char* fmt, ...) {
   va_list ap;
@@ -85,6 +92,14 @@ inline size_t seq_off(int b0, int h_kv, int64_t cap, size_t per_token) {
 extern "C" {
 
 const char* tq_last_error(void) { return g_err; }
+
+int tq_time_next_launch(int32_t kernel, void* ev_begin, void* ev_end) {
+  g_err[0] = 0;
+  if (kernel < 0 || kernel > 2) return fail(TQ_ERR_INVALID, "unknown kernel id %d", kernel);
+  g_timed[kernel].begin = (hipEvent_t)ev_begin;
+  g_timed[kernel].end = (hipEvent_t)ev_end;
+  return TQ_OK;
+}
 
 const char* tq_version(void) { return "tq 0.1 gfx950"; }
 
@@ -197,12 +212,13 @@ int tq_encode_kv(const tq_layout* layout, const tq_params* params, const void* k
     // tile_start has kMaxSeqPerLaunch entries; the kernels stop their search at
     // `batch`, and num_tiles bounds the last sequence.
     a.num_tiles = (int32_t)tiles;
-    hipError_t e = tq::launch_encode_keys(a, bf16, layout->key_mse_bits, layout->key_qjl, st);
+    hipError_t e = tq::launch_encode_keys(a, bf16, layout->key_mse_bits, layout->key_qjl, st,
+                                          take_timed(TQ_KERNEL_ENCODE_KEYS));
     if (e != hipSuccess) return hip_fail(e, "encode keys launch");
     if (layout->value_kind == TQ_V_MSE)
-      e = tq::launch_encode_values_mse(a, bf16, layout->value_bits, st);
+      e = tq::launch_encode_values_mse(a, bf16, layout->value_bits, st, take_timed(TQ_KERNEL_ENCODE_VALUES));
     else
-      e = tq::launch_encode_values_minmax(a, bf16, layout->value_bits, st);
+      e = tq::launch_encode_values_minmax(a, bf16, layout->value_bits, st, take_timed(TQ_KERNEL_ENCODE_VALUES));
     if (e != hipSuccess) return hip_fail(e, "encode values launch");
   }
   return TQ_OK;
@@ -327,7 +343,7 @@ int tq_decode_attn(const tq_layout* layout, const tq_params* params, const void*
     (void)mt;
     hipError_t e = tq::launch_decode(a, layout->key_mse_bits, layout->key_qjl,
                                      layout->value_kind == TQ_V_MSE, layout->value_bits,
-                                     (hipStream_t)stream);
+                                     (hipStream_t)stream, take_timed(TQ_KERNEL_DECODE_SCAN));
     if (e != hipSuccess) return hip_fail(e, "decode launch");
   }
   return TQ_OK;

@@ -384,31 +384,34 @@ __global__ void ring_append_kernel(const void* k_new, const void* v_new, int in_
 }
 
 template <int KB, bool QJL, bool VMSE, int VB>
-hipError_t launch_scan(const DecodeArgs& a, hipStream_t st) {
+hipError_t launch_scan(const DecodeArgs& a, hipStream_t st, TimedLaunch tl) {
+  if (tl.begin) (void)hipEventRecord(tl.begin, st);
   hipLaunchKernelGGL((scan_kernel<KB, QJL, VMSE, VB>), dim3(a.splits, a.batch * a.h_kv),
                      dim3(kScanThreads), 0, st, a);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (tl.end) (void)hipEventRecord(tl.end, st);
+  return e;
 }
 
 template <int KB, bool QJL, bool VMSE>
-hipError_t dispatch_vb(const DecodeArgs& a, int vb, hipStream_t st) {
+hipError_t dispatch_vb(const DecodeArgs& a, int vb, hipStream_t st, TimedLaunch tl) {
   switch (vb) {
-    case 1: return launch_scan<KB, QJL, VMSE, 1>(a, st);
-    case 2: return launch_scan<KB, QJL, VMSE, 2>(a, st);
-    case 3: return launch_scan<KB, QJL, VMSE, 3>(a, st);
-    case 4: return launch_scan<KB, QJL, VMSE, 4>(a, st);
+    case 1: return launch_scan<KB, QJL, VMSE, 1>(a, st, tl);
+    case 2: return launch_scan<KB, QJL, VMSE, 2>(a, st, tl);
+    case 3: return launch_scan<KB, QJL, VMSE, 3>(a, st, tl);
+    case 4: return launch_scan<KB, QJL, VMSE, 4>(a, st, tl);
   }
   return hipErrorInvalidValue;
 }
 
 template <int KB, bool QJL>
-hipError_t dispatch_vk(const DecodeArgs& a, int vmse, int vb, hipStream_t st) {
-  return vmse ? dispatch_vb<KB, QJL, true>(a, vb, st) : dispatch_vb<KB, QJL, false>(a, vb, st);
+hipError_t dispatch_vk(const DecodeArgs& a, int vmse, int vb, hipStream_t st, TimedLaunch tl) {
+  return vmse ? dispatch_vb<KB, QJL, true>(a, vb, st, tl) : dispatch_vb<KB, QJL, false>(a, vb, st, tl);
 }
 
 template <int KB>
-hipError_t dispatch_qjl(const DecodeArgs& a, int qjl, int vmse, int vb, hipStream_t st) {
-  return qjl ? dispatch_vk<KB, true>(a, vmse, vb, st) : dispatch_vk<KB, false>(a, vmse, vb, st);
+hipError_t dispatch_qjl(const DecodeArgs& a, int qjl, int vmse, int vb, hipStream_t st, TimedLaunch tl) {
+  return qjl ? dispatch_vk<KB, true>(a, vmse, vb, st, tl) : dispatch_vk<KB, false>(a, vmse, vb, st, tl);
 }
 
 }  // namespace
@@ -427,15 +430,15 @@ void decode_split(int64_t max_tokens, int64_t units, int32_t* splits, int32_t* s
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int key_mse_bits, int key_qjl, int value_mse,
-                         int value_bits, hipStream_t stream) {
+                         int value_bits, hipStream_t stream, TimedLaunch tl) {
   hipLaunchKernelGGL(qprep_kernel, dim3(a.batch * a.h_kv), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   switch (key_mse_bits) {
-    case 1: e = dispatch_qjl<1>(a, key_qjl, value_mse, value_bits, stream); break;
-    case 2: e = dispatch_qjl<2>(a, key_qjl, value_mse, value_bits, stream); break;
-    case 3: e = dispatch_qjl<3>(a, key_qjl, value_mse, value_bits, stream); break;
-    case 4: e = dispatch_qjl<4>(a, key_qjl, value_mse, value_bits, stream); break;
+    case 1: e = dispatch_qjl<1>(a, key_qjl, value_mse, value_bits, stream, tl); break;
+    case 2: e = dispatch_qjl<2>(a, key_qjl, value_mse, value_bits, stream, tl); break;
+    case 3: e = dispatch_qjl<3>(a, key_qjl, value_mse, value_bits, stream, tl); break;
+    case 4: e = dispatch_qjl<4>(a, key_qjl, value_mse, value_bits, stream, tl); break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;

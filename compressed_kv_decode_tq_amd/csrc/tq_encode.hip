@@ -433,44 +433,50 @@ int encode_grid(int tiles, int waves_per_block) {
 }
 
 template <bool BF16, int MB, bool QJL, bool VALUE>
-hipError_t launch_rot(const EncodeArgs& a, hipStream_t st) {
+hipError_t launch_rot(const EncodeArgs& a, hipStream_t st, TimedLaunch tl) {
   int grid = encode_grid(a.num_tiles, kEncThreads / 64);
   const int cus = device_cu_count();
   if (grid > cus) grid = cus;  // persistent: the LDS staging is paid once per work-group
+  if (tl.begin) (void)hipEventRecord(tl.begin, st);
   hipLaunchKernelGGL((encode_rot_kernel<BF16, MB, QJL, VALUE>), dim3(grid), dim3(kEncThreads), 0, st, a);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (tl.end) (void)hipEventRecord(tl.end, st);
+  return e;
 }
 
 template <bool BF16, bool QJL, bool VALUE>
-hipError_t dispatch_rot_bits(const EncodeArgs& a, int bits, hipStream_t st) {
+hipError_t dispatch_rot_bits(const EncodeArgs& a, int bits, hipStream_t st, TimedLaunch tl) {
   switch (bits) {
-    case 1: return launch_rot<BF16, 1, QJL, VALUE>(a, st);
-    case 2: return launch_rot<BF16, 2, QJL, VALUE>(a, st);
-    case 3: return launch_rot<BF16, 3, QJL, VALUE>(a, st);
-    case 4: return launch_rot<BF16, 4, QJL, VALUE>(a, st);
+    case 1: return launch_rot<BF16, 1, QJL, VALUE>(a, st, tl);
+    case 2: return launch_rot<BF16, 2, QJL, VALUE>(a, st, tl);
+    case 3: return launch_rot<BF16, 3, QJL, VALUE>(a, st, tl);
+    case 4: return launch_rot<BF16, 4, QJL, VALUE>(a, st, tl);
   }
   return hipErrorInvalidValue;
 }
 
 template <bool BF16, int BITS>
-hipError_t launch_mm(const EncodeArgs& a, hipStream_t st) {
+hipError_t launch_mm(const EncodeArgs& a, hipStream_t st, TimedLaunch tl) {
   const int grid = encode_grid(a.num_tiles, 4);
+  if (tl.begin) (void)hipEventRecord(tl.begin, st);
   switch (a.value_group) {
     case 16: hipLaunchKernelGGL((encode_minmax_kernel<BF16, BITS, 16>), dim3(grid), dim3(256), 0, st, a); break;
     case 32: hipLaunchKernelGGL((encode_minmax_kernel<BF16, BITS, 32>), dim3(grid), dim3(256), 0, st, a); break;
     case 64: hipLaunchKernelGGL((encode_minmax_kernel<BF16, BITS, 64>), dim3(grid), dim3(256), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (tl.end) (void)hipEventRecord(tl.end, st);
+  return e;
 }
 
 template <bool BF16>
-hipError_t dispatch_mm(const EncodeArgs& a, int bits, hipStream_t st) {
+hipError_t dispatch_mm(const EncodeArgs& a, int bits, hipStream_t st, TimedLaunch tl) {
   switch (bits) {
-    case 1: return launch_mm<BF16, 1>(a, st);
-    case 2: return launch_mm<BF16, 2>(a, st);
-    case 3: return launch_mm<BF16, 3>(a, st);
-    case 4: return launch_mm<BF16, 4>(a, st);
+    case 1: return launch_mm<BF16, 1>(a, st, tl);
+    case 2: return launch_mm<BF16, 2>(a, st, tl);
+    case 3: return launch_mm<BF16, 3>(a, st, tl);
+    case 4: return launch_mm<BF16, 4>(a, st, tl);
   }
   return hipErrorInvalidValue;
 }
@@ -484,25 +490,26 @@ hipError_t launch_prepare_params(const float* pi, const float* s, uint16_t* deri
 }
 
 hipError_t launch_encode_keys(const EncodeArgs& a, int in_bf16, int mse_bits, int qjl,
-                              hipStream_t stream) {
+                              hipStream_t stream, TimedLaunch tl) {
   if (a.num_tiles == 0) return hipSuccess;
   if (in_bf16)
-    return qjl ? dispatch_rot_bits<true, true, false>(a, mse_bits, stream)
-               : dispatch_rot_bits<true, false, false>(a, mse_bits, stream);
-  return qjl ? dispatch_rot_bits<false, true, false>(a, mse_bits, stream)
-             : dispatch_rot_bits<false, false, false>(a, mse_bits, stream);
+    return qjl ? dispatch_rot_bits<true, true, false>(a, mse_bits, stream, tl)
+               : dispatch_rot_bits<true, false, false>(a, mse_bits, stream, tl);
+  return qjl ? dispatch_rot_bits<false, true, false>(a, mse_bits, stream, tl)
+             : dispatch_rot_bits<false, false, false>(a, mse_bits, stream, tl);
 }
 
-hipError_t launch_encode_values_mse(const EncodeArgs& a, int in_bf16, int bits, hipStream_t stream) {
+hipError_t launch_encode_values_mse(const EncodeArgs& a, int in_bf16, int bits, hipStream_t stream,
+                                    TimedLaunch tl) {
   if (a.num_tiles == 0) return hipSuccess;
-  return in_bf16 ? dispatch_rot_bits<true, false, true>(a, bits, stream)
-                 : dispatch_rot_bits<false, false, true>(a, bits, stream);
+  return in_bf16 ? dispatch_rot_bits<true, false, true>(a, bits, stream, tl)
+                 : dispatch_rot_bits<false, false, true>(a, bits, stream, tl);
 }
 
 hipError_t launch_encode_values_minmax(const EncodeArgs& a, int in_bf16, int bits,
-                                       hipStream_t stream) {
+                                       hipStream_t stream, TimedLaunch tl) {
   if (a.num_tiles == 0) return hipSuccess;
-  return in_bf16 ? dispatch_mm<true>(a, bits, stream) : dispatch_mm<false>(a, bits, stream);
+  return in_bf16 ? dispatch_mm<true>(a, bits, stream, tl) : dispatch_mm<false>(a, bits, stream, tl);
 }
 
 }  // namespace tq

@@ -98,21 +98,27 @@ struct DecodeArgs {
   SeqValues n_ring;
 };
 
+// Events recorded around one kernel launch (both null: none).
+struct TimedLaunch {
+  hipEvent_t begin = nullptr;
+  hipEvent_t end = nullptr;
+};
+
 // Launchers (defined in the .hip files).  Each returns hipSuccess or the
 // launch error.
 hipError_t launch_prepare_params(const float* pi, const float* s, uint16_t* derived,
                                  hipStream_t stream);
 hipError_t launch_encode_keys(const EncodeArgs& a, int in_bf16, int mse_bits, int qjl,
-                              hipStream_t stream);
+                              hipStream_t stream, TimedLaunch t);
 hipError_t launch_encode_values_mse(const EncodeArgs& a, int in_bf16, int bits,
-                                    hipStream_t stream);
+                                    hipStream_t stream, TimedLaunch t);
 hipError_t launch_encode_values_minmax(const EncodeArgs& a, int in_bf16, int bits,
-                                       hipStream_t stream);
+                                       hipStream_t stream, TimedLaunch t);
 hipError_t launch_ring_append(const void* k_new, const void* v_new, int in_bf16, int batch,
                               int h_kv, uint16_t* ring_k, uint16_t* ring_v, int ring_cap,
                               const SeqValues& n_ring, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int key_mse_bits, int key_qjl, int value_mse,
-                         int value_bits, hipStream_t stream);
+                         int value_bits, hipStream_t stream, TimedLaunch scan);
 
 // Decode work split used for the workspace size and the launch.
 void decode_split(int64_t max_tokens, int64_t units, int32_t* splits, int32_t* split_len);

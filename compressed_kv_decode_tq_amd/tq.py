@@ -25,7 +25,8 @@ MAX_LEVELS = 16
 #: Every symbol include/tq.h declares.
 EXPORTS = ("tq_make_codebook", "tq_memory_bytes", "tq_params_derived_bytes", "tq_prepare_params",
            "tq_encode_kv", "tq_ring_append", "tq_decode_workspace_bytes", "tq_decode_attn",
-           "tq_last_error", "tq_version")
+           "tq_time_next_launch", "tq_last_error", "tq_version")
+TQ_KERNEL_DECODE_SCAN, TQ_KERNEL_ENCODE_KEYS, TQ_KERNEL_ENCODE_VALUES = 0, 1, 2
 
 
 class TqError(RuntimeError):
@@ -86,6 +87,8 @@ def lib() -> ctypes.CDLL:
         L.tq_decode_attn.argtypes = [P(_Layout), P(_Params), vp, i32, i32, P(_Cache), P(i64), vp, vp,
                                      i32, P(i32), ctypes.c_float, vp, vp, sz, vp]
         L.tq_decode_attn.restype = ctypes.c_int
+        L.tq_time_next_launch.argtypes = [i32, vp, vp]
+        L.tq_time_next_launch.restype = ctypes.c_int
         L.tq_last_error.argtypes = []
         L.tq_last_error.restype = ctypes.c_char_p
         L.tq_version.argtypes = []
@@ -277,6 +280,12 @@ def decode_attn(params: Params, q: torch.Tensor, cache: Cache, n_compressed, rin
                                 float(scale), _ptr(out), _ptr(workspace), workspace.numel(),
                                 _stream(stream)))
     return out
+
+
+def time_next_launch(kernel: int, ev_begin, ev_end):
+    """Record the caller's hipEvent_t handles around the next launch of
+    `kernel` (TQ_KERNEL_*) on this thread."""
+    _check(lib().tq_time_next_launch(kernel, ev_begin, ev_end))
 
 
 def version() -> str:

@@ -176,6 +176,14 @@ int tq_decode_attn(const tq_layout* layout, const tq_params* params, const void*
                    int32_t ring_cap, const int32_t* n_ring_host, float softmax_scale, float* out,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* Measurement hook.  The next launch of `kernel` (TQ_KERNEL_*) made by the
+ * calling thread records ev_begin just before it and ev_end just after it on
+ * the launch stream (both hipEvent_t created by the caller), so the caller can
+ * time that one kernel with hipEventElapsedTime.  The registration is used
+ * once; NULL events cancel it.  Errors: TQ_ERR_INVALID for an unknown kernel. */
+enum { TQ_KERNEL_DECODE_SCAN = 0, TQ_KERNEL_ENCODE_KEYS = 1, TQ_KERNEL_ENCODE_VALUES = 2 };
+int tq_time_next_launch(int32_t kernel, void* ev_begin, void* ev_end);
+
 /* Text of the most recent error of the calling thread ("" if none). */
 const char* tq_last_error(void);
 
