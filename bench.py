@@ -266,14 +266,17 @@ def main():
     scan_avg_ms = sum(scan_ms) / len(scan_ms)
     scan_avg_bytes = sum(scan_bytes) / len(scan_bytes)
     scan_gbs = scan_avg_bytes / (scan_avg_ms * 1e-3) / 1e9
-    sha = _source_sha("tq_decode.hip", "tq_common.h", "tq_internal.h")
+    sha = _source_sha("tq_decode_mfma.hip", "tq_decode.hip", "tq_common.h", "tq_internal.h")
     traffic = _traffic("decode_scan", sha)
+    scan_kernel_name = ("scan_kernel (VALU split scan over the compressed cache)"
+                        if os.environ.get("TQ_DECODE_PATH") == "generic"
+                        else "scan_mfma_kernel (int8-MFMA split scan over the compressed cache)")
 
     res = {
         "metric": "decode-attn effective HBM GB/s (% peak) and encode tokens/s, 1xMI355X",
         "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16",
+        "vs_baseline": None, "dtype": "i8-mfma+f32",
         "data": "synthetic (seeded N(0,1) K/V/q with outlier channels; no dataset, no weights)",
         "config": {"workload": w.name, "batch": w.batch, "h_q": w.h_q, "h_kv": w.h_kv, "head_dim": w.d,
                    "n_compressed": w.n_tokens, "ring_cap": w.ring_cap, "ring_tokens_in_timed_steps": f"1..{args.steps}",
@@ -281,7 +284,7 @@ def main():
                    "value_code": f"{w.value_bits}-bit {w.value_kind}" + (f" g{w.value_group}" if w.value_kind == "minmax" else ""),
                    "scalars": w.scalar_dtype, "bytes_per_token_head": per_th, "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "roofline": {"kernel": "scan_kernel (split scan over the compressed cache)", "bound": "hbm",
+        "roofline": {"kernel": scan_kernel_name, "bound": "hbm",
                      "achieved": round(scan_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(scan_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "avg_launch_ms": round(scan_avg_ms, 5),

@@ -17,8 +17,11 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtq.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["tq_api.cpp", "tq_codebook.cpp", "tq_encode.hip", "tq_decode.hip"]
+SOURCES = ["tq_api.cpp", "tq_codebook.cpp", "tq_encode.hip", "tq_decode.hip", "tq_decode_mfma.hip"]
 ARCH = os.environ.get("TQ_OFFLOAD_ARCH", "gfx950")
+# MFMA results land in ordinary VGPRs in the decode scan (no accumulator-register
+# copies: every result is consumed by VALU code right away)
+SOURCE_FLAGS = {"tq_decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc() -> str:
@@ -45,7 +48,7 @@ def build(verbose: bool = False) -> str:
     def compile_one(src: str) -> str:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [cc, *_flags(), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *_flags(), *SOURCE_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         res = subprocess.run(cmd, capture_output=True, text=True)
         msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
                          if "packed-fp32-ops" not in l)

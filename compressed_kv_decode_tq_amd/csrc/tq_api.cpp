@@ -4,7 +4,9 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
+#include <algorithm>
 
 #include "tq_internal.h"
 
@@ -259,7 +261,8 @@ size_t tq_decode_workspace_bytes(const tq_layout* layout, int32_t batch, int32_t
   tq::decode_split(max_tokens, (int64_t)nb * num_kv_heads, &splits, &split_len);
   const size_t qprep = (size_t)nb * num_q_heads * 2 * tq::kD * 4;
   const size_t part = (size_t)splits * nb * num_q_heads * (tq::kD + 2) * 4;
-  return qprep + part;
+  const size_t base = (qprep + part + 255) & ~(size_t)255;
+  return base + tq::mfma_workspace_bytes(nb, num_q_heads, num_q_heads / num_kv_heads);
 }
 
 int tq_decode_attn(const tq_layout* layout, const tq_params* params, const void* q,
@@ -341,9 +344,23 @@ int tq_decode_attn(const tq_layout* layout, const tq_params* params, const void*
     std::memcpy(a.k_cent, kc, sizeof(kc));
     std::memcpy(a.v_cent, vc, sizeof(vc));
     (void)mt;
-    hipError_t e = tq::launch_decode(a, layout->key_mse_bits, layout->key_qjl,
-                                     layout->value_kind == TQ_V_MSE, layout->value_bits,
-                                     (hipStream_t)stream, take_timed(TQ_KERNEL_DECODE_SCAN));
+    const size_t base_ws = (size_t)nb * num_q_heads * 2 * tq::kD * 4 +
+                           (size_t)a.splits * nb * num_q_heads * (tq::kD + 2) * 4;
+    a.qdig = (int8_t*)((char*)workspace + ((base_ws + 255) & ~(size_t)255));
+    a.qconst = (float*)((char*)a.qdig + (size_t)nb * h_kv * ((group + 3) / 4) * 5 * 2 * 64 * 16);
+    const bool vmse = layout->value_kind == TQ_V_MSE;
+    const int kpl = tq::plane_expansion(kc, layout->key_mse_bits, a.key_w, &a.key_cst);
+    const int vpl = vmse ? tq::plane_expansion(vc, layout->value_bits, a.val_w, &a.val_cst) : 0;
+    const char* path = std::getenv("TQ_DECODE_PATH");
+    const bool generic_only = path && std::strcmp(path, "generic") == 0;
+    const tq::TimedLaunch tl = take_timed(TQ_KERNEL_DECODE_SCAN);
+    hipError_t e = hipErrorNotSupported;
+    if (!generic_only && kpl > 0 && (!vmse || vpl > 0))
+      e = tq::launch_decode_mfma(a, layout->key_mse_bits, layout->key_qjl, vmse, layout->value_bits, kpl,
+                                 vpl, (hipStream_t)stream, tl);
+    if (e == hipErrorNotSupported)
+      e = tq::launch_decode(a, layout->key_mse_bits, layout->key_qjl, vmse, layout->value_bits,
+                            (hipStream_t)stream, tl);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
   }
   return TQ_OK;

@@ -90,4 +90,38 @@ int make_codebook(int d, int bits, double* cent, double* thr) {
   return TQ_OK;
 }
 
+// Walsh-Hadamard expansion of a codebook over the bits of its index.  With
+// x_k = 2 b_k - 1, any table is c[idx] = sum_S a_S prod_{k in S} x_k, with
+// a_S = 2^-b sum_idx c[idx] prod_{k in S} x_k(idx).  An antisymmetric table
+// (c[2^b-1-i] = -c[i], as every Lloyd-Max table of a symmetric law is) has
+// a_S = 0 for every even |S|, and for odd |S| the product is 2 par_S - 1
+// (par_S = XOR of the bits in S), so c[idx] = -sum a_S + sum 2 a_S par_S.
+int plane_expansion(const float* cent, int bits, float* w, float* cst) {
+  if (bits < 1 || bits > 3) return 0;
+  const int levels = 1 << bits;
+  double amax = 0.0;
+  for (int i = 0; i < levels; ++i) amax = std::fmax(amax, std::fabs((double)cent[i]));
+  for (int i = 0; i < levels; ++i)
+    if (std::fabs((double)cent[i] + (double)cent[levels - 1 - i]) > 1e-6 * amax) return 0;
+  // odd subsets in plane order: {0}, {1}, {2}, {0,1,2}
+  const int subsets[4] = {1, 2, 4, 7};
+  const int planes = 1 << (bits - 1);
+  double c0 = 0.0;
+  for (int p = 0; p < planes; ++p) {
+    const int s = subsets[p];
+    double acc = 0.0;
+    for (int idx = 0; idx < levels; ++idx) {
+      double prod = 1.0;
+      for (int k = 0; k < bits; ++k)
+        if (s & (1 << k)) prod *= ((idx >> k) & 1) ? 1.0 : -1.0;
+      acc += (double)cent[idx] * prod;
+    }
+    const double a = acc / levels;
+    w[p] = (float)(2.0 * a);
+    c0 -= a;
+  }
+  *cst = (float)c0;
+  return planes;
+}
+
 }  // namespace tq

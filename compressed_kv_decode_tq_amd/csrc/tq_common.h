@@ -11,6 +11,14 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
+// Bit position, inside a value-plane word, of token slot u (0..31) of its
+// 32-token block: u = 16c + 4g + j sits in bit 8j + 4c + g.  With this order a
+// single AND with 0x01010101 << s extracts, as bytes, the four tokens that one
+// int8 MFMA lane supplies (see the decode scan).
+__host__ __device__ __forceinline__ int vbit(int u) { return 8 * (u & 3) + 4 * (u >> 4) + ((u >> 2) & 3); }
+// Inverse: token slot held in bit position b.
+__host__ __device__ __forceinline__ int vslot(int b) { return 16 * ((b >> 2) & 1) + 4 * (b & 3) + (b >> 3); }
+
 // fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
 __device__ __forceinline__ uint32_t f2bf(float f) {
   uint32_t u = __float_as_uint(f);

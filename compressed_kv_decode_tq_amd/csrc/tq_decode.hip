@@ -220,8 +220,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(DecodeArgs a) {
         uint32_t code0 = 0, code1 = 0;
 #pragma unroll
         for (int p = 0; p < VB; ++p) {
-          code0 |= ((w[blk][p][0] >> tb) & 1u) << p;
-          code1 |= ((w[blk][p][1] >> tb) & 1u) << p;
+          code0 |= ((w[blk][p][0] >> vbit(tb)) & 1u) << p;
+          code1 |= ((w[blk][p][1] >> vbit(tb)) & 1u) << p;
         }
         float v0, v1;
         if (VMSE) {
@@ -442,6 +442,10 @@ hipError_t launch_decode(const DecodeArgs& a, int key_mse_bits, int key_qjl, int
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
+  return launch_combine(a, value_mse, stream);
+}
+
+hipError_t launch_combine(const DecodeArgs& a, int value_mse, hipStream_t stream) {
   if (value_mse)
     hipLaunchKernelGGL(combine_kernel<true>, dim3(a.batch * a.h_q), dim3(kD), 0, stream, a);
   else

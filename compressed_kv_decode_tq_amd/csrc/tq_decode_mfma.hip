@@ -1,0 +1,689 @@
+// Decode on the int8 matrix cores of gfx950: the compressed scan as integer
+// MFMAs over the stored bit planes.
+//
+// What is computed (page "03. Results & Benchmarks", "Latency Benchmarks":
+// scores, QJL correction, online softmax and value accumulation in one pass;
+// page "TurboQuant — Random rotation trước khi quantize, 3-bit KV cache không
+// mất accuracy", "Tại sao nó hoạt động": the query is rotated once per step and
+// keys are never reconstructed) is the same as the generic scan; only the
+// arithmetic is reorganised:
+//
+// * A symmetric b-bit codebook is affine in the bit planes of the index:
+//   c[idx] = cst + sum_p w_p plane_p(idx) (planes bit0..bit2 and bit0^bit1^bit2),
+//   so <q_rot, c[idx]> = cst sum(q_rot) + sum_p w_p <q_rot, plane_p>, and the
+//   QJL term is <q_s, 2 bit - 1> = 2 <q_s, bit> - sum(q_s).  Every score term is
+//   a 0/1-vector times a query vector.
+// * Those products run as v_mfma_i32_16x16x64_i8: one operand is the bit plane
+//   itself (a byte per bit, taken from a 32-bit plane word with ONE AND against
+//   0x01010101 << s, so the byte holds 2^s), the other the query in fixed point
+//   split into four signed base-128 digits (one digit per MFMA row/column),
+//   pre-scaled by 2^-s to cancel the byte's 2^s.  Integer sums are exact; the
+//   fixed point keeps 20+ significant bits of every query coordinate.
+// * The value sum sum_t p_t v~_t runs the same way with the roles swapped: the
+//   weights p_t delta_t (min/max) or p_t |v_t| (MSE values) in fixed-point
+//   digits, times the value bit planes.  The score MFMA leaves each lane holding
+//   exactly the 16 tokens its digit row needs for the value MFMA, so no data
+//   moves between the two.
+// * A byte holding 2^7 reads as -128 in int8; the matching digits are negated.
+#include "tq_common.h"
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+constexpr float kQjlScale = 0.0097916519f;  // sqrt(pi/2) / 128
+constexpr int kScanThreads = 256;           // 4 waves, each scanning its own 64-token chunks
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4 mfma_i8(u32x4 a, u32x4 b, i32x4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b),
+                                               c, 0, 0, 0);
+}
+
+// Sum over the 4 lanes of a quad (xor 1, then xor 2) with DPP.
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, true));
+  return x;
+}
+
+// Bytes of a plane word: byte j of the result is bit (8j + s) of w, scaled by 2^s.
+__device__ __forceinline__ uint32_t plane_bytes(uint32_t w, int s) { return w & (0x01010101u << s); }
+
+// Signed base-128 digits of q (|q| < 2^27), most significant first.
+__device__ __forceinline__ void digits128(int q, int d[4]) {
+#pragma unroll
+  for (int L = 3; L >= 1; --L) {
+    const int r = ((q + 64) & 127) - 64;
+    d[L] = r;
+    q = (q - r) >> 7;
+  }
+  d[0] = q;
+}
+
+// Query digits: for head tile ht, score plane pl, contraction half hf and lane
+// (g, n), 16 bytes: byte 4d + j holds digit n%4 of head 4ht + n/4 at
+// coordinate k = 32g + 8j + 4hf + d, pre-scaled by 2^-(k%8) (negated for
+// k%8 == 7).  Plane pl < PM multiplies w_pl * (Pi q); plane PM (QJL) 2 * (S q).
+__global__ __launch_bounds__(256) void qprep_mfma_kernel(DecodeArgs a, int pm, int npl, int nht) {
+  __shared__ float qv[kMaxGroup][kD];
+  __shared__ float qr[kMaxGroup][kD];
+  __shared__ float qs[kMaxGroup][kD];
+  __shared__ int e_mse[kMaxGroup], e_qjl[kMaxGroup];
+  const int b = blockIdx.x / a.h_kv, h = blockIdx.x % a.h_kv;
+  const int G = a.group;
+  for (int i = threadIdx.x; i < kMaxGroup * kD; i += blockDim.x) {
+    const int gq = i / kD, c = i % kD;
+    float x = 0.f;
+    if (gq < G) {
+      const size_t off = ((size_t)b * a.h_q + h * G + gq) * kD + c;
+      x = a.q_bf16 ? bf2f(reinterpret_cast<const uint16_t*>(a.q)[off]) : reinterpret_cast<const float*>(a.q)[off];
+    }
+    qv[gq][c] = x;
+  }
+  __syncthreads();
+  {
+    const int i = threadIdx.x & (kD - 1);
+    const int which = threadIdx.x >> 7;  // 0: Pi, 1: S
+    const float* m = which == 0 ? a.pi : a.s;
+    float acc[kMaxGroup];
+#pragma unroll
+    for (int gq = 0; gq < kMaxGroup; ++gq) acc[gq] = 0.f;
+    const floatx4* row = reinterpret_cast<const floatx4*>(m + (size_t)i * kD);
+    for (int j4 = 0; j4 < kD / 4; ++j4) {
+      const floatx4 w = row[j4];
+#pragma unroll
+      for (int gq = 0; gq < kMaxGroup; ++gq) {
+        acc[gq] = fmaf(w[0], qv[gq][4 * j4 + 0], acc[gq]);
+        acc[gq] = fmaf(w[1], qv[gq][4 * j4 + 1], acc[gq]);
+        acc[gq] = fmaf(w[2], qv[gq][4 * j4 + 2], acc[gq]);
+        acc[gq] = fmaf(w[3], qv[gq][4 * j4 + 3], acc[gq]);
+      }
+    }
+#pragma unroll
+    for (int gq = 0; gq < kMaxGroup; ++gq) (which == 0 ? qr : qs)[gq][i] = acc[gq];
+  }
+  __syncthreads();
+  // per-head exponents and constants: one wave per head
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  for (int gq = wv; gq < kMaxGroup; gq += 4) {
+    float mr = 0.f, ms = 0.f, sr = 0.f, ssum = 0.f;
+    for (int c = lane; c < kD; c += 64) {
+      mr = fmaxf(mr, fabsf(qr[gq][c]));
+      ms = fmaxf(ms, fabsf(qs[gq][c]));
+      sr += qr[gq][c];
+      ssum += qs[gq][c];
+    }
+    mr = wave_max(mr);
+    ms = wave_max(ms);
+    sr = wave_sum(sr);
+    ssum = wave_sum(ssum);
+    float wmax = 0.f;
+    for (int p = 0; p < pm; ++p) wmax = fmaxf(wmax, fabsf(a.key_w[p]));
+    int ex_r, ex_s;
+    frexpf(mr * wmax, &ex_r);  // |w_p q_rot| < 2^ex_r
+    frexpf(2.f * ms, &ex_s);
+    const int er = 26 - ex_r, es = 26 - ex_s;  // scaled values stay below 2^26
+    if (lane == 0) {
+      e_mse[gq] = er;
+      e_qjl[gq] = es;
+      if (gq < G) {
+        float* cst = a.qconst + ((size_t)b * a.h_q + h * G + gq) * 4;
+        cst[0] = a.key_cst * sr;     // constant part of <q_rot, c[idx]>
+        cst[1] = ldexpf(1.f, -er);   // digit scale of the MSE planes
+        cst[2] = ldexpf(1.f, -es);   // digit scale of the QJL plane
+        cst[3] = ssum;               // sum(q_s)
+      }
+    }
+  }
+  __syncthreads();
+  const int ndw = nht * npl * 2 * 64 * 4;  // dwords of digit operands for this (sequence, KV head)
+  uint32_t* out = reinterpret_cast<uint32_t*>(a.qdig) + (size_t)(b * a.h_kv + h) * ndw;
+  for (int i = threadIdx.x; i < ndw; i += blockDim.x) {
+    const int d = i & 3;
+    const int ln = (i >> 2) & 63;
+    const int hf = (i >> 8) & 1;
+    const int rest = i >> 9;
+    const int pl = rest % npl, ht = rest / npl;
+    const int g = ln >> 4, n = ln & 15;
+    const int gq = 4 * ht + (n >> 2), L = n & 3;
+    uint32_t word = 0;
+    if (gq < G) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int k = 32 * g + 8 * j + 4 * hf + d;
+        const int s = k & 7;
+        float x;
+        int e;
+        if (pl < pm) {
+          x = a.key_w[pl] * qr[gq][k];
+          e = e_mse[gq];
+        } else {
+          x = 2.f * qs[gq][k];
+          e = e_qjl[gq];
+        }
+        const int q = (int)rintf(ldexpf(x, e - s));
+        int dg[4];
+        digits128(q, dg);
+        const int v = s == 7 ? -dg[L] : dg[L];
+        word |= (uint32_t)(v & 0xff) << (8 * j);
+      }
+    }
+    out[i] = word;
+  }
+}
+
+template <int PM, bool QJL, bool VMSE, int PVB, int NHT>
+__global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
+  constexpr int KB = PM == 1 ? 1 : (PM == 2 ? 2 : 3);  // stored key index planes
+  constexpr int KP = KB + (QJL ? 1 : 0);               // stored key planes
+  constexpr int NPL = PM + (QJL ? 1 : 0);              // score planes
+  constexpr int VB = VMSE ? (PVB == 1 ? 1 : (PVB == 2 ? 2 : 3)) : PVB;  // stored value planes
+  constexpr int NG = 4;                                // min/max groups of 32 channels
+  constexpr int NHEAD = 4 * NHT;
+
+  // per-wave staging of the current chunk, reused at the end for the merge
+  constexpr int kStageMeta = 64 * NG;           // dwords
+  constexpr int kStageNg = 64 * 2;              // floats: per token u = tau log2e n, w = u kappa gamma
+  constexpr int kStageVw = 2 * VB * kD;         // dwords
+  constexpr int kStage = kStageMeta + kStageNg + kStageVw;
+  constexpr int kMerge = NHEAD * (kD + 2);
+  constexpr int kStride = kStage > kMerge ? kStage : kMerge;
+  __shared__ __attribute__((aligned(16))) uint32_t smem[4 * kStride];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, n = lane & 15;
+  const int sh = blockIdx.y;
+  const int b = sh / a.h_kv, h = sh % a.h_kv;
+  const int G = a.group;
+  const int64_t n_c = a.n_comp.v[b];
+  const int64_t t_begin = (int64_t)blockIdx.x * a.split_len;
+  const int64_t t_end = t_begin + a.split_len < n_c ? t_begin + a.split_len : n_c;
+
+  uint32_t* s_meta = smem + wave * kStride;
+  float* s_ng = reinterpret_cast<float*>(s_meta + kStageMeta);
+  uint32_t* s_vw = s_meta + kStageMeta + kStageNg;
+
+  // query digit operands and per-head constants (score layout: head 4ht + n/4)
+  u32x4 qb[NHT][NPL][2];
+  {
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.qdig) + (size_t)sh * NHT * NPL * 2 * 64;
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+      for (int pl = 0; pl < NPL; ++pl)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) qb[ht][pl][hf] = src[((ht * NPL + pl) * 2 + hf) * 64 + lane];
+  }
+  // score of (head, token) in log2 units: u (K1 Dm + c0) + w (K2 Ds - c3), where
+  // u = tau log2(e) n, w = u kappa gamma and Dm, Ds are quad sums of digit partials
+  const float lscale = (float)(1u << (7 * (3 - (n & 3))));  // weight of this lane's query digit
+  float k1[NHT], k2[NHT], c0[NHT], c3[NHT];
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht) {
+    const int hq = 4 * ht + (n >> 2);
+    if (hq < G) {
+      const floatx4 cs = *reinterpret_cast<const floatx4*>(a.qconst + ((size_t)b * a.h_q + h * G + hq) * 4);
+      c0[ht] = cs[0];
+      k1[ht] = cs[1] * lscale;
+      k2[ht] = cs[2] * lscale;
+      c3[ht] = cs[3];
+    } else {
+      c0[ht] = k1[ht] = k2[ht] = c3[ht] = 0.f;
+    }
+  }
+  const float u_scale = a.scale * 1.4426950409f;  // exp(x) = exp2(x log2 e)
+
+  const size_t rec = (size_t)KP * (kD / 8);
+  const uint8_t* kp = a.k_planes + (size_t)sh * a.capacity * rec;
+  const size_t sidx0 = (size_t)sh * a.capacity;
+  const uint32_t* vp = a.v_planes + (size_t)sh * (a.capacity >> 5) * VB * kD;
+
+  // running max (log2 units) starts at a finite floor so exp2(-inf - m) is 0, never NaN
+  float m_run[NHT], l_part[NHT], acc[NHT][8];
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht) {
+    m_run[ht] = -1e30f;
+    l_part[ht] = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) acc[ht][nt] = 0.f;
+  }
+
+  // Chunk loads are issued one chunk ahead: the registers below hold chunk
+  // c0t + 256 of this wave while chunk c0t is being computed.
+  uint32_t pX[4][KP];       // key plane words: token 16ct + n, plane word g
+  float pNrm = 0.f, pGam = 0.f;
+  u32x4 pMeta = u32x4{0u, 0u, 0u, 0u};
+  u32x4 pVw[VB];
+  const int64_t first = t_begin + 64 * wave;
+  const int ssz = a.scalar_f16 ? 2 : 4;
+  // per-lane addresses at the wave's first chunk; every later chunk is 256 tokens on
+  const uint8_t* p_k = kp + (first + n) * (int64_t)rec + 4 * g;
+  const char* p_n = reinterpret_cast<const char*>(a.k_norm) + (int64_t)(sidx0 + first + lane) * ssz;
+  const char* p_g = QJL ? reinterpret_cast<const char*>(a.k_rnorm) + (int64_t)(sidx0 + first + lane) * ssz : nullptr;
+  const char* p_m = VMSE ? reinterpret_cast<const char*>(a.v_norm) + (int64_t)(sidx0 + first + lane) * ssz
+                         : reinterpret_cast<const char*>(a.v_meta) + (int64_t)(sidx0 + first + lane) * (NG * 4);
+  const uint32_t* p_v = vp + (first >> 5) * VB * kD + lane * 4;
+  auto scalar_at = [&](const char* p) -> float {
+    return a.scalar_f16 ? __half2float(*reinterpret_cast<const __half*>(p)) : *reinterpret_cast<const float*>(p);
+  };
+  auto load_chunk = [&](int it) {
+    const int64_t c = first + (int64_t)it * 256;
+    const int rem_c = (int)(t_end - c < 64 ? t_end - c : 64);
+    const uint8_t* xk = p_k + (int64_t)it * 256 * rec;
+    const int64_t so = (int64_t)it * 256 * ssz;
+    const uint32_t* xv = p_v + (int64_t)it * 8 * VB * kD;
+    if (rem_c == 64) {  // full chunk: no per-lane guards
+      pNrm = scalar_at(p_n + so);
+      if (QJL) pGam = scalar_at(p_g + so);
+      if (VMSE)
+        pMeta[0] = __float_as_uint(scalar_at(p_m + so));
+      else
+        pMeta = *reinterpret_cast<const u32x4*>(p_m + (int64_t)it * 256 * NG * 4);
+#pragma unroll
+      for (int i = 0; i < VB; ++i) pVw[i] = *reinterpret_cast<const u32x4*>(xv + i * 256);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int sp = 0; sp < KP; ++sp)
+          pX[ct][sp] = *reinterpret_cast<const uint32_t*>(xk + 16 * ct * rec + sp * (kD / 8));
+    } else {
+      const bool valid = lane < rem_c;
+      pNrm = valid ? scalar_at(p_n + so) : 0.f;
+      pGam = (QJL && valid) ? scalar_at(p_g + so) : 0.f;
+      if (VMSE)
+        pMeta[0] = valid ? __float_as_uint(scalar_at(p_m + so)) : 0u;
+      else
+        pMeta = valid ? *reinterpret_cast<const u32x4*>(p_m + (int64_t)it * 256 * NG * 4) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < VB; ++i) {
+        const int idx = (i * 64 + lane) * 4;  // dword index inside [2][VB][128]
+        pVw[i] = (idx < VB * kD || rem_c > 32) ? *reinterpret_cast<const u32x4*>(xv + i * 256) : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const bool v2 = 16 * ct + n < rem_c;
+#pragma unroll
+        for (int sp = 0; sp < KP; ++sp)
+          pX[ct][sp] = v2 ? *reinterpret_cast<const uint32_t*>(xk + 16 * ct * rec + sp * (kD / 8)) : 0u;
+      }
+    }
+  };
+  if (first < t_end) load_chunk(0);
+
+  int it = 0;
+  for (int64_t c0t = first; c0t < t_end; c0t += 256, ++it) {
+    const int rem = (int)(t_end - c0t < 64 ? t_end - c0t : 64);  // valid tokens of this chunk
+    // ---- stage this chunk's per-token data and value words in LDS
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    {
+      const float u = u_scale * pNrm;
+      s_ng[2 * lane] = u;
+      s_ng[2 * lane + 1] = QJL ? u * kQjlScale * pGam : 0.f;
+      if (VMSE)
+        s_meta[lane * NG] = pMeta[0];
+      else
+        *reinterpret_cast<u32x4*>(s_meta + lane * NG) = pMeta;
+#pragma unroll
+      for (int i = 0; i < VB; ++i) *reinterpret_cast<u32x4*>(s_vw + (i * 64 + lane) * 4) = pVw[i];
+    }
+    uint32_t X[4][KP];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int sp = 0; sp < KP; ++sp) X[ct][sp] = pX[ct][sp];
+    if (c0t + 256 < t_end) load_chunk(it + 1);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+
+    // ---- scores (log2 units): lane (g, n) gets tokens 16ct + 4g + r of head 4ht + n/4
+    float p[NHT][4][4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      uint32_t P[PM];
+      P[0] = X[ct][0];
+      if (PM >= 2) P[1 % PM] = X[ct][1 % KP];
+      if (PM == 4) {
+        P[2 % PM] = X[ct][2 % KP];
+        P[3 % PM] = X[ct][0] ^ X[ct][1 % KP] ^ X[ct][2 % KP];
+      }
+      i32x4 am[NHT], as[NHT];
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) am[ht] = as[ht] = i32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int pl = 0; pl < PM; ++pl) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const u32x4 A = {plane_bytes(P[pl], 4 * hf), plane_bytes(P[pl], 4 * hf + 1),
+                           plane_bytes(P[pl], 4 * hf + 2), plane_bytes(P[pl], 4 * hf + 3)};
+#pragma unroll
+          for (int ht = 0; ht < NHT; ++ht) am[ht] = mfma_i8(A, qb[ht][pl][hf], am[ht]);
+        }
+      }
+      if (QJL) {
+        const uint32_t Ps = X[ct][KP - 1];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const u32x4 A = {plane_bytes(Ps, 4 * hf), plane_bytes(Ps, 4 * hf + 1), plane_bytes(Ps, 4 * hf + 2),
+                           plane_bytes(Ps, 4 * hf + 3)};
+#pragma unroll
+          for (int ht = 0; ht < NHT; ++ht) as[ht] = mfma_i8(A, qb[ht][NPL - 1][hf], as[ht]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int u = 16 * ct + 4 * g + r;  // token inside the chunk
+        const float ut = s_ng[2 * u], wt = s_ng[2 * u + 1];
+        const bool valid = u < rem;
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht) {
+          float part = (float)am[ht][r] * (ut * k1[ht]);
+          if (QJL) part = fmaf((float)as[ht][r], wt * k2[ht], part);
+          const float sc = quad_sum(part) + fmaf(ut, c0[ht], -wt * c3[ht]);
+          p[ht][ct][r] = valid ? sc : -INFINITY;
+        }
+      }
+    }
+
+    // ---- online softmax in log2 units; alpha rescales the running sums
+    float alpha_pv[NHT];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      float mloc = p[ht][0][0];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mloc = fmaxf(mloc, p[ht][ct][r]);
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+      const float m_new = fmaxf(m_run[ht], mloc);
+      const float alpha = exp2f(m_run[ht] - m_new);
+      m_run[ht] = m_new;
+      float lsum = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = exp2f(p[ht][ct][r] - m_new);  // 0 for tokens past the end
+          p[ht][ct][r] = e;
+          lsum += e;
+        }
+      l_part[ht] = fmaf(l_part[ht], alpha, lsum);
+      // value layout: lane (g, n) accumulates head 4ht + g, held by score lane 4g
+      alpha_pv[ht] = __shfl(alpha, 4 * g);
+    }
+
+    // ---- values
+    if (!VMSE) {
+      // Rows of the value MFMA are (head 4ht + n/4, group n%4): this lane turns
+      // its 16 weights p_t delta_t(group) into signed base-256 fixed point.
+      const int grp = n & 3;
+      uint32_t mb = 0;
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) mb = max(mb, s_meta[lane * NG + gi] & 0x7fffu);
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, o));
+      const int ev = 44 - (int)(mb >> 10);  // every delta < 2^(e - 14): |W| < 2^30
+      const float inv_sv = ldexpf(1.f, -ev);
+      // tokens of dword ct sit at bit shift s = 4(ct&1) + g of the value words;
+      // their weights carry 2^-s, negated where s = 7 (the byte 0x80 reads -128)
+      const float scl0 = ldexpf(1.f, ev - g);
+      const float scl1 = g == 3 ? -ldexpf(1.f, ev - 7) : ldexpf(1.f, ev - 4 - g);
+      u32x4 A[NHT][4];
+      float M[NHT];
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) {
+        M[ht] = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const float scl = (ct & 1) ? scl1 : scl0;
+          const float rnd = scl < 0.f ? -0.5f : 0.5f;
+          uint32_t V[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t mm = s_meta[(16 * ct + 4 * g + r) * NG + grp];
+            const float dl = __half2float(__ushort_as_half((unsigned short)(mm & 0xffffu)));
+            const float mn = __half2float(__ushort_as_half((unsigned short)(mm >> 16)));
+            const float pe = p[ht][ct][r];
+            const int W = (int)fmaf(pe * scl, dl, rnd);
+            V[r] = ((uint32_t)W + 0x00808080u) ^ 0x00808080u;  // bytes = signed base-256 digits
+            M[ht] = fmaf(pe, mn, M[ht]);
+          }
+          // 4x4 byte transpose: digit plane k holds byte k of the four tokens
+          const uint32_t t01lo = __builtin_amdgcn_perm(V[1], V[0], 0x05010400u);
+          const uint32_t t01hi = __builtin_amdgcn_perm(V[1], V[0], 0x07030602u);
+          const uint32_t t23lo = __builtin_amdgcn_perm(V[3], V[2], 0x05010400u);
+          const uint32_t t23hi = __builtin_amdgcn_perm(V[3], V[2], 0x07030602u);
+          A[ht][3][ct] = __builtin_amdgcn_perm(t23lo, t01lo, 0x05040100u);  // least significant digit
+          A[ht][2][ct] = __builtin_amdgcn_perm(t23lo, t01lo, 0x07060302u);
+          A[ht][1][ct] = __builtin_amdgcn_perm(t23hi, t01hi, 0x05040100u);
+          A[ht][0][ct] = __builtin_amdgcn_perm(t23hi, t01hi, 0x07060302u);  // most significant digit
+        }
+      }
+      // sum_t p_t min_t per (head, group): reduce over the four token quarters,
+      // then fetch (head g, group gi) for the value layout
+      float Mpv[NHT][NG];
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) {
+        float x = M[ht];
+        x += __shfl_xor(x, 16);
+        x += __shfl_xor(x, 32);
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) Mpv[ht][gi] = __shfl(x, 4 * g + gi);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        const int ch = 16 * nt + n;
+        const int gi = nt >> 1;  // group of channels 16nt..16nt+15
+        int hi[NHT], lo[NHT];
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht) hi[ht] = lo[ht] = 0;
+#pragma unroll
+        for (int pv = 0; pv < VB; ++pv) {
+          u32x4 B;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) B[d] = plane_bytes(s_vw[((d >> 1) * VB + pv) * kD + ch], 4 * (d & 1) + g);
+#pragma unroll
+          for (int ht = 0; ht < NHT; ++ht) {
+            // row (head g, group gi) of the four digit products
+            const int d0 = mfma_i8(A[ht][0], B, i32x4{0, 0, 0, 0})[gi];
+            const int d1 = mfma_i8(A[ht][1], B, i32x4{0, 0, 0, 0})[gi];
+            const int d2 = mfma_i8(A[ht][2], B, i32x4{0, 0, 0, 0})[gi];
+            const int d3 = mfma_i8(A[ht][3], B, i32x4{0, 0, 0, 0})[gi];
+            hi[ht] += ((d0 << 8) + d1) << pv;  // plane pv carries weight 2^pv
+            lo[ht] += ((d2 << 8) + d3) << pv;
+          }
+        }
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht) {
+          const float v = fmaf((float)hi[ht], 65536.f, (float)lo[ht]);
+          acc[ht][nt] = fmaf(acc[ht][nt], alpha_pv[ht], fmaf(v, inv_sv, Mpv[ht][gi]));
+        }
+      }
+    } else {
+      // MSE values: weights p_t |v_t| (same for every value plane), rows (head,
+      // digit); accumulated in rotated space
+      const int mydig_shift = 7 * (3 - (n & 3));
+      uint32_t mb = s_meta[lane * NG];  // |v| as fp32 bits (non-negative: integer order is float order)
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, o));
+      int ex;
+      frexpf(__uint_as_float(mb), &ex);
+      const int ev = 26 - ex;
+      const float inv_sv = ldexpf(1.f, -ev);
+      u32x4 A[NHT];
+      float PN[NHT];
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) {
+        A[ht] = u32x4{0u, 0u, 0u, 0u};
+        PN[ht] = 0.f;
+      }
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const int s_tok = 4 * (ct & 1) + g;
+        const float sc = ldexpf(1.f, ev - s_tok);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int u = 16 * ct + 4 * g + r;
+          const float nv = __uint_as_float(s_meta[u * NG]);
+#pragma unroll
+          for (int ht = 0; ht < NHT; ++ht) {
+            const uint32_t W = (uint32_t)fmaf(p[ht][ct][r], nv * sc, 0.5f);
+            int dg = (int)((W >> mydig_shift) & 127u);
+            if (s_tok == 7) dg = -dg;
+            A[ht][ct] |= (uint32_t)(dg & 0xff) << (8 * r);
+            PN[ht] = fmaf(p[ht][ct][r], nv, PN[ht]);
+          }
+        }
+      }
+      float PNpv[NHT];
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) {
+        float x = PN[ht];
+        x += __shfl_xor(x, 16);
+        x += __shfl_xor(x, 32);
+        PNpv[ht] = __shfl(x, 4 * g);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        const int ch = 16 * nt + n;
+        float vs[NHT];
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht) vs[ht] = 0.f;
+        uint32_t Wd[4][VB];
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+          for (int pv = 0; pv < VB; ++pv) Wd[d][pv] = s_vw[((d >> 1) * VB + pv) * kD + ch];
+#pragma unroll
+        for (int pl = 0; pl < PVB; ++pl) {
+          u32x4 B;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const uint32_t w = pl < VB ? Wd[d][pl % VB] : (Wd[d][0] ^ Wd[d][1 % VB] ^ Wd[d][2 % VB]);
+            B[d] = plane_bytes(w, 4 * (d & 1) + g);
+          }
+#pragma unroll
+          for (int ht = 0; ht < NHT; ++ht) {
+            const i32x4 C = mfma_i8(A[ht], B, i32x4{0, 0, 0, 0});
+            const int hi = (C[0] << 7) + C[1], lo = (C[2] << 7) + C[3];
+            const float v = fmaf((float)hi, 16384.f, (float)lo);
+            vs[ht] = fmaf(v, a.val_w[pl], vs[ht]);
+          }
+        }
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht)
+          acc[ht][nt] = fmaf(acc[ht][nt], alpha_pv[ht], fmaf(vs[ht], inv_sv, a.val_cst * PNpv[ht]));
+      }
+    }
+  }
+
+  // ---- merge the four waves: one (m, l, acc[128]) partial per query head,
+  // with m converted back to natural-log units
+  float lsum[NHT];
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht) {
+    float x = l_part[ht];
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    lsum[ht] = x;  // score layout; the four lanes of a quad hold the same tokens
+  }
+  __syncthreads();
+  float* mrg = reinterpret_cast<float*>(smem) + wave * kStride;
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht) {
+    if (g == 0 && (n & 3) == 0) {
+      const int hh = 4 * ht + (n >> 2);
+      mrg[hh * (kD + 2)] = lsum[ht] > 0.f ? m_run[ht] * 0.6931471806f : -INFINITY;
+      mrg[hh * (kD + 2) + 1] = lsum[ht];
+    }
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) mrg[(4 * ht + g) * (kD + 2) + 2 + 16 * nt + n] = acc[ht][nt];
+  }
+  __syncthreads();
+  const float* base = reinterpret_cast<const float*>(smem);
+  for (int i = threadIdx.x; i < G * kD; i += blockDim.x) {
+    const int hh = i / kD, c = i % kD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, base[w * kStride + hh * (kD + 2)]);
+    float L = 0.f, Acc = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float mw = base[w * kStride + hh * (kD + 2)];
+        const float f = mw == -INFINITY ? 0.f : __expf(mw - M);
+        L += f * base[w * kStride + hh * (kD + 2) + 1];
+        Acc += f * base[w * kStride + hh * (kD + 2) + 2 + c];
+      }
+    }
+    float* part = a.partial + (((size_t)blockIdx.x * a.batch + b) * a.h_q + h * G + hh) * (kD + 2);
+    if (c == 0) {
+      part[0] = M;
+      part[1] = L;
+    }
+    part[2 + c] = Acc;
+  }
+}
+
+template <int PM, bool QJL, bool VMSE, int PVB, int NHT>
+hipError_t launch_scan_mfma(const DecodeArgs& a, hipStream_t st, TimedLaunch tl) {
+  if (tl.begin) (void)hipEventRecord(tl.begin, st);
+  hipLaunchKernelGGL((scan_mfma_kernel<PM, QJL, VMSE, PVB, NHT>), dim3(a.splits, a.batch * a.h_kv),
+                     dim3(kScanThreads), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (tl.end) (void)hipEventRecord(tl.end, st);
+  return e;
+}
+
+template <int NHT>
+hipError_t dispatch_mfma(const DecodeArgs& a, int kb, int qjl, int vmse, int vb, hipStream_t st,
+                         TimedLaunch tl) {
+  if (!qjl) return hipErrorNotSupported;
+  if (kb == 2 && !vmse && vb == 2) return launch_scan_mfma<2, true, false, 2, NHT>(a, st, tl);
+  if (kb == 3 && !vmse && vb == 2) return launch_scan_mfma<4, true, false, 2, NHT>(a, st, tl);
+  if (kb == 2 && vmse && vb == 3) return launch_scan_mfma<2, true, true, 4, NHT>(a, st, tl);
+  if (kb == 3 && vmse && vb == 3) return launch_scan_mfma<4, true, true, 4, NHT>(a, st, tl);
+  return hipErrorNotSupported;
+}
+
+}  // namespace
+
+size_t mfma_workspace_bytes(int batch, int h_q, int group) {
+  const int nht = (group + 3) / 4;
+  const int h_kv = h_q / group;
+  const size_t dig = (size_t)batch * h_kv * nht * 5 * 2 * 64 * 16;  // up to 5 score planes
+  const size_t cst = (size_t)batch * h_q * 4 * 4;
+  return dig + cst + 256;
+}
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, int key_mse_bits, int key_qjl, int value_mse,
+                              int value_bits, int key_planes, int value_planes, hipStream_t stream,
+                              TimedLaunch tl) {
+  // covered: QJL keys with 2- or 3-bit indices, 2-bit min/max values in groups
+  // of 32 or 3-bit MSE values, antisymmetric codebooks, up to 8 query heads per
+  // KV head
+  if (!key_qjl || (key_mse_bits != 2 && key_mse_bits != 3)) return hipErrorNotSupported;
+  if (key_planes != (1 << (key_mse_bits - 1))) return hipErrorNotSupported;
+  if (value_mse) {
+    if (value_bits != 3 || value_planes != 4) return hipErrorNotSupported;
+  } else if (value_bits != 2 || a.value_group != 32) {
+    return hipErrorNotSupported;
+  }
+  if (a.group > 8) return hipErrorNotSupported;
+  const int nht = a.group > 4 ? 2 : 1;
+  const int pm = 1 << (key_mse_bits - 1);
+  const int npl = pm + 1;
+  hipLaunchKernelGGL(qprep_mfma_kernel, dim3(a.batch * a.h_kv), dim3(256), 0, stream, a, pm, npl, nht);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = nht == 1 ? dispatch_mfma<1>(a, key_mse_bits, key_qjl, value_mse, value_bits, stream, tl)
+               : dispatch_mfma<2>(a, key_mse_bits, key_qjl, value_mse, value_bits, stream, tl);
+  if (e != hipSuccess) return e;
+  return launch_combine(a, value_mse, stream);
+}
+
+}  // namespace tq

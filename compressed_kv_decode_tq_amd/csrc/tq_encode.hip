@@ -59,16 +59,6 @@ __device__ __forceinline__ void tile_coords(const EncodeArgs& a, int tile, int& 
   blk = blk0 + r % nblk;
 }
 
-// Valid-token mask of a 32-token destination block (bit t: position 32*blk+t
-// receives a new token in this call).
-__device__ __forceinline__ uint32_t block_mask(int64_t blk, int64_t pos, int64_t n_new) {
-  const int64_t lo = pos - blk * 32, hi = pos + n_new - blk * 32;  // [lo, hi) in block coordinates
-  const int64_t a = lo < 0 ? 0 : lo, e = hi > 32 ? 32 : hi;
-  if (e <= a) return 0u;
-  const uint32_t upto = e >= 32 ? 0xffffffffu : ((1u << e) - 1u);
-  return upto & ~((1u << a) - 1u);
-}
-
 // Store one word of a value bit plane; words of partly covered blocks keep the
 // bits of tokens this call does not write.
 __device__ __forceinline__ void store_plane_word(uint32_t* p, uint32_t w, uint32_t vmask) {
@@ -121,7 +111,9 @@ __global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
     int64_t dpos[2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-      dpos[ct] = blk * 32 + 16 * ct + tc;
+      // value planes: column tc of tile ct holds the token whose bit position
+      // in the plane word is 16ct + tc, so the ballots below land in place
+      dpos[ct] = blk * 32 + (VALUE ? vslot(16 * ct + tc) : 16 * ct + tc);
       const int64_t t = dpos[ct] - pos;
       valid[ct] = t >= 0 && t < a.n_new;
       ss[ct] = 0.f;
@@ -253,7 +245,9 @@ __global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
     }
 
     if (VALUE) {
-      const uint32_t vmask = block_mask(blk, pos, a.n_new);
+      // word bit 16ct + tc belongs to column tc of tile ct: valid-token mask
+      const uint32_t vmask = (uint32_t)(__ballot(valid[0]) & 0xffffu) |
+                             ((uint32_t)(__ballot(valid[1]) & 0xffffu) << 16);
       const int64_t nblk_cap = a.capacity >> 5;
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
@@ -341,7 +335,9 @@ __global__ __launch_bounds__(256) void encode_minmax_kernel(EncodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nwaves = blockDim.x >> 6;
-  const int tok = lane & 31, half = lane >> 5;
+  // lane l (mod 32) encodes the token whose bit position in a plane word is
+  // l mod 32, so a ballot over the wave is already the plane word
+  const int tok = vslot(lane & 31), half = lane >> 5;
   for (int tile = blockIdx.x * nwaves + wave; tile < a.num_tiles; tile += gridDim.x * nwaves) {
     int b, h;
     int64_t blk;
@@ -416,7 +412,7 @@ __global__ __launch_bounds__(256) void encode_minmax_kernel(EncodeArgs a) {
         }
       }
     }
-    const uint32_t vmask = block_mask(blk, pos, a.n_new);
+    const uint32_t vmask = (uint32_t)__ballot(valid);  // bit l: lane l's token is written
     const int64_t nblk_cap = a.capacity >> 5;
 #pragma unroll
     for (int p = 0; p < BITS; ++p) {

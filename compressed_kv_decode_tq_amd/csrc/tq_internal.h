@@ -94,9 +94,23 @@ struct DecodeArgs {
   float scale;            // softmax scale tau
   float k_cent[16];
   float v_cent[16];
+  // Bit-plane expansion of the codebooks (MFMA path): c[idx] = cst + sum_p w[p] * plane_p(idx)
+  // with planes bit0, bit1, bit2, bit0^bit1^bit2 (see plane_expansion).
+  float key_w[4];
+  float key_cst;
+  float val_w[4];
+  float val_cst;
+  int8_t* qdig;           // workspace: query digit operands of the MFMA scan
+  float* qconst;          // workspace: [batch][h_q][4] per-head score constants
   SeqValues n_comp;
   SeqValues n_ring;
 };
+
+// Expansion of a symmetric codebook over bit planes: for idx = sum_k b_k 2^k,
+//   c[idx] = cst + sum_p w[p] * plane_p, plane_0..2 = b_0..b_2, plane_3 = b_0^b_1^b_2.
+// Returns the number of planes (2^(bits-1)), or 0 when the table is not
+// antisymmetric (c[2^b - 1 - i] = -c[i]) to 1e-6 relative, bits > 3, or bits < 1.
+int plane_expansion(const float* cent, int bits, float* w, float* cst);
 
 // Events recorded around one kernel launch (both null: none).
 struct TimedLaunch {
@@ -119,6 +133,15 @@ hipError_t launch_ring_append(const void* k_new, const void* v_new, int in_bf16,
                               const SeqValues& n_ring, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int key_mse_bits, int key_qjl, int value_mse,
                          int value_bits, hipStream_t stream, TimedLaunch scan);
+// MFMA decode (tq_decode_mfma.hip).  Returns hipErrorNotSupported, having
+// launched nothing, for layouts it does not cover.
+hipError_t launch_decode_mfma(const DecodeArgs& a, int key_mse_bits, int key_qjl, int value_mse,
+                              int value_bits, int key_planes, int value_planes, hipStream_t stream,
+                              TimedLaunch scan);
+// Workspace bytes of the MFMA path's query digits and constants.
+size_t mfma_workspace_bytes(int batch, int h_q, int group);
+// The combine step shared by both decode paths.
+hipError_t launch_combine(const DecodeArgs& a, int value_mse, hipStream_t stream);
 
 // Decode work split used for the workspace size and the launch.
 void decode_split(int64_t max_tokens, int64_t units, int32_t* splits, int32_t* split_len);

@@ -40,9 +40,9 @@
  *                (1 = non-negative); coordinate i is bit i%8 of byte i/8.
  *      k_norm    [batch][h_kv][capacity] scalar_dtype   |k|
  *      k_rnorm   [batch][h_kv][capacity] scalar_dtype   |r| (QJL keys only)
- *      v_planes  uint32 [batch][h_kv][capacity/32][value_bits][d]: bit t of
- *                word (blk, p, c) is bit p of the code of token 32*blk+t,
- *                channel c.
+ *      v_planes  uint32 [batch][h_kv][capacity/32][value_bits][d]: word
+ *                (blk, p, c) holds bit p of the code of token 32*blk+u,
+ *                channel c, in bit 8*(u%4) + 4*(u/16) + (u/4)%4.
  *      v_meta    fp16 [batch][h_kv][capacity][d/value_group][2] = (scale, min)
  *                (min/max values only)
  *      v_norm    [batch][h_kv][capacity] scalar_dtype   |v| (MSE values only)

@@ -12,8 +12,10 @@ Per (sequence, KV head) slot of ``capacity`` tokens:
   plane key_mse_bits holds the QJL sign bits (1 = non-negative).  Inside a
   plane, coordinate i is bit i % 8 of byte i // 8 (LSB first).
 * key norm, key residual norm   [capacity] fp32 or fp16.
-* value planes uint32 [capacity/32][value_bits][d]: word (blk, p, c) holds, in
-  bit t, bit p of the code of token 32*blk + t at channel c.
+* value planes uint32 [capacity/32][value_bits][d]: word (blk, p, c) holds bit
+  p of the code of token 32*blk + u at channel c, for u = 0..31, in bit
+  value_bit(u) = 8*(u % 4) + 4*(u // 16) + (u // 4) % 4 (a fixed permutation of
+  the 32 token slots of a block).
 * value meta (min/max values)   fp16 [capacity][d/group][2] = (scale, min).
 * value norm (MSE values)       [capacity] fp32 or fp16.
 
@@ -104,6 +106,12 @@ def unpack_key_planes(packed: np.ndarray, d: int, mse_bits: int, qjl: bool):
     return idx, (bits[:, mse_bits, :].astype(np.uint8) if qjl else None)
 
 
+def value_bit(u) -> np.ndarray:
+    """Bit position, inside a value-plane word, of token slot u (0..31) of its block."""
+    u = np.asarray(u)
+    return 8 * (u % 4) + 4 * (u // 16) + (u // 4) % 4
+
+
 def pack_value_planes(code: np.ndarray, bits: int, capacity: int | None = None) -> np.ndarray:
     """(T, d) codes -> (capacity/32, bits, d) uint32 token-transposed planes.
     Tokens T..capacity-1 are zero."""
@@ -114,11 +122,12 @@ def pack_value_planes(code: np.ndarray, bits: int, capacity: int | None = None) 
         raise ValueError("capacity must be a multiple of 32 and hold every token")
     full = np.zeros((cap, d), dtype=np.int64)
     full[:t] = code
-    blocks = full.reshape(cap // 32, 32, d)  # (blk, t, c)
+    blocks = full.reshape(cap // 32, 32, d)  # (blk, u, c)
+    pos = value_bit(np.arange(32)).astype(np.uint64)
     out = np.zeros((cap // 32, bits, d), dtype=np.uint64)
     for p in range(bits):
-        bit = ((blocks >> p) & 1).astype(np.uint64)  # (blk, t, c)
-        out[:, p, :] = np.sum(bit << np.arange(32, dtype=np.uint64)[None, :, None], axis=1)
+        bit = ((blocks >> p) & 1).astype(np.uint64)  # (blk, u, c)
+        out[:, p, :] = np.sum(bit << pos[None, :, None], axis=1)
     return out.astype(np.uint32)
 
 
@@ -126,7 +135,7 @@ def unpack_value_planes(words: np.ndarray, n_tokens: int) -> np.ndarray:
     """(capacity/32, bits, d) uint32 -> (n_tokens, d) codes."""
     w = np.asarray(words, dtype=np.uint64)
     nblk, bits, d = w.shape
-    tt = np.arange(32, dtype=np.uint64)
+    tt = value_bit(np.arange(32)).astype(np.uint64)
     code = np.zeros((nblk, 32, d), dtype=np.int64)
     for p in range(bits):
         code |= (((w[:, p, None, :] >> tt[None, :, None]) & 1).astype(np.int64)) << p

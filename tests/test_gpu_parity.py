@@ -204,11 +204,16 @@ def _decode_case(w, n_comp, n_ring, tag, steps_kv=None):
     return got
 
 
+@pytest.mark.parametrize("path", ["mfma", "generic"])
 @pytest.mark.parametrize("name", list(SMALL))
-def test_decode_parity(name):
+def test_decode_parity(name, path, monkeypatch):
+    """Both decode paths: the int8-MFMA bit-plane scan (taken for symmetric
+    codebooks) and the generic scan (forced with TQ_DECODE_PATH=generic)."""
+    if path == "generic":
+        monkeypatch.setenv("TQ_DECODE_PATH", "generic")
     w = SMALL[name]
     nr = [1] * w.batch if w.ring_cap else [0] * w.batch
-    _decode_case(w, [w.n_tokens] * w.batch, nr, name)
+    _decode_case(w, [w.n_tokens] * w.batch, nr, f"{name} ({path})")
 
 
 def test_decode_ragged_lengths_and_ring_sizes():
@@ -216,6 +221,15 @@ def test_decode_ragged_lengths_and_ring_sizes():
     _decode_case(w, [0, 37, 1000, 513, 64], [5, 0, 128, 127, 1], "ragged minmax")
     w = SMALL["long_small"].replace(batch=3, n_tokens=700)
     _decode_case(w, [700, 1, 256], [0, 0, 0], "ragged mse")
+
+
+def test_decode_layouts_outside_the_mfma_path():
+    """Layouts the MFMA scan does not cover run on the generic scan."""
+    base = SMALL["batched_small"].replace(batch=2, n_tokens=300)
+    _decode_case(base.replace(key_mse_bits=1, value_bits=4, value_group=16), [300, 200], [2, 0], "k1 v4 g16")
+    _decode_case(base.replace(key_mse_bits=4, value_bits=1, value_group=64), [300, 5], [0, 1], "k4 v1 g64")
+    _decode_case(base.replace(key_qjl=0), [300, 256], [1, 1], "no qjl")
+    _decode_case(SMALL["long_small"].replace(value_bits=2, n_tokens=300), [300], [0], "mse v2")
 
 
 def test_decode_empty_sequence_gives_zero():

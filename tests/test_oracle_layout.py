@@ -40,11 +40,19 @@ def test_value_planes_round_trip_and_bit_positions():
         assert words.shape == (3, bits, 128) and words.dtype == np.uint32
         assert np.array_equal(oracle.unpack_value_planes(words, 70), code)
         assert np.all(oracle.unpack_value_planes(words, 96)[70:] == 0)
-    # worked example: token 33 (block 1, bit 1), channel 5, code 3 = planes 0 and 1
+    # the token slots of a block map one to one onto the 32 bits of a word
+    from oracle.layout import value_bit
+    assert sorted(value_bit(np.arange(32)).tolist()) == list(range(32))
+    # worked examples: token 33 (block 1, slot 1 -> bit 8*1 = 8), channel 5,
+    # code 3 = planes 0 and 1; token 22 (block 0, slot 22 -> 8*2 + 4*1 + 1 = 21),
+    # channel 0, code 2 = plane 1 only
     code = np.zeros((64, 128), dtype=np.int64)
     code[33, 5] = 3
+    code[22, 0] = 2
     w = oracle.pack_value_planes(code, 2)
-    assert w[1, 0, 5] == 2 and w[1, 1, 5] == 2 and np.count_nonzero(w) == 2
+    assert w[1, 0, 5] == 1 << 8 and w[1, 1, 5] == 1 << 8
+    assert w[0, 1, 0] == 1 << 21 and w[0, 0, 0] == 0
+    assert np.count_nonzero(w) == 3
 
 
 def _gold(golden_dir):

@@ -117,10 +117,12 @@ def read_key_planes(planes: np.ndarray, d: int, mse_bits: int, qjl: bool):
 
 
 def read_value_planes(words: np.ndarray, n_tokens: int) -> np.ndarray:
-    """Codes [n_tokens, d] from token-transposed words [blocks, bits, d]."""
+    """Codes [n_tokens, d] from token-transposed words [blocks, bits, d]; token
+    slot u of a block sits in bit 8*(u%4) + 4*(u//16) + (u//4)%4 of its word."""
     w = np.ascontiguousarray(words).view(np.uint32).astype(np.uint64)
     nblk, bits, d = w.shape
-    t = np.arange(32, dtype=np.uint64)
+    u = np.arange(32)
+    t = (8 * (u % 4) + 4 * (u // 16) + (u // 4) % 4).astype(np.uint64)
     code = np.zeros((nblk, 32, d), dtype=np.int64)
     for p in range(bits):
         code |= ((w[:, p, None, :] >> t[None, :, None]) & 1).astype(np.int64) << p
