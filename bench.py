@@ -77,10 +77,17 @@ def _source_sha(*names):
     return h.hexdigest()[:16]
 
 
-def _traffic(kernel: str, sha: str, launches_per_unit: float = 1.0):
-    """HBM traffic per launch from committed rocprofv3 PMC summaries, or None
+SCAN_KERNEL = "scan_mfma_kernel"
+
+
+def _traffic_path(kernel: str, workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+
+
+def _traffic(kernel: str, workload: str, sha: str):
+    """HBM bytes per launch from a committed rocprofv3 PMC summary, or None
     when absent or taken on a different kernel source."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
+    path = _traffic_path(kernel, workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -88,6 +95,62 @@ def _traffic(kernel: str, sha: str, launches_per_unit: float = 1.0):
     if t.get("source_sha") != sha:
         return None
     return t.get("bytes_per_launch")
+
+
+def _pmc_rows(d: str, counter: str):
+    """(kernel name, value) per dispatch from a rocprofv3 --pmc csv run under d."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    per = {}
+    for fn in files:
+        with open(fn, newline="") as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") != counter:
+                    continue
+                key = (fn, r["Dispatch_Id"])
+                name, val = per.get(key, (r["Kernel_Name"], 0.0))
+                per[key] = (name, val + float(r["Counter_Value"]))
+    return list(per.values())
+
+
+def pmc_summary(args):
+    """Scale the scan kernel's FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what
+    the same counters read for the known-size probe (y = -x over M MiB: M MiB
+    read, M MiB written), and store bytes per launch under profiles/."""
+    fetch_dir, write_dir = args.pmc_summary
+    with open(os.path.join(fetch_dir, "bench.json")) as f:
+        run = json.loads([l for l in f if l.startswith("{")][-1])
+    mib = run["copy_probe_mib"]
+    probe_bytes = float(mib) * (1 << 20)
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _pmc_rows(d, counter)
+        probe = [v for n, v in rows if "neg" in n.lower()]
+        scan = [v for n, v in rows if SCAN_KERNEL in n]
+        if not probe or not scan:
+            raise SystemExit(f"{counter}: probe dispatches {len(probe)}, scan dispatches {len(scan)}; kernels seen: "
+                             + ", ".join(sorted({n[:60] for n, _ in rows})))
+        probe_kib = sorted(probe)[len(probe) // 2]
+        factor = probe_bytes / (probe_kib * 1024.0)
+        scan_kib = sum(scan) / len(scan)
+        out[counter] = {"scan_kib_per_dispatch": scan_kib, "scan_dispatches": len(scan),
+                        "probe_kib_per_dispatch": probe_kib, "probe_dispatches": len(probe),
+                        "factor": factor, "bytes_per_launch": scan_kib * 1024.0 * factor}
+    total = out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"]
+    alg = run["roofline"]["algorithmic_bytes_per_launch"]
+    wname = run["config"]["workload"]
+    summary = {"kernel": SCAN_KERNEL, "workload": wname, "source_sha": run["roofline"]["source_sha"],
+               "bytes_per_launch": int(total), "algorithmic_bytes_per_launch": alg,
+               "traffic_over_algorithmic": round(total / alg, 4), "copy_probe_mib": mib,
+               "counters": out, "command": args.pmc_command}
+    path = _traffic_path(SCAN_KERNEL, wname)
+    with open(path, "w") as f:
+        json.dump(summary, f, indent=1)
+        f.write("\n")
+    print(json.dumps(summary, indent=1))
 
 
 def cpu_baseline(w, seconds_budget: float = 25.0):
@@ -152,7 +215,17 @@ def main():
     ap.add_argument("--workload", default="batched-b32-hkv8-n32768")
     ap.add_argument("--encode-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="first run a plain elementwise kernel (y = -x, fp32) over this many MiB, "
+                         "the known-size reference for HBM byte counters")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU work: turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) "
+                         "made with --copy-probe-mib into the decode scan's traffic summary under profiles/")
+    ap.add_argument("--pmc-command", default="", help="the rocprofv3 command line, recorded in the summary")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
               f"(the path shards by KV head or sequence with no communication, but no multi-GPU run is made).",
@@ -166,6 +239,13 @@ def main():
 
     w = wl.by_name(args.workload)
     dev = "cuda"
+    if args.copy_probe_mib:
+        x = torch.ones(args.copy_probe_mib << 18, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            torch.neg(x, out=y)
+        torch.cuda.synchronize()
+        del x, y
     lay = tq.Layout(head_dim=w.d, key_mse_bits=w.key_mse_bits, key_qjl=w.key_qjl,
                     value_kind=tq.TQ_V_MINMAX if w.value_kind == "minmax" else tq.TQ_V_MSE,
                     value_bits=w.value_bits, value_group=w.value_group,
@@ -267,9 +347,10 @@ def main():
     scan_avg_bytes = sum(scan_bytes) / len(scan_bytes)
     scan_gbs = scan_avg_bytes / (scan_avg_ms * 1e-3) / 1e9
     sha = _source_sha("tq_decode_mfma.hip", "tq_decode.hip", "tq_common.h", "tq_internal.h")
-    traffic = _traffic("decode_scan", sha)
+    generic = os.environ.get("TQ_DECODE_PATH") == "generic"
+    traffic = None if generic else _traffic(SCAN_KERNEL, w.name, sha)
     scan_kernel_name = ("scan_kernel (VALU split scan over the compressed cache)"
-                        if os.environ.get("TQ_DECODE_PATH") == "generic"
+                        if generic
                         else "scan_mfma_kernel (int8-MFMA split scan over the compressed cache)")
 
     res = {
@@ -288,7 +369,7 @@ def main():
                      "achieved": round(scan_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(scan_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "avg_launch_ms": round(scan_avg_ms, 5),
-                     "algorithmic_bytes_per_launch": int(scan_avg_bytes)},
+                     "algorithmic_bytes_per_launch": int(scan_avg_bytes), "source_sha": sha},
         "encode": {"tokens_per_s": round(enc_tokens_per_s, 1), "ms_per_bulk_encode": round(enc_wall * 1e3, 3),
                    "tokens": w.batch * w.n_tokens, "key_vectors": n_vec,
                    "roofline": {"kernel": "encode_rot_kernel (keys: Pi and S' rotations)", "bound": "mfma",
@@ -297,6 +378,8 @@ def main():
                                 "avg_launch_ms": round(enc_key_ms, 4),
                                 "note": "algorithmic flops 4 d^2 per key vector; the split-bf16 passes issue 2.5x that"}},
     }
+    if args.copy_probe_mib:
+        res["copy_probe_mib"] = args.copy_probe_mib
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (float64 oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w)
