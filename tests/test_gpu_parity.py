@@ -13,8 +13,8 @@ import torch
 import oracle
 from compressed_kv_decode_tq_amd import tq
 from compressed_kv_decode_tq_amd import workloads as wl
-from tq_testlib import (OUT_RTOL, WINDOW, books, dequant_slot, encode_slot, key_plane_mismatches,
-                        layout_of, max_rel_err, read_key_planes, read_value_planes, say, upload_slot)
+from tq_testlib import (OUT_RTOL, books, check_encode_slot, dequant_slot, encode_slot, key_plane_mismatches,
+                        layout_of, max_rel_err, read_value_planes, say, upload_slot)
 
 pytestmark = pytest.mark.gpu
 
@@ -43,63 +43,6 @@ def _params(w):
     return pi, s, tq.Params(layout_of(w), pi, s, device=DEV)
 
 
-def _check_encode_slot(w, bk, cache, b, h, ref, start, n, tag):
-    """Compare the device cache slot (b, h) positions start..start+n-1 with the
-    oracle code `ref`; returns excused counts."""
-    lay = layout_of(w)
-    kp = cache.k_planes[b, h, start:start + n].cpu().numpy()
-    bad, ex_m, ex_q = key_plane_mismatches(w, bk, kp, ref.key)
-    assert bad == 0, f"{tag}: {bad} key bits differ outside the {WINDOW} window"
-    flip = np.any(read_key_planes_mask(w, bk, kp, ref), axis=1)
-    f16 = w.scalar_dtype == "f16"
-    kn = cache.k_norm[b, h, start:start + n].float().cpu().double().numpy()
-    if f16:
-        ulp = np.spacing(ref.key.norm.astype(np.float16)).astype(np.float64)
-        assert np.all(np.abs(kn - ref.key.norm) <= ulp * 1.01), tag
-    else:
-        assert np.max(np.abs(kn - ref.key.norm) / np.maximum(ref.key.norm, 1e-30)) <= 1e-6, tag
-    if w.key_qjl:
-        kr = cache.k_rnorm[b, h, start:start + n].float().cpu().double().numpy()
-        ok = ~flip
-        if f16:
-            ulp = np.spacing(ref.key.rnorm.astype(np.float16)).astype(np.float64)
-            assert np.all(np.abs(kr - ref.key.rnorm)[ok] <= ulp[ok] * 1.01), tag
-        else:
-            # the rotation uses Pi = Pi_hi + Pi_lo in bf16 (each entry within
-            # 2^-18 |Pi_ij|), and fp32 inputs are split the same way, so
-            # |dr| <= 2 * 2^-18 * |Pi|_F = 2^-17 sqrt(d) bounds |d gamma|
-            bound = 2.0 ** -17 * np.sqrt(w.d)
-            assert np.all(np.abs(kr - ref.key.rnorm)[ok] <= bound), (tag, np.max(np.abs(kr - ref.key.rnorm)[ok]))
-    # values
-    blk0 = start // 32
-    nblk = (start + n + 31) // 32 - blk0
-    words = cache.v_planes[b, h, blk0:blk0 + nblk].cpu().numpy()
-    codes = read_value_planes(words, nblk * 32)[start - blk0 * 32: start - blk0 * 32 + n]
-    if w.value_kind == "minmax":
-        assert np.array_equal(codes, ref.val.code), f"{tag}: min/max codes differ"
-        meta = cache.v_meta[b, h, start:start + n].cpu().numpy()
-        assert np.array_equal(meta[..., 0].view(np.uint16), ref.val.scale16.view(np.uint16)), tag
-        assert np.array_equal(meta[..., 1].view(np.uint16), ref.val.min16.view(np.uint16)), tag
-        ex_v = 0
-    else:
-        bad_v = codes != ref.val.idx
-        near = np.min(np.abs(ref.val.y[..., None] - bk.v.thresholds[None, None, :]), axis=-1) < WINDOW
-        assert np.sum(bad_v & ~near) == 0, f"{tag}: MSE value codes differ outside the window"
-        ex_v = int(np.sum(bad_v))
-        vn = cache.v_norm[b, h, start:start + n].float().cpu().double().numpy()
-        if f16:
-            ulp = np.spacing(ref.val.norm.astype(np.float16)).astype(np.float64)
-            assert np.all(np.abs(vn - ref.val.norm) <= ulp * 1.01), tag
-        else:
-            assert np.max(np.abs(vn - ref.val.norm) / np.maximum(ref.val.norm, 1e-30)) <= 1e-6, tag
-    return ex_m, ex_q, ex_v
-
-
-def read_key_planes_mask(w, bk, kp, ref):
-    idx_g, _ = read_key_planes(kp, w.d, w.key_mse_bits, bool(w.key_qjl))
-    return idx_g != ref.key.idx
-
-
 @pytest.mark.parametrize("name", list(SMALL))
 def test_encode_parity(name):
     w = SMALL[name]
@@ -115,7 +58,7 @@ def test_encode_parity(name):
     for b in range(w.batch):
         for h in range(w.h_kv):
             ref = encode_slot(w, bk, pi, s, k[b, :, h].double().numpy(), v[b, :, h].double().numpy())
-            tot += _check_encode_slot(w, bk, cache, b, h, ref, 0, w.n_tokens, f"{name} b{b} h{h}")
+            tot += check_encode_slot(w, bk, cache, b, h, ref, 0, w.n_tokens, f"{name} b{b} h{h}")
     n_coord = w.batch * w.h_kv * w.n_tokens * w.d
     say(f"  excused flips: key MSE {tot[0]}, key QJL {tot[1]}, value MSE {tot[2]} of {n_coord} coordinates")
 
@@ -151,7 +94,7 @@ def test_encode_ragged_positions_preserve_neighbours(value_kind):
             vbh = read_value_planes(before["v_planes"][b, h].cpu().numpy(), cap)
             assert np.array_equal(va[mask.numpy()], vbh[mask.numpy()])
             ref = encode_slot(w, bk, pi, s, k[b, :, h].double().numpy(), v[b, :, h].double().numpy())
-            _check_encode_slot(w, bk, cache, b, h, ref, p0, 77, f"ragged b{b} h{h}")
+            check_encode_slot(w, bk, cache, b, h, ref, p0, 77, f"ragged b{b} h{h}")
 
 
 def _oracle_cache(w, bk, pi, s, k, v, n_comp):

@@ -148,3 +148,77 @@ def key_plane_mismatches(w: wl.Workload, bk: OracleBooks, gpu_planes: np.ndarray
         unexcused += int(np.sum(q_bad & ~ok))
         excused_qjl = int(np.sum(q_bad & ok))
     return unexcused, excused_mse, excused_qjl
+
+
+def check_encode_slot(w, bk, cache, b, h, ref, start, n, tag):
+    """Compare the device cache slot (b, h) positions start..start+n-1 with the
+    oracle code `ref`; returns excused counts."""
+    kp = cache.k_planes[b, h, start:start + n].cpu().numpy()
+    bad, ex_m, ex_q = key_plane_mismatches(w, bk, kp, ref.key)
+    assert bad == 0, f"{tag}: {bad} key bits differ outside the {WINDOW} window"
+    flip = np.any(_flip_mask(w, bk, kp, ref), axis=1)
+    f16 = w.scalar_dtype == "f16"
+    kn = cache.k_norm[b, h, start:start + n].float().cpu().double().numpy()
+    if f16:
+        ulp = np.spacing(ref.key.norm.astype(np.float16)).astype(np.float64)
+        assert np.all(np.abs(kn - ref.key.norm) <= ulp * 1.01), tag
+    else:
+        assert np.max(np.abs(kn - ref.key.norm) / np.maximum(ref.key.norm, 1e-30)) <= 1e-6, tag
+    if w.key_qjl:
+        kr = cache.k_rnorm[b, h, start:start + n].float().cpu().double().numpy()
+        ok = ~flip
+        if f16:
+            ulp = np.spacing(ref.key.rnorm.astype(np.float16)).astype(np.float64)
+            assert np.all(np.abs(kr - ref.key.rnorm)[ok] <= ulp[ok] * 1.01), tag
+        else:
+            # the rotation uses Pi = Pi_hi + Pi_lo in bf16 (each entry within
+            # 2^-18 |Pi_ij|), and fp32 inputs are split the same way, so
+            # |dr| <= 2 * 2^-18 * |Pi|_F = 2^-17 sqrt(d) bounds |d gamma|
+            bound = 2.0 ** -17 * np.sqrt(w.d)
+            assert np.all(np.abs(kr - ref.key.rnorm)[ok] <= bound), (tag, np.max(np.abs(kr - ref.key.rnorm)[ok]))
+    # values
+    blk0 = start // 32
+    nblk = (start + n + 31) // 32 - blk0
+    words = cache.v_planes[b, h, blk0:blk0 + nblk].cpu().numpy()
+    codes = read_value_planes(words, nblk * 32)[start - blk0 * 32: start - blk0 * 32 + n]
+    if w.value_kind == "minmax":
+        assert np.array_equal(codes, ref.val.code), f"{tag}: min/max codes differ"
+        meta = cache.v_meta[b, h, start:start + n].cpu().numpy()
+        assert np.array_equal(meta[..., 0].view(np.uint16), ref.val.scale16.view(np.uint16)), tag
+        assert np.array_equal(meta[..., 1].view(np.uint16), ref.val.min16.view(np.uint16)), tag
+        ex_v = 0
+    else:
+        bad_v = codes != ref.val.idx
+        near = np.min(np.abs(ref.val.y[..., None] - bk.v.thresholds[None, None, :]), axis=-1) < WINDOW
+        assert np.sum(bad_v & ~near) == 0, f"{tag}: MSE value codes differ outside the window"
+        ex_v = int(np.sum(bad_v))
+        vn = cache.v_norm[b, h, start:start + n].float().cpu().double().numpy()
+        if f16:
+            ulp = np.spacing(ref.val.norm.astype(np.float16)).astype(np.float64)
+            assert np.all(np.abs(vn - ref.val.norm) <= ulp * 1.01), tag
+        else:
+            assert np.max(np.abs(vn - ref.val.norm) / np.maximum(ref.val.norm, 1e-30)) <= 1e-6, tag
+    return ex_m, ex_q, ex_v
+
+
+def _flip_mask(w, bk, kp, ref):
+    idx_g, _ = read_key_planes(kp, w.d, w.key_mse_bits, bool(w.key_qjl))
+    return idx_g != ref.key.idx
+
+
+def slot_from_cache(w: wl.Workload, cache: tq.Cache, b: int, h: int, n: int) -> SlotCode:
+    """The codes of device cache slot (b, h), positions 0..n-1, read back into
+    the oracle's code records (so the oracle can decode a GPU-encoded cache)."""
+    kp = cache.k_planes[b, h, :n].cpu().numpy()
+    idx, qjl = read_key_planes(kp, w.d, w.key_mse_bits, bool(w.key_qjl))
+    norm = cache.k_norm[b, h, :n].float().cpu().double().numpy()
+    rnorm = cache.k_rnorm[b, h, :n].float().cpu().double().numpy() if w.key_qjl else None
+    key = oracle.KeyCode(idx=idx, qjl=qjl, norm=norm, rnorm=rnorm, y=None, z=None)
+    codes = read_value_planes(cache.v_planes[b, h, :(n + 31) // 32].cpu().numpy(), n)
+    if w.value_kind == "minmax":
+        meta = cache.v_meta[b, h, :n].cpu().numpy()
+        val = oracle.ValueMinMax(code=codes, scale16=meta[..., 0].copy(), min16=meta[..., 1].copy(), ratio=None)
+    else:
+        vn = cache.v_norm[b, h, :n].float().cpu().double().numpy()
+        val = oracle.ValueMSE(idx=codes, norm=vn, y=None)
+    return SlotCode(key, val)
