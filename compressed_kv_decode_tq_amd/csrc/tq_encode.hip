@@ -22,7 +22,7 @@ namespace tq {
 namespace {
 
 constexpr int kLdsStride = kD + 8;  // bf16 elements per LDS row (16 B pad: no bank conflicts)
-constexpr int kEncThreads = 256;    // 4 waves; each wave encodes one 32-token tile at a time
+constexpr int kEncThreads = 512;    // 8 waves (2 per SIMD); each wave encodes one 32-token tile at a time
 
 // Derive the bf16 operands from Pi and S (fp32, row-major [128][128]).
 __global__ void prepare_params_kernel(const float* __restrict__ pi, const float* __restrict__ s,
@@ -68,7 +68,29 @@ __device__ __forceinline__ void store_plane_word(uint32_t* p, uint32_t w, uint32
     *p = (*p & ~vmask) | (w & vmask);
 }
 
-// Rotation-based encode of one 32-token tile per wave.
+// Two fp32 values rounded to bf16 (nearest even), packed low | high << 16.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
+}
+
+// Bit p of the Lloyd-Max index from the threshold tests gt[k] = (y > t_k).
+// The tests are monotone (gt[k] implies gt[k-1]), so idx = sum_k gt[k] and
+// bit p of idx flips exactly at the tests k with k + 1 a multiple of 2^p:
+// bit p = XOR of gt[k] over k = 2^p - 1 (mod 2^p).
+template <int LV>
+__device__ __forceinline__ bool index_bit(const bool (&gt)[LV - 1], int p) {
+  bool x = false;
+#pragma unroll
+  for (int k = 0; k < LV - 1; ++k)
+    if (((k + 1) & ((1 << p) - 1)) == 0) x ^= gt[k];
+  return x;
+}
+
+// Rotation-based encode: each wave encodes one 32-token tile at a time (two
+// 16-token column tiles of the MFMA), eight waves of a work-group share the
+// bf16 split matrices staged in LDS.
 //   VALUE = false: TurboQuantProd keys (MSE_BITS-bit Lloyd-Max + QJL if QJL),
 //                  token-major key planes, |k| and |r|.
 //   VALUE = true : TurboQuant-MSE values, token-transposed value planes, |v|.
@@ -88,8 +110,11 @@ __global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
   }
   __syncthreads();
 
-  const float* cent = VALUE ? a.v_cent : a.k_cent;
-  const float* thr = VALUE ? a.v_thr : a.k_thr;
+  float cent[LV], thr[LV - 1];
+#pragma unroll
+  for (int k = 0; k < LV; ++k) cent[k] = VALUE ? a.v_cent[k] : a.k_cent[k];
+#pragma unroll
+  for (int k = 0; k < LV - 1; ++k) thr[k] = VALUE ? a.v_thr[k] : a.k_thr[k];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nwaves = blockDim.x >> 6;
@@ -128,8 +153,9 @@ __global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
           kin[ct][ks] = x;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float lo = bf2f(x[e] & 0xffffu), hi = bf2f(x[e] >> 16);
-            ss[ct] += lo * lo + hi * hi;
+            const float lo = __uint_as_float(x[e] << 16), hi = __uint_as_float(x[e] & 0xffff0000u);
+            ss[ct] = fmaf(lo, lo, ss[ct]);
+            ss[ct] = fmaf(hi, hi, ss[ct]);
           }
         } else {
           const float* fp = reinterpret_cast<const float*>(src) + row * kD + c0;
@@ -138,11 +164,12 @@ __global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
           for (int e = 0; e < 8; ++e) f[e] = valid[ct] ? fp[e] : 0.f;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const uint32_t h0 = f2bf(f[2 * e]), h1 = f2bf(f[2 * e + 1]);
-            const uint32_t l0 = f2bf(f[2 * e] - bf2f(h0)), l1 = f2bf(f[2 * e + 1] - bf2f(h1));
-            kin[ct][ks][e] = h0 | (h1 << 16);
-            klo[ct][ks][e] = l0 | (l1 << 16);
-            ss[ct] += f[2 * e] * f[2 * e] + f[2 * e + 1] * f[2 * e + 1];
+            const uint32_t hp = pack_bf16x2(f[2 * e], f[2 * e + 1]);
+            kin[ct][ks][e] = hp;
+            klo[ct][ks][e] = pack_bf16x2(f[2 * e] - __uint_as_float(hp << 16),
+                                         f[2 * e + 1] - __uint_as_float(hp & 0xffff0000u));
+            ss[ct] = fmaf(f[2 * e], f[2 * e], ss[ct]);
+            ss[ct] = fmaf(f[2 * e + 1], f[2 * e + 1], ss[ct]);
           }
         }
       }
@@ -157,14 +184,16 @@ __global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
       inv[ct] = nrm[ct] > 0.f ? 1.0f / nrm[ct] : 0.f;
     }
 
-    // ---- GEMM 1: Y = Pi K^T (row tile rt = coordinates 16rt..16rt+15); bucketing
-    uint32_t words[NP][2][4];  // [plane][ct][m]: bits of coordinates 32m..32m+31
+    // ---- GEMM 1: Y = Pi K^T (row tile rt = coordinates 16rt..16rt+15); bucketing.
+    // Plane bits are gathered lane-locally first: bit (rt&1)*4 + rr of lw[p][ct][rt/2]
+    // is coordinate 16rt + 4g + rr of token 16ct + tc.
+    uint32_t lw[NP][2][4];
 #pragma unroll
     for (int p = 0; p < NP; ++p)
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-        for (int m = 0; m < 4; ++m) words[p][ct][m] = 0u;
+        for (int m = 0; m < 4; ++m) lw[p][ct][m] = 0u;
     u32x4 rhi[2][4], rlo[2][4];
     float gg[2] = {0.f, 0.f};
     uint32_t vw[VALUE ? NP : 1][2];  // value planes: words of channels lane and lane+64
@@ -187,59 +216,64 @@ __global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
           if (!IN_BF16) acc[ct] = mfma_bf16(ahi, klo[ct][ks], acc[ct]);
         }
       }
-      int idxs[2][4];
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
+        // one column tile's bucketing at a time keeps few lane masks live
+        __builtin_amdgcn_sched_barrier(0);
+        float res[4];
+        bool bits[4][MSE_BITS];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
+          __builtin_amdgcn_sched_barrier(0);
           const float y = acc[ct][rr] * inv[ct];
-          int idx = 0;
+          bool gt[LV - 1];
           float c = cent[0];
 #pragma unroll
           for (int k = 0; k < LV - 1; ++k) {
-            const bool gt = y > thr[k];
-            idx += gt ? 1 : 0;
-            c = gt ? cent[k + 1] : c;
+            gt[k] = y > thr[k];
+            c = gt[k] ? cent[k + 1] : c;
           }
-          idxs[ct][rr] = idx;
-          const int bit = (rt & 1) * 16 + 4 * g + rr;
-          if (!VALUE) {
 #pragma unroll
-            for (int p = 0; p < MSE_BITS; ++p) words[p][ct][rt >> 1] |= (uint32_t)((idx >> p) & 1) << bit;
-          }
-          if (QJL) {
-            const float res = y - c;
-            gg[ct] += res * res;
-            const uint32_t rh = f2bf(res), rl = f2bf(res - bf2f(rh));
-            const int e = (rt & 1) * 4 + rr;  // element of the k-step rt/2 B operand
-            const int sh = (e & 1) * 16;
-            if ((e & 1) == 0) {
-              rhi[ct][rt >> 1][e >> 1] = rh;
-              rlo[ct][rt >> 1][e >> 1] = rl;
-            } else {
-              rhi[ct][rt >> 1][e >> 1] |= rh << sh;
-              rlo[ct][rt >> 1][e >> 1] |= rl << sh;
+          for (int p = 0; p < MSE_BITS; ++p) bits[rr][p] = index_bit<LV>(gt, p);
+          res[rr] = y - c;
+          if (!VALUE) {
+            const int j = (rt & 1) * 4 + rr;
+#pragma unroll
+            for (int p = 0; p < MSE_BITS; ++p) {
+              lw[p][ct][rt >> 1] |= bits[rr][p] ? (1u << j) : 0u;
+              // fold the bit in now: a lane mask kept for later would hold two SGPRs
+              asm volatile("" : "+v"(lw[p][ct][rt >> 1]));
             }
           }
         }
-      }
-      if (VALUE) {
-        // token-transposed planes: one ballot gives, in bits 16g'..16g'+15, the
-        // bit of channel 16rt + 4g' + rr for the 16 tokens of a column tile
+        if (QJL) {
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
+          for (int rr = 0; rr < 4; ++rr) gg[ct] = fmaf(res[rr], res[rr], gg[ct]);
+          // element e = (rt&1)*4 + rr of the k-step rt/2 B operand of GEMM 2
 #pragma unroll
-          for (int p = 0; p < NP; ++p) {
-            const uint64_t m0 = __ballot((idxs[0][rr] >> p) & 1);
-            const uint64_t m1 = __ballot((idxs[1][rr] >> p) & 1);
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-              const int ch = 16 * rt + 4 * gq + rr;
-              const uint32_t w = (uint32_t)((m0 >> (16 * gq)) & 0xffffu) |
-                                 ((uint32_t)((m1 >> (16 * gq)) & 0xffffu) << 16);
-              if (lane == (ch & 63)) vw[p][ch >> 6] = w;
-            }
+          for (int hp = 0; hp < 2; ++hp) {
+            const float r0 = res[2 * hp], r1 = res[2 * hp + 1];
+            const uint32_t hi = pack_bf16x2(r0, r1);
+            const uint32_t lo = pack_bf16x2(r0 - __uint_as_float(hi << 16), r1 - __uint_as_float(hi & 0xffff0000u));
+            rhi[ct][rt >> 1][(rt & 1) * 2 + hp] = hi;
+            rlo[ct][rt >> 1][(rt & 1) * 2 + hp] = lo;
           }
+        }
+        if (VALUE) {
+          // token-transposed planes: one ballot gives, in bits 16g'..16g'+15, the
+          // bit of channel 16rt + 4g' + rr for the 16 tokens of column tile ct
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+              const uint64_t m = __ballot(bits[rr][p]);
+#pragma unroll
+              for (int gq = 0; gq < 4; ++gq) {
+                const int ch = 16 * rt + 4 * gq + rr;
+                const uint32_t w = (uint32_t)((m >> (16 * gq)) & 0xffffu) << (16 * ct);
+                if (lane == (ch & 63)) vw[p][ch >> 6] |= w;
+              }
+            }
         }
       }
     }
@@ -290,18 +324,24 @@ __global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr)
-            words[NP - 1][ct][rt >> 1] |= (z[ct][rr] >= 0.f ? 1u : 0u) << ((rt & 1) * 16 + 4 * g + rr);
+          for (int rr = 0; rr < 4; ++rr) {
+            lw[NP - 1][ct][rt >> 1] |= z[ct][rr] >= 0.f ? (1u << ((rt & 1) * 4 + rr)) : 0u;
+            asm volatile("" : "+v"(lw[NP - 1][ct][rt >> 1]));
+          }
       }
     }
 
-    // ---- gather plane words: lane group g ends with the word of coordinates 32g..32g+31
+    // ---- plane words: spread the lane-local bits to coordinate positions
+    // 4g + j (j < 4) and 16 + 4g + j - 4, then gather so that lane group g ends
+    // with the word of coordinates 32g..32g+31
     const size_t rec = (size_t)NP * (kD / 8);
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        const uint32_t* w = words[p][ct];
+        uint32_t w[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) w[m] = ((lw[p][ct][m] & 0xfu) | ((lw[p][ct][m] & 0xf0u) << 12)) << (4 * g);
         uint32_t ka = (g & 2) ? w[2] : w[0], kb = (g & 2) ? w[3] : w[1];
         const uint32_t sa = (g & 2) ? w[0] : w[2], sb = (g & 2) ? w[1] : w[3];
         ka |= __shfl_xor(sa, 32);
