@@ -15,13 +15,21 @@
 // add a third pass with k split into hi + lo.  The residual is fp32, so the QJL
 // GEMM uses three passes (S' hi/lo x r hi/lo, dropping lo x lo).  fp32
 // accumulation throughout.
+#include <type_traits>
+
 #include "tq_common.h"
 #include "tq_internal.h"
 
 namespace tq {
 namespace {
 
-constexpr int kLdsStride = kD + 8;  // bf16 elements per LDS row (16 B pad: no bank conflicts)
+// LDS holds each bf16 matrix as 128 rows of 16 16-byte chunks; chunk c of row r
+// sits in slot c ^ 8*((c >> 1) & 1) ^ (r & 15).  The MFMA operand reads (lane
+// (g, tc) takes chunk 4ks + g of row 16rt + tc) then fall on distinct banks
+// within every group of lanes the LDS serves together.
+__host__ __device__ constexpr int lds_slot(int row, int chunk) {
+  return (chunk ^ (8 * ((chunk >> 1) & 1))) ^ (row & 15);
+}
 constexpr int kEncThreads = 512;    // 8 waves (2 per SIMD); each wave encodes one 32-token tile at a time
 
 // Derive the bf16 operands from Pi and S (fp32, row-major [128][128]).
@@ -59,6 +67,23 @@ __device__ __forceinline__ void tile_coords(const EncodeArgs& a, int tile, int& 
   blk = blk0 + r % nblk;
 }
 
+// Lane LANE of `old` replaced by the wave-uniform value `val` (v_writelane:
+// one VALU instruction, no lane masks).
+template <int LANE>
+__device__ __forceinline__ uint32_t write_lane(uint32_t old, uint32_t val) {
+  asm("v_writelane_b32 %0, %1, %2" : "+v"(old) : "s"(val), "n"(LANE));
+  return old;
+}
+
+// f(std::integral_constant<int, I>{}) for I = B .. E-1, unrolled at compile time.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // Store one word of a value bit plane; words of partly covered blocks keep the
 // bits of tokens this call does not write.
 __device__ __forceinline__ void store_plane_word(uint32_t* p, uint32_t w, uint32_t vmask) {
@@ -73,6 +98,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
+}
+
+// Sum over the four 16-lane rows of the wave (every lane gets the total),
+// through the cross-row lane swaps (no LDS traffic).
+__device__ __forceinline__ float row_sum4(float x) {
+  auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(t[0]) + __uint_as_float(t[1]);
+  auto u = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(u[0]) + __uint_as_float(u[1]);
 }
 
 // Bit p of the Lloyd-Max index from the threshold tests gt[k] = (y > t_k).
@@ -99,13 +133,13 @@ __global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
   constexpr int NMAT = QJL ? 4 : 2;
   constexpr int NP = MSE_BITS + (QJL ? 1 : 0);  // bit planes written per token
   constexpr int LV = 1 << MSE_BITS;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[NMAT][kD][kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[NMAT][kD][kD];
 
   // Stage Pi_hi, Pi_lo (and S'_hi, S'_lo) once per work-group.
   for (int idx = threadIdx.x; idx < NMAT * kD * (kD / 8); idx += blockDim.x) {
     const int m = idx / (kD * kD / 8), rem = idx % (kD * kD / 8);
     const int row = rem / (kD / 8), c8 = rem % (kD / 8);
-    *reinterpret_cast<u32x4*>(&lds[m][row][c8 * 8]) =
+    *reinterpret_cast<u32x4*>(&lds[m][row][8 * lds_slot(row, c8)]) =
         *reinterpret_cast<const u32x4*>(a.derived + (size_t)m * kD * kD + row * kD + c8 * 8);
   }
   __syncthreads();
@@ -116,52 +150,75 @@ __global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
 #pragma unroll
   for (int k = 0; k < LV - 1; ++k) thr[k] = VALUE ? a.v_thr[k] : a.k_thr[k];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave index as a scalar: tile indices, and the per-sequence lookups they
+  // drive, stay in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nwaves = blockDim.x >> 6;
   const int tc = lane & 15;  // token inside a 16-token column tile
   const int g = lane >> 4;   // lane group: coordinates 8g..8g+7 of each k-step
   const void* src = VALUE ? a.v : a.k;
+  // slot of chunk 4ks + g of row 16rt + tc is lslot ^ 4ks (ks only touches bits 2, 3)
+  const int lslot = lds_slot(tc, g);
 
+  // Source row and destination position of column tc of column tile ct.
+  // Value planes: column tc of tile ct holds the token whose bit position in
+  // the plane word is 16ct + tc, so the ballots below land in place.
+  auto tile_rows = [&](int tl, int64_t (&row)[2], int64_t (&dp)[2], bool (&ok)[2]) {
+    int b, h;
+    int64_t blk;
+    tile_coords(a, tl, b, h, blk);
+    const int64_t pos = a.pos.v[b];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      dp[ct] = blk * 32 + (VALUE ? vslot(16 * ct + tc) : 16 * ct + tc);
+      const int64_t t = dp[ct] - pos;
+      ok[ct] = t >= 0 && t < a.n_new;
+      row[ct] = ((int64_t)b * a.n_new + (ok[ct] ? t : 0)) * a.h_kv + h;
+    }
+  };
   for (int tile = blockIdx.x * nwaves + wave; tile < a.num_tiles; tile += gridDim.x * nwaves) {
     int b, h;
     int64_t blk;
     tile_coords(a, tile, b, h, blk);
-    const int64_t pos = a.pos.v[b];
     const int64_t slot = (int64_t)b * a.h_kv + h;
-
-    // ---- load the tile: two 16-token column tiles, 32 coordinates per lane
-    u32x4 kin[2][4], klo[2][4];
-    float ss[2];
+    int64_t row[2], dpos[2];
     bool valid[2];
-    int64_t dpos[2];
+    tile_rows(tile, row, dpos, valid);
+
+    // ---- the tile: two 16-token column tiles, 32 coordinates per lane
+    u32x4 kin[2][4], klo[2][4];
+    float ss[2] = {0.f, 0.f};
+    if (IN_BF16) {
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      // value planes: column tc of tile ct holds the token whose bit position
-      // in the plane word is 16ct + tc, so the ballots below land in place
-      dpos[ct] = blk * 32 + (VALUE ? vslot(16 * ct + tc) : 16 * ct + tc);
-      const int64_t t = dpos[ct] - pos;
-      valid[ct] = t >= 0 && t < a.n_new;
-      ss[ct] = 0.f;
-      const int64_t row = ((int64_t)b * a.n_new + (valid[ct] ? t : 0)) * a.h_kv + h;
+      for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int c0 = 32 * ks + 8 * g;
-        if (IN_BF16) {
-          u32x4 x = valid[ct] ? *reinterpret_cast<const u32x4*>(
-                                    reinterpret_cast<const uint16_t*>(src) + row * kD + c0)
-                              : u32x4{0u, 0u, 0u, 0u};
-          kin[ct][ks] = x;
+        for (int ks = 0; ks < 4; ++ks)
+          // Rows of columns outside the written range are clamped to a real
+          // token: the load stays in bounds and holds finite values.  MFMA
+          // output columns depend only on their own input column, and such
+          // columns are never stored, so they need no masking.
+          kin[ct][ks] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(src) + row[ct] * kD +
+                                                        32 * ks + 8 * g);
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float lo = __uint_as_float(x[e] << 16), hi = __uint_as_float(x[e] & 0xffff0000u);
+            const float lo = __uint_as_float(kin[ct][ks][e] << 16);
+            const float hi = __uint_as_float(kin[ct][ks][e] & 0xffff0000u);
             ss[ct] = fmaf(lo, lo, ss[ct]);
             ss[ct] = fmaf(hi, hi, ss[ct]);
           }
-        } else {
-          const float* fp = reinterpret_cast<const float*>(src) + row * kD + c0;
+    } else {
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const float* fp = reinterpret_cast<const float*>(src) + row[ct] * kD + 32 * ks + 8 * g;
           float f[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) f[e] = valid[ct] ? fp[e] : 0.f;
+          for (int e = 0; e < 8; ++e) f[e] = fp[e];  // clamped row: in bounds, finite, never stored
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const uint32_t hp = pack_bf16x2(f[2 * e], f[2 * e + 1]);
@@ -177,9 +234,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
     float nrm[2], inv[2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-      float s2 = ss[ct];
-      s2 += __shfl_xor(s2, 16);
-      s2 += __shfl_xor(s2, 32);
+      const float s2 = row_sum4(ss[ct]);
       nrm[ct] = sqrtf(s2);
       inv[ct] = nrm[ct] > 0.f ? 1.0f / nrm[ct] : 0.f;
     }
@@ -200,15 +255,16 @@ __global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
 #pragma unroll
     for (int p = 0; p < (VALUE ? NP : 1); ++p) vw[p][0] = vw[p][1] = 0u;
 
-#pragma unroll
-    for (int rt = 0; rt < 8; ++rt) {
-      // keep the scheduler from hoisting every row tile's LDS operands at once
-      __builtin_amdgcn_sched_barrier(0);
-      floatx4 acc[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+    // Software pipeline over the row tiles: step st issues the LDS reads and
+    // MFMAs of row tile st next to the VALU epilogue of row tile st - 1 (they
+    // are independent), so operand latency and matrix work hide behind it.
+    auto gemm1 = [&](auto RT, floatx4 (&acc)[2]) __attribute__((always_inline)) {
+      constexpr int rt = decltype(RT)::value;
+      acc[0] = acc[1] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const u32x4 ahi = *reinterpret_cast<const u32x4*>(&lds[0][16 * rt + tc][32 * ks + 8 * g]);
-        const u32x4 alo = *reinterpret_cast<const u32x4*>(&lds[1][16 * rt + tc][32 * ks + 8 * g]);
+        const u32x4 ahi = *reinterpret_cast<const u32x4*>(&lds[0][16 * rt + tc][8 * (lslot ^ (4 * ks))]);
+        const u32x4 alo = *reinterpret_cast<const u32x4*>(&lds[1][16 * rt + tc][8 * (lslot ^ (4 * ks))]);
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
           acc[ct] = mfma_bf16(ahi, kin[ct][ks], acc[ct]);
@@ -216,22 +272,27 @@ __global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
           if (!IN_BF16) acc[ct] = mfma_bf16(ahi, klo[ct][ks], acc[ct]);
         }
       }
+    };
+    auto epilogue = [&](auto RT, const floatx4 (&acc)[2]) __attribute__((always_inline)) {
+      constexpr int rt = decltype(RT)::value;
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        // one column tile's bucketing at a time keeps few lane masks live
-        __builtin_amdgcn_sched_barrier(0);
         float res[4];
         bool bits[4][MSE_BITS];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          __builtin_amdgcn_sched_barrier(0);
           const float y = acc[ct][rr] * inv[ct];
           bool gt[LV - 1];
+          // centroids pass through an empty asm: opaque scalars, so the select
+          // chain is not folded into a per-lane table lookup in memory
           float c = cent[0];
+          asm("" : "+s"(c));
 #pragma unroll
           for (int k = 0; k < LV - 1; ++k) {
+            float ck = cent[k + 1];
+            asm("" : "+s"(ck));
             gt[k] = y > thr[k];
-            c = gt[k] ? cent[k + 1] : c;
+            c = gt[k] ? ck : c;
           }
 #pragma unroll
           for (int p = 0; p < MSE_BITS; ++p) bits[rr][p] = index_bit<LV>(gt, p);
@@ -276,7 +337,27 @@ __global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
             }
         }
       }
-    }
+        };
+    // (row tiles are compile-time constants, so every register array index is)
+    floatx4 acc_c[2], acc_n[2];
+    auto step = [&](auto ST) __attribute__((always_inline)) {
+      constexpr int st = decltype(ST)::value;
+      // one step at a time: later row tiles' operands are not hoisted
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (st < 8) gemm1(std::integral_constant<int, st>{}, acc_n);
+      if constexpr (st >= 1) epilogue(std::integral_constant<int, (st >= 1 ? st - 1 : 0)>{}, acc_c);
+      acc_c[0] = acc_n[0];
+      acc_c[1] = acc_n[1];
+    };
+    step(std::integral_constant<int, 0>{});
+    step(std::integral_constant<int, 1>{});
+    step(std::integral_constant<int, 2>{});
+    step(std::integral_constant<int, 3>{});
+    step(std::integral_constant<int, 4>{});
+    step(std::integral_constant<int, 5>{});
+    step(std::integral_constant<int, 6>{});
+    step(std::integral_constant<int, 7>{});
+    step(std::integral_constant<int, 8>{});
 
     if (VALUE) {
       // word bit 16ct + tc belongs to column tc of tile ct: valid-token mask
@@ -297,12 +378,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
 
     float gam[2];
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      float s2 = gg[ct];
-      s2 += __shfl_xor(s2, 16);
-      s2 += __shfl_xor(s2, 32);
-      gam[ct] = sqrtf(s2);
-    }
+    for (int ct = 0; ct < 2; ++ct) gam[ct] = sqrtf(row_sum4(gg[ct]));
 
     // ---- GEMM 2: Z = S' R (QJL projection of the rotated residual), signs
     if (QJL) {
@@ -312,8 +388,8 @@ __global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
         floatx4 z[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const u32x4 ahi = *reinterpret_cast<const u32x4*>(&lds[2 % NMAT][16 * rt + tc][32 * ks + 8 * g]);
-          const u32x4 alo = *reinterpret_cast<const u32x4*>(&lds[3 % NMAT][16 * rt + tc][32 * ks + 8 * g]);
+          const u32x4 ahi = *reinterpret_cast<const u32x4*>(&lds[2 % NMAT][16 * rt + tc][8 * (lslot ^ (4 * ks))]);
+          const u32x4 alo = *reinterpret_cast<const u32x4*>(&lds[3 % NMAT][16 * rt + tc][8 * (lslot ^ (4 * ks))]);
 #pragma unroll
           for (int ct = 0; ct < 2; ++ct) {
             z[ct] = mfma_bf16(ahi, rhi[ct][ks], z[ct]);
@@ -321,14 +397,20 @@ __global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
             z[ct] = mfma_bf16(ahi, rlo[ct][ks], z[ct]);
           }
         }
+        // shift the sign bit of z in at the bottom: after the 8 elements of
+        // plane word m, bit 7 - j holds the sign of element j = (rt&1)*4 + rr
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            lw[NP - 1][ct][rt >> 1] |= z[ct][rr] >= 0.f ? (1u << ((rt & 1) * 4 + rr)) : 0u;
-            asm volatile("" : "+v"(lw[NP - 1][ct][rt >> 1]));
-          }
+          for (int rr = 0; rr < 4; ++rr)
+            lw[NP - 1][ct][rt >> 1] = __builtin_amdgcn_alignbit(lw[NP - 1][ct][rt >> 1], __float_as_uint(z[ct][rr]), 31);
       }
+      // bit j = (z_j >= 0): reverse the 8 sign bits and invert them (a z of
+      // -0.0 reads as negative; its oracle value lies inside the boundary window)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) lw[NP - 1][ct][m] = (~__builtin_bitreverse32(lw[NP - 1][ct][m]) >> 24) & 0xffu;
     }
 
     // ---- plane words: spread the lane-local bits to coordinate positions
@@ -342,13 +424,13 @@ __global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
         uint32_t w[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) w[m] = ((lw[p][ct][m] & 0xfu) | ((lw[p][ct][m] & 0xf0u) << 12)) << (4 * g);
-        uint32_t ka = (g & 2) ? w[2] : w[0], kb = (g & 2) ? w[3] : w[1];
-        const uint32_t sa = (g & 2) ? w[0] : w[2], sb = (g & 2) ? w[1] : w[3];
-        ka |= __shfl_xor(sa, 32);
-        kb |= __shfl_xor(sb, 32);
-        const uint32_t send = (g & 1) ? ka : kb;
-        const uint32_t keep = (g & 1) ? kb : ka;
-        const uint32_t fin = keep | __shfl_xor(send, 16);
+        // lanes g and g^2 merge: rows 0,1 keep words 0,1 and rows 2,3 words 2,3
+        const auto s02 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+        const auto s13 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+        const uint32_t ka = s02[0] | s02[1], kb = s13[0] | s13[1];
+        // then rows g and g^1: row g ends with word g
+        const auto sf = __builtin_amdgcn_permlane16_swap(ka, kb, false, false);
+        const uint32_t fin = sf[0] | sf[1];
         if (valid[ct])
           *reinterpret_cast<uint32_t*>(a.k_planes + (slot * a.capacity + dpos[ct]) * rec + p * (kD / 8) + 4 * g) = fin;
       }
@@ -373,7 +455,9 @@ __global__ __launch_bounds__(256) void encode_minmax_kernel(EncodeArgs a) {
   constexpr int L = (1 << BITS) - 1;
   constexpr int NG = 64 / GS;  // groups per lane
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave index as a scalar: tile indices, and the per-sequence lookups they
+  // drive, stay in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nwaves = blockDim.x >> 6;
   // lane l (mod 32) encodes the token whose bit position in a plane word is
   // l mod 32, so a ballot over the wave is already the plane word
@@ -441,17 +525,16 @@ __global__ __launch_bounds__(256) void encode_minmax_kernel(EncodeArgs a) {
     uint32_t w[BITS][2];
 #pragma unroll
     for (int p = 0; p < BITS; ++p) w[p][0] = w[p][1] = 0u;
-#pragma unroll
-    for (int e = 0; e < 64; ++e) {
+    static_for<0, 64>([&](auto E) {
+      constexpr int e = decltype(E)::value;
 #pragma unroll
       for (int p = 0; p < BITS; ++p) {
         const uint64_t m = __ballot((code[e] >> p) & 1u);
-        if (lane == e) {
-          w[p][0] = (uint32_t)m;
-          w[p][1] = (uint32_t)(m >> 32);
-        }
+        // the ballot is wave-uniform: write its halves straight into lane e
+        w[p][0] = write_lane<e>(w[p][0], (uint32_t)m);
+        w[p][1] = write_lane<e>(w[p][1], (uint32_t)(m >> 32));
       }
-    }
+    });
     const uint32_t vmask = (uint32_t)__ballot(valid);  // bit l: lane l's token is written
     const int64_t nblk_cap = a.capacity >> 5;
 #pragma unroll
