@@ -48,6 +48,24 @@ __device__ __forceinline__ float quad_sum(float x) {
   return x;
 }
 
+// Max / sum over the 16 lanes of a DPP row (every lane gets the result).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, dpp<0xB1>(x));   // quad_perm 1,0,3,2
+  x = fmaxf(x, dpp<0x4E>(x));   // quad_perm 2,3,0,1
+  x = fmaxf(x, dpp<0x124>(x));  // row_ror 4
+  return fmaxf(x, dpp<0x128>(x));  // row_ror 8
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  x += dpp<0x124>(x);
+  return x + dpp<0x128>(x);
+}
+
 // Bytes of a plane word: byte j of the result is bit (8j + s) of w, scaled by 2^s.
 __device__ __forceinline__ uint32_t plane_bytes(uint32_t w, int s) { return w & (0x01010101u << s); }
 
@@ -187,7 +205,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
   constexpr int kStageMeta = 64 * NG;           // dwords
   constexpr int kStageNg = 64 * 2;              // floats: per token u = tau log2e n, w = u kappa gamma
   constexpr int kStageVw = 2 * VB * kD;         // dwords
-  constexpr int kStage = kStageMeta + kStageNg + kStageVw;
+  constexpr int kStageP = NHEAD * 64;           // floats: p of (head, token) for the value MFMA
+  constexpr int kStage = kStageMeta + kStageNg + kStageVw + kStageP;
   constexpr int kMerge = NHEAD * (kD + 2);
   constexpr int kStride = kStage > kMerge ? kStage : kMerge;
   __shared__ __attribute__((aligned(16))) uint32_t smem[4 * kStride];
@@ -204,6 +223,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
   uint32_t* s_meta = smem + wave * kStride;
   float* s_ng = reinterpret_cast<float*>(s_meta + kStageMeta);
   uint32_t* s_vw = s_meta + kStageMeta + kStageNg;
+  float* s_p = reinterpret_cast<float*>(s_vw + kStageVw);
 
   // query digit operands and per-head constants (score layout: head 4ht + n/4)
   u32x4 qb[NHT][NPL][2];
@@ -217,17 +237,17 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
         for (int hf = 0; hf < 2; ++hf) qb[ht][pl][hf] = src[((ht * NPL + pl) * 2 + hf) * 64 + lane];
   }
   // score of (head, token) in log2 units: u (K1 Dm + c0) + w (K2 Ds - c3), where
-  // u = tau log2(e) n, w = u kappa gamma and Dm, Ds are quad sums of digit partials
-  const float lscale = (float)(1u << (7 * (3 - (n & 3))));  // weight of this lane's query digit
+  // u = tau log2(e) n, w = u kappa gamma and Dm, Ds are the digit-combined
+  // integer dot products; lane (g, n) scores head 4ht + g
   float k1[NHT], k2[NHT], c0[NHT], c3[NHT];
 #pragma unroll
   for (int ht = 0; ht < NHT; ++ht) {
-    const int hq = 4 * ht + (n >> 2);
+    const int hq = 4 * ht + g;
     if (hq < G) {
       const floatx4 cs = *reinterpret_cast<const floatx4*>(a.qconst + ((size_t)b * a.h_q + h * G + hq) * 4);
       c0[ht] = cs[0];
-      k1[ht] = cs[1] * lscale;
-      k2[ht] = cs[2] * lscale;
+      k1[ht] = cs[1];
+      k2[ht] = cs[2];
       c3[ht] = cs[3];
     } else {
       c0[ht] = k1[ht] = k2[ht] = c3[ht] = 0.f;
@@ -339,8 +359,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 
-    // ---- scores (log2 units): lane (g, n) gets tokens 16ct + 4g + r of head 4ht + n/4
-    float p[NHT][4][4];
+    // ---- scores (log2 units).  The query digits are the A operand and the
+    // key bits the B operand, so lane (g, n) receives, for token 16ct + n and
+    // head 4ht + g, all four digit partial sums (accumulator element r = digit r).
+    float sc[NHT][4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
       uint32_t P[PM];
@@ -357,64 +379,69 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
       for (int pl = 0; pl < PM; ++pl) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-          const u32x4 A = {plane_bytes(P[pl], 4 * hf), plane_bytes(P[pl], 4 * hf + 1),
-                           plane_bytes(P[pl], 4 * hf + 2), plane_bytes(P[pl], 4 * hf + 3)};
+          const u32x4 Bk = {plane_bytes(P[pl], 4 * hf), plane_bytes(P[pl], 4 * hf + 1),
+                            plane_bytes(P[pl], 4 * hf + 2), plane_bytes(P[pl], 4 * hf + 3)};
 #pragma unroll
-          for (int ht = 0; ht < NHT; ++ht) am[ht] = mfma_i8(A, qb[ht][pl][hf], am[ht]);
+          for (int ht = 0; ht < NHT; ++ht) am[ht] = mfma_i8(qb[ht][pl][hf], Bk, am[ht]);
         }
       }
       if (QJL) {
         const uint32_t Ps = X[ct][KP - 1];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-          const u32x4 A = {plane_bytes(Ps, 4 * hf), plane_bytes(Ps, 4 * hf + 1), plane_bytes(Ps, 4 * hf + 2),
-                           plane_bytes(Ps, 4 * hf + 3)};
+          const u32x4 Bk = {plane_bytes(Ps, 4 * hf), plane_bytes(Ps, 4 * hf + 1), plane_bytes(Ps, 4 * hf + 2),
+                            plane_bytes(Ps, 4 * hf + 3)};
 #pragma unroll
-          for (int ht = 0; ht < NHT; ++ht) as[ht] = mfma_i8(A, qb[ht][NPL - 1][hf], as[ht]);
+          for (int ht = 0; ht < NHT; ++ht) as[ht] = mfma_i8(qb[ht][NPL - 1][hf], Bk, as[ht]);
         }
       }
+      const int u = 16 * ct + n;  // token inside the chunk
+      const float ut = s_ng[2 * u], wt = s_ng[2 * u + 1];
+      const bool valid = u < rem;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int u = 16 * ct + 4 * g + r;  // token inside the chunk
-        const float ut = s_ng[2 * u], wt = s_ng[2 * u + 1];
-        const bool valid = u < rem;
-#pragma unroll
-        for (int ht = 0; ht < NHT; ++ht) {
-          float part = (float)am[ht][r] * (ut * k1[ht]);
-          if (QJL) part = fmaf((float)as[ht][r], wt * k2[ht], part);
-          const float sc = quad_sum(part) + fmaf(ut, c0[ht], -wt * c3[ht]);
-          p[ht][ct][r] = valid ? sc : -INFINITY;
+      for (int ht = 0; ht < NHT; ++ht) {
+        // digits carry 2^21, 2^14, 2^7, 1: two exact integer halves, then float
+        const float dm = fmaf((float)((am[ht][0] << 7) + am[ht][1]), 16384.f, (float)((am[ht][2] << 7) + am[ht][3]));
+        float sv = ut * fmaf(k1[ht], dm, c0[ht]);
+        if (QJL) {
+          const float ds = fmaf((float)((as[ht][0] << 7) + as[ht][1]), 16384.f, (float)((as[ht][2] << 7) + as[ht][3]));
+          sv = fmaf(wt, fmaf(k2[ht], ds, -c3[ht]), sv);
         }
+        sc[ht][ct] = valid ? sv : -INFINITY;
       }
     }
 
-    // ---- online softmax in log2 units; alpha rescales the running sums
-    float alpha_pv[NHT];
+    // ---- online softmax in log2 units over the 16 lanes of a head (one DPP
+    // row); alpha rescales the running sums.  p goes to LDS for the value MFMA.
+    float alpha[NHT];
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
-      float mloc = p[ht][0][0];
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mloc = fmaxf(mloc, p[ht][ct][r]);
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+      const float mloc = row_max16(fmaxf(fmaxf(sc[ht][0], sc[ht][1]), fmaxf(sc[ht][2], sc[ht][3])));
       const float m_new = fmaxf(m_run[ht], mloc);
-      const float alpha = exp2f(m_run[ht] - m_new);
+      alpha[ht] = exp2f(m_run[ht] - m_new);
       m_run[ht] = m_new;
       float lsum = 0.f;
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float e = exp2f(p[ht][ct][r] - m_new);  // 0 for tokens past the end
-          p[ht][ct][r] = e;
-          lsum += e;
-        }
-      l_part[ht] = fmaf(l_part[ht], alpha, lsum);
-      // value layout: lane (g, n) accumulates head 4ht + g, held by score lane 4g
-      alpha_pv[ht] = __shfl(alpha, 4 * g);
+      for (int ct = 0; ct < 4; ++ct) {
+        const float e = exp2f(sc[ht][ct] - m_new);  // 0 for tokens past the end
+        s_p[(4 * ht + g) * 64 + 16 * ct + n] = e;
+        lsum += e;
+      }
+      l_part[ht] = fmaf(l_part[ht], alpha[ht], lsum);
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    // value-MFMA rows are (head 4ht + n/4, .): this lane's 16 tokens 16ct + 4g + r
+    floatx4 pv[NHT][4];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+        pv[ht][ct] = *reinterpret_cast<const floatx4*>(s_p + (4 * ht + (n >> 2)) * 64 + 16 * ct + 4 * g);
+    float alpha_pv[NHT];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) alpha_pv[ht] = alpha[ht];  // accumulator rows: head 4ht + g
 
     // ---- values
     if (!VMSE) {
@@ -447,7 +474,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
             const uint32_t mm = s_meta[(16 * ct + 4 * g + r) * NG + grp];
             const float dl = __half2float(__ushort_as_half((unsigned short)(mm & 0xffffu)));
             const float mn = __half2float(__ushort_as_half((unsigned short)(mm >> 16)));
-            const float pe = p[ht][ct][r];
+            const float pe = pv[ht][ct][r];
             const int W = (int)fmaf(pe * scl, dl, rnd);
             V[r] = ((uint32_t)W + 0x00808080u) ^ 0x00808080u;  // bytes = signed base-256 digits
             M[ht] = fmaf(pe, mn, M[ht]);
@@ -531,11 +558,11 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
           const float nv = __uint_as_float(s_meta[u * NG]);
 #pragma unroll
           for (int ht = 0; ht < NHT; ++ht) {
-            const uint32_t W = (uint32_t)fmaf(p[ht][ct][r], nv * sc, 0.5f);
+            const uint32_t W = (uint32_t)fmaf(pv[ht][ct][r], nv * sc, 0.5f);
             int dg = (int)((W >> mydig_shift) & 127u);
             if (s_tok == 7) dg = -dg;
             A[ht][ct] |= (uint32_t)(dg & 0xff) << (8 * r);
-            PN[ht] = fmaf(p[ht][ct][r], nv, PN[ht]);
+            PN[ht] = fmaf(pv[ht][ct][r], nv, PN[ht]);
           }
         }
       }
@@ -585,18 +612,13 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
   // with m converted back to natural-log units
   float lsum[NHT];
 #pragma unroll
-  for (int ht = 0; ht < NHT; ++ht) {
-    float x = l_part[ht];
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    lsum[ht] = x;  // score layout; the four lanes of a quad hold the same tokens
-  }
+  for (int ht = 0; ht < NHT; ++ht) lsum[ht] = row_sum16(l_part[ht]);  // the 16 lanes of head 4ht + g
   __syncthreads();
   float* mrg = reinterpret_cast<float*>(smem) + wave * kStride;
 #pragma unroll
   for (int ht = 0; ht < NHT; ++ht) {
-    if (g == 0 && (n & 3) == 0) {
-      const int hh = 4 * ht + (n >> 2);
+    if (n == 0) {
+      const int hh = 4 * ht + g;
       mrg[hh * (kD + 2)] = lsum[ht] > 0.f ? m_run[ht] * 0.6931471806f : -INFINITY;
       mrg[hh * (kD + 2) + 1] = lsum[ht];
     }
