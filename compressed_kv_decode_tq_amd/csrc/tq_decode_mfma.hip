@@ -453,13 +453,15 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
       for (int gi = 0; gi < NG; ++gi) mb = max(mb, s_meta[lane * NG + gi] & 0x7fffu);
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, o));
-      const int ev = 44 - (int)(mb >> 10);  // every delta < 2^(e - 14): |W| < 2^30
+      // every delta < 2^(e - 14), so |W| < 2^22: three signed base-256 digits
+      // (the top byte of the digit form is zero)
+      const int ev = 36 - (int)(mb >> 10);
       const float inv_sv = ldexpf(1.f, -ev);
       // tokens of dword ct sit at bit shift s = 4(ct&1) + g of the value words;
       // their weights carry 2^-s, negated where s = 7 (the byte 0x80 reads -128)
       const float scl0 = ldexpf(1.f, ev - g);
       const float scl1 = g == 3 ? -ldexpf(1.f, ev - 7) : ldexpf(1.f, ev - 4 - g);
-      u32x4 A[NHT][4];
+      u32x4 A[NHT][3];
       float M[NHT];
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) {
@@ -484,10 +486,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
           const uint32_t t01hi = __builtin_amdgcn_perm(V[1], V[0], 0x07030602u);
           const uint32_t t23lo = __builtin_amdgcn_perm(V[3], V[2], 0x05010400u);
           const uint32_t t23hi = __builtin_amdgcn_perm(V[3], V[2], 0x07030602u);
-          A[ht][3][ct] = __builtin_amdgcn_perm(t23lo, t01lo, 0x05040100u);  // least significant digit
-          A[ht][2][ct] = __builtin_amdgcn_perm(t23lo, t01lo, 0x07060302u);
-          A[ht][1][ct] = __builtin_amdgcn_perm(t23hi, t01hi, 0x05040100u);
-          A[ht][0][ct] = __builtin_amdgcn_perm(t23hi, t01hi, 0x07060302u);  // most significant digit
+          A[ht][2][ct] = __builtin_amdgcn_perm(t23lo, t01lo, 0x05040100u);  // least significant digit
+          A[ht][1][ct] = __builtin_amdgcn_perm(t23lo, t01lo, 0x07060302u);
+          A[ht][0][ct] = __builtin_amdgcn_perm(t23hi, t01hi, 0x05040100u);  // most significant digit
         }
       }
       // sum_t p_t min_t per (head, group): reduce over the four token quarters,
@@ -515,13 +516,12 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
           for (int d = 0; d < 4; ++d) B[d] = plane_bytes(s_vw[((d >> 1) * VB + pv) * kD + ch], 4 * (d & 1) + g);
 #pragma unroll
           for (int ht = 0; ht < NHT; ++ht) {
-            // row (head g, group gi) of the four digit products
+            // row (head g, group gi) of the three digit products (each |d| < 2^20)
             const int d0 = mfma_i8(A[ht][0], B, i32x4{0, 0, 0, 0})[gi];
             const int d1 = mfma_i8(A[ht][1], B, i32x4{0, 0, 0, 0})[gi];
             const int d2 = mfma_i8(A[ht][2], B, i32x4{0, 0, 0, 0})[gi];
-            const int d3 = mfma_i8(A[ht][3], B, i32x4{0, 0, 0, 0})[gi];
-            hi[ht] += ((d0 << 8) + d1) << pv;  // plane pv carries weight 2^pv
-            lo[ht] += ((d2 << 8) + d3) << pv;
+            hi[ht] += d0 << pv;  // plane pv carries weight 2^pv
+            lo[ht] += ((d1 << 8) + d2) << pv;
           }
         }
 #pragma unroll
