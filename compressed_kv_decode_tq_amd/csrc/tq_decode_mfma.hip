@@ -469,6 +469,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
           const float scl = (ct & 1) ? scl1 : scl0;
+          const float rnd = scl < 0.f ? -0.5f : 0.5f;  // round half away from zero under truncation
           uint32_t V[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -476,10 +477,11 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
             const float dl = __half2float(__ushort_as_half((unsigned short)(mm & 0xffffu)));
             const float mn = __half2float(__ushort_as_half((unsigned short)(mm >> 16)));
             const float pe = pv[ht][ct][r];
-            // W + 0x808080 (positive, below 2^24) rounded to an integer in one
-            // FMA; the XOR turns its three bytes into the signed base-256 digits of W
-            const uint32_t Wb = (uint32_t)fmaf(pe * scl, dl, 8421504.5f);
-            V[r] = Wb ^ 0x00808080u;
+            // W rounded to an integer (|W| < 2^22, so pe*scl*dl +- 0.5 is exact
+            // enough in fp32); biasing each low byte by 128 and flipping its top
+            // bit gives the signed base-256 digits of W
+            const int W = (int)fmaf(pe * scl, dl, rnd);
+            V[r] = ((uint32_t)W + 0x00808080u) ^ 0x00808080u;
             M[ht] = fmaf(pe, mn, M[ht]);
           }
           // 4x4 byte transpose: digit plane k holds byte k of the four tokens
