@@ -453,15 +453,13 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
       for (int gi = 0; gi < NG; ++gi) mb = max(mb, s_meta[lane * NG + gi] & 0x7fffu);
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, o));
-      // every delta < 2^(e - 14), so |W| < 2^22: three signed base-256 digits
-      // (the top byte of the digit form is zero)
-      const int ev = 36 - (int)(mb >> 10);
+      const int ev = 44 - (int)(mb >> 10);  // every delta < 2^(e - 14): |W| < 2^30
       const float inv_sv = ldexpf(1.f, -ev);
       // tokens of dword ct sit at bit shift s = 4(ct&1) + g of the value words;
       // their weights carry 2^-s, negated where s = 7 (the byte 0x80 reads -128)
       const float scl0 = ldexpf(1.f, ev - g);
       const float scl1 = g == 3 ? -ldexpf(1.f, ev - 7) : ldexpf(1.f, ev - 4 - g);
-      u32x4 A[NHT][3];
+      u32x4 A[NHT][4];
       float M[NHT];
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) {
@@ -469,7 +467,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
           const float scl = (ct & 1) ? scl1 : scl0;
-          const float rnd = scl < 0.f ? -0.5f : 0.5f;  // round half away from zero under truncation
+          const float rnd = scl < 0.f ? -0.5f : 0.5f;
           uint32_t V[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -477,11 +475,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
             const float dl = __half2float(__ushort_as_half((unsigned short)(mm & 0xffffu)));
             const float mn = __half2float(__ushort_as_half((unsigned short)(mm >> 16)));
             const float pe = pv[ht][ct][r];
-            // W rounded to an integer (|W| < 2^22, so pe*scl*dl +- 0.5 is exact
-            // enough in fp32); biasing each low byte by 128 and flipping its top
-            // bit gives the signed base-256 digits of W
             const int W = (int)fmaf(pe * scl, dl, rnd);
-            V[r] = ((uint32_t)W + 0x00808080u) ^ 0x00808080u;
+            V[r] = ((uint32_t)W + 0x00808080u) ^ 0x00808080u;  // bytes = signed base-256 digits
             M[ht] = fmaf(pe, mn, M[ht]);
           }
           // 4x4 byte transpose: digit plane k holds byte k of the four tokens
@@ -489,9 +484,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
           const uint32_t t01hi = __builtin_amdgcn_perm(V[1], V[0], 0x07030602u);
           const uint32_t t23lo = __builtin_amdgcn_perm(V[3], V[2], 0x05010400u);
           const uint32_t t23hi = __builtin_amdgcn_perm(V[3], V[2], 0x07030602u);
-          A[ht][2][ct] = __builtin_amdgcn_perm(t23lo, t01lo, 0x05040100u);  // least significant digit
-          A[ht][1][ct] = __builtin_amdgcn_perm(t23lo, t01lo, 0x07060302u);
-          A[ht][0][ct] = __builtin_amdgcn_perm(t23hi, t01hi, 0x05040100u);  // most significant digit
+          A[ht][3][ct] = __builtin_amdgcn_perm(t23lo, t01lo, 0x05040100u);  // least significant digit
+          A[ht][2][ct] = __builtin_amdgcn_perm(t23lo, t01lo, 0x07060302u);
+          A[ht][1][ct] = __builtin_amdgcn_perm(t23hi, t01hi, 0x05040100u);
+          A[ht][0][ct] = __builtin_amdgcn_perm(t23hi, t01hi, 0x07060302u);  // most significant digit
         }
       }
       // sum_t p_t min_t per (head, group): reduce over the four token quarters,
@@ -519,12 +515,13 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
           for (int d = 0; d < 4; ++d) B[d] = plane_bytes(s_vw[((d >> 1) * VB + pv) * kD + ch], 4 * (d & 1) + g);
 #pragma unroll
           for (int ht = 0; ht < NHT; ++ht) {
-            // row (head g, group gi) of the three digit products (each |d| < 2^20)
+            // row (head g, group gi) of the four digit products
             const int d0 = mfma_i8(A[ht][0], B, i32x4{0, 0, 0, 0})[gi];
             const int d1 = mfma_i8(A[ht][1], B, i32x4{0, 0, 0, 0})[gi];
             const int d2 = mfma_i8(A[ht][2], B, i32x4{0, 0, 0, 0})[gi];
-            hi[ht] += d0 << pv;  // plane pv carries weight 2^pv
-            lo[ht] += ((d1 << 8) + d2) << pv;
+            const int d3 = mfma_i8(A[ht][3], B, i32x4{0, 0, 0, 0})[gi];
+            hi[ht] += ((d0 << 8) + d1) << pv;  // plane pv carries weight 2^pv
+            lo[ht] += ((d2 << 8) + d3) << pv;
           }
         }
 #pragma unroll
