@@ -257,8 +257,7 @@ size_t tq_decode_workspace_bytes(const tq_layout* layout, int32_t batch, int32_t
                                  int32_t num_kv_heads, int64_t max_tokens) {
   if (!layout || batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_tokens < 0) return 0;
   const int nb = std::min(batch, tq::kMaxSeqPerLaunch);
-  int32_t splits, split_len;
-  tq::decode_split(max_tokens, (int64_t)nb * num_kv_heads, &splits, &split_len);
+  const int32_t splits = tq::decode_max_splits(max_tokens, (int64_t)nb * num_kv_heads);
   const size_t qprep = (size_t)nb * num_q_heads * 2 * tq::kD * 4;
   const size_t part = (size_t)splits * nb * num_q_heads * (tq::kD + 2) * 4;
   const size_t base = (qprep + part + 255) & ~(size_t)255;

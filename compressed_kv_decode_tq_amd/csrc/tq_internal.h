@@ -145,5 +145,7 @@ hipError_t launch_combine(const DecodeArgs& a, int value_mse, hipStream_t stream
 
 // Decode work split used for the workspace size and the launch.
 void decode_split(int64_t max_tokens, int64_t units, int32_t* splits, int32_t* split_len);
+// Upper bound of decode_split's split count over all token counts <= max_tokens.
+int32_t decode_max_splits(int64_t max_tokens, int64_t units);
 
 }  // namespace tq

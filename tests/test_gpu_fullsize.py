@@ -6,8 +6,10 @@ Workloads:
   Lloyd-Max + QJL, values 2-bit min/max.
 - Long context: 1 x 8 x 131072, keys 3-bit Lloyd-Max + QJL, values 3-bit
   Lloyd-Max.
+- The Qwen2.5-1.5B-shaped layer (12 query heads, 2 KV heads) at N = 16384, and
+  its literal 3-bit-MSE + QJL key variant with fp32 scalars.
 
-Both run with the launch shapes bench.py times (the same library calls on the
+All run with the launch shapes bench.py times (the same library calls on the
 same tensor sizes; the split of the decode grid follows from the sizes).
 
 Checks:
@@ -146,3 +148,32 @@ def test_fullsize_long_b1_hkv8_n131072():
         torch.cuda.synchronize()
         if step in (0, 2):
             _check_decode(w, bk, pi, s, cache, q, out, slots, n_c, tag=f"step {step}")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["qwen2.5-1.5b-layer-n16384", "qwen2.5-1.5b-layer-n4096-k4bit-f32scalars"])
+def test_fullsize_qwen_layer(name):
+    """The Qwen2.5-1.5B-shaped layer (12 query heads on 2 KV heads: 6 per KV
+    head, two 4-head MFMA tiles) at its longest sweep length, and the literal
+    3-bit-MSE + QJL key variant with fp32 scalars; every slot checked."""
+    w = wl.by_name(name)
+    say(f"[full size] {w.name}")
+    bk = books(w)
+    pi, s = wl.params(w)
+    prm = tq.Params(layout_of(w), pi, s, device=DEV)
+    k, v = wl.prefill_kv(w)
+    cap = ((w.n_tokens + 31) // 32) * 32
+    cache = tq.Cache(layout_of(w), w.batch, w.h_kv, cap, device=DEV)
+    tq.encode_kv(prm, k.to(DEV), v.to(DEV), [0] * w.batch, cache)
+    torch.cuda.synchronize()
+    slots = [(b, h) for b in range(w.batch) for h in range(w.h_kv)]
+    tot = np.zeros(3, dtype=np.int64)
+    for b, h in slots:
+        ref = encode_slot(w, bk, pi, s, k[b, :, h].double().numpy(), v[b, :, h].double().numpy())
+        tot += check_encode_slot(w, bk, cache, b, h, ref, 0, w.n_tokens, f"b{b} h{h}")
+    say(f"  encode: all {len(slots)} slots match outside the window; excused flips key MSE {tot[0]}, "
+        f"key QJL {tot[1]}, value MSE {tot[2]} of {len(slots) * w.n_tokens * w.d} coordinates")
+    q = wl.query(w, 0)
+    out = tq.decode_attn(prm, q.to(DEV), cache, [w.n_tokens] * w.batch)
+    torch.cuda.synchronize()
+    _check_decode(w, bk, pi, s, cache, q, out, slots, w.n_tokens, tag="decode")

@@ -139,3 +139,17 @@ def test_encode_and_decode_argument_checks():
     nr_full = (ctypes.c_int32 * 2)(0, 128)
     assert L.tq_ring_append(16, 16, tq.TQ_BF16, 2, 1, 128, 16, 16, 128, nr_full, None) == tq.TQ_ERR_CAPACITY
     assert L.tq_ring_append(16, 16, tq.TQ_BF16, 2, 1, 64, 16, 16, 128, nr, None) == tq.TQ_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("batch,h_q,h_kv", [(1, 1, 1), (1, 32, 8), (32, 32, 8), (1, 12, 2), (100, 32, 8)])
+def test_decode_workspace_never_shrinks_with_more_tokens(batch, h_q, h_kv):
+    """A workspace sized for a capacity fits every call with fewer tokens: the
+    required size never decreases as max_tokens grows (the split count of a
+    shorter sequence can exceed that of a longer one, so the bound must cover
+    all lengths up to max_tokens)."""
+    lay = tq.Layout()
+    prev = 0
+    for n in list(range(0, 5000, 37)) + [32768, 32769, 32896, 131072, 131088, 1 << 20]:
+        need = tq.decode_workspace_bytes(lay, batch, h_q, h_kv, n)
+        assert need >= prev, (n, need, prev)
+        prev = need
