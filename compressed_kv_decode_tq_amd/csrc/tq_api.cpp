@@ -274,6 +274,7 @@ int tq_decode_attn(const tq_layout* layout, const tq_params* params, const void*
   if (rc) return rc;
   if ((rc = check_cache(layout, cache))) return rc;
   if (!params || !params->pi || !params->s) return fail(TQ_ERR_INVALID, "params pi and s must be set");
+  if (!params->derived) return fail(TQ_ERR_INVALID, "params.derived must be filled by tq_prepare_params");
   if (!q || !out || !n_compressed_host) return fail(TQ_ERR_INVALID, "q, out and n_compressed_host must be non-NULL");
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return fail(TQ_ERR_INVALID, "q_dtype must be TQ_F32 or TQ_BF16");
   const int h_kv = cache->num_kv_heads;
@@ -324,6 +325,7 @@ int tq_decode_attn(const tq_layout* layout, const tq_params* params, const void*
     a.v_norm = cache->v_norm ? (const char*)cache->v_norm + seq_off(b0, h_kv, cap, sz) : nullptr;
     a.pi = params->pi;
     a.s = params->s;
+    a.mat_t = reinterpret_cast<const float*>(static_cast<const char*>(params->derived) + tq::kOffPiT);
     const size_t ring_off = (size_t)b0 * ring_cap * h_kv * tq::kD;
     a.ring_k = ring_cap > 0 ? (const uint16_t*)ring_k + ring_off : nullptr;
     a.ring_v = ring_cap > 0 ? (const uint16_t*)ring_v + ring_off : nullptr;

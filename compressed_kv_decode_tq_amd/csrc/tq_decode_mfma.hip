@@ -84,6 +84,7 @@ __device__ __forceinline__ void digits128(int q, int d[4]) {
 // (g, n), 16 bytes: byte 4d + j holds digit n%4 of head 4ht + n/4 at
 // coordinate k = 32g + 8j + 4hf + d, pre-scaled by 2^-(k%8) (negated for
 // k%8 == 7).  Plane pl < PM multiplies w_pl * (Pi q); plane PM (QJL) 2 * (S q).
+template <int MAXG>
 __global__ __launch_bounds__(256) void qprep_mfma_kernel(DecodeArgs a, int pm, int npl, int nht) {
   __shared__ float qv[kMaxGroup][kD];
   __shared__ float qr[kMaxGroup][kD];
@@ -102,30 +103,28 @@ __global__ __launch_bounds__(256) void qprep_mfma_kernel(DecodeArgs a, int pm, i
   }
   __syncthreads();
   {
+    // thread (which, i): row i of Pi q (which 0) or S q (which 1) for every
+    // head; column j of the matrix is row j of its transpose, so consecutive
+    // threads read consecutive words
     const int i = threadIdx.x & (kD - 1);
-    const int which = threadIdx.x >> 7;  // 0: Pi, 1: S
-    const float* m = which == 0 ? a.pi : a.s;
-    float acc[kMaxGroup];
+    const int which = threadIdx.x >> 7;
+    const float* mt = a.mat_t + (size_t)which * kD * kD + i;
+    float acc[MAXG];
 #pragma unroll
-    for (int gq = 0; gq < kMaxGroup; ++gq) acc[gq] = 0.f;
-    const floatx4* row = reinterpret_cast<const floatx4*>(m + (size_t)i * kD);
-    for (int j4 = 0; j4 < kD / 4; ++j4) {
-      const floatx4 w = row[j4];
+    for (int gq = 0; gq < MAXG; ++gq) acc[gq] = 0.f;
+#pragma unroll 8
+    for (int j = 0; j < kD; ++j) {
+      const float w = mt[(size_t)j * kD];
 #pragma unroll
-      for (int gq = 0; gq < kMaxGroup; ++gq) {
-        acc[gq] = fmaf(w[0], qv[gq][4 * j4 + 0], acc[gq]);
-        acc[gq] = fmaf(w[1], qv[gq][4 * j4 + 1], acc[gq]);
-        acc[gq] = fmaf(w[2], qv[gq][4 * j4 + 2], acc[gq]);
-        acc[gq] = fmaf(w[3], qv[gq][4 * j4 + 3], acc[gq]);
-      }
+      for (int gq = 0; gq < MAXG; ++gq) acc[gq] = fmaf(w, qv[gq][j], acc[gq]);
     }
 #pragma unroll
-    for (int gq = 0; gq < kMaxGroup; ++gq) (which == 0 ? qr : qs)[gq][i] = acc[gq];
+    for (int gq = 0; gq < MAXG; ++gq) (which == 0 ? qr : qs)[gq][i] = acc[gq];
   }
   __syncthreads();
   // per-head exponents and constants: one wave per head
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  for (int gq = wv; gq < kMaxGroup; gq += 4) {
+  for (int gq = wv; gq < MAXG; gq += 4) {
     float mr = 0.f, ms = 0.f, sr = 0.f, ssum = 0.f;
     for (int c = lane; c < kD; c += 64) {
       mr = fmaxf(mr, fabsf(qr[gq][c]));
@@ -699,7 +698,10 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int key_mse_bits, int key_qjl
   const int nht = a.group > 4 ? 2 : 1;
   const int pm = 1 << (key_mse_bits - 1);
   const int npl = pm + 1;
-  hipLaunchKernelGGL(qprep_mfma_kernel, dim3(a.batch * a.h_kv), dim3(256), 0, stream, a, pm, npl, nht);
+  if (nht == 1)
+    hipLaunchKernelGGL(qprep_mfma_kernel<4>, dim3(a.batch * a.h_kv), dim3(256), 0, stream, a, pm, npl, nht);
+  else
+    hipLaunchKernelGGL(qprep_mfma_kernel<8>, dim3(a.batch * a.h_kv), dim3(256), 0, stream, a, pm, npl, nht);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = nht == 1 ? dispatch_mfma<1>(a, key_mse_bits, key_qjl, value_mse, value_bits, stream, tl)

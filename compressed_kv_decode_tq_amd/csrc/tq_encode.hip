@@ -52,6 +52,10 @@ __global__ void prepare_params_kernel(const float* __restrict__ pi, const float*
   const uint32_t slo = f2bf((float)(acc - (double)bf2f(shi)));
   out[kOffSpHi / 2 + i * kD + k] = (uint16_t)shi;
   out[kOffSpLo / 2 + i * kD + k] = (uint16_t)slo;
+  // fp32 transposes for the decode's query rotation
+  float* ft = reinterpret_cast<float*>(out);
+  ft[kOffPiT / 4 + k * kD + i] = p;
+  ft[kOffST / 4 + k * kD + i] = s[i * kD + k];
 }
 
 // Map a tile index to (sequence, head, 32-token destination block).

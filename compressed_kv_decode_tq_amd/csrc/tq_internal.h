@@ -14,16 +14,20 @@ constexpr int kMaxSeqPerLaunch = 64; // per-sequence host values travel in kerne
 constexpr int kMaxGroup = 8;       // query heads per KV head handled by one decode work-group
 constexpr int kMaxRing = 128;      // ring tokens attended per sequence
 
-// Byte offsets of the operands tq_prepare_params derives from Pi and S.  Each is
-// a bf16 [128][128] row-major matrix.
-//   pi_hi/pi_lo : Pi = pi_hi + pi_lo + O(2^-17 |Pi|)
-//   sp_hi/sp_lo : S' = S Pi^T with its columns permuted into the order in which
-//                 the encode kernel holds the rotated residual (see sp_column).
+// Byte offsets of the operands tq_prepare_params derives from Pi and S.
+//   pi_hi/pi_lo : bf16 [128][128] row-major, Pi = pi_hi + pi_lo + O(2^-17 |Pi|)
+//   sp_hi/sp_lo : bf16 [128][128], S' = S Pi^T with its columns permuted into the
+//                 order in which the encode kernel holds the rotated residual
+//                 (see sp_column)
+//   pi_t/s_t    : fp32 [128][128], Pi^T and S^T (column j of Pi is row j), so the
+//                 decode's query rotation reads them coalesced
 constexpr size_t kOffPiHi = 0;
 constexpr size_t kOffPiLo = kOffPiHi + kD * kD * 2;
 constexpr size_t kOffSpHi = kOffPiLo + kD * kD * 2;
 constexpr size_t kOffSpLo = kOffSpHi + kD * kD * 2;
-constexpr size_t kDerivedBytes = kOffSpLo + kD * kD * 2;
+constexpr size_t kOffPiT = kOffSpLo + kD * kD * 2;
+constexpr size_t kOffST = kOffPiT + kD * kD * 4;
+constexpr size_t kDerivedBytes = kOffST + kD * kD * 4;
 
 // Column of S' that the encode kernel's second GEMM meets at contraction index
 // k.  The first GEMM leaves, in lane group g of a 16x16x32 MFMA, the rotated
@@ -75,6 +79,7 @@ struct DecodeArgs {
   const void* v_norm;
   const float* pi;        // fp32 [d][d]
   const float* s;
+  const float* mat_t;     // fp32 Pi^T then S^T ([2][d][d], from the derived buffer)
   const uint16_t* ring_k; // bf16 [batch][ring_cap][h_kv][d]
   const uint16_t* ring_v;
   float* out;             // [batch][h_q][d]
