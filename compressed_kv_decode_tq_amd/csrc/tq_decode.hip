@@ -298,73 +298,129 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(DecodeArgs a) {
 }
 
 // Combine: work-group per (sequence, query head), thread per channel.
+// Largest split count the combine kernel stages in LDS (decode_max_splits never
+// exceeds 2048 work-groups' worth of splits of one (sequence, KV head)).
+constexpr int kMaxCombineSplits = 2048;
+
+// Sum / max over a 128-thread block (two waves), result in every thread.
+__device__ __forceinline__ float block2_sum(float x, float* red2) {
+  x = wave_sum(x);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red2[w] = x;
+  __syncthreads();
+  return red2[0] + red2[1];
+}
+__device__ __forceinline__ float block2_max(float x, float* red2) {
+  x = wave_max(x);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red2[w] = x;
+  __syncthreads();
+  return fmaxf(red2[0], red2[1]);
+}
+
+// Merge of the split partials (m, l, acc) of one (sequence, query head) with
+// the exact ring tokens; MSE values are rotated back with Pi^T once.  Loads
+// are batched so the merge costs a few memory round trips, not one per split.
 template <bool VMSE>
 __global__ __launch_bounds__(kD) void combine_kernel(DecodeArgs a) {
   __shared__ float qv[kD];
-  __shared__ float red[kD];
-  __shared__ float pr[kD];  // ring probabilities (ring_cap <= 128 per pass)
+  __shared__ float s_f[kMaxCombineSplits];  // per split: m, then its merge factor
+  __shared__ float s_l[kMaxCombineSplits];
+  __shared__ float pr[kD];                  // ring probabilities (ring_cap <= 128 per pass)
   __shared__ float arot[kD];
+  __shared__ float red2[2];
   const int b = blockIdx.x / a.h_q, hq = blockIdx.x % a.h_q;
   const int h = hq / a.group;
   const int c = threadIdx.x;
   const size_t qoff = ((size_t)b * a.h_q + hq) * kD + c;
   qv[c] = a.q_bf16 ? bf2f(reinterpret_cast<const uint16_t*>(a.q)[qoff]) : reinterpret_cast<const float*>(a.q)[qoff];
   const int nr = (int)a.n_ring.v[b];
-  __syncthreads();
+  const int S = a.splits;
+  const float* part0 = a.partial + ((size_t)b * a.h_q + hq) * (kD + 2);
+  const size_t sstride = (size_t)a.batch * a.h_q * (kD + 2);
 
-  // ring scores: thread j scores ring token j
+  // split headers (m, l): thread c takes splits c, c + 128, ...
+  float M = -INFINITY;
+  for (int sp = c; sp < S; sp += kD) {
+    const float* ph = part0 + (size_t)sp * sstride;
+    const float m = ph[0], l = ph[1];
+    s_f[sp] = m;
+    s_l[sp] = l;
+    M = fmaxf(M, m);
+  }
+  __syncthreads();  // qv
+
+  // ring scores: thread j scores ring token j (its 256-byte key row in 16 loads)
   float sj = -INFINITY;
   if (c < nr) {
-    const uint16_t* kr = a.ring_k + (((size_t)b * a.ring_cap + c) * a.h_kv + h) * kD;
+    const u32x4* kr = reinterpret_cast<const u32x4*>(a.ring_k + (((size_t)b * a.ring_cap + c) * a.h_kv + h) * kD);
+    u32x4 kw[kD / 8];
+#pragma unroll
+    for (int i = 0; i < kD / 8; ++i) kw[i] = kr[i];
     float acc = 0.f;
-    for (int i = 0; i < kD; i += 2) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(kr + i);
-      acc = fmaf(qv[i], bf2f(w & 0xffffu), acc);
-      acc = fmaf(qv[i + 1], bf2f(w >> 16), acc);
-    }
+#pragma unroll
+    for (int i = 0; i < kD / 8; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc = fmaf(qv[8 * i + 2 * e], bf2f(kw[i][e] & 0xffffu), acc);
+        acc = fmaf(qv[8 * i + 2 * e + 1], bf2f(kw[i][e] >> 16), acc);
+      }
     sj = a.scale * acc;
   }
-  // global max over split partials and ring scores
-  float M = sj;
-  for (int s = 0; s < a.splits; ++s) {
-    const float* part = a.partial + (((size_t)s * a.batch + b) * a.h_q + hq) * (kD + 2);
-    M = fmaxf(M, part[0]);
-  }
-  red[c] = M;
-  __syncthreads();
-  for (int o = kD / 2; o > 0; o >>= 1) {
-    if (c < o) red[c] = fmaxf(red[c], red[c + o]);
-    __syncthreads();
-  }
-  M = red[0];
-  __syncthreads();
+  M = block2_max(fmaxf(M, sj), red2);
   float* outp = a.out + ((size_t)b * a.h_q + hq) * kD;
   if (M == -INFINITY) {  // no token at all
     outp[c] = 0.f;
     return;
   }
-  float L = 0.f, A = 0.f;
-  for (int s = 0; s < a.splits; ++s) {
-    const float* part = a.partial + (((size_t)s * a.batch + b) * a.h_q + hq) * (kD + 2);
-    const float ms = part[0];
-    if (ms == -INFINITY) continue;
-    const float f = __expf(ms - M);
-    L += f * part[1];
-    A += f * part[2 + c];
+
+  // merge factors of the splits and of the ring tokens; L in one block sum
+  float Lp = 0.f;
+  for (int sp = c; sp < S; sp += kD) {
+    const float m = s_f[sp];
+    const float f = m == -INFINITY ? 0.f : __expf(m - M);
+    s_f[sp] = f;
+    Lp = fmaf(f, s_l[sp], Lp);
   }
-  if (VMSE) {  // accumulated in rotated space: apply Pi^T once
+  const float pj = c < nr ? __expf(sj - M) : 0.f;
+  pr[c] = pj;
+  const float L = block2_sum(Lp + pj, red2);  // its barriers also publish s_f and pr
+
+  // channel c: sum over splits of f_s acc_s[c], eight partial loads in flight
+  float A = 0.f;
+  int sp = 0;
+  for (; sp + 8 <= S; sp += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = part0[(size_t)(sp + u) * sstride + 2 + c];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) A = fmaf(s_f[sp + u], v[u], A);
+  }
+  for (; sp < S; ++sp) A = fmaf(s_f[sp], part0[(size_t)sp * sstride + 2 + c], A);
+
+  if (VMSE) {  // accumulated in rotated space: apply Pi^T once (column c of Pi)
     arot[c] = A;
     __syncthreads();
     float o = 0.f;
-    for (int i = 0; i < kD; ++i) o = fmaf(a.pi[(size_t)i * kD + c], arot[i], o);
+    for (int i0 = 0; i0 < kD; i0 += 16) {
+      float w[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) w[u] = a.pi[(size_t)(i0 + u) * kD + c];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) o = fmaf(w[u], arot[i0 + u], o);
+    }
     A = o;
   }
-  pr[c] = c < nr ? __expf(sj - M) : 0.f;
-  __syncthreads();
-  for (int j = 0; j < nr; ++j) {
-    const float p = pr[j];
-    L += p;
-    A = fmaf(p, bf2f(a.ring_v[(((size_t)b * a.ring_cap + j) * a.h_kv + h) * kD + c]), A);
+  // ring values (original space)
+  for (int j0 = 0; j0 < nr; j0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = j0 + u < nr ? bf2f(a.ring_v[(((size_t)b * a.ring_cap + j0 + u) * a.h_kv + h) * kD + c]) : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) A = fmaf(j0 + u < nr ? pr[j0 + u] : 0.f, v[u], A);
   }
   outp[c] = L > 0.f ? A / L : 0.f;
 }

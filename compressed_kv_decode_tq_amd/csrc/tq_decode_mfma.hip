@@ -109,15 +109,18 @@ __global__ __launch_bounds__(256) void qprep_mfma_kernel(DecodeArgs a, int pm, i
     const int i = threadIdx.x & (kD - 1);
     const int which = threadIdx.x >> 7;
     const float* mt = a.mat_t + (size_t)which * kD * kD + i;
+    // all 128 loads are issued before the first use: one memory round trip
+    float w[kD];
+#pragma unroll
+    for (int j = 0; j < kD; ++j) w[j] = mt[(size_t)j * kD];
+    __builtin_amdgcn_sched_barrier(0);  // no use moves above the loads
     float acc[MAXG];
 #pragma unroll
     for (int gq = 0; gq < MAXG; ++gq) acc[gq] = 0.f;
-#pragma unroll 8
-    for (int j = 0; j < kD; ++j) {
-      const float w = mt[(size_t)j * kD];
 #pragma unroll
-      for (int gq = 0; gq < MAXG; ++gq) acc[gq] = fmaf(w, qv[gq][j], acc[gq]);
-    }
+    for (int j = 0; j < kD; ++j)
+#pragma unroll
+      for (int gq = 0; gq < MAXG; ++gq) acc[gq] = fmaf(w[j], qv[gq][j], acc[gq]);
 #pragma unroll
     for (int gq = 0; gq < MAXG; ++gq) (which == 0 ? qr : qs)[gq][i] = acc[gq];
   }
