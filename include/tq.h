@@ -134,14 +134,23 @@ int64_t tq_memory_bytes(const tq_layout* layout, int32_t batch, int32_t num_kv_h
 size_t tq_params_derived_bytes(int32_t d);
 
 /* Derive, on the device, the per-layer operands the kernels use from Pi and
- * S: bf16 hi/lo splits of Pi and of S Pi^T (the QJL projection expressed on
- * the rotated residual).  Run once per layer.  derived must hold
- * tq_params_derived_bytes(d) bytes. */
+ * S: bf16 hi/lo splits of Pi and of S Pi^T (the QJL projection of AUDIT 3 of
+ * page "turboquant/audit_claims.py" expressed on the rotated residual, since
+ * Pi is orthogonal) for the encode, and fp32 Pi^T and S^T for the decode's
+ * query rotation and sketch (page "TurboQuant — ...", section "Tại sao nó
+ * hoạt động": the query is rotated, the keys never are).  Run once per layer
+ * and whenever pi or s change; tq_encode_kv and tq_decode_attn read
+ * params->derived.  derived must hold tq_params_derived_bytes(d) bytes
+ * (256 KiB at d = 128).  Errors: TQ_ERR_UNSUPPORTED for a d other than 128
+ * that is a positive multiple of 32, else TQ_ERR_INVALID for a bad d, a NULL
+ * pointer or a derived_bytes below that size. */
 int tq_prepare_params(int32_t d, const float* pi, const float* s, void* derived,
                       size_t derived_bytes, void* stream);
 
-/* Encode n_new tokens of every sequence and KV head into the cache at token
- * positions dst_pos_host[b] .. dst_pos_host[b] + n_new - 1.  k, v:
+/* Encode (page "TurboQuant — ...", section "Ý tưởng cốt lõi"; page
+ * "turboquant/audit_claims.py", AUDIT 1 for the value code and AUDIT 3 for
+ * TurboQuantProd) n_new tokens of every sequence and KV head into the cache
+ * at token positions dst_pos_host[b] .. dst_pos_host[b] + n_new - 1.  k, v:
  * [batch][n_new][h_kv][d] in in_dtype (TQ_F32 or TQ_BF16).  Writes the key
  * planes and norms and the value planes and scalars of those positions only;
  * other positions of a shared 32-token value block are preserved.  Errors:
@@ -151,7 +160,8 @@ int tq_encode_kv(const tq_layout* layout, const tq_params* params, const void* k
                  const void* v, int32_t in_dtype, int64_t n_new, const int64_t* dst_pos_host,
                  const tq_cache* cache, void* stream);
 
-/* Append one token per sequence to the bf16 ring at position n_ring_host[b]
+/* Append (page "turboquant/audit_claims.py", AUDIT 1: the store keeps the
+ * most recent tokens uncompressed) one token per sequence to the bf16 ring at position n_ring_host[b]
  * (which must be < ring_cap), rounding to bf16.  k_new, v_new:
  * [batch][1][h_kv][d] in in_dtype (TQ_F32 or TQ_BF16). */
 int tq_ring_append(const void* k_new, const void* v_new, int32_t in_dtype, int32_t batch,
@@ -163,13 +173,19 @@ int tq_ring_append(const void* k_new, const void* v_new, int32_t in_dtype, int32
 size_t tq_decode_workspace_bytes(const tq_layout* layout, int32_t batch, int32_t num_q_heads,
                                  int32_t num_kv_heads, int64_t max_tokens);
 
-/* One decode step: for every sequence b and query head hq, attention of
+/* One decode step (page "03. Results & Benchmarks", sections "Latency
+ * Benchmarks" and "Next Steps": scores, QJL correction, online softmax and
+ * value accumulation fused over the compressed cache; page "TurboQuant —
+ * ...", section "Tại sao nó hoạt động" for the rotated query): for every
+ * sequence b and query head hq, attention of
  * q[b][hq] over the n_compressed_host[b] compressed tokens of KV head
  * hq / (h_q / h_kv) and the first n_ring_host[b] ring tokens, with scores
  * softmax_scale * <q, k>.  out: [batch][h_q][d] fp32.  q_dtype: TQ_F32 or
  * TQ_BF16.  ring_k/ring_v may be NULL when ring_cap is 0.  A sequence with no
- * token at all gets a zero output.  Errors: TQ_ERR_WORKSPACE when
- * workspace_bytes is below tq_decode_workspace_bytes. */
+ * token at all gets a zero output.  params->derived must have been filled by
+ * tq_prepare_params.  Errors: TQ_ERR_INVALID for a NULL derived buffer or
+ * inconsistent sizes, TQ_ERR_WORKSPACE when workspace_bytes is below
+ * tq_decode_workspace_bytes. */
 int tq_decode_attn(const tq_layout* layout, const tq_params* params, const void* q,
                    int32_t q_dtype, int32_t num_q_heads, const tq_cache* cache,
                    const int64_t* n_compressed_host, const void* ring_k, const void* ring_v,

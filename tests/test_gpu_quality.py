@@ -18,7 +18,7 @@ Protocols, following the pages:
   sqrt(3) pi^2 / (d 4^b), and the mean error is zero.
 - Attention fidelity (page "03. Results & Benchmarks", "Attention Quality"):
   the GPU decode output against exact softmax attention over the unquantized
-  K and V, beside the oracle's encode-then-attend path and its keys-only and
+  K and V, for random queries and for queries equal to a cached key, beside the oracle's encode-then-attend path and its keys-only and
   values-only splits.  On i.i.d. synthetic keys attention is diffuse, so the
   cosine is far below what the page reports for real model caches; the check
   is that the GPU path matches the oracle path's figure.
@@ -178,20 +178,31 @@ def test_attention_fidelity(name):
             vr.append(c_)
         kq.append(kr)
         vq.append(vr)
+    # eight probes per query head, as on the results page: four random
+    # queries, then four equal to a key of the head's own cache
+    rng = np.random.default_rng(11)
     res = {"gpu": [], "oracle": [], "keys only": [], "values only": []}
-    for step in range(4):
-        q = wl.query(w, step)
+    kprobe = {k_: [] for k_ in res}
+    for step in range(8):
+        if step < 4:
+            q = wl.query(w, step)
+        else:
+            pos = rng.integers(w.n_tokens, size=(w.batch, w.h_q))
+            q = torch.stack([torch.stack([k[b, pos[b, j], j // w.group] for j in range(w.h_q)])
+                             for b in range(w.batch)])
         qd = q.double().numpy()
         ref = oracle.decode_attention(qd, kk, vv)
         out = tq.decode_attn(prm, q.to(DEV), cache, [w.n_tokens] * w.batch).cpu().double().numpy()
-        res["gpu"].extend(_cosine(out, ref))
-        res["oracle"].extend(_cosine(oracle.decode_attention(qd, kq, vq), ref))
-        res["keys only"].extend(_cosine(oracle.decode_attention(qd, kq, vv), ref))
-        res["values only"].extend(_cosine(oracle.decode_attention(qd, kk, vq), ref))
-    res = {k_: np.array(v_) for k_, v_ in res.items()}
-    say(f"[attention fidelity] {name}, cosine to exact attention over {res['gpu'].size} head-steps:")
-    for k_, v_ in res.items():
-        say(f"  {k_:>12}: mean {v_.mean():.4f}  min {v_.min():.4f}")
-    # identical up to the rare boundary-window code flips of the GPU encode
-    assert abs(res["gpu"].mean() - res["oracle"].mean()) < 0.01
-    assert np.median(np.abs(res["gpu"] - res["oracle"])) < 1e-3
+        dst = res if step < 4 else kprobe
+        dst["gpu"].extend(_cosine(out, ref))
+        dst["oracle"].extend(_cosine(oracle.decode_attention(qd, kq, vq), ref))
+        dst["keys only"].extend(_cosine(oracle.decode_attention(qd, kq, vv), ref))
+        dst["values only"].extend(_cosine(oracle.decode_attention(qd, kk, vq), ref))
+    for tag, r in (("random queries", res), ("key queries", kprobe)):
+        r = {k_: np.array(v_) for k_, v_ in r.items()}
+        say(f"[attention fidelity] {name}, {tag}: cosine to exact attention over {r['gpu'].size} head-probes")
+        for k_, v_ in r.items():
+            say(f"  {k_:>12}: mean {v_.mean():.4f}  min {v_.min():.4f}")
+        # identical up to the rare boundary-window code flips of the GPU encode
+        assert abs(r["gpu"].mean() - r["oracle"].mean()) < 0.01, tag
+        assert np.median(np.abs(r["gpu"] - r["oracle"])) < 1e-3, tag
