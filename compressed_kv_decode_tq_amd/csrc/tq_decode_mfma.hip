@@ -66,6 +66,27 @@ __device__ __forceinline__ float row_sum16(float x) {
   return x + dpp<0x128>(x);
 }
 
+// Max of a non-negative integer over the wave, returned in a scalar register:
+// DPP within each 16-lane row, then the four row results through readlane.
+__device__ __forceinline__ uint32_t wave_max_u32_uniform(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, true));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, true));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xF, 0xF, true));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, true));
+  const uint32_t r0 = __builtin_amdgcn_readlane(x, 0), r1 = __builtin_amdgcn_readlane(x, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(x, 32), r3 = __builtin_amdgcn_readlane(x, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+
+// Sum over the four 16-lane rows (every lane gets the sum of its column)
+// through the cross-row lane swaps.
+__device__ __forceinline__ float col_sum4(float x) {
+  auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(t[0]) + __uint_as_float(t[1]);
+  auto u = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(u[0]) + __uint_as_float(u[1]);
+}
+
 // Bytes of a plane word: byte j of the result is bit (8j + s) of w, scaled by 2^s.
 __device__ __forceinline__ uint32_t plane_bytes(uint32_t w, int s) { return w & (0x01010101u << s); }
 
@@ -213,7 +234,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
   constexpr int kStride = kStage > kMerge ? kStage : kMerge;
   __shared__ __attribute__((aligned(16))) uint32_t smem[4 * kStride];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index is uniform: reading it from the first lane keeps the chunk
+  // loop, its bounds and the full/partial chunk test in scalar registers
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, n = lane & 15;
   const int sh = blockIdx.y;
   const int b = sh / a.h_kv, h = sh % a.h_kv;
@@ -241,7 +264,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
   // score of (head, token) in log2 units: u (K1 Dm + c0) + w (K2 Ds - c3), where
   // u = tau log2(e) n, w = u kappa gamma and Dm, Ds are the digit-combined
   // integer dot products; lane (g, n) scores head 4ht + g
-  float k1[NHT], k2[NHT], c0[NHT], c3[NHT];
+  float k1[NHT], k2[NHT], c0[NHT], c3[NHT], k1h[NHT], k2h[NHT];
 #pragma unroll
   for (int ht = 0; ht < NHT; ++ht) {
     const int hq = 4 * ht + g;
@@ -254,6 +277,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
     } else {
       c0[ht] = k1[ht] = k2[ht] = c3[ht] = 0.f;
     }
+    k1h[ht] = 16384.f * k1[ht];
+    k2h[ht] = 16384.f * k2[ht];
   }
   const float u_scale = a.scale * 1.4426950409f;  // exp(x) = exp2(x log2 e)
 
@@ -337,7 +362,13 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
   int it = 0;
   for (int64_t c0t = first; c0t < t_end; c0t += 256, ++it) {
     const int rem = (int)(t_end - c0t < 64 ? t_end - c0t : 64);  // valid tokens of this chunk
-    // ---- stage this chunk's per-token data and value words in LDS
+    // ---- stage this chunk's per-token data and value words in LDS; the
+    // value-weight exponent comes from the largest delta (min/max values) or
+    // |v| (MSE values) of the chunk, as bits (non-negative: integer order is
+    // float order)
+    const uint32_t mb_lane = VMSE ? pMeta[0]
+                                  : max(max(pMeta[0] & 0x7fffu, pMeta[1] & 0x7fffu),
+                                        max(pMeta[2] & 0x7fffu, pMeta[3] & 0x7fffu));
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     {
@@ -402,12 +433,13 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
       const bool valid = u < rem;
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) {
-        // digits carry 2^21, 2^14, 2^7, 1: two exact integer halves, then float
-        const float dm = fmaf((float)((am[ht][0] << 7) + am[ht][1]), 16384.f, (float)((am[ht][2] << 7) + am[ht][3]));
-        float sv = ut * fmaf(k1[ht], dm, c0[ht]);
+        // digits carry 2^21, 2^14, 2^7, 1: two exact integer halves, each
+        // scaled in float (the 2^14 of the upper half is folded into k1h, k2h)
+        const float dmh = (float)((am[ht][0] << 7) + am[ht][1]), dml = (float)((am[ht][2] << 7) + am[ht][3]);
+        float sv = ut * fmaf(dmh, k1h[ht], fmaf(dml, k1[ht], c0[ht]));
         if (QJL) {
-          const float ds = fmaf((float)((as[ht][0] << 7) + as[ht][1]), 16384.f, (float)((as[ht][2] << 7) + as[ht][3]));
-          sv = fmaf(wt, fmaf(k2[ht], ds, -c3[ht]), sv);
+          const float dsh = (float)((as[ht][0] << 7) + as[ht][1]), dsl = (float)((as[ht][2] << 7) + as[ht][3]);
+          sv = fmaf(wt, fmaf(dsh, k2h[ht], fmaf(dsl, k2[ht], -c3[ht])), sv);
         }
         sc[ht][ct] = valid ? sv : -INFINITY;
       }
@@ -420,12 +452,12 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
     for (int ht = 0; ht < NHT; ++ht) {
       const float mloc = row_max16(fmaxf(fmaxf(sc[ht][0], sc[ht][1]), fmaxf(sc[ht][2], sc[ht][3])));
       const float m_new = fmaxf(m_run[ht], mloc);
-      alpha[ht] = exp2f(m_run[ht] - m_new);
+      alpha[ht] = __builtin_amdgcn_exp2f(m_run[ht] - m_new);
       m_run[ht] = m_new;
       float lsum = 0.f;
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
-        const float e = exp2f(sc[ht][ct] - m_new);  // 0 for tokens past the end
+        const float e = __builtin_amdgcn_exp2f(sc[ht][ct] - m_new);  // 0 for tokens past the end
         s_p[(4 * ht + g) * 64 + 16 * ct + n] = e;
         lsum += e;
       }
@@ -450,11 +482,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
       // Rows of the value MFMA are (head 4ht + n/4, group n%4): this lane turns
       // its 16 weights p_t delta_t(group) into signed base-256 fixed point.
       const int grp = n & 3;
-      uint32_t mb = 0;
-#pragma unroll
-      for (int gi = 0; gi < NG; ++gi) mb = max(mb, s_meta[lane * NG + gi] & 0x7fffu);
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, o));
+      const uint32_t mb = wave_max_u32_uniform(mb_lane);
       const int ev = 44 - (int)(mb >> 10);  // every delta < 2^(e - 14): |W| < 2^30
       const float inv_sv = ldexpf(1.f, -ev);
       // tokens of dword ct sit at bit shift s = 4(ct&1) + g of the value words;
@@ -497,9 +525,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
       float Mpv[NHT][NG];
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) {
-        float x = M[ht];
-        x += __shfl_xor(x, 16);
-        x += __shfl_xor(x, 32);
+        const float x = col_sum4(M[ht]);
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) Mpv[ht][gi] = __shfl(x, 4 * g + gi);
       }
@@ -536,9 +562,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
       // MSE values: weights p_t |v_t| (same for every value plane), rows (head,
       // digit); accumulated in rotated space
       const int mydig_shift = 7 * (3 - (n & 3));
-      uint32_t mb = s_meta[lane * NG];  // |v| as fp32 bits (non-negative: integer order is float order)
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, o));
+      const uint32_t mb = wave_max_u32_uniform(mb_lane);
       int ex;
       frexpf(__uint_as_float(mb), &ex);
       const int ev = 26 - ex;
@@ -571,9 +595,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
       float PNpv[NHT];
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) {
-        float x = PN[ht];
-        x += __shfl_xor(x, 16);
-        x += __shfl_xor(x, 32);
+        const float x = col_sum4(PN[ht]);
         PNpv[ht] = __shfl(x, 4 * g);
       }
 #pragma unroll
