@@ -19,6 +19,73 @@ __host__ __device__ __forceinline__ int vbit(int u) { return 8 * (u & 3) + 4 * (
 // Inverse: token slot held in bit position b.
 __host__ __device__ __forceinline__ int vslot(int b) { return 16 * ((b >> 2) & 1) + 4 * (b & 3) + (b >> 3); }
 
+// Min/max value codes of width 2 or 4 are stored packed rather than as bit
+// planes: word h of a 32-token block holds the tokens (32/b) h + i, i < 32/b,
+// with the code of token i in bits 8 (i % 4) + b (i / 4) .. + b - 1, so an AND
+// leaves whole codes in byte lanes.  Width 1 is the same as one bit plane, and
+// width 3 and the Lloyd-Max (MSE) value codes keep bit planes.
+__host__ __device__ constexpr bool packed_value_codes(bool mse, int bits) { return !mse && (bits == 2 || bits == 4); }
+
+// Code of token slot u (0..31) of a block from its `bits` value words.
+template <int BITS, bool PACKED>
+__device__ __forceinline__ uint32_t value_code(const uint32_t (&w)[BITS], int u) {
+  if (PACKED) {
+    constexpr int per = 32 / BITS;
+    const int i = u % per;
+    return (w[u / per] >> (8 * (i & 3) + BITS * (i >> 2))) & ((1u << BITS) - 1u);
+  }
+  uint32_t c = 0;
+#pragma unroll
+  for (int p = 0; p < BITS; ++p) c |= ((w[p] >> vbit(u)) & 1u) << p;
+  return c;
+}
+
+// Bit-plane words (bit p of token u in bit vbit(u) of word p) -> packed words,
+// for BITS = 2 or 4.  Byte j of every word is handled in place.
+template <int BITS>
+__device__ __forceinline__ void planes_to_packed(const uint32_t (&pl)[BITS], uint32_t (&out)[BITS]) {
+  static_assert(BITS == 2 || BITS == 4, "packed widths are 2 and 4");
+  if (BITS == 2) {
+    // token 16h + 4k + j: plane bit 8j + 4h + k -> packed word h, bits 8j + 2k + q
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t o = 0;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        uint32_t t = (pl[q] >> (4 * h)) & 0x0f0f0f0fu;  // bit k of byte j
+        t = (t | (t << 2)) & 0x33333333u;
+        t = (t | (t << 1)) & 0x55555555u;             // bit k -> bit 2k
+        o |= t << q;
+      }
+      out[h] = o;
+    }
+  } else {
+    // token 8h + 4k + j: plane bit 8j + 4(h/2) + 2(h%2) + k -> packed word h,
+    // bits 8j + 4k + q
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      uint32_t o = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t t = (pl[q] >> (4 * (h >> 1) + 2 * (h & 1))) & 0x03030303u;
+        t = (t | (t << 3)) & 0x11111111u;  // bit k -> bit 4k
+        o |= t << q;
+      }
+      out[h] = o;
+    }
+  }
+}
+
+// Valid-token mask in the bit-plane order -> the matching bit mask of each
+// packed word (all b bits of every valid token).
+template <int BITS>
+__device__ __forceinline__ void mask_to_packed(uint32_t vmask, uint32_t (&out)[BITS]) {
+  uint32_t pl[BITS];
+#pragma unroll
+  for (int p = 0; p < BITS; ++p) pl[p] = vmask;
+  planes_to_packed<BITS>(pl, out);
+}
+
 // fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
 __device__ __forceinline__ uint32_t f2bf(float f) {
   uint32_t u = __float_as_uint(f);

@@ -217,12 +217,14 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(DecodeArgs a) {
 #pragma unroll 4
       for (int j = 0; j < kChunk; ++j) {
         const int blk = j >> 5, tb = j & 31;
-        uint32_t code0 = 0, code1 = 0;
+        uint32_t w0[VB], w1[VB];
 #pragma unroll
         for (int p = 0; p < VB; ++p) {
-          code0 |= ((w[blk][p][0] >> vbit(tb)) & 1u) << p;
-          code1 |= ((w[blk][p][1] >> vbit(tb)) & 1u) << p;
+          w0[p] = w[blk][p][0];
+          w1[p] = w[blk][p][1];
         }
+        const uint32_t code0 = value_code<VB, packed_value_codes(VMSE, VB)>(w0, tb);
+        const uint32_t code1 = value_code<VB, packed_value_codes(VMSE, VB)>(w1, tb);
         float v0, v1;
         if (VMSE) {
           const float nv = __uint_as_float(mb[wave][j][0]);

@@ -466,58 +466,57 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    // value-MFMA rows are (head 4ht + n/4, .): this lane's 16 tokens 16ct + 4g + r
-    floatx4 pv[NHT][4];
-#pragma unroll
-    for (int ht = 0; ht < NHT; ++ht)
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-        pv[ht][ct] = *reinterpret_cast<const floatx4*>(s_p + (4 * ht + (n >> 2)) * 64 + 16 * ct + 4 * g);
     float alpha_pv[NHT];
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) alpha_pv[ht] = alpha[ht];  // accumulator rows: head 4ht + g
 
     // ---- values
     if (!VMSE) {
-      // Rows of the value MFMA are (head 4ht + n/4, group n%4): this lane turns
-      // its 16 weights p_t delta_t(group) into signed base-256 fixed point.
+      static_assert(VMSE || VB == 2, "min/max values on this path are 2-bit packed codes");
+      // Rows of the value MFMA are (head 4ht + n/4, group n%4) and this lane
+      // supplies tokens 16g + 4k + r (k, r < 4): the tokens of the packed code
+      // word g of the chunk, whose AND with 0x03 << 2k (k < 3), or with 0x30
+      // after a shift by 2 (k = 3), leaves code(16g + 4k + r) * 4^min(k, 2) in
+      // byte r.  The weights p_t delta_t(group) carry the inverse scale and
+      // become signed base-256 fixed point.
       const int grp = n & 3;
+      floatx4 pv[NHT][4];
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          pv[ht][k] = *reinterpret_cast<const floatx4*>(s_p + (4 * ht + (n >> 2)) * 64 + 16 * g + 4 * k);
       const uint32_t mb = wave_max_u32_uniform(mb_lane);
       const int ev = 44 - (int)(mb >> 10);  // every delta < 2^(e - 14): |W| < 2^30
       const float inv_sv = ldexpf(1.f, -ev);
-      // tokens of dword ct sit at bit shift s = 4(ct&1) + g of the value words;
-      // their weights carry 2^-s, negated where s = 7 (the byte 0x80 reads -128)
-      const float scl0 = ldexpf(1.f, ev - g);
-      const float scl1 = g == 3 ? -ldexpf(1.f, ev - 7) : ldexpf(1.f, ev - 4 - g);
       u32x4 A[NHT][4];
       float M[NHT];
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) {
         M[ht] = 0.f;
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          const float scl = (ct & 1) ? scl1 : scl0;
-          const float rnd = scl < 0.f ? -0.5f : 0.5f;
+        for (int k = 0; k < 4; ++k) {
+          const float scl = ldexpf(1.f, ev - (k < 2 ? 2 * k : 4));
           uint32_t V[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const uint32_t mm = s_meta[(16 * ct + 4 * g + r) * NG + grp];
+            const uint32_t mm = s_meta[(16 * g + 4 * k + r) * NG + grp];
             const float dl = __half2float(__ushort_as_half((unsigned short)(mm & 0xffffu)));
             const float mn = __half2float(__ushort_as_half((unsigned short)(mm >> 16)));
-            const float pe = pv[ht][ct][r];
-            const int W = (int)fmaf(pe * scl, dl, rnd);
+            const float pe = pv[ht][k][r];
+            const int W = (int)fmaf(pe * scl, dl, 0.5f);  // non-negative: rounds to nearest
             V[r] = ((uint32_t)W + 0x00808080u) ^ 0x00808080u;  // bytes = signed base-256 digits
             M[ht] = fmaf(pe, mn, M[ht]);
           }
-          // 4x4 byte transpose: digit plane k holds byte k of the four tokens
+          // 4x4 byte transpose: digit plane d holds byte d of the four tokens
           const uint32_t t01lo = __builtin_amdgcn_perm(V[1], V[0], 0x05010400u);
           const uint32_t t01hi = __builtin_amdgcn_perm(V[1], V[0], 0x07030602u);
           const uint32_t t23lo = __builtin_amdgcn_perm(V[3], V[2], 0x05010400u);
           const uint32_t t23hi = __builtin_amdgcn_perm(V[3], V[2], 0x07030602u);
-          A[ht][3][ct] = __builtin_amdgcn_perm(t23lo, t01lo, 0x05040100u);  // least significant digit
-          A[ht][2][ct] = __builtin_amdgcn_perm(t23lo, t01lo, 0x07060302u);
-          A[ht][1][ct] = __builtin_amdgcn_perm(t23hi, t01hi, 0x05040100u);
-          A[ht][0][ct] = __builtin_amdgcn_perm(t23hi, t01hi, 0x07060302u);  // most significant digit
+          A[ht][3][k] = __builtin_amdgcn_perm(t23lo, t01lo, 0x05040100u);  // least significant digit
+          A[ht][2][k] = __builtin_amdgcn_perm(t23lo, t01lo, 0x07060302u);
+          A[ht][1][k] = __builtin_amdgcn_perm(t23hi, t01hi, 0x05040100u);
+          A[ht][0][k] = __builtin_amdgcn_perm(t23hi, t01hi, 0x07060302u);  // most significant digit
         }
       }
       // sum_t p_t min_t per (head, group): reduce over the four token quarters,
@@ -531,34 +530,28 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
       }
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
-        const int ch = 16 * nt + n;
         const int gi = nt >> 1;  // group of channels 16nt..16nt+15
-        int hi[NHT], lo[NHT];
-#pragma unroll
-        for (int ht = 0; ht < NHT; ++ht) hi[ht] = lo[ht] = 0;
-#pragma unroll
-        for (int pv = 0; pv < VB; ++pv) {
-          u32x4 B;
-#pragma unroll
-          for (int d = 0; d < 4; ++d) B[d] = plane_bytes(s_vw[((d >> 1) * VB + pv) * kD + ch], 4 * (d & 1) + g);
-#pragma unroll
-          for (int ht = 0; ht < NHT; ++ht) {
-            // row (head g, group gi) of the four digit products
-            const int d0 = mfma_i8(A[ht][0], B, i32x4{0, 0, 0, 0})[gi];
-            const int d1 = mfma_i8(A[ht][1], B, i32x4{0, 0, 0, 0})[gi];
-            const int d2 = mfma_i8(A[ht][2], B, i32x4{0, 0, 0, 0})[gi];
-            const int d3 = mfma_i8(A[ht][3], B, i32x4{0, 0, 0, 0})[gi];
-            hi[ht] += ((d0 << 8) + d1) << pv;  // plane pv carries weight 2^pv
-            lo[ht] += ((d2 << 8) + d3) << pv;
-          }
-        }
+        const uint32_t w = s_vw[g * kD + 16 * nt + n];
+        const u32x4 B = {w & 0x03030303u, w & 0x0c0c0c0cu, w & 0x30303030u, (w >> 2) & 0x30303030u};
 #pragma unroll
         for (int ht = 0; ht < NHT; ++ht) {
-          const float v = fmaf((float)hi[ht], 65536.f, (float)lo[ht]);
+          // row (head g, group gi) of the four digit products
+          const int d0 = mfma_i8(A[ht][0], B, i32x4{0, 0, 0, 0})[gi];
+          const int d1 = mfma_i8(A[ht][1], B, i32x4{0, 0, 0, 0})[gi];
+          const int d2 = mfma_i8(A[ht][2], B, i32x4{0, 0, 0, 0})[gi];
+          const int d3 = mfma_i8(A[ht][3], B, i32x4{0, 0, 0, 0})[gi];
+          const float v = fmaf((float)((d0 << 8) + d1), 65536.f, (float)((d2 << 8) + d3));
           acc[ht][nt] = fmaf(acc[ht][nt], alpha_pv[ht], fmaf(v, inv_sv, Mpv[ht][gi]));
         }
       }
     } else {
+      // this lane's 16 tokens in the bit-plane order: 16ct + 4g + r
+      floatx4 pv[NHT][4];
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+          pv[ht][ct] = *reinterpret_cast<const floatx4*>(s_p + (4 * ht + (n >> 2)) * 64 + 16 * ct + 4 * g);
       // MSE values: weights p_t |v_t| (same for every value plane), rows (head,
       // digit); accumulated in rotated space
       const int mydig_shift = 7 * (3 - (n & 3));

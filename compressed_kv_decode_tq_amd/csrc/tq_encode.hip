@@ -541,11 +541,32 @@ __global__ __launch_bounds__(256) void encode_minmax_kernel(EncodeArgs a) {
     });
     const uint32_t vmask = (uint32_t)__ballot(valid);  // bit l: lane l's token is written
     const int64_t nblk_cap = a.capacity >> 5;
+    uint32_t out[BITS][2], msk[BITS];
+    if constexpr (packed_value_codes(false, BITS)) {
+      // widths 2 and 4 are stored as packed codes
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        uint32_t pl[BITS], pk[BITS];
+#pragma unroll
+        for (int p = 0; p < BITS; ++p) pl[p] = w[p][hf];
+        planes_to_packed<BITS>(pl, pk);
+#pragma unroll
+        for (int p = 0; p < BITS; ++p) out[p][hf] = pk[p];
+      }
+      mask_to_packed<BITS>(vmask, msk);
+    } else {
+#pragma unroll
+      for (int p = 0; p < BITS; ++p) {
+        out[p][0] = w[p][0];
+        out[p][1] = w[p][1];
+        msk[p] = vmask;
+      }
+    }
 #pragma unroll
     for (int p = 0; p < BITS; ++p) {
       uint32_t* base = a.v_planes + ((slot * nblk_cap + blk) * BITS + p) * kD;
-      store_plane_word(base + lane, w[p][0], vmask);
-      store_plane_word(base + 64 + lane, w[p][1], vmask);
+      store_plane_word(base + lane, out[p][0], msk[p]);
+      store_plane_word(base + 64 + lane, out[p][1], msk[p]);
     }
   }
 }

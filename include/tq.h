@@ -40,9 +40,13 @@
  *                (1 = non-negative); coordinate i is bit i%8 of byte i/8.
  *      k_norm    [batch][h_kv][capacity] scalar_dtype   |k|
  *      k_rnorm   [batch][h_kv][capacity] scalar_dtype   |r| (QJL keys only)
- *      v_planes  uint32 [batch][h_kv][capacity/32][value_bits][d]: word
+ *      v_planes  uint32 [batch][h_kv][capacity/32][value_bits][d].  Bit
+ *                planes (MSE values; min/max values of width 1 or 3): word
  *                (blk, p, c) holds bit p of the code of token 32*blk+u,
- *                channel c, in bit 8*(u%4) + 4*(u/16) + (u/4)%4.
+ *                channel c, in bit 8*(u%4) + 4*(u/16) + (u/4)%4.  Packed
+ *                codes (min/max values of width b = 2 or 4): word (blk, h, c)
+ *                holds the codes of tokens 32*blk + (32/b)*h + i, i < 32/b,
+ *                token i's code in bits 8*(i%4) + b*(i/4) .. + b-1.
  *      v_meta    fp16 [batch][h_kv][capacity][d/value_group][2] = (scale, min)
  *                (min/max values only)
  *      v_norm    [batch][h_kv][capacity] scalar_dtype   |v| (MSE values only)

@@ -39,5 +39,6 @@ from .quantize import (  # noqa: F401
 from .attention import decode_attention, decode_attention_bruteforce  # noqa: F401
 from .layout import (  # noqa: F401
     Layout, pack_key_planes, unpack_key_planes, pack_value_planes, unpack_value_planes,
+    pack_value_codes, unpack_value_codes, pack_value_words, unpack_value_words, value_words_packed,
     memory_bytes, bytes_per_token_head,
 )

@@ -12,10 +12,15 @@ Per (sequence, KV head) slot of ``capacity`` tokens:
   plane key_mse_bits holds the QJL sign bits (1 = non-negative).  Inside a
   plane, coordinate i is bit i % 8 of byte i // 8 (LSB first).
 * key norm, key residual norm   [capacity] fp32 or fp16.
-* value planes uint32 [capacity/32][value_bits][d]: word (blk, p, c) holds bit
-  p of the code of token 32*blk + u at channel c, for u = 0..31, in bit
-  value_bit(u) = 8*(u % 4) + 4*(u // 16) + (u // 4) % 4 (a fixed permutation of
-  the 32 token slots of a block).
+* value words uint32 [capacity/32][value_bits][d], in one of two forms:
+  - bit planes (MSE values, and min/max values of width 1 or 3): word (blk, p,
+    c) holds bit p of the code of token 32*blk + u at channel c, for u = 0..31,
+    in bit value_bit(u) = 8*(u % 4) + 4*(u // 16) + (u // 4) % 4 (a fixed
+    permutation of the 32 token slots of a block);
+  - packed codes (min/max values of width b = 2 or 4): word (blk, h, c) holds
+    the b-bit codes of tokens 32*blk + (32/b)*h + i, i < 32/b, at channel c,
+    the code of token i in bits 8*(i % 4) + b*(i // 4) .. + b - 1.  For b = 1
+    this is the same as one bit plane.
 * value meta (min/max values)   fp16 [capacity][d/group][2] = (scale, min).
 * value norm (MSE values)       [capacity] fp32 or fp16.
 
@@ -140,3 +145,57 @@ def unpack_value_planes(words: np.ndarray, n_tokens: int) -> np.ndarray:
     for p in range(bits):
         code |= (((w[:, p, None, :] >> tt[None, :, None]) & 1).astype(np.int64)) << p
     return code.reshape(nblk * 32, d)[:n_tokens]
+
+
+def value_words_packed(kind: str, bits: int) -> bool:
+    """True where the value words hold packed codes rather than bit planes."""
+    return kind == "minmax" and bits in (2, 4)
+
+
+def packed_code_bit(i, bits: int) -> np.ndarray:
+    """Lowest bit, inside its packed word, of the code of token i (< 32/bits)."""
+    i = np.asarray(i)
+    return 8 * (i % 4) + bits * (i // 4)
+
+
+def pack_value_codes(code: np.ndarray, bits: int, capacity: int | None = None) -> np.ndarray:
+    """(T, d) codes of width 1, 2 or 4 -> (capacity/32, bits, d) uint32 packed
+    words.  Tokens T..capacity-1 are zero."""
+    if bits not in (1, 2, 4):
+        raise ValueError("packed codes have width 1, 2 or 4")
+    code = np.asarray(code, dtype=np.int64)
+    t, d = code.shape
+    cap = t if capacity is None else capacity
+    if cap % 32 or cap < t:
+        raise ValueError("capacity must be a multiple of 32 and hold every token")
+    full = np.zeros((cap, d), dtype=np.uint64)
+    full[:t] = code
+    per = 32 // bits
+    blocks = full.reshape(cap // 32, bits, per, d)  # (blk, h, i, c)
+    shift = packed_code_bit(np.arange(per), bits).astype(np.uint64)
+    out = np.sum(blocks << shift[None, None, :, None], axis=2)
+    return out.astype(np.uint32)
+
+
+def unpack_value_codes(words: np.ndarray, n_tokens: int) -> np.ndarray:
+    """(capacity/32, bits, d) uint32 packed words -> (n_tokens, d) codes."""
+    w = np.asarray(words, dtype=np.uint64)
+    nblk, bits, d = w.shape
+    per = 32 // bits
+    shift = packed_code_bit(np.arange(per), bits).astype(np.uint64)
+    code = (w[:, :, None, :] >> shift[None, None, :, None]) & np.uint64((1 << bits) - 1)
+    return code.astype(np.int64).reshape(nblk * 32, d)[:n_tokens]
+
+
+def pack_value_words(code: np.ndarray, bits: int, kind: str, capacity: int | None = None) -> np.ndarray:
+    """Value words of the layout's form (packed codes or bit planes)."""
+    if value_words_packed(kind, bits):
+        return pack_value_codes(code, bits, capacity)
+    return pack_value_planes(code, bits, capacity)
+
+
+def unpack_value_words(words: np.ndarray, n_tokens: int, kind: str) -> np.ndarray:
+    """Inverse of pack_value_words."""
+    if value_words_packed(kind, np.asarray(words).shape[1]):
+        return unpack_value_codes(words, n_tokens)
+    return unpack_value_planes(words, n_tokens)

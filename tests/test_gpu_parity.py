@@ -90,8 +90,8 @@ def test_encode_ragged_positions_preserve_neighbours(value_kind):
         assert torch.equal(kp[:, mask], kb[:, mask])
         # value bits of untouched tokens in shared blocks are preserved
         for h in range(w.h_kv):
-            va = read_value_planes(cache.v_planes[b, h].cpu().numpy(), cap)
-            vbh = read_value_planes(before["v_planes"][b, h].cpu().numpy(), cap)
+            va = read_value_planes(cache.v_planes[b, h].cpu().numpy(), cap, w)
+            vbh = read_value_planes(before["v_planes"][b, h].cpu().numpy(), cap, w)
             assert np.array_equal(va[mask.numpy()], vbh[mask.numpy()])
             ref = encode_slot(w, bk, pi, s, k[b, :, h].double().numpy(), v[b, :, h].double().numpy())
             check_encode_slot(w, bk, cache, b, h, ref, p0, 77, f"ragged b{b} h{h}")
@@ -254,7 +254,7 @@ def test_end_to_end(name):
     flipped = np.zeros((w.batch, w.h_kv), dtype=bool)
     for (b, h), sc in codes.items():
         _, ex_m, ex_q = key_plane_mismatches(w, bk, cache.k_planes[b, h, :n].cpu().numpy(), sc.key)
-        idx_g = read_value_planes(cache.v_planes[b, h].cpu().numpy(), n)
+        idx_g = read_value_planes(cache.v_planes[b, h].cpu().numpy(), n, w)
         ex_v = 0 if w.value_kind == "minmax" else int(np.sum(idx_g != sc.val.idx))
         flipped[b, h] = (ex_m + ex_q + ex_v) > 0
     hq_flip = np.repeat(flipped, w.group, axis=1)

@@ -55,6 +55,36 @@ def test_value_planes_round_trip_and_bit_positions():
     assert np.count_nonzero(w) == 3
 
 
+def test_packed_value_codes_round_trip_and_bit_positions():
+    rng = np.random.default_rng(2)
+    for bits in (1, 2, 4):
+        code = rng.integers(0, 1 << bits, size=(70, 128))
+        words = oracle.pack_value_codes(code, bits, capacity=96)
+        assert words.shape == (3, bits, 128) and words.dtype == np.uint32
+        assert np.array_equal(oracle.unpack_value_codes(words, 70), code)
+        assert np.all(oracle.unpack_value_codes(words, 96)[70:] == 0)
+    # width 1: packed codes and bit planes are the same words
+    code = rng.integers(0, 2, size=(64, 128))
+    assert np.array_equal(oracle.pack_value_codes(code, 1), oracle.pack_value_planes(code, 1))
+    # worked examples, width 2 (16 tokens per word): token 33 = block 1, slot 1
+    # -> word 0, bits 8..9; token 22 = block 0, slot 22 -> word 1, i = 6 -> bits
+    # 8*2 + 2*1 = 18..19
+    code = np.zeros((64, 128), dtype=np.int64)
+    code[33, 5] = 3
+    code[22, 0] = 2
+    w = oracle.pack_value_codes(code, 2)
+    assert w[1, 0, 5] == 3 << 8 and w[0, 1, 0] == 1 << 19
+    assert np.count_nonzero(w) == 2
+    # width 4 (8 tokens per word): token 13 -> word 1, i = 5 -> bits 8 + 4 = 12..15
+    code = np.zeros((32, 128), dtype=np.int64)
+    code[13, 7] = 0xB
+    w = oracle.pack_value_codes(code, 4)
+    assert w[0, 1, 7] == 0xB << 12 and np.count_nonzero(w) == 1
+    # the layout picks packed codes for min/max widths 2 and 4 only
+    assert [oracle.value_words_packed("minmax", b) for b in (1, 2, 3, 4)] == [False, True, False, True]
+    assert not any(oracle.value_words_packed("mse", b) for b in (1, 2, 3, 4))
+
+
 def _gold(golden_dir):
     return json.load(open(os.path.join(golden_dir, "byte_counts.json")))
 

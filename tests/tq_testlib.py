@@ -95,7 +95,7 @@ def upload_slot(cache: tq.Cache, w: wl.Workload, b: int, h: int, sc: SlotCode, s
         codes = sc.val.idx
         cache.v_norm[b, h, start:start + t] = torch.from_numpy(sc.val.norm.astype(sd)).to(dev)
     cap = ((t + 31) // 32) * 32
-    words = oracle.pack_value_planes(codes, w.value_bits, cap).view(np.int32)
+    words = oracle.pack_value_words(codes, w.value_bits, w.value_kind, cap).view(np.int32)
     cache.v_planes[b, h, start // 32:start // 32 + cap // 32] = torch.from_numpy(words).to(dev)
 
 
@@ -116,16 +116,26 @@ def read_key_planes(planes: np.ndarray, d: int, mse_bits: int, qjl: bool):
     return idx, (bits[:, mse_bits, :].astype(np.uint8) if qjl else None)
 
 
-def read_value_planes(words: np.ndarray, n_tokens: int) -> np.ndarray:
-    """Codes [n_tokens, d] from token-transposed words [blocks, bits, d]; token
-    slot u of a block sits in bit 8*(u%4) + 4*(u//16) + (u//4)%4 of its word."""
-    w = np.ascontiguousarray(words).view(np.uint32).astype(np.uint64)
-    nblk, bits, d = w.shape
-    u = np.arange(32)
-    t = (8 * (u % 4) + 4 * (u // 16) + (u // 4) % 4).astype(np.uint64)
+def read_value_planes(words: np.ndarray, n_tokens: int, w: wl.Workload) -> np.ndarray:
+    """Codes [n_tokens, d] from the value words [blocks, bits, d] of the
+    workload's layout.  Bit planes: bit p of token slot u of a block sits in
+    bit 8*(u%4) + 4*(u//16) + (u//4)%4 of word p.  Packed codes (min/max values
+    of width b = 2 or 4): word h holds tokens (32/b)*h + i, token i's code in
+    bits 8*(i%4) + b*(i//4) upward."""
+    x = np.ascontiguousarray(words).view(np.uint32).astype(np.uint64)
+    nblk, bits, d = x.shape
     code = np.zeros((nblk, 32, d), dtype=np.int64)
-    for p in range(bits):
-        code |= ((w[:, p, None, :] >> t[None, :, None]) & 1).astype(np.int64) << p
+    if w.value_kind == "minmax" and bits in (2, 4):
+        per = 32 // bits
+        for u in range(32):
+            h, i = divmod(u, per)
+            sh = np.uint64(8 * (i % 4) + bits * (i // 4))
+            code[:, u, :] = ((x[:, h, :] >> sh) & np.uint64((1 << bits) - 1)).astype(np.int64)
+    else:
+        u = np.arange(32)
+        t = (8 * (u % 4) + 4 * (u // 16) + (u // 4) % 4).astype(np.uint64)
+        for p in range(bits):
+            code |= ((x[:, p, None, :] >> t[None, :, None]) & 1).astype(np.int64) << p
     return code.reshape(-1, d)[:n_tokens]
 
 
@@ -180,7 +190,7 @@ def check_encode_slot(w, bk, cache, b, h, ref, start, n, tag):
     blk0 = start // 32
     nblk = (start + n + 31) // 32 - blk0
     words = cache.v_planes[b, h, blk0:blk0 + nblk].cpu().numpy()
-    codes = read_value_planes(words, nblk * 32)[start - blk0 * 32: start - blk0 * 32 + n]
+    codes = read_value_planes(words, nblk * 32, w)[start - blk0 * 32: start - blk0 * 32 + n]
     if w.value_kind == "minmax":
         assert np.array_equal(codes, ref.val.code), f"{tag}: min/max codes differ"
         meta = cache.v_meta[b, h, start:start + n].cpu().numpy()
@@ -214,7 +224,7 @@ def slot_from_cache(w: wl.Workload, cache: tq.Cache, b: int, h: int, n: int) -> 
     norm = cache.k_norm[b, h, :n].float().cpu().double().numpy()
     rnorm = cache.k_rnorm[b, h, :n].float().cpu().double().numpy() if w.key_qjl else None
     key = oracle.KeyCode(idx=idx, qjl=qjl, norm=norm, rnorm=rnorm, y=None, z=None)
-    codes = read_value_planes(cache.v_planes[b, h, :(n + 31) // 32].cpu().numpy(), n)
+    codes = read_value_planes(cache.v_planes[b, h, :(n + 31) // 32].cpu().numpy(), n, w)
     if w.value_kind == "minmax":
         meta = cache.v_meta[b, h, :n].cpu().numpy()
         val = oracle.ValueMinMax(code=codes, scale16=meta[..., 0].copy(), min16=meta[..., 1].copy(), ratio=None)
