@@ -225,9 +225,12 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
   constexpr int NHEAD = 4 * NHT;
 
   // per-wave staging of the current chunk, reused at the end for the merge
-  constexpr int kStageMeta = 64 * NG;           // dwords
-  constexpr int kStageNg = 64 * 2;              // floats: per token u = tau log2e n, w = u kappa gamma
-  constexpr int kStageVw = 2 * VB * kD;         // dwords
+  // min/max staging is padded so the value-phase reads hit distinct banks:
+  // 4 dwords after every 16 tokens of metadata, 16 after every 128 value words
+  constexpr int kMetaPad = VMSE ? 0 : 4, kVwPad = VMSE ? 0 : 16;
+  constexpr int kStageMeta = 64 * NG + 4 * kMetaPad;  // dwords
+  constexpr int kStageNg = 64 * 4;              // floats: per token u = tau log2e n, w = u kappa gamma, mask
+  constexpr int kStageVw = 2 * VB * kD + 2 * VB * kVwPad;  // dwords
   constexpr int kStageP = NHEAD * 64;           // floats: p of (head, token) for the value MFMA
   constexpr int kStage = kStageMeta + kStageNg + kStageVw + kStageP;
   constexpr int kMerge = NHEAD * (kD + 2);
@@ -305,55 +308,60 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
   u32x4 pVw[VB];
   const int64_t first = t_begin + 64 * wave;
   const int ssz = a.scalar_f16 ? 2 : 4;
-  // per-lane addresses at the wave's first chunk; every later chunk is 256 tokens on
-  const uint8_t* p_k = kp + (first + n) * (int64_t)rec + 4 * g;
-  const char* p_n = reinterpret_cast<const char*>(a.k_norm) + (int64_t)(sidx0 + first + lane) * ssz;
-  const char* p_g = QJL ? reinterpret_cast<const char*>(a.k_rnorm) + (int64_t)(sidx0 + first + lane) * ssz : nullptr;
-  const char* p_m = VMSE ? reinterpret_cast<const char*>(a.v_norm) + (int64_t)(sidx0 + first + lane) * ssz
-                         : reinterpret_cast<const char*>(a.v_meta) + (int64_t)(sidx0 + first + lane) * (NG * 4);
-  const uint32_t* p_v = vp + (first >> 5) * VB * kD + lane * 4;
-  auto scalar_at = [&](const char* p) -> float {
+  // Addresses are a wave-uniform chunk base (scalar registers) plus a 32-bit
+  // per-lane byte offset, so the loads take the scalar-base form and no
+  // 64-bit per-lane pointers stay live across the loop.
+  const uint32_t k_lane = n * (uint32_t)rec + 4 * g;  // word g of token n's plane records
+  const uint32_t s_lane = lane * (uint32_t)ssz;       // token `lane`'s scalar
+  const uint32_t m_lane = VMSE ? s_lane : lane * (uint32_t)(NG * 4);
+  const uint32_t v_lane = lane * 16u;                 // four value words per lane
+  auto scalar_at = [&](const void* base, uint32_t off) -> float {
+    const char* p = reinterpret_cast<const char*>(base) + off;
     return a.scalar_f16 ? __half2float(*reinterpret_cast<const __half*>(p)) : *reinterpret_cast<const float*>(p);
   };
   auto load_chunk = [&](int it) {
     const int64_t c = first + (int64_t)it * 256;
     const int rem_c = (int)(t_end - c < 64 ? t_end - c : 64);
-    const uint8_t* xk = p_k + (int64_t)it * 256 * rec;
-    const int64_t so = (int64_t)it * 256 * ssz;
-    const uint32_t* xv = p_v + (int64_t)it * 8 * VB * kD;
+    const uint8_t* xk = kp + c * (int64_t)rec;
+    const char* xn = reinterpret_cast<const char*>(a.k_norm) + (int64_t)(sidx0 + c) * ssz;
+    const char* xg = QJL ? reinterpret_cast<const char*>(a.k_rnorm) + (int64_t)(sidx0 + c) * ssz : nullptr;
+    const char* xm = VMSE ? reinterpret_cast<const char*>(a.v_norm) + (int64_t)(sidx0 + c) * ssz
+                          : reinterpret_cast<const char*>(a.v_meta) + (int64_t)(sidx0 + c) * (NG * 4);
+    const char* xv = reinterpret_cast<const char*>(vp + (c >> 5) * VB * kD);
     if (rem_c == 64) {  // full chunk: no per-lane guards
-      pNrm = scalar_at(p_n + so);
-      if (QJL) pGam = scalar_at(p_g + so);
+      pNrm = scalar_at(xn, s_lane);
+      if (QJL) pGam = scalar_at(xg, s_lane);
       if (VMSE)
-        pMeta[0] = __float_as_uint(scalar_at(p_m + so));
+        pMeta[0] = __float_as_uint(scalar_at(xm, m_lane));
       else
-        pMeta = *reinterpret_cast<const u32x4*>(p_m + (int64_t)it * 256 * NG * 4);
+        pMeta = *reinterpret_cast<const u32x4*>(xm + m_lane);
 #pragma unroll
-      for (int i = 0; i < VB; ++i) pVw[i] = *reinterpret_cast<const u32x4*>(xv + i * 256);
+      for (int i = 0; i < VB; ++i) pVw[i] = *reinterpret_cast<const u32x4*>(xv + v_lane + i * 1024);
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
         for (int sp = 0; sp < KP; ++sp)
-          pX[ct][sp] = *reinterpret_cast<const uint32_t*>(xk + 16 * ct * rec + sp * (kD / 8));
+          pX[ct][sp] = *reinterpret_cast<const uint32_t*>(xk + k_lane + 16 * ct * rec + sp * (kD / 8));
     } else {
       const bool valid = lane < rem_c;
-      pNrm = valid ? scalar_at(p_n + so) : 0.f;
-      pGam = (QJL && valid) ? scalar_at(p_g + so) : 0.f;
+      pNrm = valid ? scalar_at(xn, s_lane) : 0.f;
+      pGam = (QJL && valid) ? scalar_at(xg, s_lane) : 0.f;
       if (VMSE)
-        pMeta[0] = valid ? __float_as_uint(scalar_at(p_m + so)) : 0u;
+        pMeta[0] = valid ? __float_as_uint(scalar_at(xm, m_lane)) : 0u;
       else
-        pMeta = valid ? *reinterpret_cast<const u32x4*>(p_m + (int64_t)it * 256 * NG * 4) : u32x4{0u, 0u, 0u, 0u};
+        pMeta = valid ? *reinterpret_cast<const u32x4*>(xm + m_lane) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int i = 0; i < VB; ++i) {
         const int idx = (i * 64 + lane) * 4;  // dword index inside [2][VB][128]
-        pVw[i] = (idx < VB * kD || rem_c > 32) ? *reinterpret_cast<const u32x4*>(xv + i * 256) : u32x4{0u, 0u, 0u, 0u};
+        pVw[i] = (idx < VB * kD || rem_c > 32) ? *reinterpret_cast<const u32x4*>(xv + v_lane + i * 1024)
+                                               : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
         const bool v2 = 16 * ct + n < rem_c;
 #pragma unroll
         for (int sp = 0; sp < KP; ++sp)
-          pX[ct][sp] = v2 ? *reinterpret_cast<const uint32_t*>(xk + 16 * ct * rec + sp * (kD / 8)) : 0u;
+          pX[ct][sp] = v2 ? *reinterpret_cast<const uint32_t*>(xk + k_lane + 16 * ct * rec + sp * (kD / 8)) : 0u;
       }
     }
   };
@@ -369,18 +377,25 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
     const uint32_t mb_lane = VMSE ? pMeta[0]
                                   : max(max(pMeta[0] & 0x7fffu, pMeta[1] & 0x7fffu),
                                         max(pMeta[2] & 0x7fffu, pMeta[3] & 0x7fffu));
+    // min/max values: the exponent of the value weights is known before the
+    // softmax, so p is produced already scaled (see the value section)
+    const int ev_mm = VMSE ? 0 : 44 - (int)(wave_max_u32_uniform(mb_lane) >> 10);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     {
+      // per token: u, w and an additive mask (-inf past the end of the chunk)
       const float u = u_scale * pNrm;
-      s_ng[2 * lane] = u;
-      s_ng[2 * lane + 1] = QJL ? u * kQjlScale * pGam : 0.f;
+      *reinterpret_cast<floatx4*>(s_ng + 4 * lane) =
+          floatx4{u, QJL ? u * kQjlScale * pGam : 0.f, lane < rem ? 0.f : -INFINITY, 0.f};
       if (VMSE)
         s_meta[lane * NG] = pMeta[0];
       else
-        *reinterpret_cast<u32x4*>(s_meta + lane * NG) = pMeta;
+        *reinterpret_cast<u32x4*>(s_meta + lane * NG + kMetaPad * (lane >> 4)) = pMeta;
 #pragma unroll
-      for (int i = 0; i < VB; ++i) *reinterpret_cast<u32x4*>(s_vw + (i * 64 + lane) * 4) = pVw[i];
+      for (int i = 0; i < VB; ++i) {
+        const int q = (i * 64 + lane) * 4;  // word index inside the chunk's value words
+        *reinterpret_cast<u32x4*>(s_vw + q + kVwPad * (q >> 7)) = pVw[i];
+      }
     }
     uint32_t X[4][KP];
 #pragma unroll
@@ -429,24 +444,27 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
         }
       }
       const int u = 16 * ct + n;  // token inside the chunk
-      const float ut = s_ng[2 * u], wt = s_ng[2 * u + 1];
-      const bool valid = u < rem;
+      const floatx4 ng = *reinterpret_cast<const floatx4*>(s_ng + 4 * u);
+      const float ut = ng[0], wt = ng[1];
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) {
         // digits carry 2^21, 2^14, 2^7, 1: two exact integer halves, each
         // scaled in float (the 2^14 of the upper half is folded into k1h, k2h)
         const float dmh = (float)((am[ht][0] << 7) + am[ht][1]), dml = (float)((am[ht][2] << 7) + am[ht][3]);
-        float sv = ut * fmaf(dmh, k1h[ht], fmaf(dml, k1[ht], c0[ht]));
+        float sv = fmaf(ut, fmaf(dmh, k1h[ht], fmaf(dml, k1[ht], c0[ht])), ng[2]);
         if (QJL) {
           const float dsh = (float)((as[ht][0] << 7) + as[ht][1]), dsl = (float)((as[ht][2] << 7) + as[ht][3]);
           sv = fmaf(wt, fmaf(dsh, k2h[ht], fmaf(dsl, k2[ht], -c3[ht])), sv);
         }
-        sc[ht][ct] = valid ? sv : -INFINITY;
+        sc[ht][ct] = sv;
       }
     }
 
     // ---- online softmax in log2 units over the 16 lanes of a head (one DPP
-    // row); alpha rescales the running sums.  p goes to LDS for the value MFMA.
+    // row); alpha rescales the running sums.  p goes to LDS for the value MFMA,
+    // for min/max values as p 2^c with c = ev - 2 min(n/4, 2): token 16ct + n
+    // is in slot n/4 of its packed code word, whose bytes carry 4^min(n/4, 2)
+    const int c_p = VMSE ? 0 : ev_mm - ((n >> 2) < 2 ? 2 * (n >> 2) : 4);
     float alpha[NHT];
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
@@ -454,14 +472,15 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
       const float m_new = fmaxf(m_run[ht], mloc);
       alpha[ht] = __builtin_amdgcn_exp2f(m_run[ht] - m_new);
       m_run[ht] = m_new;
+      const float m_p = m_new - (float)c_p;
       float lsum = 0.f;
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
-        const float e = __builtin_amdgcn_exp2f(sc[ht][ct] - m_new);  // 0 for tokens past the end
+        const float e = __builtin_amdgcn_exp2f(sc[ht][ct] - m_p);  // 0 for tokens past the end
         s_p[(4 * ht + g) * 64 + 16 * ct + n] = e;
         lsum += e;
       }
-      l_part[ht] = fmaf(l_part[ht], alpha[ht], lsum);
+      l_part[ht] = fmaf(l_part[ht], alpha[ht], VMSE ? lsum : ldexpf(lsum, -c_p));
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
@@ -486,27 +505,27 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
 #pragma unroll
         for (int k = 0; k < 4; ++k)
           pv[ht][k] = *reinterpret_cast<const floatx4*>(s_p + (4 * ht + (n >> 2)) * 64 + 16 * g + 4 * k);
-      const uint32_t mb = wave_max_u32_uniform(mb_lane);
-      const int ev = 44 - (int)(mb >> 10);  // every delta < 2^(e - 14): |W| < 2^30
-      const float inv_sv = ldexpf(1.f, -ev);
+      // ev = 44 - E(max delta): every delta < 2^(E - 14), so |W| < 2^30.  The
+      // weights p delta 2^(ev - 2 min(k, 2)) come straight from the scaled p.
+      const float inv_sv = ldexpf(1.f, -ev_mm);
       u32x4 A[NHT][4];
       float M[NHT];
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) {
-        M[ht] = 0.f;
+        float Mk[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const float scl = ldexpf(1.f, ev - (k < 2 ? 2 * k : 4));
           uint32_t V[4];
+          Mk[k] = 0.f;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const uint32_t mm = s_meta[(16 * g + 4 * k + r) * NG + grp];
+            const uint32_t mm = s_meta[(16 * g + 4 * k + r) * NG + kMetaPad * g + grp];
             const float dl = __half2float(__ushort_as_half((unsigned short)(mm & 0xffffu)));
             const float mn = __half2float(__ushort_as_half((unsigned short)(mm >> 16)));
             const float pe = pv[ht][k][r];
-            const int W = (int)fmaf(pe * scl, dl, 0.5f);  // non-negative: rounds to nearest
+            const int W = (int)fmaf(pe, dl, 0.5f);  // non-negative: rounds to nearest
             V[r] = ((uint32_t)W + 0x00808080u) ^ 0x00808080u;  // bytes = signed base-256 digits
-            M[ht] = fmaf(pe, mn, M[ht]);
+            Mk[k] = fmaf(pe, mn, Mk[k]);
           }
           // 4x4 byte transpose: digit plane d holds byte d of the four tokens
           const uint32_t t01lo = __builtin_amdgcn_perm(V[1], V[0], 0x05010400u);
@@ -518,6 +537,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
           A[ht][1][k] = __builtin_amdgcn_perm(t23hi, t01hi, 0x05040100u);
           A[ht][0][k] = __builtin_amdgcn_perm(t23hi, t01hi, 0x07060302u);  // most significant digit
         }
+        // undo the slot scales 2^(ev - 2 min(k, 2)) of the min term
+        M[ht] = ldexpf(fmaf(Mk[0], 1.f, fmaf(Mk[1], 4.f, 16.f * (Mk[2] + Mk[3]))), -ev_mm);
       }
       // sum_t p_t min_t per (head, group): reduce over the four token quarters,
       // then fetch (head g, group gi) for the value layout
@@ -531,7 +552,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
         const int gi = nt >> 1;  // group of channels 16nt..16nt+15
-        const uint32_t w = s_vw[g * kD + 16 * nt + n];
+        const uint32_t w = s_vw[g * (kD + kVwPad) + 16 * nt + n];
         const u32x4 B = {w & 0x03030303u, w & 0x0c0c0c0cu, w & 0x30303030u, (w >> 2) & 0x30303030u};
 #pragma unroll
         for (int ht = 0; ht < NHT; ++ht) {
