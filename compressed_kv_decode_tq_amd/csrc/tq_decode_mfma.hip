@@ -319,7 +319,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
     const char* p = reinterpret_cast<const char*>(base) + off;
     return a.scalar_f16 ? __half2float(*reinterpret_cast<const __half*>(p)) : *reinterpret_cast<const float*>(p);
   };
-  auto load_chunk = [&](int it) {
+  auto load_chunk = [&](int it, bool keys, bool rest) {
     const int64_t c = first + (int64_t)it * 256;
     const int rem_c = (int)(t_end - c < 64 ? t_end - c : 64);
     const uint8_t* xk = kp + c * (int64_t)rec;
@@ -328,7 +328,22 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
     const char* xm = VMSE ? reinterpret_cast<const char*>(a.v_norm) + (int64_t)(sidx0 + c) * ssz
                           : reinterpret_cast<const char*>(a.v_meta) + (int64_t)(sidx0 + c) * (NG * 4);
     const char* xv = reinterpret_cast<const char*>(vp + (c >> 5) * VB * kD);
-    if (rem_c == 64) {  // full chunk: no per-lane guards
+    if (rem_c == 64 && !rest) {
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int sp = 0; sp < KP; ++sp)
+          pX[ct][sp] = *reinterpret_cast<const uint32_t*>(xk + k_lane + 16 * ct * rec + sp * (kD / 8));
+    } else if (rem_c == 64 && !keys) {
+      pNrm = scalar_at(xn, s_lane);
+      if (QJL) pGam = scalar_at(xg, s_lane);
+      if (VMSE)
+        pMeta[0] = __float_as_uint(scalar_at(xm, m_lane));
+      else
+        pMeta = *reinterpret_cast<const u32x4*>(xm + m_lane);
+#pragma unroll
+      for (int i = 0; i < VB; ++i) pVw[i] = *reinterpret_cast<const u32x4*>(xv + v_lane + i * 1024);
+    } else if (rem_c == 64) {  // full chunk: no per-lane guards
       pNrm = scalar_at(xn, s_lane);
       if (QJL) pGam = scalar_at(xg, s_lane);
       if (VMSE)
@@ -344,28 +359,32 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
           pX[ct][sp] = *reinterpret_cast<const uint32_t*>(xk + k_lane + 16 * ct * rec + sp * (kD / 8));
     } else {
       const bool valid = lane < rem_c;
-      pNrm = valid ? scalar_at(xn, s_lane) : 0.f;
-      pGam = (QJL && valid) ? scalar_at(xg, s_lane) : 0.f;
-      if (VMSE)
-        pMeta[0] = valid ? __float_as_uint(scalar_at(xm, m_lane)) : 0u;
-      else
-        pMeta = valid ? *reinterpret_cast<const u32x4*>(xm + m_lane) : u32x4{0u, 0u, 0u, 0u};
+      if (rest) {
+        pNrm = valid ? scalar_at(xn, s_lane) : 0.f;
+        pGam = (QJL && valid) ? scalar_at(xg, s_lane) : 0.f;
+        if (VMSE)
+          pMeta[0] = valid ? __float_as_uint(scalar_at(xm, m_lane)) : 0u;
+        else
+          pMeta = valid ? *reinterpret_cast<const u32x4*>(xm + m_lane) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int i = 0; i < VB; ++i) {
-        const int idx = (i * 64 + lane) * 4;  // dword index inside [2][VB][128]
-        pVw[i] = (idx < VB * kD || rem_c > 32) ? *reinterpret_cast<const u32x4*>(xv + v_lane + i * 1024)
-                                               : u32x4{0u, 0u, 0u, 0u};
+        for (int i = 0; i < VB; ++i) {
+          const int idx = (i * 64 + lane) * 4;  // dword index inside [2][VB][128]
+          pVw[i] = (idx < VB * kD || rem_c > 32) ? *reinterpret_cast<const u32x4*>(xv + v_lane + i * 1024)
+                                                 : u32x4{0u, 0u, 0u, 0u};
+        }
       }
+      if (keys) {
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const bool v2 = 16 * ct + n < rem_c;
+        for (int ct = 0; ct < 4; ++ct) {
+          const bool v2 = 16 * ct + n < rem_c;
 #pragma unroll
-        for (int sp = 0; sp < KP; ++sp)
-          pX[ct][sp] = v2 ? *reinterpret_cast<const uint32_t*>(xk + k_lane + 16 * ct * rec + sp * (kD / 8)) : 0u;
+          for (int sp = 0; sp < KP; ++sp)
+            pX[ct][sp] = v2 ? *reinterpret_cast<const uint32_t*>(xk + k_lane + 16 * ct * rec + sp * (kD / 8)) : 0u;
+        }
       }
     }
   };
-  if (first < t_end) load_chunk(0);
+  if (first < t_end) load_chunk(0, true, true);
 
   int it = 0;
   for (int64_t c0t = first; c0t < t_end; c0t += 256, ++it) {
@@ -397,12 +416,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
         *reinterpret_cast<u32x4*>(s_vw + q + kVwPad * (q >> 7)) = pVw[i];
       }
     }
-    uint32_t X[4][KP];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-      for (int sp = 0; sp < KP; ++sp) X[ct][sp] = pX[ct][sp];
-    if (c0t + 256 < t_end) load_chunk(it + 1);
+    uint32_t(&X)[4][KP] = pX;  // the key words are reloaded once the scores are done
+    if (c0t + 256 < t_end) load_chunk(it + 1, false, true);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
@@ -459,6 +474,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
         sc[ht][ct] = sv;
       }
     }
+
+    if (c0t + 256 < t_end) load_chunk(it + 1, true, false);
 
     // ---- online softmax in log2 units over the 16 lanes of a head (one DPP
     // row); alpha rescales the running sums.  p goes to LDS for the value MFMA,
