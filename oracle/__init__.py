@@ -36,7 +36,7 @@ from .quantize import (  # noqa: F401
     dequantize_keys, dequantize_values_minmax, dequantize_values_mse,
     score_estimate, round_scalar,
 )
-from .attention import decode_attention, decode_attention_bruteforce  # noqa: F401
+from .attention import decode_attention, decode_attention_bruteforce, decode_attention_multi  # noqa: F401
 from .layout import (  # noqa: F401
     Layout, pack_key_planes, unpack_key_planes, pack_value_planes, unpack_value_planes,
     pack_value_codes, unpack_value_codes, pack_value_words, unpack_value_words, value_words_packed,

@@ -1,4 +1,5 @@
-"""Single-query decode attention over a TurboQuant cache plus a bf16 ring.
+"""Decode attention over a TurboQuant cache plus a bf16 ring: one query per
+(sequence, query head), or T queries per sequence (multi-query decode).
 
 TEST INFRASTRUCTURE (see the package docstring).
 
@@ -16,6 +17,12 @@ Readings taken where the pages are silent:
 * The ring holds the most recent tokens uncompressed in bf16 in the original
   (unrotated) space ([audit] AUDIT 1 ring term); one softmax runs over the
   compressed tokens and the ring tokens together.
+* Multi-query decode (T > 1 in the (H_kv, G, T, N) score layout of [audit]
+  AUDIT 4): the T queries of a sequence are its last T positions, already
+  appended to the cache or the ring.  The keys of a sequence are its
+  compressed tokens followed by its ring tokens, and query t (0 <= t < T) sees
+  every key except the last T - 1 - t of that order (causal among the new
+  positions; all earlier tokens are visible to every query).
 """
 from __future__ import annotations
 
@@ -52,6 +59,32 @@ def decode_attention(q: np.ndarray, k_comp: list, v_comp: list, ring_k=None, rin
             s = tau * (kk @ q[b, hq])
             p = np.exp(s - s.max())
             out[b, hq] = (p @ vv) / p.sum()
+    return out
+
+
+def decode_attention_multi(q: np.ndarray, k_comp: list, v_comp: list, ring_k=None, ring_v=None,
+                           n_ring=None, scale: float | None = None) -> np.ndarray:
+    """T queries per sequence.  q: (B, T, H_q, d); the other arguments as in
+    decode_attention.  Query t sees all but the last T - 1 - t keys of the
+    sequence's compressed-then-ring order.  Returns (B, T, H_q, d) float64."""
+    q = np.asarray(q, dtype=np.float64)
+    bsz, nq, h_q, d = q.shape
+    h_kv = len(k_comp[0])
+    out = np.zeros((bsz, nq, h_q, d))
+    for b in range(bsz):
+        nr = int(n_ring[b]) if (ring_k is not None and n_ring is not None) else 0
+        for t in range(nq):
+            hidden = nq - 1 - t
+            hide_r = min(hidden, nr)
+            hide_c = hidden - hide_r
+            kc = [np.asarray(k_comp[b][h]).reshape(-1, d) for h in range(h_kv)]
+            vc = [np.asarray(v_comp[b][h]).reshape(-1, d) for h in range(h_kv)]
+            kc = [x[: x.shape[0] - hide_c] for x in kc]
+            vc = [x[: x.shape[0] - hide_c] for x in vc]
+            out[b, t] = decode_attention(q[b:b + 1, t], [kc], [vc],
+                                         None if ring_k is None else ring_k[b:b + 1],
+                                         None if ring_v is None else ring_v[b:b + 1],
+                                         [nr - hide_r], scale)[0]
     return out
 
 
