@@ -253,22 +253,36 @@ int tq_ring_append(const void* k_new, const void* v_new, int32_t in_dtype, int32
   return TQ_OK;
 }
 
-size_t tq_decode_workspace_bytes(const tq_layout* layout, int32_t batch, int32_t num_q_heads,
-                                 int32_t num_kv_heads, int64_t max_tokens) {
-  if (!layout || batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_tokens < 0) return 0;
-  const int nb = std::min(batch, tq::kMaxSeqPerLaunch);
-  const int32_t splits = tq::decode_max_splits(max_tokens, (int64_t)nb * num_kv_heads);
-  const size_t qprep = (size_t)nb * num_q_heads * 2 * tq::kD * 4;
-  const size_t part = (size_t)splits * nb * num_q_heads * (tq::kD + 2) * 4;
+}  // extern "C"
+
+namespace {
+
+// Virtual heads one decode launch handles per KV head: all query heads of a
+// KV head for one query per sequence; for several queries, up to kMaxGroup
+// (query, head) pairs per launch.
+int decode_vgroup(int group, int nq) { return std::min(tq::kMaxGroup, group * nq); }
+
+size_t decode_ws_bytes(int nb, int h_kv, int vg, int64_t max_tokens) {
+  const int32_t splits = tq::decode_max_splits(max_tokens, (int64_t)nb * h_kv);
+  const size_t rows = (size_t)nb * h_kv * vg;
+  const size_t qprep = rows * 2 * tq::kD * 4;
+  const size_t part = (size_t)splits * rows * (tq::kD + 2) * 4;
   const size_t base = (qprep + part + 255) & ~(size_t)255;
-  return base + tq::mfma_workspace_bytes(nb, num_q_heads, num_q_heads / num_kv_heads);
+  return base + tq::mfma_workspace_bytes(nb, h_kv * vg, vg);
 }
 
-int tq_decode_attn(const tq_layout* layout, const tq_params* params, const void* q,
-                   int32_t q_dtype, int32_t num_q_heads, const tq_cache* cache,
-                   const int64_t* n_compressed_host, const void* ring_k, const void* ring_v,
-                   int32_t ring_cap, const int32_t* n_ring_host, float softmax_scale, float* out,
-                   void* workspace, size_t workspace_bytes, void* stream) {
+size_t decode_workspace_bytes_impl(const tq_layout* layout, int32_t batch, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int64_t max_tokens, int32_t nq) {
+  if (!layout || batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_tokens < 0 || nq <= 0) return 0;
+  if (num_q_heads % num_kv_heads) return 0;
+  const int nb = std::min(batch, tq::kMaxSeqPerLaunch);
+  return decode_ws_bytes(nb, num_kv_heads, decode_vgroup(num_q_heads / num_kv_heads, nq), max_tokens);
+}
+
+int decode_attn_impl(const tq_layout* layout, const tq_params* params, const void* q, int32_t q_dtype,
+                     int32_t num_q_heads, int32_t nq, const tq_cache* cache, const int64_t* n_compressed_host,
+                     const void* ring_k, const void* ring_v, int32_t ring_cap, const int32_t* n_ring_host,
+                     float softmax_scale, float* out, void* workspace, size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
   int rc = check_layout(layout);
   if (rc) return rc;
@@ -277,6 +291,7 @@ int tq_decode_attn(const tq_layout* layout, const tq_params* params, const void*
   if (!params->derived) return fail(TQ_ERR_INVALID, "params.derived must be filled by tq_prepare_params");
   if (!q || !out || !n_compressed_host) return fail(TQ_ERR_INVALID, "q, out and n_compressed_host must be non-NULL");
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return fail(TQ_ERR_INVALID, "q_dtype must be TQ_F32 or TQ_BF16");
+  if (nq <= 0) return fail(TQ_ERR_INVALID, "num_queries must be positive");
   const int h_kv = cache->num_kv_heads;
   if (num_q_heads <= 0 || num_q_heads % h_kv) return fail(TQ_ERR_INVALID, "num_q_heads must be a positive multiple of num_kv_heads");
   const int group = num_q_heads / h_kv;
@@ -294,7 +309,7 @@ int tq_decode_attn(const tq_layout* layout, const tq_params* params, const void*
       return fail(TQ_ERR_UNSUPPORTED, "sequence %d: more than %d ring tokens", b, tq::kMaxRing);
     max_tokens = std::max<int64_t>(max_tokens, n_compressed_host[b]);
   }
-  const size_t need = tq_decode_workspace_bytes(layout, cache->batch, num_q_heads, h_kv, max_tokens);
+  const size_t need = decode_workspace_bytes_impl(layout, cache->batch, num_q_heads, h_kv, max_tokens, nq);
   if (!workspace || workspace_bytes < need)
     return fail(TQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
 
@@ -303,20 +318,20 @@ int tq_decode_attn(const tq_layout* layout, const tq_params* params, const void*
   const size_t kpb = (size_t)(layout->key_mse_bits + layout->key_qjl) * tq::kD / 8;
   const size_t groups = layout->value_kind == TQ_V_MINMAX ? tq::kD / layout->value_group : 0;
   const size_t qsz = q_dtype == TQ_F32 ? 4 : 2;
+  const int vg_max = decode_vgroup(group, nq);
+  const int nvirt = group * nq;
   float kc[16], kt[15], vc[16], vt[15];
   fill_codebooks(layout, params, kc, kt, vc, vt);
   for (int b0 = 0; b0 < cache->batch; b0 += tq::kMaxSeqPerLaunch) {
     const int nb = std::min(tq::kMaxSeqPerLaunch, cache->batch - b0);
     tq::DecodeArgs a;
     std::memset(&a, 0, sizeof(a));
-    int64_t mt = 0;
     for (int b = 0; b < nb; ++b) {
       a.n_comp.v[b] = n_compressed_host[b0 + b];
       a.n_ring.v[b] = ring_cap > 0 ? n_ring_host[b0 + b] : 0;
-      mt = std::max<int64_t>(mt, a.n_comp.v[b]);
     }
     tq::decode_split(max_tokens, (int64_t)std::min(cache->batch, tq::kMaxSeqPerLaunch) * h_kv, &a.splits, &a.split_len);
-    a.q = (const char*)q + (size_t)b0 * num_q_heads * tq::kD * qsz;
+    a.q = (const char*)q + (size_t)b0 * nq * num_q_heads * tq::kD * qsz;
     a.k_planes = cache->k_planes + seq_off(b0, h_kv, cap, kpb);
     a.k_norm = (const char*)cache->k_norm + seq_off(b0, h_kv, cap, sz);
     a.k_rnorm = cache->k_rnorm ? (const char*)cache->k_rnorm + seq_off(b0, h_kv, cap, sz) : nullptr;
@@ -329,14 +344,20 @@ int tq_decode_attn(const tq_layout* layout, const tq_params* params, const void*
     const size_t ring_off = (size_t)b0 * ring_cap * h_kv * tq::kD;
     a.ring_k = ring_cap > 0 ? (const uint16_t*)ring_k + ring_off : nullptr;
     a.ring_v = ring_cap > 0 ? (const uint16_t*)ring_v + ring_off : nullptr;
-    a.out = out + (size_t)b0 * num_q_heads * tq::kD;
+    a.out = out + (size_t)b0 * nq * num_q_heads * tq::kD;
+    // workspace: qprep and partials sized for vg_max virtual heads per KV head
+    const size_t rows = (size_t)nb * h_kv * vg_max;
     a.qprep = (float*)workspace;
-    a.partial = (float*)((char*)workspace + (size_t)nb * num_q_heads * 2 * tq::kD * 4);
+    a.partial = (float*)((char*)workspace + rows * 2 * tq::kD * 4);
+    const size_t base_ws = rows * 2 * tq::kD * 4 + (size_t)a.splits * rows * (tq::kD + 2) * 4;
+    a.qdig = (int8_t*)((char*)workspace + ((base_ws + 255) & ~(size_t)255));
+    a.qconst = (float*)((char*)a.qdig + (size_t)nb * h_kv * ((vg_max + 3) / 4) * 5 * 2 * 64 * 16);
     a.capacity = cap;
     a.batch = nb;
     a.h_q = num_q_heads;
     a.h_kv = h_kv;
-    a.group = group;
+    a.nq = nq;
+    a.qgroup = group;
     a.q_bf16 = q_dtype == TQ_BF16;
     a.scalar_f16 = layout->scalar_dtype == TQ_F16;
     a.value_group = layout->value_group;
@@ -344,27 +365,60 @@ int tq_decode_attn(const tq_layout* layout, const tq_params* params, const void*
     a.scale = softmax_scale;
     std::memcpy(a.k_cent, kc, sizeof(kc));
     std::memcpy(a.v_cent, vc, sizeof(vc));
-    (void)mt;
-    const size_t base_ws = (size_t)nb * num_q_heads * 2 * tq::kD * 4 +
-                           (size_t)a.splits * nb * num_q_heads * (tq::kD + 2) * 4;
-    a.qdig = (int8_t*)((char*)workspace + ((base_ws + 255) & ~(size_t)255));
-    a.qconst = (float*)((char*)a.qdig + (size_t)nb * h_kv * ((group + 3) / 4) * 5 * 2 * 64 * 16);
     const bool vmse = layout->value_kind == TQ_V_MSE;
     const int kpl = tq::plane_expansion(kc, layout->key_mse_bits, a.key_w, &a.key_cst);
     const int vpl = vmse ? tq::plane_expansion(vc, layout->value_bits, a.val_w, &a.val_cst) : 0;
     const char* path = std::getenv("TQ_DECODE_PATH");
     const bool generic_only = path && std::strcmp(path, "generic") == 0;
-    const tq::TimedLaunch tl = take_timed(TQ_KERNEL_DECODE_SCAN);
-    hipError_t e = hipErrorNotSupported;
-    if (!generic_only && kpl > 0 && (!vmse || vpl > 0))
-      e = tq::launch_decode_mfma(a, layout->key_mse_bits, layout->key_qjl, vmse, layout->value_bits, kpl,
-                                 vpl, (hipStream_t)stream, tl);
-    if (e == hipErrorNotSupported)
-      e = tq::launch_decode(a, layout->key_mse_bits, layout->key_qjl, vmse, layout->value_bits,
-                            (hipStream_t)stream, tl);
-    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    // one set of launches (q-prep, scan, combine) per group of virtual heads;
+    // each pass reads the compressed cache once
+    for (int vbase = 0; vbase < nvirt; vbase += vg_max) {
+      a.vbase = vbase;
+      a.group = std::min(vg_max, nvirt - vbase);
+      const tq::TimedLaunch tl = take_timed(TQ_KERNEL_DECODE_SCAN);
+      hipError_t e = hipErrorNotSupported;
+      if (!generic_only && kpl > 0 && (!vmse || vpl > 0))
+        e = tq::launch_decode_mfma(a, layout->key_mse_bits, layout->key_qjl, vmse, layout->value_bits, kpl,
+                                   vpl, (hipStream_t)stream, tl);
+      if (e == hipErrorNotSupported)
+        e = tq::launch_decode(a, layout->key_mse_bits, layout->key_qjl, vmse, layout->value_bits,
+                              (hipStream_t)stream, tl);
+      if (e != hipSuccess) return hip_fail(e, "decode launch");
+    }
   }
   return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tq_decode_workspace_bytes(const tq_layout* layout, int32_t batch, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int64_t max_tokens) {
+  return decode_workspace_bytes_impl(layout, batch, num_q_heads, num_kv_heads, max_tokens, 1);
+}
+
+size_t tq_decode_workspace_bytes_multi(const tq_layout* layout, int32_t batch, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int64_t max_tokens, int32_t num_queries) {
+  return decode_workspace_bytes_impl(layout, batch, num_q_heads, num_kv_heads, max_tokens, num_queries);
+}
+
+int tq_decode_attn(const tq_layout* layout, const tq_params* params, const void* q,
+                   int32_t q_dtype, int32_t num_q_heads, const tq_cache* cache,
+                   const int64_t* n_compressed_host, const void* ring_k, const void* ring_v,
+                   int32_t ring_cap, const int32_t* n_ring_host, float softmax_scale, float* out,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_attn_impl(layout, params, q, q_dtype, num_q_heads, 1, cache, n_compressed_host, ring_k, ring_v,
+                          ring_cap, n_ring_host, softmax_scale, out, workspace, workspace_bytes, stream);
+}
+
+int tq_decode_attn_multi(const tq_layout* layout, const tq_params* params, const void* q,
+                         int32_t q_dtype, int32_t num_q_heads, int32_t num_queries, const tq_cache* cache,
+                         const int64_t* n_compressed_host, const void* ring_k, const void* ring_v,
+                         int32_t ring_cap, const int32_t* n_ring_host, float softmax_scale, float* out,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_attn_impl(layout, params, q, q_dtype, num_q_heads, num_queries, cache, n_compressed_host, ring_k,
+                          ring_v, ring_cap, n_ring_host, softmax_scale, out, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

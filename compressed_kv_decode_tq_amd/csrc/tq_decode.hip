@@ -21,14 +21,16 @@ constexpr int kScanThreads = 256;  // 4 waves, each taking 64-token chunks of th
 constexpr int kChunk = 64;
 constexpr float kQjlScale = 0.0097916519f;  // sqrt(pi/2) / 128
 
-// q_rot = Pi q and q_s = S q for the G query heads of one (sequence, KV head).
+// q_rot = Pi q and q_s = S q for the G (virtual) heads of one (sequence, KV head).
 __global__ __launch_bounds__(256) void qprep_kernel(DecodeArgs a) {
   __shared__ float qv[kMaxGroup][kD];
   const int b = blockIdx.x / a.h_kv, h = blockIdx.x % a.h_kv;
   const int G = a.group;
   for (int i = threadIdx.x; i < G * kD; i += blockDim.x) {
-    const int hq = h * G + i / kD, c = i % kD;
-    const size_t off = ((size_t)b * a.h_q + hq) * kD + c;
+    const int c = i % kD;
+    int t, hq;
+    virtual_head(a, h, i / kD, t, hq);
+    const size_t off = q_row(a, b, t, hq) * kD + c;
     qv[i / kD][c] = a.q_bf16 ? bf2f(reinterpret_cast<const uint16_t*>(a.q)[off])
                              : reinterpret_cast<const float*>(a.q)[off];
   }
@@ -54,7 +56,7 @@ __global__ __launch_bounds__(256) void qprep_kernel(DecodeArgs a) {
   }
 #pragma unroll
   for (int g = 0; g < kMaxGroup; ++g)
-    if (g < G) a.qprep[(((size_t)b * a.h_q + h * G + g) * 2 + which) * kD + i] = acc[g];
+    if (g < G) a.qprep[(ws_row(a, b, h, g) * 2 + which) * kD + i] = acc[g];
 }
 
 // Split scan: work-group (split, sequence*KV head).  Lane = token for the
@@ -80,7 +82,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(DecodeArgs a) {
 
   for (int i = threadIdx.x; i < kD * kMaxGroup; i += blockDim.x) {
     const int c = i / kMaxGroup, g = i % kMaxGroup;
-    const size_t base = ((size_t)b * a.h_q + h * G + g) * 2 * kD;
+    const size_t base = ws_row(a, b, h, g < G ? g : 0) * 2 * kD;
     qr[c][g] = g < G ? a.qprep[base + c] : 0.f;
     qs[c][g] = g < G ? a.qprep[base + kD + c] : 0.f;
   }
@@ -96,6 +98,16 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(DecodeArgs a) {
   const int ngrp = kD / a.value_group;
   const uint32_t* vp = a.v_planes + (size_t)sh * (a.capacity >> 5) * VB * kD;
 
+  // compressed tokens each (virtual) head sees: all of them for one query per
+  // sequence, fewer for the earlier of several causal queries
+  int64_t lim[kMaxGroup];
+#pragma unroll
+  for (int g = 0; g < kMaxGroup; ++g) {
+    int t, hq, hide_c, hide_r;
+    virtual_head(a, h, g, t, hq);
+    hidden_keys(a, t, (int)a.n_ring.v[b], hide_c, hide_r);
+    lim[g] = n_c - hide_c;
+  }
   float m_run[kMaxGroup], l_part[kMaxGroup], acc0[kMaxGroup], acc1[kMaxGroup];
 #pragma unroll
   for (int g = 0; g < kMaxGroup; ++g) {
@@ -170,7 +182,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(DecodeArgs a) {
       }
       const float kg = kQjlScale * gam;
 #pragma unroll
-      for (int g = 0; g < kMaxGroup; ++g) s[g] = valid ? a.scale * n * (dm[g] + kg * dq[g]) : -INFINITY;
+      for (int g = 0; g < kMaxGroup; ++g) s[g] = valid && tok < lim[g] ? a.scale * n * (dm[g] + kg * dq[g]) : -INFINITY;
     }
     // ---- online softmax update (every lane of the wave holds the same m_run)
 #pragma unroll
@@ -179,7 +191,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(DecodeArgs a) {
       const float cmax = wave_max(s[g]);
       const float m_new = fmaxf(m_run[g], cmax);
       const float alpha = m_run[g] == -INFINITY ? 0.f : __expf(m_run[g] - m_new);
-      const float p = valid ? __expf(s[g] - m_new) : 0.f;
+      const float p = s[g] != -INFINITY ? __expf(s[g] - m_new) : 0.f;  // masked: 0
       m_run[g] = m_new;
       l_part[g] = l_part[g] * alpha + p;
       acc0[g] *= alpha;
@@ -290,7 +302,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(DecodeArgs a) {
         A += f * macc[w][g][c];
       }
     }
-    float* part = a.partial + (((size_t)split * a.batch + b) * a.h_q + h * G + g) * (kD + 2);
+    float* part = a.partial + ((size_t)split * a.batch * a.h_kv * G + ws_row(a, b, h, g)) * (kD + 2);
     if (c == 0) {
       part[0] = M;
       part[1] = L;
@@ -333,15 +345,19 @@ __global__ __launch_bounds__(kD) void combine_kernel(DecodeArgs a) {
   __shared__ float pr[kD];                  // ring probabilities (ring_cap <= 128 per pass)
   __shared__ float arot[kD];
   __shared__ float red2[2];
-  const int b = blockIdx.x / a.h_q, hq = blockIdx.x % a.h_q;
-  const int h = hq / a.group;
+  // block = (sequence, KV head, virtual head of the launch)
+  const int rows = a.h_kv * a.group;
+  const int b = blockIdx.x / rows, h = (blockIdx.x % rows) / a.group, gq = blockIdx.x % a.group;
+  int t, hq, hide_c, hide_r;
+  virtual_head(a, h, gq, t, hq);
   const int c = threadIdx.x;
-  const size_t qoff = ((size_t)b * a.h_q + hq) * kD + c;
+  const size_t qoff = q_row(a, b, t, hq) * kD + c;
   qv[c] = a.q_bf16 ? bf2f(reinterpret_cast<const uint16_t*>(a.q)[qoff]) : reinterpret_cast<const float*>(a.q)[qoff];
-  const int nr = (int)a.n_ring.v[b];
+  hidden_keys(a, t, (int)a.n_ring.v[b], hide_c, hide_r);
+  const int nr = (int)a.n_ring.v[b] - hide_r;  // ring tokens this query sees
   const int S = a.splits;
-  const float* part0 = a.partial + ((size_t)b * a.h_q + hq) * (kD + 2);
-  const size_t sstride = (size_t)a.batch * a.h_q * (kD + 2);
+  const float* part0 = a.partial + ws_row(a, b, h, gq) * (kD + 2);
+  const size_t sstride = (size_t)a.batch * rows * (kD + 2);
 
   // split headers (m, l): thread c takes splits c, c + 128, ...
   float M = -INFINITY;
@@ -372,7 +388,7 @@ __global__ __launch_bounds__(kD) void combine_kernel(DecodeArgs a) {
     sj = a.scale * acc;
   }
   M = block2_max(fmaxf(M, sj), red2);
-  float* outp = a.out + ((size_t)b * a.h_q + hq) * kD;
+  float* outp = a.out + q_row(a, b, t, hq) * kD;
   if (M == -INFINITY) {  // no token at all
     outp[c] = 0.f;
     return;
@@ -531,9 +547,9 @@ hipError_t launch_decode(const DecodeArgs& a, int key_mse_bits, int key_qjl, int
 
 hipError_t launch_combine(const DecodeArgs& a, int value_mse, hipStream_t stream) {
   if (value_mse)
-    hipLaunchKernelGGL(combine_kernel<true>, dim3(a.batch * a.h_q), dim3(kD), 0, stream, a);
+    hipLaunchKernelGGL(combine_kernel<true>, dim3(a.batch * a.h_kv * a.group), dim3(kD), 0, stream, a);
   else
-    hipLaunchKernelGGL(combine_kernel<false>, dim3(a.batch * a.h_q), dim3(kD), 0, stream, a);
+    hipLaunchKernelGGL(combine_kernel<false>, dim3(a.batch * a.h_kv * a.group), dim3(kD), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -117,7 +117,9 @@ __global__ __launch_bounds__(256) void qprep_mfma_kernel(DecodeArgs a, int pm, i
     const int gq = i / kD, c = i % kD;
     float x = 0.f;
     if (gq < G) {
-      const size_t off = ((size_t)b * a.h_q + h * G + gq) * kD + c;
+      int t, hq;
+      virtual_head(a, h, gq, t, hq);
+      const size_t off = q_row(a, b, t, hq) * kD + c;
       x = a.q_bf16 ? bf2f(reinterpret_cast<const uint16_t*>(a.q)[off]) : reinterpret_cast<const float*>(a.q)[off];
     }
     qv[gq][c] = x;
@@ -170,7 +172,7 @@ __global__ __launch_bounds__(256) void qprep_mfma_kernel(DecodeArgs a, int pm, i
       e_mse[gq] = er;
       e_qjl[gq] = es;
       if (gq < G) {
-        float* cst = a.qconst + ((size_t)b * a.h_q + h * G + gq) * 4;
+        float* cst = a.qconst + ws_row(a, b, h, gq) * 4;
         cst[0] = a.key_cst * sr;     // constant part of <q_rot, c[idx]>
         cst[1] = ldexpf(1.f, -er);   // digit scale of the MSE planes
         cst[2] = ldexpf(1.f, -es);   // digit scale of the QJL plane
@@ -272,7 +274,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
   for (int ht = 0; ht < NHT; ++ht) {
     const int hq = 4 * ht + g;
     if (hq < G) {
-      const floatx4 cs = *reinterpret_cast<const floatx4*>(a.qconst + ((size_t)b * a.h_q + h * G + hq) * 4);
+      const floatx4 cs = *reinterpret_cast<const floatx4*>(a.qconst + ws_row(a, b, h, hq) * 4);
       c0[ht] = cs[0];
       k1[ht] = cs[1];
       k2[ht] = cs[2];
@@ -284,6 +286,24 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
     k2h[ht] = 16384.f * k2[ht];
   }
   const float u_scale = a.scale * 1.4426950409f;  // exp(x) = exp2(x log2 e)
+  // Several causal queries per sequence: the compressed tokens each head of
+  // this lane sees (lim) and the fewest any head of the launch sees (lim_min,
+  // wave-uniform); chunks that end at or below lim_min need no per-head mask.
+  int64_t lim[NHT];
+  const int nr_b = (int)a.n_ring.v[b];
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht) {
+    int t, hq, hide_c, hide_r;
+    virtual_head(a, h, 4 * ht + g < G ? 4 * ht + g : 0, t, hq);
+    hidden_keys(a, t, nr_b, hide_c, hide_r);
+    lim[ht] = n_c - hide_c;
+  }
+  int64_t lim_min;
+  {
+    int hide_c, hide_r;
+    hidden_keys(a, a.vbase / a.qgroup, nr_b, hide_c, hide_r);
+    lim_min = n_c - hide_c;
+  }
 
   const size_t rec = (size_t)KP * (kD / 8);
   const uint8_t* kp = a.k_planes + (size_t)sh * a.capacity * rec;
@@ -474,6 +494,12 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
         sc[ht][ct] = sv;
       }
     }
+    if (c0t + 64 > lim_min) {  // tail of the compressed part under a causal query
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) sc[ht][ct] = c0t + 16 * ct + n < lim[ht] ? sc[ht][ct] : -INFINITY;
+    }
 
     if (c0t + 256 < t_end) load_chunk(it + 1, true, false);
 
@@ -516,19 +542,18 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
       // byte r.  The weights p_t delta_t(group) carry the inverse scale and
       // become signed base-256 fixed point.
       const int grp = n & 3;
-      floatx4 pv[NHT][4];
-#pragma unroll
-      for (int ht = 0; ht < NHT; ++ht)
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          pv[ht][k] = *reinterpret_cast<const floatx4*>(s_p + (4 * ht + (n >> 2)) * 64 + 16 * g + 4 * k);
       // ev = 44 - E(max delta): every delta < 2^(E - 14), so |W| < 2^30.  The
       // weights p delta 2^(ev - 2 min(k, 2)) come straight from the scaled p.
       const float inv_sv = ldexpf(1.f, -ev_mm);
-      u32x4 A[NHT][4];
-      float M[NHT];
+      // one head tile at a time (its digit operands, then its eight channel
+      // tiles), so a second tile does not double the live registers
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) {
+        floatx4 pv[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          pv[k] = *reinterpret_cast<const floatx4*>(s_p + (4 * ht + (n >> 2)) * 64 + 16 * g + 4 * k);
+        u32x4 A[4];
         float Mk[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -539,7 +564,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
             const uint32_t mm = s_meta[(16 * g + 4 * k + r) * NG + kMetaPad * g + grp];
             const float dl = __half2float(__ushort_as_half((unsigned short)(mm & 0xffffu)));
             const float mn = __half2float(__ushort_as_half((unsigned short)(mm >> 16)));
-            const float pe = pv[ht][k][r];
+            const float pe = pv[k][r];
             const int W = (int)fmaf(pe, dl, 0.5f);  // non-negative: rounds to nearest
             V[r] = ((uint32_t)W + 0x00808080u) ^ 0x00808080u;  // bytes = signed base-256 digits
             Mk[k] = fmaf(pe, mn, Mk[k]);
@@ -549,37 +574,30 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
           const uint32_t t01hi = __builtin_amdgcn_perm(V[1], V[0], 0x07030602u);
           const uint32_t t23lo = __builtin_amdgcn_perm(V[3], V[2], 0x05010400u);
           const uint32_t t23hi = __builtin_amdgcn_perm(V[3], V[2], 0x07030602u);
-          A[ht][3][k] = __builtin_amdgcn_perm(t23lo, t01lo, 0x05040100u);  // least significant digit
-          A[ht][2][k] = __builtin_amdgcn_perm(t23lo, t01lo, 0x07060302u);
-          A[ht][1][k] = __builtin_amdgcn_perm(t23hi, t01hi, 0x05040100u);
-          A[ht][0][k] = __builtin_amdgcn_perm(t23hi, t01hi, 0x07060302u);  // most significant digit
+          A[3][k] = __builtin_amdgcn_perm(t23lo, t01lo, 0x05040100u);  // least significant digit
+          A[2][k] = __builtin_amdgcn_perm(t23lo, t01lo, 0x07060302u);
+          A[1][k] = __builtin_amdgcn_perm(t23hi, t01hi, 0x05040100u);
+          A[0][k] = __builtin_amdgcn_perm(t23hi, t01hi, 0x07060302u);  // most significant digit
         }
-        // undo the slot scales 2^(ev - 2 min(k, 2)) of the min term
-        M[ht] = ldexpf(fmaf(Mk[0], 1.f, fmaf(Mk[1], 4.f, 16.f * (Mk[2] + Mk[3]))), -ev_mm);
-      }
-      // sum_t p_t min_t per (head, group): reduce over the four token quarters,
-      // then fetch (head g, group gi) for the value layout
-      float Mpv[NHT][NG];
+        // sum_t p_t min_t per (head, group), the slot scales 2^(ev - 2 min(k, 2))
+        // undone: reduce over the four token quarters, then fetch (head g,
+        // group gi) for the value layout
+        const float x = col_sum4(ldexpf(fmaf(Mk[0], 1.f, fmaf(Mk[1], 4.f, 16.f * (Mk[2] + Mk[3]))), -ev_mm));
+        float Mpv[NG];
 #pragma unroll
-      for (int ht = 0; ht < NHT; ++ht) {
-        const float x = col_sum4(M[ht]);
+        for (int gi = 0; gi < NG; ++gi) Mpv[gi] = __shfl(x, 4 * g + gi);
 #pragma unroll
-        for (int gi = 0; gi < NG; ++gi) Mpv[ht][gi] = __shfl(x, 4 * g + gi);
-      }
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        const int gi = nt >> 1;  // group of channels 16nt..16nt+15
-        const uint32_t w = s_vw[g * (kD + kVwPad) + 16 * nt + n];
-        const u32x4 B = {w & 0x03030303u, w & 0x0c0c0c0cu, w & 0x30303030u, (w >> 2) & 0x30303030u};
-#pragma unroll
-        for (int ht = 0; ht < NHT; ++ht) {
+        for (int nt = 0; nt < 8; ++nt) {
+          const int gi = nt >> 1;  // group of channels 16nt..16nt+15
+          const uint32_t w = s_vw[g * (kD + kVwPad) + 16 * nt + n];
+          const u32x4 B = {w & 0x03030303u, w & 0x0c0c0c0cu, w & 0x30303030u, (w >> 2) & 0x30303030u};
           // row (head g, group gi) of the four digit products
-          const int d0 = mfma_i8(A[ht][0], B, i32x4{0, 0, 0, 0})[gi];
-          const int d1 = mfma_i8(A[ht][1], B, i32x4{0, 0, 0, 0})[gi];
-          const int d2 = mfma_i8(A[ht][2], B, i32x4{0, 0, 0, 0})[gi];
-          const int d3 = mfma_i8(A[ht][3], B, i32x4{0, 0, 0, 0})[gi];
+          const int d0 = mfma_i8(A[0], B, i32x4{0, 0, 0, 0})[gi];
+          const int d1 = mfma_i8(A[1], B, i32x4{0, 0, 0, 0})[gi];
+          const int d2 = mfma_i8(A[2], B, i32x4{0, 0, 0, 0})[gi];
+          const int d3 = mfma_i8(A[3], B, i32x4{0, 0, 0, 0})[gi];
           const float v = fmaf((float)((d0 << 8) + d1), 65536.f, (float)((d2 << 8) + d3));
-          acc[ht][nt] = fmaf(acc[ht][nt], alpha_pv[ht], fmaf(v, inv_sv, Mpv[ht][gi]));
+          acc[ht][nt] = fmaf(acc[ht][nt], alpha_pv[ht], fmaf(v, inv_sv, Mpv[gi]));
         }
       }
     } else {
@@ -697,7 +715,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
         Acc += f * base[w * kStride + hh * (kD + 2) + 2 + c];
       }
     }
-    float* part = a.partial + (((size_t)blockIdx.x * a.batch + b) * a.h_q + h * G + hh) * (kD + 2);
+    float* part = a.partial + ((size_t)blockIdx.x * a.batch * a.h_kv * G + ws_row(a, b, h, hh)) * (kD + 2);
     if (c == 0) {
       part[0] = M;
       part[1] = L;

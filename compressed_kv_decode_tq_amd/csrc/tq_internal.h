@@ -70,7 +70,7 @@ struct EncodeArgs {
 };
 
 struct DecodeArgs {
-  const void* q;          // [batch][h_q][d]
+  const void* q;          // [batch][nq][h_q][d]
   const uint8_t* k_planes;
   const void* k_norm;
   const void* k_rnorm;
@@ -82,14 +82,17 @@ struct DecodeArgs {
   const float* mat_t;     // fp32 Pi^T then S^T ([2][d][d], from the derived buffer)
   const uint16_t* ring_k; // bf16 [batch][ring_cap][h_kv][d]
   const uint16_t* ring_v;
-  float* out;             // [batch][h_q][d]
-  float* qprep;           // workspace: [batch][h_q][2][d] fp32 (Pi q, S q)
-  float* partial;         // workspace: [splits][batch][h_q][d + 2] (m, l, acc)
+  float* out;             // [batch][nq][h_q][d]
+  float* qprep;           // workspace: [batch][h_kv][group][2][d] fp32 (Pi q, S q)
+  float* partial;         // workspace: [splits][batch][h_kv][group][d + 2] (m, l, acc)
   int64_t capacity;
   int32_t batch;
   int32_t h_q;
   int32_t h_kv;
-  int32_t group;          // h_q / h_kv
+  int32_t group;          // virtual heads per KV head in this launch (<= kMaxGroup)
+  int32_t nq;             // queries per sequence (T)
+  int32_t qgroup;         // query heads per KV head (h_q / h_kv)
+  int32_t vbase;          // first virtual head of this launch
   int32_t q_bf16;
   int32_t scalar_f16;
   int32_t value_group;
@@ -106,10 +109,35 @@ struct DecodeArgs {
   float val_w[4];
   float val_cst;
   int8_t* qdig;           // workspace: query digit operands of the MFMA scan
-  float* qconst;          // workspace: [batch][h_q][4] per-head score constants
+  float* qconst;          // workspace: [batch][h_kv][group][4] per-head score constants
   SeqValues n_comp;
   SeqValues n_ring;
 };
+
+// Multi-query decode.  The nq queries of a sequence against one KV head form
+// nq * qgroup virtual heads v = t * qgroup + g (query t, query head
+// h * qgroup + g); one set of launches handles `group` of them from vbase on.
+// With nq = 1 and vbase = 0 a virtual head is the query head itself.
+__host__ __device__ inline void virtual_head(const DecodeArgs& a, int h, int gq, int& t, int& hq) {
+  const int v = a.vbase + gq;
+  t = v / a.qgroup;
+  hq = h * a.qgroup + v % a.qgroup;
+}
+// Keys hidden from query t: the last nq - 1 - t of the sequence's
+// compressed-then-ring order, taken from the ring first.
+__host__ __device__ inline void hidden_keys(const DecodeArgs& a, int t, int nr, int& hide_c, int& hide_r) {
+  const int hd = a.nq - 1 - t;
+  hide_r = hd < nr ? hd : nr;
+  hide_c = hd - hide_r;
+}
+// Row of (sequence b, KV head h, virtual head gq of the launch) in the
+// workspace arrays, and of (sequence b, query t, query head hq) in q and out.
+__host__ __device__ inline size_t ws_row(const DecodeArgs& a, int b, int h, int gq) {
+  return ((size_t)b * a.h_kv + h) * a.group + gq;
+}
+__host__ __device__ inline size_t q_row(const DecodeArgs& a, int b, int t, int hq) {
+  return ((size_t)b * a.nq + t) * a.h_q + hq;
+}
 
 // Expansion of a symmetric codebook over bit planes: for idx = sum_k b_k 2^k,
 //   c[idx] = cst + sum_p w[p] * plane_p, plane_0..2 = b_0..b_2, plane_3 = b_0^b_1^b_2.

@@ -25,6 +25,7 @@ MAX_LEVELS = 16
 #: Every symbol include/tq.h declares.
 EXPORTS = ("tq_make_codebook", "tq_memory_bytes", "tq_params_derived_bytes", "tq_prepare_params",
            "tq_encode_kv", "tq_ring_append", "tq_decode_workspace_bytes", "tq_decode_attn",
+           "tq_decode_workspace_bytes_multi", "tq_decode_attn_multi",
            "tq_time_next_launch", "tq_last_error", "tq_version")
 TQ_KERNEL_DECODE_SCAN, TQ_KERNEL_ENCODE_KEYS, TQ_KERNEL_ENCODE_VALUES = 0, 1, 2
 
@@ -87,6 +88,11 @@ def lib() -> ctypes.CDLL:
         L.tq_decode_attn.argtypes = [P(_Layout), P(_Params), vp, i32, i32, P(_Cache), P(i64), vp, vp,
                                      i32, P(i32), ctypes.c_float, vp, vp, sz, vp]
         L.tq_decode_attn.restype = ctypes.c_int
+        L.tq_decode_workspace_bytes_multi.argtypes = [P(_Layout), i32, i32, i32, i64, i32]
+        L.tq_decode_workspace_bytes_multi.restype = sz
+        L.tq_decode_attn_multi.argtypes = [P(_Layout), P(_Params), vp, i32, i32, i32, P(_Cache), P(i64), vp,
+                                           vp, i32, P(i32), ctypes.c_float, vp, vp, sz, vp]
+        L.tq_decode_attn_multi.restype = ctypes.c_int
         L.tq_time_next_launch.argtypes = [i32, vp, vp]
         L.tq_time_next_launch.restype = ctypes.c_int
         L.tq_last_error.argtypes = []
@@ -250,35 +256,52 @@ def ring_append(k_new: torch.Tensor, v_new: torch.Tensor, ring_k: torch.Tensor, 
                                 _ptr(ring_k), _ptr(ring_v), r, nr, _stream(stream)))
 
 
-def decode_workspace_bytes(layout: Layout, batch: int, num_q_heads: int, num_kv_heads: int, max_tokens: int) -> int:
+def decode_workspace_bytes(layout: Layout, batch: int, num_q_heads: int, num_kv_heads: int, max_tokens: int,
+                           num_queries: int = 1) -> int:
     lay = layout.c()
-    return int(lib().tq_decode_workspace_bytes(ctypes.byref(lay), batch, num_q_heads, num_kv_heads, max_tokens))
+    if num_queries == 1:
+        return int(lib().tq_decode_workspace_bytes(ctypes.byref(lay), batch, num_q_heads, num_kv_heads, max_tokens))
+    return int(lib().tq_decode_workspace_bytes_multi(ctypes.byref(lay), batch, num_q_heads, num_kv_heads,
+                                                     max_tokens, num_queries))
 
 
 def decode_attn(params: Params, q: torch.Tensor, cache: Cache, n_compressed, ring_k=None, ring_v=None,
                 n_ring=None, scale: float | None = None, out: torch.Tensor | None = None,
                 workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """One decode step: q [B, H_q, d] (fp32 or bf16) -> out [B, H_q, d] fp32."""
+    """One decode step: q [B, H_q, d] (fp32 or bf16) -> out [B, H_q, d] fp32; or
+    several causal queries per sequence: q [B, T, H_q, d] -> out [B, T, H_q, d]
+    (tq_decode_attn_multi)."""
     lay_py = params.layout
-    b, h_q, d = q.shape
+    multi = q.dim() == 4
+    if multi:
+        b, nq, h_q, d = q.shape
+    else:
+        b, h_q, d = q.shape
+        nq = 1
     if not q.is_contiguous():
         raise ValueError("q must be contiguous")
     if scale is None:
         scale = 1.0 / float(np.sqrt(d))
     if out is None:
-        out = torch.empty((b, h_q, d), dtype=torch.float32, device=q.device)
+        out = torch.empty(tuple(q.shape), dtype=torch.float32, device=q.device)
     nc = (ctypes.c_int64 * b)(*[int(x) for x in n_compressed])
     max_tokens = max(int(x) for x in n_compressed)
-    need = decode_workspace_bytes(lay_py, b, h_q, cache.num_kv_heads, max_tokens)
+    need = decode_workspace_bytes(lay_py, b, h_q, cache.num_kv_heads, max_tokens, nq)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     ring_cap = 0 if ring_k is None else ring_k.shape[1]
     nr = (ctypes.c_int32 * b)(*([int(x) for x in n_ring] if n_ring is not None else [0] * b))
     lay, prm, cc = lay_py.c(), params.c(), cache.c()
-    _check(lib().tq_decode_attn(ctypes.byref(lay), ctypes.byref(prm), _ptr(q), _dtype_code(q), h_q,
-                                ctypes.byref(cc), nc, _ptr(ring_k), _ptr(ring_v), ring_cap, nr,
-                                float(scale), _ptr(out), _ptr(workspace), workspace.numel(),
-                                _stream(stream)))
+    if multi:
+        _check(lib().tq_decode_attn_multi(ctypes.byref(lay), ctypes.byref(prm), _ptr(q), _dtype_code(q), h_q, nq,
+                                          ctypes.byref(cc), nc, _ptr(ring_k), _ptr(ring_v), ring_cap, nr,
+                                          float(scale), _ptr(out), _ptr(workspace), workspace.numel(),
+                                          _stream(stream)))
+    else:
+        _check(lib().tq_decode_attn(ctypes.byref(lay), ctypes.byref(prm), _ptr(q), _dtype_code(q), h_q,
+                                    ctypes.byref(cc), nc, _ptr(ring_k), _ptr(ring_v), ring_cap, nr,
+                                    float(scale), _ptr(out), _ptr(workspace), workspace.numel(),
+                                    _stream(stream)))
     return out
 
 

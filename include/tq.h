@@ -196,6 +196,28 @@ int tq_decode_attn(const tq_layout* layout, const tq_params* params, const void*
                    int32_t ring_cap, const int32_t* n_ring_host, float softmax_scale, float* out,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* Multi-query decode (page "turboquant/audit_claims.py", AUDIT 4: the
+ * (H_kv, G, T, N) score layout with T query positions per step): num_queries
+ * = T queries per sequence, for speculative verification or chunked prefill
+ * over the same cache.  q: [batch][T][h_q][d] in q_dtype; out: [batch][T]
+ * [h_q][d] fp32.  The T queries are the sequence's last T positions, already
+ * in the cache (compressed or ring): with the keys of a sequence ordered as
+ * its n_compressed_host[b] compressed tokens followed by its n_ring_host[b]
+ * ring tokens, query t sees every key except the last T - 1 - t of that order
+ * (causal among the new positions).  A query that sees no key gets a zero
+ * output.  Up to 8 (query, head) pairs per KV head share one pass over the
+ * compressed cache; larger T * (h_q / h_kv) takes several passes.  workspace
+ * must hold tq_decode_workspace_bytes_multi bytes; other arguments and errors
+ * as tq_decode_attn, plus TQ_ERR_INVALID for num_queries < 1.  With T = 1 it
+ * is tq_decode_attn. */
+size_t tq_decode_workspace_bytes_multi(const tq_layout* layout, int32_t batch, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int64_t max_tokens, int32_t num_queries);
+int tq_decode_attn_multi(const tq_layout* layout, const tq_params* params, const void* q,
+                         int32_t q_dtype, int32_t num_q_heads, int32_t num_queries, const tq_cache* cache,
+                         const int64_t* n_compressed_host, const void* ring_k, const void* ring_v,
+                         int32_t ring_cap, const int32_t* n_ring_host, float softmax_scale, float* out,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* Measurement hook.  The next launch of `kernel` (TQ_KERNEL_*) made by the
  * calling thread records ev_begin just before it and ev_end just after it on
  * the launch stream (both hipEvent_t created by the caller), so the caller can

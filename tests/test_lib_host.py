@@ -135,6 +135,14 @@ def test_encode_and_decode_argument_checks():
     assert L.tq_decode_attn(*args(4, 1 << 30, big)) == tq.TQ_ERR_CAPACITY
     need = L.tq_decode_workspace_bytes(ctypes.byref(lay), 2, 4, 1, 64)
     assert need > 0
+    # multi-query: one query is the single-query size; more need at least as much
+    margs = lambda nq, ws: (ctypes.byref(lay), ctypes.byref(prm), 16, tq.TQ_F32, 4, nq,  # noqa: E731
+                            ctypes.byref(cache), nc, None, None, 0, nr, 0.1, 16, 16, ws, None)
+    assert L.tq_decode_workspace_bytes_multi(ctypes.byref(lay), 2, 4, 1, 64, 1) == need
+    assert L.tq_decode_workspace_bytes_multi(ctypes.byref(lay), 2, 4, 1, 64, 3) >= need
+    assert L.tq_decode_workspace_bytes_multi(ctypes.byref(lay), 2, 4, 1, 64, 0) == 0
+    assert L.tq_decode_attn_multi(*margs(0, 1 << 30)) == tq.TQ_ERR_INVALID
+    assert L.tq_decode_attn_multi(*margs(3, 8)) == tq.TQ_ERR_WORKSPACE
     # ring append bounds
     nr_full = (ctypes.c_int32 * 2)(0, 128)
     assert L.tq_ring_append(16, 16, tq.TQ_BF16, 2, 1, 128, 16, 16, 128, nr_full, None) == tq.TQ_ERR_CAPACITY
