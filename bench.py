@@ -214,6 +214,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="batched-b32-hkv8-n32768")
     ap.add_argument("--encode-reps", type=int, default=3)
+    ap.add_argument("--queries", type=int, default=1,
+                    help="causal queries per sequence and step (multi-query decode: T new tokens are appended, "
+                         "then all T attend in one call)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run a plain elementwise kernel (y = -x, fp32) over this many MiB, "
@@ -256,9 +259,13 @@ def main():
     k, v = wl.prefill_kv(w)
     k, v = k.to(dev), v.to(dev)
     total_steps = args.warmup + args.steps
+    nq = args.queries
     ring = w.ring_cap if w.step_mode == "ring" else 0
-    flushes = (total_steps // ring + 1) if ring else 0
-    extra = (total_steps if w.step_mode == "encode" else flushes * ring)
+    if nq < 1 or (ring and nq > ring):
+        print(f"--queries must be in 1..{ring or 'any'}", file=sys.stderr)
+        sys.exit(2)
+    flushes = (total_steps * nq // ring + 1) if ring else 0
+    extra = (total_steps * nq if w.step_mode == "encode" else flushes * ring)
     cap = ((w.n_tokens + extra + 31) // 32) * 32
     cache = tq.Cache(lay, w.batch, w.h_kv, cap, device=dev)
     torch.cuda.synchronize()
@@ -287,28 +294,34 @@ def main():
 
     # ---- decode steps
     print("[bench] decode steps", file=sys.stderr, flush=True)
-    qs = [wl.query(w, i).to(dev) for i in range(total_steps)]
-    news = [tuple(x.to(dev).contiguous() for x in wl.step_kv(w, i)) for i in range(total_steps)]
+    if nq == 1:
+        qs = [wl.query(w, i).to(dev) for i in range(total_steps)]
+    else:
+        qs = [torch.stack([wl.query(w, i * nq + t) for t in range(nq)], dim=1).to(dev).contiguous()
+              for i in range(total_steps)]
+    news = [tuple(x.to(dev).contiguous() for x in wl.step_kv(w, i)) for i in range(total_steps * nq)]
     rk = torch.zeros((w.batch, max(ring, 1), w.h_kv, w.d), dtype=torch.bfloat16, device=dev)
     rv = torch.zeros_like(rk)
-    out = torch.empty((w.batch, w.h_q, w.d), dtype=torch.float32, device=dev)
-    ws = torch.empty(tq.decode_workspace_bytes(lay, w.batch, w.h_q, w.h_kv, cap), dtype=torch.uint8, device=dev)
+    out = torch.empty(tuple(qs[0].shape), dtype=torch.float32, device=dev)
+    ws = torch.empty(tq.decode_workspace_bytes(lay, w.batch, w.h_q, w.h_kv, cap, nq), dtype=torch.uint8, device=dev)
     state = {"n_c": w.n_tokens, "n_r": 0}
     per_th = tq.memory_bytes(lay, 1, 1, 1, 0, tq.TQ_BYTES_DATA)
     qbytes = 2 if w.in_dtype == "bf16" else 4
 
     def step(i, timed_pair=None):
-        kn, vn = news[i]
-        if ring:
-            if state["n_r"] == ring:  # full ring: flush its tokens into the compressed store
-                tq.encode_kv(prm, rk, rv, [state["n_c"]] * w.batch, cache)
-                state["n_c"] += ring
-                state["n_r"] = 0
-            tq.ring_append(kn, vn, rk, rv, [state["n_r"]] * w.batch)
-            state["n_r"] += 1
-        elif w.step_mode == "encode":
-            tq.encode_kv(prm, kn, vn, [state["n_c"]] * w.batch, cache)
-            state["n_c"] += 1
+        if ring and state["n_r"] + nq > ring:  # no room for the step's tokens: flush the ring
+            tq.encode_kv(prm, rk[:, :state["n_r"]].contiguous(), rv[:, :state["n_r"]].contiguous(),
+                         [state["n_c"]] * w.batch, cache)
+            state["n_c"] += state["n_r"]
+            state["n_r"] = 0
+        for t in range(nq):
+            kn, vn = news[i * nq + t]
+            if ring:
+                tq.ring_append(kn, vn, rk, rv, [state["n_r"]] * w.batch)
+                state["n_r"] += 1
+            elif w.step_mode == "encode":
+                tq.encode_kv(prm, kn, vn, [state["n_c"]] * w.batch, cache)
+                state["n_c"] += 1
         if timed_pair is not None:
             tq.time_next_launch(tq.TQ_KERNEL_DECODE_SCAN, *timed_pair)
         tq.decode_attn(prm, qs[i], cache, [state["n_c"]] * w.batch, rk if ring else None,
@@ -317,16 +330,16 @@ def main():
         # algorithmic bytes of this step
         by = per_th * w.batch * w.h_kv * state["n_c"]                       # compressed cache
         by += state["n_r"] * w.batch * w.h_kv * w.d * 2 * 2                 # ring K and V
-        by += w.batch * w.h_q * w.d * (qbytes + 4)                          # q in, out
+        by += nq * w.batch * w.h_q * w.d * (qbytes + 4)                     # q in, out
         by += 2 * w.d * w.d * 4                                             # Pi, S
         if ring:
-            by += w.batch * w.h_kv * w.d * (qbytes + 2) * 2                 # new token in, ring write
+            by += nq * w.batch * w.h_kv * w.d * (qbytes + 2) * 2            # new tokens in, ring writes
         return by, per_th * w.batch * w.h_kv * state["n_c"]
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    if ring:  # the timed steps see ring lengths 1..K
+    if ring:  # the timed steps start from an empty ring
         state["n_r"] = 0
     ev = Events(args.steps)
     torch.cuda.synchronize()
@@ -360,7 +373,9 @@ def main():
         "vs_baseline": None, "dtype": "i8-mfma+f32",
         "data": "synthetic (seeded N(0,1) K/V/q with outlier channels; no dataset, no weights)",
         "config": {"workload": w.name, "batch": w.batch, "h_q": w.h_q, "h_kv": w.h_kv, "head_dim": w.d,
-                   "n_compressed": w.n_tokens, "ring_cap": w.ring_cap, "ring_tokens_in_timed_steps": f"1..{args.steps}",
+                   "n_compressed": w.n_tokens, "ring_cap": w.ring_cap,
+                   "ring_tokens_in_timed_steps": f"{nq}..{min(args.steps * nq, ring)}" if ring else "none",
+                   "queries_per_step": nq,
                    "key_bits": f"{w.key_mse_bits}-bit Lloyd-Max + {w.key_qjl}-bit QJL",
                    "value_code": f"{w.value_bits}-bit {w.value_kind}" + (f" g{w.value_group}" if w.value_kind == "minmax" else ""),
                    "scalars": w.scalar_dtype, "bytes_per_token_head": per_th, "parallelism": "single GPU"},
