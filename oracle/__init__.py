@@ -34,11 +34,11 @@ from .quantize import (  # noqa: F401
     KeyCode, ValueMinMax, ValueMSE,
     encode_keys, encode_values_minmax, encode_values_mse,
     dequantize_keys, dequantize_values_minmax, dequantize_values_mse,
-    score_estimate, round_scalar,
+    score_estimate, round_scalar, half_bit_coordinates,
 )
 from .attention import decode_attention, decode_attention_bruteforce, decode_attention_multi  # noqa: F401
 from .layout import (  # noqa: F401
     Layout, pack_key_planes, unpack_key_planes, pack_value_planes, unpack_value_planes,
     pack_value_codes, unpack_value_codes, pack_value_words, unpack_value_words, value_words_packed,
-    memory_bytes, bytes_per_token_head,
+    memory_bytes, bytes_per_token_head, half_plane_position,
 )

@@ -7,10 +7,14 @@ can be compared bit for bit.
 
 Per (sequence, KV head) slot of ``capacity`` tokens:
 
-* key planes   uint8  [capacity][P_k * d/8], P_k = key_mse_bits + key_qjl.
-  Plane p < key_mse_bits holds bit p of every coordinate's Lloyd-Max index;
-  plane key_mse_bits holds the QJL sign bits (1 = non-negative).  Inside a
-  plane, coordinate i is bit i % 8 of byte i // 8 (LSB first).
+* key planes   uint8  [capacity][record], record = key_mse_bits full planes
+  (d/8 bytes each), then with the half-bit layout one half plane (d/16 bytes),
+  then the QJL plane (d/8 bytes) when key_qjl.  Full plane p holds bit p of
+  every coordinate's Lloyd-Max index, coordinate i in bit i % 8 of byte
+  i // 8 (LSB first).  The half plane holds bit key_mse_bits of the index of
+  the half-bit coordinates (i mod 32 < 16), coordinate i at bit position
+  h = 16 (i // 32) + i mod 32 (bit h % 8 of byte h // 8).  The QJL plane
+  holds the sign bits (1 = non-negative) in the full-plane order.
 * key norm, key residual norm   [capacity] fp32 or fp16.
 * value words uint32 [capacity/32][value_bits][d], in one of two forms:
   - bit planes (MSE values, and min/max values of width 1 or 3): word (blk, p,
@@ -43,6 +47,7 @@ class Layout:
     value_bits: int = 2
     value_group: int = 32
     scalar_dtype: str = "f32"  # "f32" | "f16"
+    key_half: int = 0  # 1: half of the rotated coordinates get key_mse_bits + 1 bits
 
     @property
     def scalar_bytes(self) -> int:
@@ -56,7 +61,7 @@ class Layout:
 def bytes_per_token_head(lay: Layout) -> dict:
     """Stored bytes for one token of one KV head, by field."""
     s = lay.scalar_bytes
-    k_bits = lay.key_planes * lay.d // 8
+    k_bits = lay.key_planes * lay.d // 8 + lay.key_half * lay.d // 16
     k_scal = s * (1 + lay.key_qjl)
     v_bits = lay.value_bits * lay.d // 8
     if lay.value_kind == "minmax":
@@ -81,6 +86,8 @@ def memory_bytes(lay: Layout, batch: int, h_kv: int, n_tokens: int, what: str,
         return bytes_per_token_head(lay)["total"] * batch * h_kv * n_tokens
     if what == "params":
         p = 2 * lay.d * lay.d * 4 + codebook_table_bytes(lay.key_mse_bits)
+        if lay.key_half:
+            p += codebook_table_bytes(lay.key_mse_bits + 1)
         if lay.value_kind == "mse":
             p += codebook_table_bytes(lay.value_bits)
         return p
@@ -89,26 +96,37 @@ def memory_bytes(lay: Layout, batch: int, h_kv: int, n_tokens: int, what: str,
     raise ValueError(what)
 
 
-def pack_key_planes(idx: np.ndarray, qjl: np.ndarray | None, mse_bits: int) -> np.ndarray:
-    """(T, d) indices and (T, d) sign bits -> (T, P_k * d/8) uint8 planes."""
+def half_plane_position(d: int) -> np.ndarray:
+    """Coordinates of the half plane in order: entry h is the coordinate i with
+    16 (i // 32) + i mod 32 == h (those with i mod 32 < 16)."""
+    i = np.arange(d)
+    return i[(i % 32) < 16]
+
+
+def pack_key_planes(idx: np.ndarray, qjl: np.ndarray | None, mse_bits: int, half: bool = False) -> np.ndarray:
+    """(T, d) indices and (T, d) sign bits -> (T, record) uint8 planes."""
     idx = np.asarray(idx, dtype=np.int64)
     t, d = idx.shape
     planes = [((idx >> p) & 1).astype(np.uint8) for p in range(mse_bits)]
+    if half:
+        planes.append(((idx[:, half_plane_position(d)] >> mse_bits) & 1).astype(np.uint8))
     if qjl is not None:
         planes.append(np.asarray(qjl, dtype=np.uint8) & 1)
-    bits = np.concatenate(planes, axis=1)  # (T, P*d)
+    bits = np.concatenate(planes, axis=1)  # (T, record bits)
     return np.packbits(bits, axis=1, bitorder="little")
 
 
-def unpack_key_planes(packed: np.ndarray, d: int, mse_bits: int, qjl: bool):
+def unpack_key_planes(packed: np.ndarray, d: int, mse_bits: int, qjl: bool, half: bool = False):
     """Inverse of pack_key_planes: returns (idx, qjl_bits or None)."""
-    p_k = mse_bits + (1 if qjl else 0)
-    bits = np.unpackbits(np.asarray(packed, dtype=np.uint8), axis=1, bitorder="little")
-    bits = bits[:, : p_k * d].reshape(-1, p_k, d).astype(np.int64)
+    bits = np.unpackbits(np.asarray(packed, dtype=np.uint8), axis=1, bitorder="little").astype(np.int64)
     idx = np.zeros((bits.shape[0], d), dtype=np.int64)
     for p in range(mse_bits):
-        idx |= bits[:, p, :] << p
-    return idx, (bits[:, mse_bits, :].astype(np.uint8) if qjl else None)
+        idx |= bits[:, p * d:(p + 1) * d] << p
+    off = mse_bits * d
+    if half:
+        idx[:, half_plane_position(d)] |= bits[:, off:off + d // 2] << mse_bits
+        off += d // 2
+    return idx, (bits[:, off:off + d].astype(np.uint8) if qjl else None)
 
 
 def value_bit(u) -> np.ndarray:

@@ -18,6 +18,13 @@ Readings taken where the pages are silent:
   score and every reconstructed value 0.
 * QJL scale: sqrt(pi/2)/m with m = d rows of S, since for s ~ N(0, I)
   E[sign(<s,r>) <s,y>] = sqrt(2/pi) <r,y>/|r|.
+* Fractional key widths (the pages' 2.5 and 3.5 bits per channel, [explainer]
+  "Ý tưởng cốt lõi" / "Ý nghĩa thực tế"; the pages do not say how the half bit
+  is spent): half of the rotated coordinates, those i with i mod 32 < 16, use a
+  Lloyd-Max quantizer with one more bit than the rest.  After the rotation
+  every coordinate has the same law, so which half gets the extra bit does
+  not change the distortion.  TurboQuantProd(3.5) = 2.5 MSE bits + QJL,
+  TurboQuantProd(2.5) = 1.5 MSE bits + QJL.
 * Stored scalars (n, gamma, value norm) are rounded once to the layout's
   scalar dtype (fp32 or fp16, round-to-nearest-even); normalisation uses the
   unrounded norm, reconstruction the stored one.
@@ -56,6 +63,24 @@ def _normalize(x: np.ndarray):
     return n, u
 
 
+def half_bit_coordinates(d: int) -> np.ndarray:
+    """Mask of the rotated coordinates that get the extra bit in the fractional
+    (half-bit) key layout: i mod 32 < 16."""
+    return (np.arange(d) % 32) < 16
+
+
+def _centroid_values(idx: np.ndarray, centroids: np.ndarray, centroids_hi=None) -> np.ndarray:
+    """c[idx] per coordinate; with centroids_hi, the half-bit coordinates read
+    the larger table."""
+    if centroids_hi is None:
+        return centroids[idx]
+    mask = half_bit_coordinates(idx.shape[-1])
+    out = np.empty(idx.shape, dtype=np.float64)
+    out[..., ~mask] = centroids[idx[..., ~mask]]
+    out[..., mask] = centroids_hi[idx[..., mask]]
+    return out
+
+
 def _bucketize(y: np.ndarray, thresholds: np.ndarray) -> np.ndarray:
     """idx = #{k : t_k < y}; a value equal to a threshold stays in the lower cell."""
     return np.searchsorted(thresholds, y, side="left").astype(np.int64)
@@ -73,7 +98,8 @@ class KeyCode:
 
 
 def encode_keys(k: np.ndarray, Pi: np.ndarray, S: np.ndarray, centroids: np.ndarray,
-                thresholds: np.ndarray, scalar_dtype: str = "f32", qjl: bool = True) -> KeyCode:
+                thresholds: np.ndarray, scalar_dtype: str = "f32", qjl: bool = True,
+                centroids_hi=None, thresholds_hi=None) -> KeyCode:
     """TurboQuantProd encode of the rows of k (any float dtype, promoted to float64).
 
     Steps, in the order of [explainer] "Ý tưởng cốt lõi" / "Tại sao nó hoạt động":
@@ -82,12 +108,17 @@ def encode_keys(k: np.ndarray, Pi: np.ndarray, S: np.ndarray, centroids: np.ndar
       3. idx_i = #{t : t < y_i}          (one scalar quantizer for every coordinate)
       4. r = u - Pi^T c[idx], gamma = |r| (residual of the MSE stage)
       5. sigma = sign(S r)               (1-bit QJL sketch of the residual)
+    With centroids_hi / thresholds_hi (one more bit), the half-bit coordinates
+    of half_bit_coordinates use those tables in step 3.
     """
     k = np.asarray(k, dtype=np.float64)
     n, u = _normalize(k)
     y = u @ Pi.T
     idx = _bucketize(y, thresholds)
-    u_mse = centroids[idx] @ Pi
+    if thresholds_hi is not None:
+        mask = half_bit_coordinates(y.shape[-1])
+        idx = np.where(mask, _bucketize(y, thresholds_hi), idx)
+    u_mse = _centroid_values(idx, centroids, centroids_hi) @ Pi
     r = u - u_mse
     gamma = np.linalg.norm(r, axis=-1)
     if qjl:
@@ -102,13 +133,13 @@ def encode_keys(k: np.ndarray, Pi: np.ndarray, S: np.ndarray, centroids: np.ndar
 
 
 def dequantize_keys(code: KeyCode, Pi: np.ndarray, S: np.ndarray, centroids: np.ndarray,
-                    qjl: bool = True) -> np.ndarray:
+                    qjl: bool = True, centroids_hi=None) -> np.ndarray:
     """k~ = n (Pi^T c[idx] + sqrt(pi/2)/d * gamma * S^T sigma), sigma = 2 bit - 1:
     the reconstruction whose inner product with any query is the unbiased
     TurboQuantProd score ([audit] AUDIT 2 dequantizes keys this way before
     its matmul; AUDIT 6 checks the unbiasedness)."""
     d = Pi.shape[0]
-    k_mse = centroids[code.idx] @ Pi
+    k_mse = _centroid_values(code.idx, centroids, centroids_hi) @ Pi
     if qjl:
         sigma = 2.0 * code.qjl.astype(np.float64) - 1.0
         k_qjl = (QJL_SCALE / d) * code.rnorm[:, None] * (sigma @ S)
@@ -118,14 +149,14 @@ def dequantize_keys(code: KeyCode, Pi: np.ndarray, S: np.ndarray, centroids: np.
 
 
 def score_estimate(q: np.ndarray, code: KeyCode, Pi: np.ndarray, S: np.ndarray,
-                   centroids: np.ndarray, qjl: bool = True) -> np.ndarray:
+                   centroids: np.ndarray, qjl: bool = True, centroids_hi=None) -> np.ndarray:
     """<q, k> estimate for every key (the quantizer's ``attention_score`` of
     [audit] AUDIT 3/5/6): the query is rotated once and the keys are never
     reconstructed ([explainer] "Tại sao nó hoạt động", rotate the query at run
     time):  n (<Pi q, c[idx]> + sqrt(pi/2)/d * gamma <S q, sigma>)."""
     q = np.asarray(q, dtype=np.float64)
     d = Pi.shape[0]
-    s = centroids[code.idx] @ (Pi @ q)
+    s = _centroid_values(code.idx, centroids, centroids_hi) @ (Pi @ q)
     if qjl:
         sigma = 2.0 * code.qjl.astype(np.float64) - 1.0
         s = s + (QJL_SCALE / d) * code.rnorm * (sigma @ (S @ q))

@@ -137,3 +137,34 @@ def test_workload_layouts_bytes():
     assert bytes_per_token_head(Layout(value_kind="mse", value_bits=3, scalar_dtype="f16"))["total"] == 102
     assert bytes_per_token_head(Layout(key_mse_bits=3, value_kind="mse", value_bits=3,
                                        scalar_dtype="f16"))["total"] == 118
+
+
+def test_half_bit_key_planes_round_trip_and_bit_positions():
+    rng = np.random.default_rng(3)
+    d = 128
+    mask = oracle.half_bit_coordinates(d)
+    for mse_bits in (1, 2):
+        idx = np.where(mask, rng.integers(0, 1 << (mse_bits + 1), size=(9, d)),
+                       rng.integers(0, 1 << mse_bits, size=(9, d)))
+        q = rng.integers(0, 2, size=(9, d)).astype(np.uint8)
+        packed = oracle.pack_key_planes(idx, q, mse_bits, half=True)
+        assert packed.shape == (9, (mse_bits * d + d // 2 + d) // 8)
+        i2, q2 = oracle.unpack_key_planes(packed, d, mse_bits, True, half=True)
+        assert np.array_equal(i2, idx) and np.array_equal(q2, q)
+    # worked example, 2 full planes: coordinate 37 (32 + 5: half plane bit
+    # 16 + 5 = 21 -> byte 32 + 2, bit 5) with index 4 = binary 100; coordinate
+    # 20 (no half-plane bit) with index 3; QJL bit of coordinate 1
+    idx = np.zeros((1, d), dtype=np.int64)
+    idx[0, 37] = 4
+    idx[0, 20] = 3
+    q = np.zeros((1, d), dtype=np.uint8)
+    q[0, 1] = 1
+    p = oracle.pack_key_planes(idx, q, 2, half=True)[0]
+    expect = np.zeros(56, dtype=np.uint8)
+    expect[2] = 1 << 4          # plane 0, coordinate 20: byte 2, bit 4
+    expect[16 + 2] = 1 << 4     # plane 1, coordinate 20
+    expect[32 + 2] = 1 << 5     # half plane, coordinate 37
+    expect[40] = 1 << 1         # QJL plane, coordinate 1
+    assert np.array_equal(p, expect)
+    assert oracle.bytes_per_token_head(oracle.Layout(key_half=1))["k_bits"] == 56
+    assert oracle.bytes_per_token_head(oracle.Layout(key_mse_bits=1, key_half=1))["k_bits"] == 40

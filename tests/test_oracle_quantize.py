@@ -194,3 +194,55 @@ def test_mse_values_reconstruction():
     # relative error of the 3-bit code is far below 1 and about sqrt(MSE per unit vector)
     rel = np.linalg.norm(rec - v, axis=1) / np.linalg.norm(v, axis=1)
     assert 0.1 < rel.mean() < 0.25
+
+
+def _cell_distortion(cb, d):
+    """E (x - c[idx(x)])^2 under the coordinate law, by adaptive quadrature per cell."""
+    from scipy import integrate
+    from oracle import codebook as cbm
+    edges = cb.boundaries
+    tot = 0.0
+    for j, c in enumerate(cb.centroids):
+        v, _ = integrate.quad(lambda t: (t - c) ** 2 * cbm.coord_density(t, d), edges[j], edges[j + 1],
+                              epsabs=1e-14, limit=200)
+        tot += v
+    return tot
+
+
+@pytest.mark.parametrize("bits", [1, 2])
+def test_half_bit_keys_split_the_coordinates(bits):
+    """Fractional key width (bits + 1/2 MSE bits): the half-bit coordinates
+    (i mod 32 < 16) carry exactly the (bits + 1)-bit code, the others the
+    bits-bit code, and the per-class squared error of the rotated unit vector
+    matches each codebook's distortion integral."""
+    d = 128
+    lo, hi = oracle.lloyd_max(d, bits), oracle.lloyd_max(d, bits + 1)
+    pi = wl.rotation(d, 3)
+    s = wl.qjl_matrix(d, 3)
+    rng = np.random.default_rng(31)
+    k = rng.standard_normal((4000, d))
+    code = oracle.encode_keys(k, pi, s, lo.centroids, lo.thresholds, centroids_hi=hi.centroids,
+                              thresholds_hi=hi.thresholds)
+    mask = oracle.half_bit_coordinates(d)
+    assert mask.sum() == d // 2 and mask[0] and mask[15] and not mask[16] and mask[32] and not mask[127]
+    ref_lo = oracle.encode_keys(k, pi, s, lo.centroids, lo.thresholds)
+    ref_hi = oracle.encode_keys(k, pi, s, hi.centroids, hi.thresholds)
+    assert np.array_equal(code.idx[:, ~mask], ref_lo.idx[:, ~mask])
+    assert np.array_equal(code.idx[:, mask], ref_hi.idx[:, mask])
+    c = np.where(mask, hi.centroids[np.minimum(code.idx, 2 ** (bits + 1) - 1)], lo.centroids[np.minimum(code.idx, 2 ** bits - 1)])
+    err = (code.y - c) ** 2
+    for sel, cb in ((mask, hi), (~mask, lo)):
+        want = _cell_distortion(cb, d)
+        got = err[:, sel].mean()
+        se = err[:, sel].std() / np.sqrt(err[:, sel].size)
+        assert abs(got - want) < 5 * se, (cb.bits, got, want)
+    # the residual and the reconstruction use the per-class centroids
+    u = k / np.linalg.norm(k, axis=1, keepdims=True)
+    r = u - c @ pi
+    assert np.allclose(np.linalg.norm(r, axis=1), code.rnorm, rtol=1e-6)
+    kd = oracle.dequantize_keys(code, pi, s, lo.centroids, centroids_hi=hi.centroids)
+    kd0 = oracle.dequantize_keys(code, pi, s, lo.centroids, qjl=False, centroids_hi=hi.centroids)
+    assert np.allclose(kd0, code.norm[:, None] * (c @ pi), rtol=1e-12, atol=1e-12)
+    q = rng.standard_normal(d)
+    assert np.allclose(kd @ q, oracle.score_estimate(q, code, pi, s, lo.centroids, centroids_hi=hi.centroids),
+                       rtol=1e-10, atol=1e-10)
