@@ -51,12 +51,16 @@ int check_layout(const tq_layout* l) {
       return fail(TQ_ERR_UNSUPPORTED, "value_group %d not built (16, 32, 64 are)", l->value_group);
   }
   if (l->scalar_dtype != TQ_F32 && l->scalar_dtype != TQ_F16) return fail(TQ_ERR_INVALID, "scalar_dtype must be TQ_F32 or TQ_F16");
+  if (l->key_half != 0 && l->key_half != 1) return fail(TQ_ERR_INVALID, "key_half must be 0 or 1");
+  if (l->key_half && (!l->key_qjl || l->key_mse_bits > 2))
+    return fail(TQ_ERR_UNSUPPORTED, "key_half is built for QJL keys with key_mse_bits 1 or 2 (2.5 and 3.5 bits)");
   return TQ_OK;
 }
 
 int64_t per_token_head_bytes(const tq_layout* l) {
   const int64_t s = l->scalar_dtype == TQ_F32 ? 4 : 2;
-  int64_t k = (int64_t)(l->key_mse_bits + l->key_qjl) * l->head_dim / 8 + s * (1 + l->key_qjl);
+  int64_t k = (int64_t)(l->key_mse_bits + l->key_qjl) * l->head_dim / 8 + (int64_t)l->key_half * l->head_dim / 16 +
+              s * (1 + l->key_qjl);
   int64_t v = (int64_t)l->value_bits * l->head_dim / 8;
   v += l->value_kind == TQ_V_MINMAX ? (int64_t)(l->head_dim / l->value_group) * 4 : s;
   return k + v;
@@ -81,6 +85,13 @@ void fill_codebooks(const tq_layout* l, const tq_params* p, float* kc, float* kt
   const bool mse = l->value_kind == TQ_V_MSE;
   for (int i = 0; i < 16; ++i) vc[i] = (mse && i < vl) ? p->v_centroids[i] : 0.f;
   for (int i = 0; i < 15; ++i) vt[i] = (mse && i < vl - 1) ? p->v_thresholds[i] : INFINITY;
+}
+
+// The (key_mse_bits + 1)-bit key table of the half-bit layout (zeros otherwise).
+void fill_hi_codebook(const tq_layout* l, const tq_params* p, float* kc, float* kt) {
+  const int kl = l->key_half ? 2 << l->key_mse_bits : 0;
+  for (int i = 0; i < 16; ++i) kc[i] = i < kl ? p->k_centroids_hi[i] : 0.f;
+  for (int i = 0; i < 15; ++i) kt[i] = i < kl - 1 ? p->k_thresholds_hi[i] : INFINITY;
 }
 
 // Byte offset of sequence b0 in a [batch][h_kv][capacity]-strided plane with
@@ -132,6 +143,7 @@ int64_t tq_memory_bytes(const tq_layout* layout, int32_t batch, int32_t num_kv_h
     case TQ_BYTES_PARAMS: {
       auto tables = [](int bits) { const int64_t L = 1 << bits; return 4 * (L + (L + 1) + (L - 1)); };
       int64_t p = 2 * d * d * 4 + tables(layout->key_mse_bits);
+      if (layout->key_half) p += tables(layout->key_mse_bits + 1);
       if (layout->value_kind == TQ_V_MSE) p += tables(layout->value_bits);
       return p;
     }
@@ -177,7 +189,7 @@ int tq_encode_kv(const tq_layout* layout, const tq_params* params, const void* k
   const int64_t cap = cache->capacity;
   const size_t esz = in_dtype == TQ_F32 ? 4 : 2;
   const size_t sz = layout->scalar_dtype == TQ_F32 ? 4 : 2;
-  const size_t kpb = (size_t)(layout->key_mse_bits + layout->key_qjl) * tq::kD / 8;
+  const size_t kpb = tq::key_record_bytes(layout->key_mse_bits, layout->key_qjl, layout->key_half);
   const size_t groups = layout->value_kind == TQ_V_MINMAX ? tq::kD / layout->value_group : 0;
   const bool bf16 = in_dtype == TQ_BF16;
   hipStream_t st = (hipStream_t)stream;
@@ -203,6 +215,7 @@ int tq_encode_kv(const tq_layout* layout, const tq_params* params, const void* k
     a.scalar_f16 = layout->scalar_dtype == TQ_F16;
     a.value_group = layout->value_group;
     fill_codebooks(layout, params, a.k_cent, a.k_thr, a.v_cent, a.v_thr);
+    fill_hi_codebook(layout, params, a.k_cent_hi, a.k_thr_hi);
     int64_t tiles = 0;
     for (int b = 0; b < nb; ++b) {
       const int64_t pos = dst_pos_host[b0 + b];
@@ -214,7 +227,7 @@ int tq_encode_kv(const tq_layout* layout, const tq_params* params, const void* k
     // tile_start has kMaxSeqPerLaunch entries; the kernels stop their search at
     // `batch`, and num_tiles bounds the last sequence.
     a.num_tiles = (int32_t)tiles;
-    hipError_t e = tq::launch_encode_keys(a, bf16, layout->key_mse_bits, layout->key_qjl, st,
+    hipError_t e = tq::launch_encode_keys(a, bf16, layout->key_mse_bits, layout->key_qjl, layout->key_half, st,
                                           take_timed(TQ_KERNEL_ENCODE_KEYS));
     if (e != hipSuccess) return hip_fail(e, "encode keys launch");
     if (layout->value_kind == TQ_V_MSE)
@@ -315,7 +328,7 @@ int decode_attn_impl(const tq_layout* layout, const tq_params* params, const voi
 
   const int64_t cap = cache->capacity;
   const size_t sz = layout->scalar_dtype == TQ_F32 ? 4 : 2;
-  const size_t kpb = (size_t)(layout->key_mse_bits + layout->key_qjl) * tq::kD / 8;
+  const size_t kpb = tq::key_record_bytes(layout->key_mse_bits, layout->key_qjl, layout->key_half);
   const size_t groups = layout->value_kind == TQ_V_MINMAX ? tq::kD / layout->value_group : 0;
   const size_t qsz = q_dtype == TQ_F32 ? 4 : 2;
   const int vg_max = decode_vgroup(group, nq);
@@ -370,6 +383,18 @@ int decode_attn_impl(const tq_layout* layout, const tq_params* params, const voi
     const int vpl = vmse ? tq::plane_expansion(vc, layout->value_bits, a.val_w, &a.val_cst) : 0;
     const char* path = std::getenv("TQ_DECODE_PATH");
     const bool generic_only = path && std::strcmp(path, "generic") == 0;
+    // half-bit keys run on the MFMA scan only: its planes come from the
+    // (key_mse_bits + 1)-bit table, the base table's weights cover its planes
+    int kbits = layout->key_mse_bits, kplanes = kpl;
+    if (layout->key_half) {
+      float kch[16], kth[15];
+      fill_hi_codebook(layout, params, kch, kth);
+      kplanes = tq::plane_expansion(kch, layout->key_mse_bits + 1, a.key_w_hi, &a.key_cst_hi);
+      kbits = layout->key_mse_bits + 1;
+      a.key_half = 1;
+      if (generic_only || kpl == 0 || kplanes == 0 || (vmse && vpl == 0))
+        return fail(TQ_ERR_UNSUPPORTED, "half-bit keys need the MFMA scan (antisymmetric key and value tables)");
+    }
     // one set of launches (q-prep, scan, combine) per group of virtual heads;
     // each pass reads the compressed cache once
     for (int vbase = 0; vbase < nvirt; vbase += vg_max) {
@@ -378,8 +403,10 @@ int decode_attn_impl(const tq_layout* layout, const tq_params* params, const voi
       const tq::TimedLaunch tl = take_timed(TQ_KERNEL_DECODE_SCAN);
       hipError_t e = hipErrorNotSupported;
       if (!generic_only && kpl > 0 && (!vmse || vpl > 0))
-        e = tq::launch_decode_mfma(a, layout->key_mse_bits, layout->key_qjl, vmse, layout->value_bits, kpl,
+        e = tq::launch_decode_mfma(a, kbits, layout->key_qjl, vmse, layout->value_bits, kplanes,
                                    vpl, (hipStream_t)stream, tl);
+      if (e == hipErrorNotSupported && layout->key_half)
+        return fail(TQ_ERR_UNSUPPORTED, "half-bit keys: this value layout or head group has no MFMA scan");
       if (e == hipErrorNotSupported)
         e = tq::launch_decode(a, layout->key_mse_bits, layout->key_qjl, vmse, layout->value_bits,
                               (hipStream_t)stream, tl);

@@ -151,19 +151,25 @@ __global__ __launch_bounds__(256) void qprep_mfma_kernel(DecodeArgs a, int pm, i
   // per-head exponents and constants: one wave per head
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   for (int gq = wv; gq < MAXG; gq += 4) {
-    float mr = 0.f, ms = 0.f, sr = 0.f, ssum = 0.f;
+    // sr: sum of q_rot over the coordinates of the base table; srh over the
+    // half-bit coordinates (i mod 32 < 16) of the fractional layout
+    float mr = 0.f, ms = 0.f, sr = 0.f, srh = 0.f, ssum = 0.f;
     for (int c = lane; c < kD; c += 64) {
       mr = fmaxf(mr, fabsf(qr[gq][c]));
       ms = fmaxf(ms, fabsf(qs[gq][c]));
-      sr += qr[gq][c];
+      if (a.key_half && (c & 31) < 16)
+        srh += qr[gq][c];
+      else
+        sr += qr[gq][c];
       ssum += qs[gq][c];
     }
     mr = wave_max(mr);
     ms = wave_max(ms);
     sr = wave_sum(sr);
+    srh = wave_sum(srh);
     ssum = wave_sum(ssum);
     float wmax = 0.f;
-    for (int p = 0; p < pm; ++p) wmax = fmaxf(wmax, fabsf(a.key_w[p]));
+    for (int p = 0; p < pm; ++p) wmax = fmaxf(wmax, fmaxf(fabsf(a.key_w[p]), fabsf(a.key_w_hi[p])));
     int ex_r, ex_s;
     frexpf(mr * wmax, &ex_r);  // |w_p q_rot| < 2^ex_r
     frexpf(2.f * ms, &ex_s);
@@ -173,7 +179,7 @@ __global__ __launch_bounds__(256) void qprep_mfma_kernel(DecodeArgs a, int pm, i
       e_qjl[gq] = es;
       if (gq < G) {
         float* cst = a.qconst + ws_row(a, b, h, gq) * 4;
-        cst[0] = a.key_cst * sr;     // constant part of <q_rot, c[idx]>
+        cst[0] = a.key_cst * sr + a.key_cst_hi * srh;  // constant part of <q_rot, c[idx]>
         cst[1] = ldexpf(1.f, -er);   // digit scale of the MSE planes
         cst[2] = ldexpf(1.f, -es);   // digit scale of the QJL plane
         cst[3] = ssum;               // sum(q_s)
@@ -200,7 +206,9 @@ __global__ __launch_bounds__(256) void qprep_mfma_kernel(DecodeArgs a, int pm, i
         float x;
         int e;
         if (pl < pm) {
-          x = a.key_w[pl] * qr[gq][k];
+          // half-bit layout: per-coordinate table; key_w holds zeros past the
+          // base table's planes
+          x = (a.key_half && (k & 31) < 16 ? a.key_w_hi[pl] : a.key_w[pl]) * qr[gq][k];
           e = e_mse[gq];
         } else {
           x = 2.f * qs[gq][k];
@@ -217,10 +225,12 @@ __global__ __launch_bounds__(256) void qprep_mfma_kernel(DecodeArgs a, int pm, i
   }
 }
 
-template <int PM, bool QJL, bool VMSE, int PVB, int NHT>
+template <int PM, bool QJL, bool VMSE, int PVB, int NHT, bool HALF = false>
 __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
   constexpr int KB = PM == 1 ? 1 : (PM == 2 ? 2 : 3);  // stored key index planes
   constexpr int KP = KB + (QJL ? 1 : 0);               // stored key planes
+  // HALF: index plane KB - 1 is the half plane (16-bit chunk per lane group)
+  static_assert(!HALF || (QJL && KB >= 2), "the half-bit layout has QJL and a full plane below the half plane");
   constexpr int NPL = PM + (QJL ? 1 : 0);              // score planes
   constexpr int VB = VMSE ? (PVB == 1 ? 1 : (PVB == 2 ? 2 : 3)) : PVB;  // stored value planes
   constexpr int NG = 4;                                // min/max groups of 32 channels
@@ -305,7 +315,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
     lim_min = n_c - hide_c;
   }
 
-  const size_t rec = (size_t)KP * (kD / 8);
+  // key record: full planes of 16 bytes; with HALF the last index plane has 8
+  const size_t rec = (size_t)KP * (kD / 8) - (HALF ? kD / 16 : 0);
   const uint8_t* kp = a.k_planes + (size_t)sh * a.capacity * rec;
   const size_t sidx0 = (size_t)sh * a.capacity;
   const uint32_t* vp = a.v_planes + (size_t)sh * (a.capacity >> 5) * VB * kD;
@@ -332,6 +343,17 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
   // per-lane byte offset, so the loads take the scalar-base form and no
   // 64-bit per-lane pointers stay live across the loop.
   const uint32_t k_lane = n * (uint32_t)rec + 4 * g;  // word g of token n's plane records
+  // byte offset of stored plane sp inside a record, for lane group g: full
+  // planes at 16 sp + 4g; the half plane's 16-bit chunk g (its coordinates
+  // 32g..32g+15) at 16 (KB - 1) + 2g; the QJL plane 8 bytes earlier than a
+  // full-plane record would put it
+  auto key_off = [&](int sp) -> int {
+    if (HALF && sp == KB - 1) return (KB - 1) * (kD / 8) - 2 * g;  // k_lane adds 4g
+    if (HALF && sp == KP - 1) return sp * (kD / 8) - kD / 16;
+    return sp * (kD / 8);
+  };
+  auto key_word = [&](const uint8_t* p) -> uint32_t { return *reinterpret_cast<const uint32_t*>(p); };
+  auto key_half_word = [&](const uint8_t* p) -> uint32_t { return *reinterpret_cast<const uint16_t*>(p); };
   const uint32_t s_lane = lane * (uint32_t)ssz;       // token `lane`'s scalar
   const uint32_t m_lane = VMSE ? s_lane : lane * (uint32_t)(NG * 4);
   const uint32_t v_lane = lane * 16u;                 // four value words per lane
@@ -353,7 +375,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
       for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
         for (int sp = 0; sp < KP; ++sp)
-          pX[ct][sp] = *reinterpret_cast<const uint32_t*>(xk + k_lane + 16 * ct * rec + sp * (kD / 8));
+          pX[ct][sp] = (HALF && sp == KB - 1) ? key_half_word(xk + k_lane + 16 * ct * rec + key_off(sp))
+                                               : key_word(xk + k_lane + 16 * ct * rec + key_off(sp));
     } else if (rem_c == 64 && !keys) {
       pNrm = scalar_at(xn, s_lane);
       if (QJL) pGam = scalar_at(xg, s_lane);
@@ -376,7 +399,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
       for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
         for (int sp = 0; sp < KP; ++sp)
-          pX[ct][sp] = *reinterpret_cast<const uint32_t*>(xk + k_lane + 16 * ct * rec + sp * (kD / 8));
+          pX[ct][sp] = (HALF && sp == KB - 1) ? key_half_word(xk + k_lane + 16 * ct * rec + key_off(sp))
+                                               : key_word(xk + k_lane + 16 * ct * rec + key_off(sp));
     } else {
       const bool valid = lane < rem_c;
       if (rest) {
@@ -399,7 +423,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
           const bool v2 = 16 * ct + n < rem_c;
 #pragma unroll
           for (int sp = 0; sp < KP; ++sp)
-            pX[ct][sp] = v2 ? *reinterpret_cast<const uint32_t*>(xk + k_lane + 16 * ct * rec + sp * (kD / 8)) : 0u;
+            pX[ct][sp] = !v2 ? 0u
+                         : (HALF && sp == KB - 1) ? key_half_word(xk + k_lane + 16 * ct * rec + key_off(sp))
+                                                  : key_word(xk + k_lane + 16 * ct * rec + key_off(sp));
         }
       }
     }
@@ -724,10 +750,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
   }
 }
 
-template <int PM, bool QJL, bool VMSE, int PVB, int NHT>
+template <int PM, bool QJL, bool VMSE, int PVB, int NHT, bool HALF = false>
 hipError_t launch_scan_mfma(const DecodeArgs& a, hipStream_t st, TimedLaunch tl) {
   if (tl.begin) (void)hipEventRecord(tl.begin, st);
-  hipLaunchKernelGGL((scan_mfma_kernel<PM, QJL, VMSE, PVB, NHT>), dim3(a.splits, a.batch * a.h_kv),
+  hipLaunchKernelGGL((scan_mfma_kernel<PM, QJL, VMSE, PVB, NHT, HALF>), dim3(a.splits, a.batch * a.h_kv),
                      dim3(kScanThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (tl.end) (void)hipEventRecord(tl.end, st);
@@ -738,6 +764,13 @@ template <int NHT>
 hipError_t dispatch_mfma(const DecodeArgs& a, int kb, int qjl, int vmse, int vb, hipStream_t st,
                          TimedLaunch tl) {
   if (!qjl) return hipErrorNotSupported;
+  if (a.key_half) {  // kb counts the half plane: 1 + 1/2 or 2 + 1/2 MSE bits
+    if (kb == 2 && !vmse && vb == 2) return launch_scan_mfma<2, true, false, 2, NHT, true>(a, st, tl);
+    if (kb == 3 && !vmse && vb == 2) return launch_scan_mfma<4, true, false, 2, NHT, true>(a, st, tl);
+    if (kb == 2 && vmse && vb == 3) return launch_scan_mfma<2, true, true, 4, NHT, true>(a, st, tl);
+    if (kb == 3 && vmse && vb == 3) return launch_scan_mfma<4, true, true, 4, NHT, true>(a, st, tl);
+    return hipErrorNotSupported;
+  }
   if (kb == 2 && !vmse && vb == 2) return launch_scan_mfma<2, true, false, 2, NHT>(a, st, tl);
   if (kb == 3 && !vmse && vb == 2) return launch_scan_mfma<4, true, false, 2, NHT>(a, st, tl);
   if (kb == 2 && vmse && vb == 3) return launch_scan_mfma<2, true, true, 4, NHT>(a, st, tl);

@@ -132,11 +132,16 @@ __device__ __forceinline__ bool index_bit(const bool (&gt)[LV - 1], int p) {
 //   VALUE = false: TurboQuantProd keys (MSE_BITS-bit Lloyd-Max + QJL if QJL),
 //                  token-major key planes, |k| and |r|.
 //   VALUE = true : TurboQuant-MSE values, token-transposed value planes, |v|.
-template <bool IN_BF16, int MSE_BITS, bool QJL, bool VALUE>
+//   HALF         : keys of fractional width MSE_BITS + 1/2: the coordinates of
+//                  the even row tiles (i mod 32 < 16) use the (MSE_BITS + 1)-bit
+//                  table, and their extra bit goes to a half plane.
+template <bool IN_BF16, int MSE_BITS, bool QJL, bool VALUE, bool HALF = false>
 __global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
+  static_assert(!(HALF && VALUE), "the half-bit layout is a key layout");
   constexpr int NMAT = QJL ? 4 : 2;
-  constexpr int NP = MSE_BITS + (QJL ? 1 : 0);  // bit planes written per token
+  constexpr int NP = MSE_BITS + (HALF ? 1 : 0) + (QJL ? 1 : 0);  // bit planes written per token
   constexpr int LV = 1 << MSE_BITS;
+  constexpr int LVH = HALF ? 2 * LV : LV;  // levels of the half-bit coordinates
   __shared__ __attribute__((aligned(16))) uint16_t lds[NMAT][kD][kD];
 
   // Stage Pi_hi, Pi_lo (and S'_hi, S'_lo) once per work-group.
@@ -148,11 +153,15 @@ __global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
   }
   __syncthreads();
 
-  float cent[LV], thr[LV - 1];
+  float cent[LV], thr[LV - 1], cent_hi[LVH], thr_hi[LVH - 1];
 #pragma unroll
   for (int k = 0; k < LV; ++k) cent[k] = VALUE ? a.v_cent[k] : a.k_cent[k];
 #pragma unroll
   for (int k = 0; k < LV - 1; ++k) thr[k] = VALUE ? a.v_thr[k] : a.k_thr[k];
+#pragma unroll
+  for (int k = 0; k < LVH; ++k) cent_hi[k] = HALF ? a.k_cent_hi[k] : cent[k < LV ? k : 0];
+#pragma unroll
+  for (int k = 0; k < LVH - 1; ++k) thr_hi[k] = HALF ? a.k_thr_hi[k] : thr[k < LV - 1 ? k : 0];
   const int lane = threadIdx.x & 63;
   // wave index as a scalar: tile indices, and the per-sequence lookups they
   // drive, stay in scalar registers
@@ -279,32 +288,50 @@ __global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
     };
     auto epilogue = [&](auto RT, const floatx4 (&acc)[2]) __attribute__((always_inline)) {
       constexpr int rt = decltype(RT)::value;
+      // half-bit layout: the even row tiles (coordinates i mod 32 < 16) use
+      // the table with one more bit
+      constexpr bool HI = HALF && (rt % 2 == 0);
+      constexpr int LVR = HI ? LVH : LV;
+      constexpr int MBR = HI ? MSE_BITS + 1 : MSE_BITS;
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         float res[4];
-        bool bits[4][MSE_BITS];
+        bool bits[4][MSE_BITS + 1];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const float y = acc[ct][rr] * inv[ct];
-          bool gt[LV - 1];
+          bool gt[LVR - 1];
           // centroids pass through an empty asm: opaque scalars, so the select
           // chain is not folded into a per-lane table lookup in memory
-          float c = cent[0];
-          asm("" : "+s"(c));
+          float c;
+          if constexpr (HI) {
+            c = cent_hi[0];
+            asm("" : "+s"(c));
 #pragma unroll
-          for (int k = 0; k < LV - 1; ++k) {
-            float ck = cent[k + 1];
-            asm("" : "+s"(ck));
-            gt[k] = y > thr[k];
-            c = gt[k] ? ck : c;
+            for (int k = 0; k < LVR - 1; ++k) {
+              float ck = cent_hi[k + 1];
+              asm("" : "+s"(ck));
+              gt[k] = y > thr_hi[k];
+              c = gt[k] ? ck : c;
+            }
+          } else {
+            c = cent[0];
+            asm("" : "+s"(c));
+#pragma unroll
+            for (int k = 0; k < LVR - 1; ++k) {
+              float ck = cent[k + 1];
+              asm("" : "+s"(ck));
+              gt[k] = y > thr[k];
+              c = gt[k] ? ck : c;
+            }
           }
 #pragma unroll
-          for (int p = 0; p < MSE_BITS; ++p) bits[rr][p] = index_bit<LV>(gt, p);
+          for (int p = 0; p < MBR; ++p) bits[rr][p] = index_bit<LVR>(gt, p);
           res[rr] = y - c;
           if (!VALUE) {
             const int j = (rt & 1) * 4 + rr;
 #pragma unroll
-            for (int p = 0; p < MSE_BITS; ++p) {
+            for (int p = 0; p < MBR; ++p) {
               lw[p][ct][rt >> 1] |= bits[rr][p] ? (1u << j) : 0u;
               // fold the bit in now: a lane mask kept for later would hold two SGPRs
               asm volatile("" : "+v"(lw[p][ct][rt >> 1]));
@@ -420,7 +447,9 @@ __global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
     // ---- plane words: spread the lane-local bits to coordinate positions
     // 4g + j (j < 4) and 16 + 4g + j - 4, then gather so that lane group g ends
     // with the word of coordinates 32g..32g+31
-    const size_t rec = (size_t)NP * (kD / 8);
+    // record: full planes at 16p, the half plane (16 coordinates per lane
+    // group) at 16 MSE_BITS, the QJL plane after it
+    constexpr size_t rec = (size_t)(MSE_BITS + (QJL ? 1 : 0)) * (kD / 8) + (HALF ? kD / 16 : 0);
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
 #pragma unroll
@@ -435,8 +464,14 @@ __global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
         // then rows g and g^1: row g ends with word g
         const auto sf = __builtin_amdgcn_permlane16_swap(ka, kb, false, false);
         const uint32_t fin = sf[0] | sf[1];
-        if (valid[ct])
-          *reinterpret_cast<uint32_t*>(a.k_planes + (slot * a.capacity + dpos[ct]) * rec + p * (kD / 8) + 4 * g) = fin;
+        uint8_t* recp = a.k_planes + (slot * a.capacity + dpos[ct]) * rec;
+        if (valid[ct]) {
+          if (HALF && p == MSE_BITS)  // coordinates 32g..32g+15: the low half of the word
+            *reinterpret_cast<uint16_t*>(recp + MSE_BITS * (kD / 8) + 2 * g) = (uint16_t)fin;
+          else
+            *reinterpret_cast<uint32_t*>(recp + (p < MSE_BITS ? p * (kD / 8) : MSE_BITS * (kD / 8) + (HALF ? kD / 16 : 0)) +
+                                         4 * g) = fin;
+        }
       }
     }
 #pragma unroll
@@ -576,13 +611,13 @@ int encode_grid(int tiles, int waves_per_block) {
   return want < 1 ? 1 : want;
 }
 
-template <bool BF16, int MB, bool QJL, bool VALUE>
+template <bool BF16, int MB, bool QJL, bool VALUE, bool HALF = false>
 hipError_t launch_rot(const EncodeArgs& a, hipStream_t st, TimedLaunch tl) {
   int grid = encode_grid(a.num_tiles, kEncThreads / 64);
   const int cus = device_cu_count();
   if (grid > cus) grid = cus;  // persistent: the LDS staging is paid once per work-group
   if (tl.begin) (void)hipEventRecord(tl.begin, st);
-  hipLaunchKernelGGL((encode_rot_kernel<BF16, MB, QJL, VALUE>), dim3(grid), dim3(kEncThreads), 0, st, a);
+  hipLaunchKernelGGL((encode_rot_kernel<BF16, MB, QJL, VALUE, HALF>), dim3(grid), dim3(kEncThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (tl.end) (void)hipEventRecord(tl.end, st);
   return e;
@@ -633,9 +668,17 @@ hipError_t launch_prepare_params(const float* pi, const float* s, uint16_t* deri
   return hipGetLastError();
 }
 
-hipError_t launch_encode_keys(const EncodeArgs& a, int in_bf16, int mse_bits, int qjl,
+hipError_t launch_encode_keys(const EncodeArgs& a, int in_bf16, int mse_bits, int qjl, int half,
                               hipStream_t stream, TimedLaunch tl) {
   if (a.num_tiles == 0) return hipSuccess;
+  if (half) {  // fractional widths 1.5 and 2.5 MSE bits, QJL keys only
+    if (!qjl || mse_bits < 1 || mse_bits > 2) return hipErrorInvalidValue;
+    if (in_bf16)
+      return mse_bits == 1 ? launch_rot<true, 1, true, false, true>(a, stream, tl)
+                           : launch_rot<true, 2, true, false, true>(a, stream, tl);
+    return mse_bits == 1 ? launch_rot<false, 1, true, false, true>(a, stream, tl)
+                         : launch_rot<false, 2, true, false, true>(a, stream, tl);
+  }
   if (in_bf16)
     return qjl ? dispatch_rot_bits<true, true, false>(a, mse_bits, stream, tl)
                : dispatch_rot_bits<true, false, false>(a, mse_bits, stream, tl);

@@ -29,6 +29,12 @@ constexpr size_t kOffPiT = kOffSpLo + kD * kD * 2;
 constexpr size_t kOffST = kOffPiT + kD * kD * 4;
 constexpr size_t kDerivedBytes = kOffST + kD * kD * 4;
 
+// Bytes of one token's key record: full planes, the half plane of the
+// fractional layout (coordinates i with i mod 32 < 16), the QJL plane.
+inline size_t key_record_bytes(int mse_bits, int qjl, int half) {
+  return (size_t)(mse_bits + qjl) * (kD / 8) + (size_t)half * (kD / 16);
+}
+
 // Column of S' that the encode kernel's second GEMM meets at contraction index
 // k.  The first GEMM leaves, in lane group g of a 16x16x32 MFMA, the rotated
 // coordinates 16*rt + 4*g + r (row tile rt, accumulator r); the kernel feeds
@@ -65,6 +71,8 @@ struct EncodeArgs {
   float k_thr[15];
   float v_cent[16];
   float v_thr[15];
+  float k_cent_hi[16];    // key_half: table of the half-bit coordinates
+  float k_thr_hi[15];
   SeqValues pos;          // first destination position per sequence
   SeqValues tile_start;   // prefix count of tiles per sequence (tile_start.v[batch] = total)
 };
@@ -106,6 +114,9 @@ struct DecodeArgs {
   // with planes bit0, bit1, bit2, bit0^bit1^bit2 (see plane_expansion).
   float key_w[4];
   float key_cst;
+  float key_w_hi[4];      // key_half: expansion of the half-bit coordinates' table
+  float key_cst_hi;
+  int32_t key_half;
   float val_w[4];
   float val_cst;
   int8_t* qdig;           // workspace: query digit operands of the MFMA scan
@@ -155,7 +166,7 @@ struct TimedLaunch {
 // launch error.
 hipError_t launch_prepare_params(const float* pi, const float* s, uint16_t* derived,
                                  hipStream_t stream);
-hipError_t launch_encode_keys(const EncodeArgs& a, int in_bf16, int mse_bits, int qjl,
+hipError_t launch_encode_keys(const EncodeArgs& a, int in_bf16, int mse_bits, int qjl, int half,
                               hipStream_t stream, TimedLaunch t);
 hipError_t launch_encode_values_mse(const EncodeArgs& a, int in_bf16, int bits,
                                     hipStream_t stream, TimedLaunch t);

@@ -40,7 +40,7 @@ class _Layout(ctypes.Structure):
     _fields_ = [("head_dim", ctypes.c_int32), ("key_mse_bits", ctypes.c_int32),
                 ("key_qjl", ctypes.c_int32), ("value_kind", ctypes.c_int32),
                 ("value_bits", ctypes.c_int32), ("value_group", ctypes.c_int32),
-                ("scalar_dtype", ctypes.c_int32)]
+                ("scalar_dtype", ctypes.c_int32), ("key_half", ctypes.c_int32)]
 
 
 class _Params(ctypes.Structure):
@@ -48,7 +48,9 @@ class _Params(ctypes.Structure):
                 ("k_centroids", ctypes.c_float * MAX_LEVELS),
                 ("k_thresholds", ctypes.c_float * (MAX_LEVELS - 1)),
                 ("v_centroids", ctypes.c_float * MAX_LEVELS),
-                ("v_thresholds", ctypes.c_float * (MAX_LEVELS - 1))]
+                ("v_thresholds", ctypes.c_float * (MAX_LEVELS - 1)),
+                ("k_centroids_hi", ctypes.c_float * MAX_LEVELS),
+                ("k_thresholds_hi", ctypes.c_float * (MAX_LEVELS - 1))]
 
 
 class _Cache(ctypes.Structure):
@@ -117,10 +119,11 @@ class Layout:
     value_bits: int = 2
     value_group: int = 32
     scalar_dtype: int = TQ_F32
+    key_half: int = 0  # 1: half of the rotated coordinates get key_mse_bits + 1 bits
 
     def c(self) -> _Layout:
         return _Layout(self.head_dim, self.key_mse_bits, self.key_qjl, self.value_kind,
-                       self.value_bits, self.value_group, self.scalar_dtype)
+                       self.value_bits, self.value_group, self.scalar_dtype, self.key_half)
 
     @property
     def key_planes(self) -> int:
@@ -181,6 +184,10 @@ class Params:
         self.derived = torch.empty(nbytes, dtype=torch.uint8, device=device)
         _check(lib().tq_prepare_params(d, _ptr(self.pi), _ptr(self.s), _ptr(self.derived), nbytes, _stream(stream)))
         self.k_centroids, self.k_thresholds = k_codebook or make_codebook(d, layout.key_mse_bits)
+        if layout.key_half:
+            self.k_centroids_hi, self.k_thresholds_hi = make_codebook(d, layout.key_mse_bits + 1)
+        else:
+            self.k_centroids_hi = self.k_thresholds_hi = np.zeros(0, dtype=np.float32)
         if layout.value_kind == TQ_V_MSE:
             self.v_centroids, self.v_thresholds = v_codebook or make_codebook(d, layout.value_bits)
         else:
@@ -197,6 +204,10 @@ class Params:
             p.v_centroids[i] = float(x)
         for i, x in enumerate(self.v_thresholds):
             p.v_thresholds[i] = float(x)
+        for i, x in enumerate(self.k_centroids_hi):
+            p.k_centroids_hi[i] = float(x)
+        for i, x in enumerate(self.k_thresholds_hi):
+            p.k_thresholds_hi[i] = float(x)
         return p
 
 
@@ -210,7 +221,8 @@ class Cache:
         self.layout, self.batch, self.num_kv_heads, self.capacity = layout, batch, num_kv_heads, capacity
         sd = layout.scalar_torch_dtype
         shp = (batch, num_kv_heads, capacity)
-        self.k_planes = torch.zeros(*shp, layout.key_planes * d // 8, dtype=torch.uint8, device=device)
+        self.k_planes = torch.zeros(*shp, layout.key_planes * d // 8 + layout.key_half * d // 16,
+                                    dtype=torch.uint8, device=device)
         self.k_norm = torch.zeros(shp, dtype=sd, device=device)
         self.k_rnorm = torch.zeros(shp, dtype=sd, device=device) if layout.key_qjl else None
         self.v_planes = torch.zeros(batch, num_kv_heads, capacity // 32, layout.value_bits, d,

@@ -53,6 +53,7 @@ class Workload:
     d: int = 128
     key_qjl: int = 1
     value_group: int = 32
+    key_half: int = 0  # 1: half of the rotated coordinates get key_mse_bits + 1 bits
 
     @property
     def group(self) -> int:

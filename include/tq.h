@@ -34,10 +34,14 @@
  *    describes the most recent failure of the calling thread.
  *  - Layout of the compressed cache, per (sequence b, KV head h) slot of
  *    `capacity` token positions (capacity a multiple of 32):
- *      k_planes  uint8 [batch][h_kv][capacity][(key_mse_bits+key_qjl)*d/8]
- *                plane p < key_mse_bits holds bit p of each coordinate's
- *                Lloyd-Max index, plane key_mse_bits the QJL sign bits
- *                (1 = non-negative); coordinate i is bit i%8 of byte i/8.
+ *      k_planes  uint8 [batch][h_kv][capacity][record], record =
+ *                (key_mse_bits + key_qjl)*d/8 + key_half*d/16 bytes: plane
+ *                p < key_mse_bits holds bit p of each coordinate's Lloyd-Max
+ *                index (coordinate i is bit i%8 of byte i/8); with key_half
+ *                a half plane of d/16 bytes follows, bit key_mse_bits of the
+ *                index of coordinate i (i mod 32 < 16) at bit position
+ *                16*(i/32) + i%32; then the QJL sign bits (1 = non-negative)
+ *                in the full-plane order.
  *      k_norm    [batch][h_kv][capacity] scalar_dtype   |k|
  *      k_rnorm   [batch][h_kv][capacity] scalar_dtype   |r| (QJL keys only)
  *      v_planes  uint32 [batch][h_kv][capacity/32][value_bits][d].  Bit
@@ -89,6 +93,13 @@ typedef struct tq_layout {
   int32_t value_bits;   /* 1..4                                                */
   int32_t value_group;  /* min/max group of consecutive channels; divides d    */
   int32_t scalar_dtype; /* TQ_F32 | TQ_F16: storage of |k|, |r| and |v|        */
+  int32_t key_half;     /* 0, or 1: fractional key width key_mse_bits + 1/2;
+                           the rotated coordinates i with i mod 32 < 16 use a
+                           (key_mse_bits + 1)-bit Lloyd-Max code (page
+                           "TurboQuant — ...", sections "Ý tưởng cốt lõi" and
+                           "Ý nghĩa thực tế": 2.5 and 3.5 bits per channel).
+                           Requires key_qjl = 1 and key_mse_bits 1 or 2, so
+                           TurboQuantProd(2.5) and TurboQuantProd(3.5).       */
 } tq_layout;
 
 /* Per-layer parameters.  pi, s and derived are device pointers; the codebook
@@ -101,6 +112,9 @@ typedef struct tq_params {
   float k_thresholds[TQ_MAX_LEVELS - 1]; /* 2^key_mse_bits - 1 decision bounds */
   float v_centroids[TQ_MAX_LEVELS];      /* MSE values: 2^value_bits levels    */
   float v_thresholds[TQ_MAX_LEVELS - 1];
+  float k_centroids_hi[TQ_MAX_LEVELS];   /* key_half: the (key_mse_bits + 1)-bit
+                                            table of the half-bit coordinates */
+  float k_thresholds_hi[TQ_MAX_LEVELS - 1];
 } tq_params;
 
 /* Compressed cache: device planes as described above. */

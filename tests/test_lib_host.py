@@ -55,13 +55,15 @@ def _olay(l: tq.Layout) -> OLayout:
     return OLayout(d=l.head_dim, key_mse_bits=l.key_mse_bits, key_qjl=l.key_qjl,
                    value_kind="minmax" if l.value_kind == tq.TQ_V_MINMAX else "mse",
                    value_bits=l.value_bits, value_group=l.value_group,
-                   scalar_dtype="f32" if l.scalar_dtype == tq.TQ_F32 else "f16")
+                   scalar_dtype="f32" if l.scalar_dtype == tq.TQ_F32 else "f16", key_half=l.key_half)
 
 
 @pytest.mark.parametrize("kw", [{}, {"scalar_dtype": tq.TQ_F16},
                                 {"value_kind": tq.TQ_V_MSE, "value_bits": 3, "scalar_dtype": tq.TQ_F16},
                                 {"key_mse_bits": 3, "value_kind": tq.TQ_V_MSE, "value_bits": 3},
-                                {"key_qjl": 0, "value_bits": 4, "value_group": 16}])
+                                {"key_qjl": 0, "value_bits": 4, "value_group": 16},
+                                {"key_half": 1}, {"key_mse_bits": 1, "key_half": 1, "scalar_dtype": tq.TQ_F16},
+                                {"key_half": 1, "value_kind": tq.TQ_V_MSE, "value_bits": 3}])
 def test_memory_bytes_matches_oracle(kw):
     l = _lay(**kw)
     ol = _olay(l)
@@ -76,7 +78,9 @@ def test_bad_layouts_are_rejected():
                      ({"key_mse_bits": 0}, tq.TQ_ERR_INVALID), ({"key_mse_bits": 5}, tq.TQ_ERR_INVALID),
                      ({"value_bits": 0}, tq.TQ_ERR_INVALID), ({"value_group": 48}, tq.TQ_ERR_INVALID),
                      ({"value_group": 128}, tq.TQ_ERR_UNSUPPORTED), ({"scalar_dtype": 7}, tq.TQ_ERR_INVALID),
-                     ({"value_kind": 3}, tq.TQ_ERR_INVALID), ({"key_qjl": 2}, tq.TQ_ERR_INVALID)]:
+                     ({"value_kind": 3}, tq.TQ_ERR_INVALID), ({"key_qjl": 2}, tq.TQ_ERR_INVALID),
+                     ({"key_half": 2}, tq.TQ_ERR_INVALID), ({"key_half": 1, "key_qjl": 0}, tq.TQ_ERR_UNSUPPORTED),
+                     ({"key_half": 1, "key_mse_bits": 3}, tq.TQ_ERR_UNSUPPORTED)]:
         l = _lay(**kw)
         lay = l.c()
         r = tq.lib().tq_memory_bytes(ctypes.byref(lay), 1, 1, 1, 0, tq.TQ_BYTES_DATA)

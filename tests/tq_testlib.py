@@ -26,24 +26,30 @@ def layout_of(w: wl.Workload) -> tq.Layout:
     return tq.Layout(head_dim=w.d, key_mse_bits=w.key_mse_bits, key_qjl=w.key_qjl,
                      value_kind=tq.TQ_V_MINMAX if w.value_kind == "minmax" else tq.TQ_V_MSE,
                      value_bits=w.value_bits, value_group=w.value_group,
-                     scalar_dtype=tq.TQ_F32 if w.scalar_dtype == "f32" else tq.TQ_F16)
+                     scalar_dtype=tq.TQ_F32 if w.scalar_dtype == "f32" else tq.TQ_F16, key_half=w.key_half)
 
 
 def olayout_of(w: wl.Workload) -> oracle.Layout:
     return oracle.Layout(d=w.d, key_mse_bits=w.key_mse_bits, key_qjl=w.key_qjl,
                          value_kind=w.value_kind, value_bits=w.value_bits,
-                         value_group=w.value_group, scalar_dtype=w.scalar_dtype)
+                         value_group=w.value_group, scalar_dtype=w.scalar_dtype, key_half=w.key_half)
 
 
 @dataclasses.dataclass
 class OracleBooks:
     k: oracle.Codebook
     v: oracle.Codebook | None
+    k_hi: oracle.Codebook | None = None  # half-bit keys: the (key_mse_bits + 1)-bit table
 
 
 def books(w: wl.Workload) -> OracleBooks:
     return OracleBooks(oracle.lloyd_max(w.d, w.key_mse_bits),
-                       oracle.lloyd_max(w.d, w.value_bits) if w.value_kind == "mse" else None)
+                       oracle.lloyd_max(w.d, w.value_bits) if w.value_kind == "mse" else None,
+                       oracle.lloyd_max(w.d, w.key_mse_bits + 1) if w.key_half else None)
+
+
+def _hi(bk: OracleBooks):
+    return (bk.k_hi.centroids, bk.k_hi.thresholds) if bk.k_hi is not None else (None, None)
 
 
 @dataclasses.dataclass
@@ -54,7 +60,9 @@ class SlotCode:
 
 
 def encode_slot(w: wl.Workload, bk: OracleBooks, pi, s, k: np.ndarray, v: np.ndarray) -> SlotCode:
-    key = oracle.encode_keys(k, pi, s, bk.k.centroids, bk.k.thresholds, w.scalar_dtype, qjl=bool(w.key_qjl))
+    ch, th = _hi(bk)
+    key = oracle.encode_keys(k, pi, s, bk.k.centroids, bk.k.thresholds, w.scalar_dtype, qjl=bool(w.key_qjl),
+                             centroids_hi=ch, thresholds_hi=th)
     if w.value_kind == "minmax":
         val = oracle.encode_values_minmax(v, w.value_bits, w.value_group)
     else:
@@ -63,7 +71,7 @@ def encode_slot(w: wl.Workload, bk: OracleBooks, pi, s, k: np.ndarray, v: np.nda
 
 
 def dequant_slot(w: wl.Workload, bk: OracleBooks, pi, s, sc: SlotCode):
-    kd = oracle.dequantize_keys(sc.key, pi, s, bk.k.centroids, qjl=bool(w.key_qjl))
+    kd = oracle.dequantize_keys(sc.key, pi, s, bk.k.centroids, qjl=bool(w.key_qjl), centroids_hi=_hi(bk)[0])
     if w.value_kind == "minmax":
         vd = oracle.dequantize_values_minmax(sc.val, w.value_group)
     else:
@@ -81,7 +89,7 @@ def upload_slot(cache: tq.Cache, w: wl.Workload, b: int, h: int, sc: SlotCode, s
     assert start % 32 == 0
     t = sc.key.idx.shape[0]
     dev = cache.k_planes.device
-    kp = oracle.pack_key_planes(sc.key.idx, sc.key.qjl if w.key_qjl else None, w.key_mse_bits)
+    kp = oracle.pack_key_planes(sc.key.idx, sc.key.qjl if w.key_qjl else None, w.key_mse_bits, half=bool(w.key_half))
     cache.k_planes[b, h, start:start + t] = torch.from_numpy(kp).to(dev)
     sd = np.float32 if w.scalar_dtype == "f32" else np.float16
     cache.k_norm[b, h, start:start + t] = torch.from_numpy(sc.key.norm.astype(sd)).to(dev)
@@ -106,14 +114,20 @@ def max_rel_err(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
     return np.where(den > 0, num / np.where(den > 0, den, 1), num)
 
 
-def read_key_planes(planes: np.ndarray, d: int, mse_bits: int, qjl: bool):
-    """Read codes back from key plane bytes [T, P * d/8] (bit i%8 of byte i/8 of
-    plane p is bit p of coordinate i's index; the last plane holds QJL bits)."""
-    bits = np.unpackbits(np.ascontiguousarray(planes, dtype=np.uint8), axis=1, bitorder="little")
-    p_k = mse_bits + (1 if qjl else 0)
-    bits = bits[:, : p_k * d].reshape(-1, p_k, d).astype(np.int64)
-    idx = sum(bits[:, p, :] << p for p in range(mse_bits))
-    return idx, (bits[:, mse_bits, :].astype(np.uint8) if qjl else None)
+def read_key_planes(planes: np.ndarray, d: int, mse_bits: int, qjl: bool, half: bool = False):
+    """Read codes back from key plane bytes (bit i%8 of byte i/8 of plane p is
+    bit p of coordinate i's index; with the half-bit layout a d/16-byte plane
+    follows holding bit mse_bits of coordinate i (i mod 32 < 16) at bit
+    16*(i//32) + i%32; the last plane holds QJL bits)."""
+    bits = np.unpackbits(np.ascontiguousarray(planes, dtype=np.uint8), axis=1, bitorder="little").astype(np.int64)
+    idx = sum(bits[:, p * d:(p + 1) * d] << p for p in range(mse_bits))
+    off = mse_bits * d
+    if half:
+        for i in range(d):
+            if i % 32 < 16:
+                idx[:, i] |= bits[:, off + 16 * (i // 32) + i % 32] << mse_bits
+        off += d // 2
+    return idx, (bits[:, off:off + d].astype(np.uint8) if qjl else None)
 
 
 def read_value_planes(words: np.ndarray, n_tokens: int, w: wl.Workload) -> np.ndarray:
@@ -145,9 +159,12 @@ def key_plane_mismatches(w: wl.Workload, bk: OracleBooks, gpu_planes: np.ndarray
     the oracle's rotated coordinate lies within WINDOW of a decision boundary; a
     mismatching QJL bit when |z_i| < WINDOW or the token has an excused MSE flip."""
     t, d = ref.idx.shape
-    idx_g, qjl_g = read_key_planes(gpu_planes, d, w.key_mse_bits, bool(w.key_qjl))
+    idx_g, qjl_g = read_key_planes(gpu_planes, d, w.key_mse_bits, bool(w.key_qjl), bool(w.key_half))
     mse_bad = idx_g != ref.idx
     near = np.min(np.abs(ref.y[..., None] - bk.k.thresholds[None, None, :]), axis=-1) < WINDOW
+    if w.key_half:  # the half-bit coordinates decide against the larger table
+        near_hi = np.min(np.abs(ref.y[..., None] - bk.k_hi.thresholds[None, None, :]), axis=-1) < WINDOW
+        near = np.where(oracle.half_bit_coordinates(d)[None, :], near_hi, near)
     unexcused = int(np.sum(mse_bad & ~near))
     excused_mse = int(np.sum(mse_bad & near))
     excused_qjl = 0
@@ -212,7 +229,7 @@ def check_encode_slot(w, bk, cache, b, h, ref, start, n, tag):
 
 
 def _flip_mask(w, bk, kp, ref):
-    idx_g, _ = read_key_planes(kp, w.d, w.key_mse_bits, bool(w.key_qjl))
+    idx_g, _ = read_key_planes(kp, w.d, w.key_mse_bits, bool(w.key_qjl), bool(w.key_half))
     return idx_g != ref.key.idx
 
 
@@ -220,7 +237,7 @@ def slot_from_cache(w: wl.Workload, cache: tq.Cache, b: int, h: int, n: int) -> 
     """The codes of device cache slot (b, h), positions 0..n-1, read back into
     the oracle's code records (so the oracle can decode a GPU-encoded cache)."""
     kp = cache.k_planes[b, h, :n].cpu().numpy()
-    idx, qjl = read_key_planes(kp, w.d, w.key_mse_bits, bool(w.key_qjl))
+    idx, qjl = read_key_planes(kp, w.d, w.key_mse_bits, bool(w.key_qjl), bool(w.key_half))
     norm = cache.k_norm[b, h, :n].float().cpu().double().numpy()
     rnorm = cache.k_rnorm[b, h, :n].float().cpu().double().numpy() if w.key_qjl else None
     key = oracle.KeyCode(idx=idx, qjl=qjl, norm=norm, rnorm=rnorm, y=None, z=None)
