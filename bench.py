@@ -164,6 +164,8 @@ def cpu_baseline(w, seconds_budget: float = 25.0):
 
     pi, s = wl.params(w)
     cb = oracle.lloyd_max(w.d, w.key_mse_bits)
+    hi = oracle.lloyd_max(w.d, w.key_mse_bits + 1) if w.key_half else None
+    khi = {"centroids_hi": hi.centroids} if hi else {}
     vcb = oracle.lloyd_max(w.d, w.value_bits) if w.value_kind == "mse" else None
     n = min(w.n_tokens, 32768)
     t_enc = t_dec = 0.0
@@ -177,13 +179,14 @@ def cpu_baseline(w, seconds_budget: float = 25.0):
             k = wl.slot_tokens(w, "k", b, h, n).double().numpy()
             v = wl.slot_tokens(w, "v", b, h, n).double().numpy()
             t0 = time.perf_counter()
-            kc = oracle.encode_keys(k, pi, s, cb.centroids, cb.thresholds, w.scalar_dtype)
+            kc = oracle.encode_keys(k, pi, s, cb.centroids, cb.thresholds, w.scalar_dtype,
+                                    **({"centroids_hi": hi.centroids, "thresholds_hi": hi.thresholds} if hi else {}))
             if vcb is None:
                 vc = oracle.encode_values_minmax(v, w.value_bits, w.value_group)
             else:
                 vc = oracle.encode_values_mse(v, pi, vcb.centroids, vcb.thresholds, w.scalar_dtype)
             t1 = time.perf_counter()
-            kd[0].append(oracle.dequantize_keys(kc, pi, s, cb.centroids))
+            kd[0].append(oracle.dequantize_keys(kc, pi, s, cb.centroids, **khi))
             vd[0].append(oracle.dequantize_values_minmax(vc, w.value_group) if vcb is None
                          else oracle.dequantize_values_mse(vc, pi, vcb.centroids))
             t_enc += t1 - t0
@@ -194,7 +197,8 @@ def cpu_baseline(w, seconds_budget: float = 25.0):
         seqs += 1
     per_th = oracle.bytes_per_token_head(oracle.Layout(
         d=w.d, key_mse_bits=w.key_mse_bits, key_qjl=w.key_qjl, value_kind=w.value_kind,
-        value_bits=w.value_bits, value_group=w.value_group, scalar_dtype=w.scalar_dtype))["total"]
+        value_bits=w.value_bits, value_group=w.value_group, scalar_dtype=w.scalar_dtype,
+        key_half=w.key_half))["total"]
     nbytes = per_th * w.h_kv * n * seqs
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {
@@ -230,7 +234,7 @@ def main():
         pmc_summary(args)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               f"(the path shards by KV head or sequence with no communication, but no multi-GPU run is made).",
               file=sys.stderr)
         sys.exit(2)
@@ -252,7 +256,7 @@ def main():
     lay = tq.Layout(head_dim=w.d, key_mse_bits=w.key_mse_bits, key_qjl=w.key_qjl,
                     value_kind=tq.TQ_V_MINMAX if w.value_kind == "minmax" else tq.TQ_V_MSE,
                     value_bits=w.value_bits, value_group=w.value_group,
-                    scalar_dtype=tq.TQ_F32 if w.scalar_dtype == "f32" else tq.TQ_F16)
+                    scalar_dtype=tq.TQ_F32 if w.scalar_dtype == "f32" else tq.TQ_F16, key_half=w.key_half)
     print(f"[bench] workload {w.name}: generating inputs", file=sys.stderr, flush=True)
     pi, s = wl.params(w)
     prm = tq.Params(lay, pi, s, device=dev)
@@ -376,7 +380,7 @@ def main():
                    "n_compressed": w.n_tokens, "ring_cap": w.ring_cap,
                    "ring_tokens_in_timed_steps": f"{nq}..{min(args.steps * nq, ring)}" if ring else "none",
                    "queries_per_step": nq,
-                   "key_bits": f"{w.key_mse_bits}-bit Lloyd-Max + {w.key_qjl}-bit QJL",
+                   "key_bits": f"{w.key_mse_bits + 0.5 * w.key_half:g}-bit Lloyd-Max + {w.key_qjl}-bit QJL",
                    "value_code": f"{w.value_bits}-bit {w.value_kind}" + (f" g{w.value_group}" if w.value_kind == "minmax" else ""),
                    "scalars": w.scalar_dtype, "bytes_per_token_head": per_th, "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),

@@ -102,9 +102,15 @@ QWEN_SWEEP = [_qwen_layer(n) for n in (512, 1024, 2048, 4096, 8192, 16384)]
 QWEN_VARIANTS = [_qwen_layer(4096, key_mse_bits=3), _qwen_layer(4096, scalar_dtype="f32"),
                  _qwen_layer(4096, key_mse_bits=3, scalar_dtype="f32")]
 
+#: Fractional key widths: the batched 32K-token decode and the Qwen-shaped
+#: layer with 3.5-bit keys (2.5 MSE bits + QJL) and 2.5-bit keys (1.5 + QJL).
+FRACTIONAL = [WORKLOADS[3].replace(name="batched-b32-hkv8-n32768-k3.5bit", key_half=1),
+              WORKLOADS[3].replace(name="batched-b32-hkv8-n32768-k2.5bit", key_mse_bits=1, key_half=1),
+              _qwen_layer(4096).replace(name="qwen2.5-1.5b-layer-n4096-k3.5bit", key_half=1)]
+
 
 def by_name(name: str) -> Workload:
-    for w in WORKLOADS + QWEN_SWEEP + QWEN_VARIANTS:
+    for w in WORKLOADS + QWEN_SWEEP + QWEN_VARIANTS + FRACTIONAL:
         if w.name == name:
             return w
     raise KeyError(name)
