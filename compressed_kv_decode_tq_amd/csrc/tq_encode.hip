@@ -113,19 +113,6 @@ __device__ __forceinline__ float row_sum4(float x) {
   return __uint_as_float(u[0]) + __uint_as_float(u[1]);
 }
 
-// Bit p of the Lloyd-Max index from the threshold tests gt[k] = (y > t_k).
-// The tests are monotone (gt[k] implies gt[k-1]), so idx = sum_k gt[k] and
-// bit p of idx flips exactly at the tests k with k + 1 a multiple of 2^p:
-// bit p = XOR of gt[k] over k = 2^p - 1 (mod 2^p).
-template <int LV>
-__device__ __forceinline__ bool index_bit(const bool (&gt)[LV - 1], int p) {
-  bool x = false;
-#pragma unroll
-  for (int k = 0; k < LV - 1; ++k)
-    if (((k + 1) & ((1 << p) - 1)) == 0) x ^= gt[k];
-  return x;
-}
-
 // Rotation-based encode: each wave encodes one 32-token tile at a time (two
 // 16-token column tiles of the MFMA), eight waves of a work-group share the
 // bf16 split matrices staged in LDS.
@@ -293,51 +280,53 @@ __global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
       constexpr bool HI = HALF && (rt % 2 == 0);
       constexpr int LVR = HI ? LVH : LV;
       constexpr int MBR = HI ? MSE_BITS + 1 : MSE_BITS;
+      constexpr int NPOS = LVR / 2 - 1;  // positive thresholds of the symmetric table
+      const float* cen = HI ? cent_hi : cent;
+      const float* thp = HI ? thr_hi : thr;
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         float res[4];
-        bool bits[4][MSE_BITS + 1];
+        // sign words: bit p of the index is the inverted sign bit of t[rr][p]
+        uint32_t t[4][MSE_BITS + 1];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const float y = acc[ct][rr] * inv[ct];
-          bool gt[LVR - 1];
+          const uint32_t yb = __float_as_uint(y);
+          const float ay = fabsf(y);
           // centroids pass through an empty asm: opaque scalars, so the select
           // chain is not folded into a per-lane table lookup in memory
-          float c;
-          if constexpr (HI) {
-            c = cent_hi[0];
-            asm("" : "+s"(c));
+          float cm = cen[LVR / 2];
+          asm("" : "+s"(cm));
 #pragma unroll
-            for (int k = 0; k < LVR - 1; ++k) {
-              float ck = cent_hi[k + 1];
-              asm("" : "+s"(ck));
-              gt[k] = y > thr_hi[k];
-              c = gt[k] ? ck : c;
-            }
-          } else {
-            c = cent[0];
-            asm("" : "+s"(c));
+          for (int p = 0; p < MBR - 1; ++p) t[rr][p] = yb;
 #pragma unroll
-            for (int k = 0; k < LVR - 1; ++k) {
-              float ck = cent[k + 1];
-              asm("" : "+s"(ck));
-              gt[k] = y > thr[k];
-              c = gt[k] ? ck : c;
-            }
+          for (int k = 1; k <= NPOS; ++k) {
+            const float dk = ay - thp[LVR / 2 - 1 + k];
+            float ck = cen[LVR / 2 + k];
+            asm("" : "+s"(ck));
+            cm = (int)__float_as_uint(dk) >= 0 ? ck : cm;  // the same sign bit as the index bits
+#pragma unroll
+            for (int p = 0; p < MBR - 1; ++p)
+              if ((k & ((1 << p) - 1)) == 0) t[rr][p] ^= __float_as_uint(dk);
           }
-#pragma unroll
-          for (int p = 0; p < MBR; ++p) bits[rr][p] = index_bit<LVR>(gt, p);
-          res[rr] = y - c;
+          t[rr][MBR - 1] = yb;
+          res[rr] = y - __uint_as_float(__float_as_uint(cm) | (yb & 0x80000000u));
           if (!VALUE) {
-            const int j = (rt & 1) * 4 + rr;
 #pragma unroll
             for (int p = 0; p < MBR; ++p) {
-              lw[p][ct][rt >> 1] |= bits[rr][p] ? (1u << j) : 0u;
-              // fold the bit in now: a lane mask kept for later would hold two SGPRs
+              lw[p][ct][rt >> 1] = __builtin_amdgcn_alignbit(lw[p][ct][rt >> 1], t[rr][p], 31);
+              // fold the bit in now, so the sign words of a row tile are not all kept live
               asm volatile("" : "+v"(lw[p][ct][rt >> 1]));
             }
           }
         }
+        if (!VALUE && rt % 2 == 0) {
+          // elements 0..3 of the word move up by 12: after the bit reversal
+          // they sit 16 bits below elements 4..7
+#pragma unroll
+          for (int p = 0; p < MBR; ++p) lw[p][ct][rt >> 1] <<= 12;
+        }
+        if (HALF && !HI) lw[MSE_BITS][ct][rt >> 1] <<= 4;  // no half-plane bits in this tile
         if (QJL) {
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) gg[ct] = fmaf(res[rr], res[rr], gg[ct]);
@@ -358,7 +347,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
           for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
-              const uint64_t m = __ballot(bits[rr][p]);
+              const uint64_t m = __ballot((int)t[rr][p] >= 0);
 #pragma unroll
               for (int gq = 0; gq < 4; ++gq) {
                 const int ch = 16 * rt + 4 * gq + rr;
@@ -435,18 +424,23 @@ __global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr)
             lw[NP - 1][ct][rt >> 1] = __builtin_amdgcn_alignbit(lw[NP - 1][ct][rt >> 1], __float_as_uint(z[ct][rr]), 31);
+        if (rt % 2 == 0) {
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) lw[NP - 1][ct][rt >> 1] <<= 12;
+        }
       }
-      // bit j = (z_j >= 0): reverse the 8 sign bits and invert them (a z of
-      // -0.0 reads as negative; its oracle value lies inside the boundary window)
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) lw[NP - 1][ct][m] = (~__builtin_bitreverse32(lw[NP - 1][ct][m]) >> 24) & 0xffu;
     }
-
-    // ---- plane words: spread the lane-local bits to coordinate positions
-    // 4g + j (j < 4) and 16 + 4g + j - 4, then gather so that lane group g ends
-    // with the word of coordinates 32g..32g+31
+    // ---- plane words.  Every plane bit went in as a sign bit shifted in at
+    // the bottom, with a gap of 12 after element 3 of a word (element j =
+    // (rt&1)*4 + rr of word rt/2): bit reversal puts element j at bit 12 + j
+    // (j < 4) or 24 + j.  Inverted, bit j is 1 where the sign word was
+    // non-negative.  The Lloyd-Max index bits are the sign of y (top bit) and
+    // the parity of the magnitude tests against the positive thresholds XOR
+    // that sign (lower bits); each of them has an odd number of tests, hence
+    // the inversion.  Ties (|y| on a threshold, y = 0, z = -0.0) lie inside
+    // the boundary window of the oracle's values.  A shift then spreads the
+    // bits to coordinate positions 4g + j (j < 4) and 16 + 4g + j - 4, and the
+    // lane swaps gather the word of coordinates 32g..32g+31 into lane group g.
     // record: full planes at 16p, the half plane (16 coordinates per lane
     // group) at 16 MSE_BITS, the QJL plane after it
     constexpr size_t rec = (size_t)(MSE_BITS + (QJL ? 1 : 0)) * (kD / 8) + (HALF ? kD / 16 : 0);
@@ -456,7 +450,7 @@ __global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
       for (int ct = 0; ct < 2; ++ct) {
         uint32_t w[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) w[m] = ((lw[p][ct][m] & 0xfu) | ((lw[p][ct][m] & 0xf0u) << 12)) << (4 * g);
+        for (int m = 0; m < 4; ++m) w[m] = (~__builtin_bitreverse32(lw[p][ct][m]) >> (12 - 4 * g)) & (0x000f000fu << (4 * g));
         // lanes g and g^2 merge: rows 0,1 keep words 0,1 and rows 2,3 words 2,3
         const auto s02 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
         const auto s13 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
