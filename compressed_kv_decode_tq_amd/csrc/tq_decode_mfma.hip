@@ -244,7 +244,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
   constexpr int kStageNg = 64 * 4;              // floats: per token u = tau log2e n, w = u kappa gamma, mask
   constexpr int kStageVw = 2 * VB * kD + 2 * VB * kVwPad;  // dwords
   constexpr int kStageP = NHEAD * 64;           // floats: p of (head, token) for the value MFMA
-  constexpr int kStage = kStageMeta + kStageNg + kStageVw + kStageP;
+  constexpr int kStageTr = VMSE ? 0 : 64 * 16;  // dwords: value-weight digit blocks, exchanged between lanes
+  constexpr int kStage = kStageMeta + kStageNg + kStageVw + kStageP + kStageTr;
   constexpr int kMerge = NHEAD * (kD + 2);
   constexpr int kStride = kStage > kMerge ? kStage : kMerge;
   __shared__ __attribute__((aligned(16))) uint32_t smem[4 * kStride];
@@ -264,6 +265,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
   float* s_ng = reinterpret_cast<float*>(s_meta + kStageMeta);
   uint32_t* s_vw = s_meta + kStageMeta + kStageNg;
   float* s_p = reinterpret_cast<float*>(s_vw + kStageVw);
+  uint32_t* s_tr = s_vw + kStageVw + kStageP;
 
   // query digit operands and per-head constants (score layout: head 4ht + n/4)
   u32x4 qb[NHT][NPL][2];
@@ -612,17 +614,31 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
         float Mpv[NG];
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) Mpv[gi] = __shfl(x, 4 * g + gi);
+        // Exchange the digit blocks inside each quad of lanes: lane (g, 4h + G)
+        // holds digit d of row (head h, group G) in A[d]; the value MFMA of
+        // group G takes rows (head h, digit d) from lane (g, 4h + d), so one
+        // MFMA per channel tile yields all four digits of its own group.  Block
+        // d of lane L sits at slot d * 64 + (L ^ d): writes and reads both
+        // cover all banks once per 16 lanes.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int d = 0; d < 4; ++d) *reinterpret_cast<u32x4*>(s_tr + 4 * (d * 64 + (lane ^ d))) = A[d];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        u32x4 AG[NG];
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi)
+          AG[gi] = *reinterpret_cast<const u32x4*>(s_tr + 4 * ((n & 3) * 64 + ((lane & ~3) | (gi ^ (n & 3)))));
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) {
           const int gi = nt >> 1;  // group of channels 16nt..16nt+15
           const uint32_t w = s_vw[g * (kD + kVwPad) + 16 * nt + n];
           const u32x4 B = {w & 0x03030303u, w & 0x0c0c0c0cu, w & 0x30303030u, (w >> 2) & 0x30303030u};
-          // row (head g, group gi) of the four digit products
-          const int d0 = mfma_i8(A[0], B, i32x4{0, 0, 0, 0})[gi];
-          const int d1 = mfma_i8(A[1], B, i32x4{0, 0, 0, 0})[gi];
-          const int d2 = mfma_i8(A[2], B, i32x4{0, 0, 0, 0})[gi];
-          const int d3 = mfma_i8(A[3], B, i32x4{0, 0, 0, 0})[gi];
-          const float v = fmaf((float)((d0 << 8) + d1), 65536.f, (float)((d2 << 8) + d3));
+          // rows (head g, digit r) of group gi: element r is digit r's product
+          const i32x4 C = mfma_i8(AG[gi], B, i32x4{0, 0, 0, 0});
+          const float v = fmaf((float)((C[0] << 8) + C[1]), 65536.f, (float)((C[2] << 8) + C[3]));
           acc[ht][nt] = fmaf(acc[ht][nt], alpha_pv[ht], fmaf(v, inv_sv, Mpv[gi]));
         }
       }
