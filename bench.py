@@ -225,6 +225,9 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run a plain elementwise kernel (y = -x, fp32) over this many MiB, "
                          "the known-size reference for HBM byte counters")
+    ap.add_argument("--achievable-mib", type=int, default=1024,
+                    help="after the timed steps, time a plain device copy of this many MiB (0: skip); "
+                         "its read + write GB/s is reported as the achievable bandwidth")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU work: turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) "
                          "made with --copy-probe-mib into the decode scan's traffic summary under profiles/")
@@ -363,6 +366,26 @@ def main():
     scan_avg_ms = sum(scan_ms) / len(scan_ms)
     scan_avg_bytes = sum(scan_bytes) / len(scan_bytes)
     scan_gbs = scan_avg_bytes / (scan_avg_ms * 1e-3) / 1e9
+    scan_sorted = sorted(scan_ms)
+    launch_spread = {"median": round(scan_sorted[len(scan_sorted) // 2], 5), "min": round(scan_sorted[0], 5),
+                     "max": round(scan_sorted[-1], 5)}
+    copy_gbs = None
+    if args.achievable_mib:
+        # a plain device copy (read and write) on the same device: what HBM
+        # delivers to the simplest streaming kernel
+        x = torch.ones(args.achievable_mib << 18, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        y.copy_(x)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        e0.record()
+        for _ in range(reps):
+            y.copy_(x)
+        e1.record()
+        torch.cuda.synchronize()
+        copy_gbs = 2.0 * x.numel() * 4 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        del x, y
+        torch.cuda.empty_cache()
     sha = _source_sha("tq_decode_mfma.hip", "tq_decode.hip", "tq_common.h", "tq_internal.h")
     generic = os.environ.get("TQ_DECODE_PATH") == "generic"
     traffic = None if generic else _traffic(SCAN_KERNEL, w.name, sha)
@@ -387,8 +410,12 @@ def main():
         "roofline": {"kernel": scan_kernel_name, "bound": "hbm",
                      "achieved": round(scan_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(scan_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "avg_launch_ms": round(scan_avg_ms, 5),
+                     "avg_launch_ms": round(scan_avg_ms, 5), "launch_ms": launch_spread,
                      "algorithmic_bytes_per_launch": int(scan_avg_bytes), "source_sha": sha},
+        "achievable": None if copy_gbs is None else {
+            "copy_gbs": round(copy_gbs, 1), "copy_mib": args.achievable_mib,
+            "scan_over_copy": round(scan_gbs / copy_gbs, 4),
+            "note": "device copy y = x (read + write) timed with torch events after the decode steps"},
         "encode": {"tokens_per_s": round(enc_tokens_per_s, 1), "ms_per_bulk_encode": round(enc_wall * 1e3, 3),
                    "tokens": w.batch * w.n_tokens, "key_vectors": n_vec,
                    "roofline": {"kernel": "encode_rot_kernel (keys: Pi and S' rotations)", "bound": "mfma",

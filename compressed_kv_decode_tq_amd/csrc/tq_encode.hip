@@ -417,8 +417,8 @@ __global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
             z[ct] = mfma_bf16(ahi, rlo[ct][ks], z[ct]);
           }
         }
-        // shift the sign bit of z in at the bottom: after the 8 elements of
-        // plane word m, bit 7 - j holds the sign of element j = (rt&1)*4 + rr
+        // shift the sign bit of z in at the bottom, with the gap of 12 after
+        // the even row tile (the bit layout of the plane words below)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
