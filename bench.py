@@ -321,9 +321,10 @@ def main():
                          [state["n_c"]] * w.batch, cache)
             state["n_c"] += state["n_r"]
             state["n_r"] = 0
+        fused = ring and nq == 1  # one call appends the token and attends
         for t in range(nq):
             kn, vn = news[i * nq + t]
-            if ring:
+            if ring and not fused:
                 tq.ring_append(kn, vn, rk, rv, [state["n_r"]] * w.batch)
                 state["n_r"] += 1
             elif w.step_mode == "encode":
@@ -331,9 +332,15 @@ def main():
                 state["n_c"] += 1
         if timed_pair is not None:
             tq.time_next_launch(tq.TQ_KERNEL_DECODE_SCAN, *timed_pair)
-        tq.decode_attn(prm, qs[i], cache, [state["n_c"]] * w.batch, rk if ring else None,
-                       rv if ring else None, [state["n_r"]] * w.batch if ring else None,
-                       out=out, workspace=ws)
+        if fused:
+            kn, vn = news[i]
+            tq.decode_attn_append(prm, qs[i], cache, [state["n_c"]] * w.batch, kn, vn, rk, rv,
+                                  [state["n_r"]] * w.batch, out=out, workspace=ws)
+            state["n_r"] += 1
+        else:
+            tq.decode_attn(prm, qs[i], cache, [state["n_c"]] * w.batch, rk if ring else None,
+                           rv if ring else None, [state["n_r"]] * w.batch if ring else None,
+                           out=out, workspace=ws)
         # algorithmic bytes of this step
         by = per_th * w.batch * w.h_kv * state["n_c"]                       # compressed cache
         by += state["n_r"] * w.batch * w.h_kv * w.d * 2 * 2                 # ring K and V

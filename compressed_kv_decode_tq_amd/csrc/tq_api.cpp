@@ -292,11 +292,23 @@ size_t decode_workspace_bytes_impl(const tq_layout* layout, int32_t batch, int32
   return decode_ws_bytes(nb, num_kv_heads, decode_vgroup(num_q_heads / num_kv_heads, nq), max_tokens);
 }
 
+// One decode call.  With k_new (fused append, nq = 1): the token k_new[b],
+// v_new[b] is first written to ring position n_ring_host[b], and attention
+// covers n_ring_host[b] + 1 ring tokens.
 int decode_attn_impl(const tq_layout* layout, const tq_params* params, const void* q, int32_t q_dtype,
                      int32_t num_q_heads, int32_t nq, const tq_cache* cache, const int64_t* n_compressed_host,
                      const void* ring_k, const void* ring_v, int32_t ring_cap, const int32_t* n_ring_host,
-                     float softmax_scale, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+                     float softmax_scale, float* out, void* workspace, size_t workspace_bytes, void* stream,
+                     const void* k_new = nullptr, const void* v_new = nullptr, int32_t new_dtype = 0) {
   g_err[0] = 0;
+  const bool append = k_new != nullptr || v_new != nullptr;
+  if (append) {
+    if (!k_new || !v_new) return fail(TQ_ERR_INVALID, "k_new and v_new must both be non-NULL");
+    if (new_dtype != TQ_F32 && new_dtype != TQ_BF16) return fail(TQ_ERR_INVALID, "new_dtype must be TQ_F32 or TQ_BF16");
+    if (ring_cap <= 0) return fail(TQ_ERR_INVALID, "the fused append needs a ring (ring_cap > 0)");
+    if (!ring_k || !ring_v || !n_ring_host) return fail(TQ_ERR_INVALID, "ring buffers and n_ring_host required");
+    if (nq != 1) return fail(TQ_ERR_INVALID, "the fused append takes one query per sequence");
+  }
   int rc = check_layout(layout);
   if (rc) return rc;
   if ((rc = check_cache(layout, cache))) return rc;
@@ -316,9 +328,10 @@ int decode_attn_impl(const tq_layout* layout, const tq_params* params, const voi
   for (int b = 0; b < cache->batch; ++b) {
     if (n_compressed_host[b] < 0 || n_compressed_host[b] > cache->capacity)
       return fail(TQ_ERR_CAPACITY, "sequence %d: n_compressed %lld outside [0, capacity]", b, (long long)n_compressed_host[b]);
-    if (ring_cap > 0 && (n_ring_host[b] < 0 || n_ring_host[b] > ring_cap))
-      return fail(TQ_ERR_CAPACITY, "sequence %d: n_ring %d outside [0, ring_cap]", b, n_ring_host[b]);
-    if (ring_cap > 0 && n_ring_host[b] > tq::kMaxRing)
+    if (ring_cap > 0 && (n_ring_host[b] < 0 || n_ring_host[b] + (append ? 1 : 0) > ring_cap))
+      return fail(TQ_ERR_CAPACITY, "sequence %d: n_ring %d%s outside [0, ring_cap]", b, n_ring_host[b],
+                  append ? " + 1 appended" : "");
+    if (ring_cap > 0 && n_ring_host[b] + (append ? 1 : 0) > tq::kMaxRing)
       return fail(TQ_ERR_UNSUPPORTED, "sequence %d: more than %d ring tokens", b, tq::kMaxRing);
     max_tokens = std::max<int64_t>(max_tokens, n_compressed_host[b]);
   }
@@ -341,8 +354,9 @@ int decode_attn_impl(const tq_layout* layout, const tq_params* params, const voi
     std::memset(&a, 0, sizeof(a));
     for (int b = 0; b < nb; ++b) {
       a.n_comp.v[b] = n_compressed_host[b0 + b];
-      a.n_ring.v[b] = ring_cap > 0 ? n_ring_host[b0 + b] : 0;
+      a.n_ring.v[b] = ring_cap > 0 ? n_ring_host[b0 + b] + (append ? 1 : 0) : 0;
     }
+    const size_t new_off = (size_t)b0 * h_kv * tq::kD * (new_dtype == TQ_F32 ? 4 : 2);
     tq::decode_split(max_tokens, (int64_t)std::min(cache->batch, tq::kMaxSeqPerLaunch) * h_kv, &a.splits, &a.split_len);
     a.q = (const char*)q + (size_t)b0 * nq * num_q_heads * tq::kD * qsz;
     a.k_planes = cache->k_planes + seq_off(b0, h_kv, cap, kpb);
@@ -357,6 +371,13 @@ int decode_attn_impl(const tq_layout* layout, const tq_params* params, const voi
     const size_t ring_off = (size_t)b0 * ring_cap * h_kv * tq::kD;
     a.ring_k = ring_cap > 0 ? (const uint16_t*)ring_k + ring_off : nullptr;
     a.ring_v = ring_cap > 0 ? (const uint16_t*)ring_v + ring_off : nullptr;
+    if (append) {
+      a.app_k = (const char*)k_new + new_off;
+      a.app_v = (const char*)v_new + new_off;
+      a.app_ring_k = const_cast<uint16_t*>(a.ring_k);
+      a.app_ring_v = const_cast<uint16_t*>(a.ring_v);
+      a.app_bf16 = new_dtype == TQ_BF16;
+    }
     a.out = out + (size_t)b0 * nq * num_q_heads * tq::kD;
     // workspace: qprep and partials sized for vg_max virtual heads per KV head
     const size_t rows = (size_t)nb * h_kv * vg_max;
@@ -407,6 +428,15 @@ int decode_attn_impl(const tq_layout* layout, const tq_params* params, const voi
                                    vpl, (hipStream_t)stream, tl);
       if (e == hipErrorNotSupported && layout->key_half)
         return fail(TQ_ERR_UNSUPPORTED, "half-bit keys: this value layout or head group has no MFMA scan");
+      if (e == hipErrorNotSupported && append) {
+        // the generic path appends with its own launch (the write is idempotent)
+        tq::SeqValues pos;
+        for (int b = 0; b < nb; ++b) pos.v[b] = n_ring_host[b0 + b];
+        e = tq::launch_ring_append(a.app_k, a.app_v, a.app_bf16, nb, h_kv, a.app_ring_k, a.app_ring_v, ring_cap,
+                                   pos, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "ring append launch");
+        e = hipErrorNotSupported;
+      }
       if (e == hipErrorNotSupported)
         e = tq::launch_decode(a, layout->key_mse_bits, layout->key_qjl, vmse, layout->value_bits,
                               (hipStream_t)stream, tl);
@@ -437,6 +467,20 @@ int tq_decode_attn(const tq_layout* layout, const tq_params* params, const void*
                    void* workspace, size_t workspace_bytes, void* stream) {
   return decode_attn_impl(layout, params, q, q_dtype, num_q_heads, 1, cache, n_compressed_host, ring_k, ring_v,
                           ring_cap, n_ring_host, softmax_scale, out, workspace, workspace_bytes, stream);
+}
+
+int tq_decode_attn_append(const tq_layout* layout, const tq_params* params, const void* q, int32_t q_dtype,
+                          int32_t num_q_heads, const tq_cache* cache, const int64_t* n_compressed_host,
+                          const void* k_new, const void* v_new, int32_t new_dtype, void* ring_k, void* ring_v,
+                          int32_t ring_cap, const int32_t* n_ring_host, float softmax_scale, float* out,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (!k_new || !v_new) {
+    g_err[0] = 0;
+    return fail(TQ_ERR_INVALID, "k_new and v_new must both be non-NULL");
+  }
+  return decode_attn_impl(layout, params, q, q_dtype, num_q_heads, 1, cache, n_compressed_host, ring_k, ring_v,
+                          ring_cap, n_ring_host, softmax_scale, out, workspace, workspace_bytes, stream, k_new,
+                          v_new, new_dtype);
 }
 
 int tq_decode_attn_multi(const tq_layout* layout, const tq_params* params, const void* q,

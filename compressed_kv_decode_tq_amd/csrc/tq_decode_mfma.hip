@@ -113,6 +113,17 @@ __global__ __launch_bounds__(256) void qprep_mfma_kernel(DecodeArgs a, int pm, i
   __shared__ int e_mse[kMaxGroup], e_qjl[kMaxGroup];
   const int b = blockIdx.x / a.h_kv, h = blockIdx.x % a.h_kv;
   const int G = a.group;
+  if (a.app_k && a.vbase == 0) {
+    // fused ring append: threads 0..127 write the key row, 128..255 the value
+    // row of this (sequence, KV head), rounded to bf16 as the ring append does
+    const int c = threadIdx.x & (kD - 1), which = threadIdx.x >> 7;
+    const size_t src = ((size_t)b * a.h_kv + h) * kD + c;
+    const size_t dst = (((size_t)b * a.ring_cap + a.n_ring.v[b] - 1) * a.h_kv + h) * kD + c;
+    const void* in = which ? a.app_v : a.app_k;
+    uint16_t* ring = which ? a.app_ring_v : a.app_ring_k;
+    ring[dst] = a.app_bf16 ? reinterpret_cast<const uint16_t*>(in)[src]
+                           : (uint16_t)f2bf(reinterpret_cast<const float*>(in)[src]);
+  }
   for (int i = threadIdx.x; i < kMaxGroup * kD; i += blockDim.x) {
     const int gq = i / kD, c = i % kD;
     float x = 0.f;

@@ -123,6 +123,15 @@ struct DecodeArgs {
   float* qconst;          // workspace: [batch][h_kv][group][4] per-head score constants
   SeqValues n_comp;
   SeqValues n_ring;
+  // Fused ring append (single query): the new token of sequence b and KV head
+  // h (app_k, app_v: [batch][h_kv][d], bf16 if app_bf16 else fp32) goes to
+  // ring position n_ring[b] - 1 before attention; the MFMA q-prep kernel
+  // writes it.  NULL app_k: no append.
+  const void* app_k;
+  const void* app_v;
+  uint16_t* app_ring_k;
+  uint16_t* app_ring_v;
+  int32_t app_bf16;
 };
 
 // Multi-query decode.  The nq queries of a sequence against one KV head form

@@ -25,7 +25,7 @@ MAX_LEVELS = 16
 #: Every symbol include/tq.h declares.
 EXPORTS = ("tq_make_codebook", "tq_memory_bytes", "tq_params_derived_bytes", "tq_prepare_params",
            "tq_encode_kv", "tq_ring_append", "tq_decode_workspace_bytes", "tq_decode_attn",
-           "tq_decode_workspace_bytes_multi", "tq_decode_attn_multi",
+           "tq_decode_workspace_bytes_multi", "tq_decode_attn_multi", "tq_decode_attn_append",
            "tq_time_next_launch", "tq_last_error", "tq_version")
 TQ_KERNEL_DECODE_SCAN, TQ_KERNEL_ENCODE_KEYS, TQ_KERNEL_ENCODE_VALUES = 0, 1, 2
 
@@ -95,6 +95,9 @@ def lib() -> ctypes.CDLL:
         L.tq_decode_attn_multi.argtypes = [P(_Layout), P(_Params), vp, i32, i32, i32, P(_Cache), P(i64), vp,
                                            vp, i32, P(i32), ctypes.c_float, vp, vp, sz, vp]
         L.tq_decode_attn_multi.restype = ctypes.c_int
+        L.tq_decode_attn_append.argtypes = [P(_Layout), P(_Params), vp, i32, i32, P(_Cache), P(i64), vp, vp, i32,
+                                            vp, vp, i32, P(i32), ctypes.c_float, vp, vp, sz, vp]
+        L.tq_decode_attn_append.restype = ctypes.c_int
         L.tq_time_next_launch.argtypes = [i32, vp, vp]
         L.tq_time_next_launch.restype = ctypes.c_int
         L.tq_last_error.argtypes = []
@@ -314,6 +317,39 @@ def decode_attn(params: Params, q: torch.Tensor, cache: Cache, n_compressed, rin
                                     ctypes.byref(cc), nc, _ptr(ring_k), _ptr(ring_v), ring_cap, nr,
                                     float(scale), _ptr(out), _ptr(workspace), workspace.numel(),
                                     _stream(stream)))
+    return out
+
+
+def decode_attn_append(params: Params, q: torch.Tensor, cache: Cache, n_compressed, k_new: torch.Tensor,
+                       v_new: torch.Tensor, ring_k: torch.Tensor, ring_v: torch.Tensor, n_ring,
+                       scale: float | None = None, out: torch.Tensor | None = None,
+                       workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """One decode step with the ring append fused in (tq_decode_attn_append):
+    k_new, v_new [B, 1, H_kv, d] (fp32 or bf16) go to ring positions n_ring[b],
+    then q [B, H_q, d] attends over the compressed tokens and n_ring[b] + 1
+    ring tokens.  n_ring holds the lengths before the append."""
+    lay_py = params.layout
+    b, h_q, d = q.shape
+    for t in (q, k_new, v_new, ring_k, ring_v):
+        if not t.is_contiguous():
+            raise ValueError("q, k_new, v_new and the ring buffers must be contiguous")
+    if k_new.dtype != v_new.dtype:
+        raise ValueError("k_new and v_new must have the same dtype")
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(d))
+    if out is None:
+        out = torch.empty(tuple(q.shape), dtype=torch.float32, device=q.device)
+    nc = (ctypes.c_int64 * b)(*[int(x) for x in n_compressed])
+    max_tokens = max(int(x) for x in n_compressed)
+    need = decode_workspace_bytes(lay_py, b, h_q, cache.num_kv_heads, max_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    nr = (ctypes.c_int32 * b)(*[int(x) for x in n_ring])
+    lay, prm, cc = lay_py.c(), params.c(), cache.c()
+    _check(lib().tq_decode_attn_append(ctypes.byref(lay), ctypes.byref(prm), _ptr(q), _dtype_code(q), h_q,
+                                       ctypes.byref(cc), nc, _ptr(k_new), _ptr(v_new), _dtype_code(k_new),
+                                       _ptr(ring_k), _ptr(ring_v), ring_k.shape[1], nr, float(scale), _ptr(out),
+                                       _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
 
 

@@ -210,6 +210,28 @@ int tq_decode_attn(const tq_layout* layout, const tq_params* params, const void*
                    int32_t ring_cap, const int32_t* n_ring_host, float softmax_scale, float* out,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* One decode step with the ring append fused in (page
+ * "turboquant/audit_claims.py", AUDIT 1: the store keeps the most recent
+ * tokens uncompressed; page "03. Results & Benchmarks", section "Latency
+ * Benchmarks": one pass per step).  The result equals tq_ring_append of
+ * (k_new, v_new) at ring positions n_ring_host[b], followed by tq_decode_attn
+ * with n_ring_host[b] + 1 ring tokens.  The append is done by the decode's own
+ * query-preparation kernel, with no launch of its own.  k_new, v_new:
+ * [batch][1][h_kv][d] in new_dtype (TQ_F32 or TQ_BF16), rounded to bf16 in the
+ * ring.  ring_k, ring_v: the caller's bf16 ring [batch][ring_cap][h_kv][d],
+ * written at those positions and read for attention.  n_ring_host holds the
+ * ring lengths before the append; the caller advances them by one after the
+ * call.  One query per sequence; q, out, workspace and the other arguments as
+ * tq_decode_attn.  Errors as tq_decode_attn, plus TQ_ERR_INVALID for a NULL
+ * k_new, v_new, ring buffer or n_ring_host, a bad new_dtype or ring_cap 0,
+ * and TQ_ERR_CAPACITY when n_ring_host[b] + 1 exceeds ring_cap.  A failed
+ * check writes nothing. */
+int tq_decode_attn_append(const tq_layout* layout, const tq_params* params, const void* q, int32_t q_dtype,
+                          int32_t num_q_heads, const tq_cache* cache, const int64_t* n_compressed_host,
+                          const void* k_new, const void* v_new, int32_t new_dtype, void* ring_k, void* ring_v,
+                          int32_t ring_cap, const int32_t* n_ring_host, float softmax_scale, float* out,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Multi-query decode (page "turboquant/audit_claims.py", AUDIT 4: the
  * (H_kv, G, T, N) score layout with T query positions per step): num_queries
  * = T queries per sequence, for speculative verification or chunked prefill

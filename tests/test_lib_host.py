@@ -147,6 +147,18 @@ def test_encode_and_decode_argument_checks():
     assert L.tq_decode_workspace_bytes_multi(ctypes.byref(lay), 2, 4, 1, 64, 0) == 0
     assert L.tq_decode_attn_multi(*margs(0, 1 << 30)) == tq.TQ_ERR_INVALID
     assert L.tq_decode_attn_multi(*margs(3, 8)) == tq.TQ_ERR_WORKSPACE
+    # fused append: NULL token, bad dtype, no ring, a ring with no room left;
+    # each fails its checks before any launch
+    rk = ctypes.c_void_p(16)
+    aargs = lambda kn, dt, rcap, nrv: (ctypes.byref(lay), ctypes.byref(prm), 16, tq.TQ_F32, 4,  # noqa: E731
+                                       ctypes.byref(cache), nc, kn, kn, dt, rk, rk, rcap, nrv, 0.1, 16, 16,
+                                       1 << 30, None)
+    assert L.tq_decode_attn_append(*aargs(None, tq.TQ_BF16, 128, nr)) == tq.TQ_ERR_INVALID
+    assert L.tq_decode_attn_append(*aargs(16, tq.TQ_F16, 128, nr)) == tq.TQ_ERR_INVALID
+    assert L.tq_decode_attn_append(*aargs(16, tq.TQ_BF16, 0, nr)) == tq.TQ_ERR_INVALID
+    nr_last = (ctypes.c_int32 * 2)(0, 128)
+    assert L.tq_decode_attn_append(*aargs(16, tq.TQ_BF16, 128, nr_last)) == tq.TQ_ERR_CAPACITY
+    assert "appended" in L.tq_last_error().decode()
     # ring append bounds
     nr_full = (ctypes.c_int32 * 2)(0, 128)
     assert L.tq_ring_append(16, 16, tq.TQ_BF16, 2, 1, 128, 16, 16, 128, nr_full, None) == tq.TQ_ERR_CAPACITY
