@@ -493,11 +493,12 @@ hipError_t dispatch_qjl(const DecodeArgs& a, int qjl, int vmse, int vb, hipStrea
 // Split of the token range for the decode grid, in whole 256-token rounds of
 // the four waves.  About kSplitTarget work-groups over the device; when that
 // makes splits shorter than kLongSplit tokens, they are lengthened towards
-// kLongSplit as long as at least kFloorGroups work-groups (two waves per SIMD)
-// remain, so per-work-group set-up and merge stay small next to the scan while
-// short sequences still spread over the device.
+// kLongSplit as long as at least kFloorGroups work-groups (eight per compute
+// unit) remain, so per-work-group set-up and merge stay small next to the scan
+// while a few long sequences still spread over every wave slot of the device
+// (8 sequence-heads of 131072 tokens: 512-token splits, 2048 work-groups).
 constexpr int64_t kSplitTarget = 2048;
-constexpr int64_t kFloorGroups = 512;
+constexpr int64_t kFloorGroups = 2048;
 constexpr int64_t kLongSplit = 2048;
 constexpr int64_t kMinSplit = 256;
 
