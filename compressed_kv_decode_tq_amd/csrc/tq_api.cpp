@@ -208,6 +208,7 @@ int tq_encode_kv(const tq_layout* layout, const tq_params* params, const void* k
     a.v_meta = cache->v_meta ? (uint16_t*)((char*)cache->v_meta + seq_off(b0, h_kv, cap, groups * 4)) : nullptr;
     a.v_norm = cache->v_norm ? (char*)cache->v_norm + seq_off(b0, h_kv, cap, sz) : nullptr;
     a.derived = (const uint16_t*)params->derived;
+    a.pi = params->pi;
     a.n_new = n_new;
     a.capacity = cap;
     a.batch = nb;

@@ -15,6 +15,8 @@
 // add a third pass with k split into hi + lo.  The residual is fp32, so the QJL
 // GEMM uses three passes (S' hi/lo x r hi/lo, dropping lo x lo).  fp32
 // accumulation throughout.
+#include <cstdlib>
+#include <cstring>
 #include <type_traits>
 
 #include "tq_common.h"
@@ -478,6 +480,143 @@ __global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
   }
 }
 
+// Bit position, in a 32-token value-plane word, of the token at position u of
+// its block (the inverse of vslot).
+__device__ __forceinline__ int vslot_inv(int u) { return 8 * (u & 3) + 4 * (u >> 4) + ((u >> 2) & 3); }
+
+// Sum over the 128 threads of a work-group (two waves), every thread gets it.
+__device__ __forceinline__ float block_sum128(float x, float* red) {
+  x = wave_sum(x);
+  __syncthreads();  // red is free again
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  return red[0] + red[1];
+}
+
+// Few-token encode (a decode step's new tokens): one work-group of 128
+// threads per (sequence, head, 32-token block) tile, one thread per
+// coordinate, in fp32 with coalesced column reads of fp32 matrices.  Per
+// token: n = |k|, y = Pi k / n (Pi^T from the derived buffer), the Lloyd-Max
+// index #{t < y_i} with the coordinate's own table, and for QJL keys the
+// residual in the original space r = Pi^T (y - c) (Pi from the caller's
+// parameters), z = S r (S^T from the derived buffer), gamma = |y - c|.  No
+// LDS staging of the matrices: for a handful of tokens that staging would
+// cost more than the products.
+template <bool IN_BF16, int MSE_BITS, bool QJL, bool VALUE, bool HALF>
+__global__ __launch_bounds__(kD) void encode_small_kernel(EncodeArgs a) {
+  static_assert(!(HALF && VALUE), "the half-bit layout is a key layout");
+  constexpr int LV = 1 << MSE_BITS;
+  __shared__ float xs[kD];
+  __shared__ float red[2];
+  const int i = threadIdx.x, lane = i & 63, wv = i >> 6;
+  int b, h;
+  int64_t blk;
+  tile_coords(a, blockIdx.x, b, h, blk);
+  const int64_t pos = a.pos.v[b];
+  const int64_t slot = (int64_t)b * a.h_kv + h;
+  const float* pit = reinterpret_cast<const float*>(reinterpret_cast<const char*>(a.derived) + kOffPiT);
+  const float* stt = reinterpret_cast<const float*>(reinterpret_cast<const char*>(a.derived) + kOffST);
+  const void* src = VALUE ? a.v : a.k;
+  const bool hi = HALF && (i & 31) < 16;  // this coordinate uses the table with one more bit
+  constexpr size_t rec = (size_t)(MSE_BITS + (QJL ? 1 : 0)) * (kD / 8) + (HALF ? kD / 16 : 0);
+  uint32_t vw[MSE_BITS];  // value planes: this channel's word of each plane for the block
+#pragma unroll
+  for (int p = 0; p < MSE_BITS; ++p) vw[p] = 0u;
+  uint32_t vmask = 0u;
+  for (int u = 0; u < 32; ++u) {
+    const int64_t dp = blk * 32 + u;
+    const int64_t t = dp - pos;
+    if (t < 0 || t >= a.n_new) continue;  // the same for every thread
+    const int64_t row = ((int64_t)b * a.n_new + t) * a.h_kv + h;
+    const float x = IN_BF16 ? bf2f(reinterpret_cast<const uint16_t*>(src)[row * kD + i])
+                            : reinterpret_cast<const float*>(src)[row * kD + i];
+    const float n = sqrtf(block_sum128(x * x, red));
+    const float inv = n > 0.f ? 1.0f / n : 0.f;
+    xs[i] = x;
+    __syncthreads();
+    float acc = 0.f;
+#pragma unroll 16
+    for (int k = 0; k < kD; ++k) acc = fmaf(pit[k * kD + i], xs[k], acc);
+    const float y = acc * inv;
+    int idx = 0;
+    float c;
+    if (hi) {
+#pragma unroll
+      for (int k = 0; k < 2 * LV - 1; ++k) idx += y > a.k_thr_hi[k] ? 1 : 0;
+      c = a.k_cent_hi[idx];
+    } else {
+      const float* thr = VALUE ? a.v_thr : a.k_thr;
+#pragma unroll
+      for (int k = 0; k < LV - 1; ++k) idx += y > thr[k] ? 1 : 0;
+      c = VALUE ? a.v_cent[idx] : a.k_cent[idx];
+    }
+    if (VALUE) {
+      const int bp = vslot_inv(u);
+#pragma unroll
+      for (int p = 0; p < MSE_BITS; ++p) vw[p] |= (uint32_t)((idx >> p) & 1) << bp;
+      vmask |= 1u << bp;
+      if (i == 0) store_scalar(a.v_norm, slot * a.capacity + dp, n, a.scalar_f16);
+      __syncthreads();  // xs is rewritten by the next token
+      continue;
+    }
+    const float r = y - c;
+    bool zbit = false;
+    float gam = 0.f;
+    if (QJL) {
+      gam = sqrtf(block_sum128(r * r, red));  // its barriers also end the reads of xs
+      xs[i] = r;
+      __syncthreads();
+      float ro = 0.f;  // (Pi^T r)_i = sum_j Pi[j][i] r_j
+#pragma unroll 16
+      for (int j = 0; j < kD; ++j) ro = fmaf(a.pi[j * kD + i], xs[j], ro);
+      __syncthreads();
+      xs[i] = ro;
+      __syncthreads();
+      float z = 0.f;  // (S ro)_i = sum_j S^T[j][i] ro_j
+#pragma unroll 16
+      for (int j = 0; j < kD; ++j) z = fmaf(stt[j * kD + i], xs[j], z);
+      zbit = z >= 0.f;
+    }
+    // plane words by ballot: wave wv holds coordinates 64 wv .. 64 wv + 63,
+    // the words 2 wv and 2 wv + 1 of every plane
+    uint8_t* recp = a.k_planes + (slot * a.capacity + dp) * rec;
+#pragma unroll
+    for (int p = 0; p < MSE_BITS; ++p) {
+      const uint64_t m = __ballot((idx >> p) & 1);
+      if (lane == 0) {
+        *reinterpret_cast<uint32_t*>(recp + p * (kD / 8) + 8 * wv) = (uint32_t)m;
+        *reinterpret_cast<uint32_t*>(recp + p * (kD / 8) + 8 * wv + 4) = (uint32_t)(m >> 32);
+      }
+    }
+    if (HALF) {  // the extra bit of the half-bit coordinates: the low 16 bits of each word
+      const uint64_t m = __ballot(hi && ((idx >> MSE_BITS) & 1));
+      if (lane == 0) {
+        *reinterpret_cast<uint16_t*>(recp + MSE_BITS * (kD / 8) + 4 * wv) = (uint16_t)(m & 0xffffu);
+        *reinterpret_cast<uint16_t*>(recp + MSE_BITS * (kD / 8) + 4 * wv + 2) = (uint16_t)((m >> 32) & 0xffffu);
+      }
+    }
+    if (QJL) {
+      const uint64_t m = __ballot(zbit);
+      const int off = MSE_BITS * (kD / 8) + (HALF ? kD / 16 : 0);
+      if (lane == 0) {
+        *reinterpret_cast<uint32_t*>(recp + off + 8 * wv) = (uint32_t)m;
+        *reinterpret_cast<uint32_t*>(recp + off + 8 * wv + 4) = (uint32_t)(m >> 32);
+      }
+    }
+    if (i == 0) {
+      store_scalar(a.k_norm, slot * a.capacity + dp, n, a.scalar_f16);
+      if (QJL) store_scalar(a.k_rnorm, slot * a.capacity + dp, gam, a.scalar_f16);
+    }
+    __syncthreads();  // xs is rewritten by the next token
+  }
+  if (VALUE && vmask) {
+    const int64_t nblk_cap = a.capacity >> 5;
+#pragma unroll
+    for (int p = 0; p < MSE_BITS; ++p)
+      store_plane_word(a.v_planes + ((slot * nblk_cap + blk) * MSE_BITS + p) * kD + i, vw[p], vmask);
+  }
+}
+
 // Asymmetric min/max value code, one 32-token tile per wave: lane = (token,
 // half of the channels).  IEEE fp32 arithmetic in a fixed order so the codes
 // are reproducible bit for bit:
@@ -617,13 +756,34 @@ hipError_t launch_rot(const EncodeArgs& a, hipStream_t st, TimedLaunch tl) {
   return e;
 }
 
+// Calls with at most this many new tokens per sequence take the few-token
+// encode (TQ_ENCODE_PATH=small or =mfma forces one path).
+constexpr int64_t kSmallEncodeTokens = 4;
+
+bool use_small_encode(const EncodeArgs& a) {
+  const char* path = std::getenv("TQ_ENCODE_PATH");
+  if (path && std::strcmp(path, "small") == 0) return true;
+  if (path && std::strcmp(path, "mfma") == 0) return false;
+  return a.n_new <= kSmallEncodeTokens;
+}
+
+template <bool BF16, int MB, bool QJL, bool VALUE, bool HALF = false>
+hipError_t launch_enc(const EncodeArgs& a, hipStream_t st, TimedLaunch tl) {
+  if (!use_small_encode(a)) return launch_rot<BF16, MB, QJL, VALUE, HALF>(a, st, tl);
+  if (tl.begin) (void)hipEventRecord(tl.begin, st);
+  hipLaunchKernelGGL((encode_small_kernel<BF16, MB, QJL, VALUE, HALF>), dim3(a.num_tiles), dim3(kD), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (tl.end) (void)hipEventRecord(tl.end, st);
+  return e;
+}
+
 template <bool BF16, bool QJL, bool VALUE>
 hipError_t dispatch_rot_bits(const EncodeArgs& a, int bits, hipStream_t st, TimedLaunch tl) {
   switch (bits) {
-    case 1: return launch_rot<BF16, 1, QJL, VALUE>(a, st, tl);
-    case 2: return launch_rot<BF16, 2, QJL, VALUE>(a, st, tl);
-    case 3: return launch_rot<BF16, 3, QJL, VALUE>(a, st, tl);
-    case 4: return launch_rot<BF16, 4, QJL, VALUE>(a, st, tl);
+    case 1: return launch_enc<BF16, 1, QJL, VALUE>(a, st, tl);
+    case 2: return launch_enc<BF16, 2, QJL, VALUE>(a, st, tl);
+    case 3: return launch_enc<BF16, 3, QJL, VALUE>(a, st, tl);
+    case 4: return launch_enc<BF16, 4, QJL, VALUE>(a, st, tl);
   }
   return hipErrorInvalidValue;
 }
@@ -668,10 +828,10 @@ hipError_t launch_encode_keys(const EncodeArgs& a, int in_bf16, int mse_bits, in
   if (half) {  // fractional widths 1.5 and 2.5 MSE bits, QJL keys only
     if (!qjl || mse_bits < 1 || mse_bits > 2) return hipErrorInvalidValue;
     if (in_bf16)
-      return mse_bits == 1 ? launch_rot<true, 1, true, false, true>(a, stream, tl)
-                           : launch_rot<true, 2, true, false, true>(a, stream, tl);
-    return mse_bits == 1 ? launch_rot<false, 1, true, false, true>(a, stream, tl)
-                         : launch_rot<false, 2, true, false, true>(a, stream, tl);
+      return mse_bits == 1 ? launch_enc<true, 1, true, false, true>(a, stream, tl)
+                           : launch_enc<true, 2, true, false, true>(a, stream, tl);
+    return mse_bits == 1 ? launch_enc<false, 1, true, false, true>(a, stream, tl)
+                         : launch_enc<false, 2, true, false, true>(a, stream, tl);
   }
   if (in_bf16)
     return qjl ? dispatch_rot_bits<true, true, false>(a, mse_bits, stream, tl)

@@ -59,6 +59,7 @@ struct EncodeArgs {
   uint16_t* v_meta;
   void* v_norm;
   const uint16_t* derived;  // bf16 matrices at the kOff* offsets (in elements: /2)
+  const float* pi;          // fp32 Pi, row-major [d][d] (the few-token encode)
   int64_t n_new;
   int64_t capacity;
   int32_t batch;          // sequences in this launch
