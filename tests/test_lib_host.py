@@ -177,3 +177,34 @@ def test_decode_workspace_never_shrinks_with_more_tokens(batch, h_q, h_kv):
         need = tq.decode_workspace_bytes(lay, batch, h_q, h_kv, n)
         assert need >= prev, (n, need, prev)
         prev = need
+
+
+def test_product_path_fails_loudly_without_the_library(monkeypatch):
+    """No fallback: with libtq.so absent every call of the binding raises."""
+    monkeypatch.setattr(tq, "_LIB_PATH", os.path.join(ROOT, "no-such-dir", "libtq.so"))
+    monkeypatch.setattr(tq, "_lib", None)
+    with pytest.raises(ImportError):
+        tq.lib()
+    with pytest.raises(ImportError):
+        tq.make_codebook(128, 2)
+    with pytest.raises(ImportError):
+        tq.memory_bytes(_lay(), 1, 1, 1, 0, tq.TQ_BYTES_DATA)
+
+
+def test_product_package_does_not_import_the_oracle():
+    """The product path (the binding, the build, the input generators) never
+    imports the oracle; only tests, the smoke test and the CPU baseline of the
+    bench do."""
+    import ast
+    pkg = os.path.join(ROOT, "compressed_kv_decode_tq_amd")
+    for fn in sorted(os.listdir(pkg)):
+        if not fn.endswith(".py"):
+            continue
+        tree = ast.parse(open(os.path.join(pkg, fn)).read())
+        for node in ast.walk(tree):
+            names = []
+            if isinstance(node, ast.Import):
+                names = [a.name for a in node.names]
+            elif isinstance(node, ast.ImportFrom):
+                names = [node.module or ""]
+            assert not any(n == "oracle" or n.startswith("oracle.") for n in names), (fn, names)
