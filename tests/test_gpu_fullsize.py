@@ -94,7 +94,8 @@ def test_fullsize_batched_b32_hkv8_n32768():
         f"key QJL {tot[1]} of {len(slots) * w.n_tokens * w.d} coordinates")
     del k, v
 
-    # decode steps as bench.py runs them: append the step token to the ring, then attend
+    # decode steps as bench.py runs them: one call appends the step token to
+    # the ring and attends (step 1 takes the two-call form, which must agree)
     rk = torch.zeros((w.batch, w.ring_cap, w.h_kv, w.d), dtype=torch.bfloat16, device=DEV)
     rv = torch.zeros_like(rk)
     ws = torch.empty(tq.decode_workspace_bytes(layout_of(w), w.batch, w.h_q, w.h_kv, cap),
@@ -103,10 +104,15 @@ def test_fullsize_batched_b32_hkv8_n32768():
     n_r = 0
     for step in range(3):
         kn, vn = wl.step_kv(w, step)
-        tq.ring_append(kn.to(DEV).contiguous(), vn.to(DEV).contiguous(), rk, rv, [n_r] * w.batch)
-        n_r += 1
         q = wl.query(w, step)
-        tq.decode_attn(prm, q.to(DEV), cache, [w.n_tokens] * w.batch, rk, rv, [n_r] * w.batch, out=out, workspace=ws)
+        if step == 1:
+            tq.ring_append(kn.to(DEV).contiguous(), vn.to(DEV).contiguous(), rk, rv, [n_r] * w.batch)
+            tq.decode_attn(prm, q.to(DEV), cache, [w.n_tokens] * w.batch, rk, rv, [n_r + 1] * w.batch, out=out,
+                           workspace=ws)
+        else:
+            tq.decode_attn_append(prm, q.to(DEV), cache, [w.n_tokens] * w.batch, kn.to(DEV).contiguous(),
+                                  vn.to(DEV).contiguous(), rk, rv, [n_r] * w.batch, out=out, workspace=ws)
+        n_r += 1
         torch.cuda.synchronize()
         if step in (0, 2):
             _check_decode(w, bk, pi, s, cache, q, out, slots, w.n_tokens, rk, rv, n_r, tag=f"step {step}")
