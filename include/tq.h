@@ -19,6 +19,8 @@
  *    decoded on chip (page "03. Results & Benchmarks", sections "Latency
  *    Benchmarks" and "Next Steps"; rotate the query at run time: page
  *    "TurboQuant — ...", section "Tại sao nó hoạt động").
+ *    Variants: several causal queries per sequence (AUDIT 4's T axis) and a
+ *    decode step with the ring append fused in.
  *  - Byte accounting of the cache (page "turboquant/audit_claims.py", AUDIT 1).
  *
  * Conventions for every entry point:
@@ -57,6 +59,14 @@
  *  - K/V inputs are [batch][n][h_kv][d] row-major; queries [batch][h_q][d];
  *    the bf16 ring is [batch][ring_cap][h_kv][d] for K and for V.  Query head
  *    hq reads KV head hq / (h_q / h_kv).
+ *  - Kernel paths.  Decode runs the int8-MFMA scan for QJL keys of 2 or 3
+ *    index bits (or 1.5 / 2.5) with 2-bit min/max values in groups of 32 or
+ *    3-bit MSE values, else a VALU scan; environment variable
+ *    TQ_DECODE_PATH=generic forces the VALU scan.  Encode of at most 4 new
+ *    tokens per sequence runs a few-token fp32 kernel, else the MFMA rotation
+ *    kernels; TQ_ENCODE_PATH=small or =mfma forces one.  All paths compute the
+ *    same codes up to the boundary window and the same outputs within
+ *    rounding.
  */
 #ifndef TQ_H_
 #define TQ_H_
