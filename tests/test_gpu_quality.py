@@ -47,11 +47,15 @@ def _gpu():
     tq.lib()
 
 
-def _key_workload(bits: int, h_kv: int, n: int) -> wl.Workload:
-    """TurboQuantProd(bits) keys: bits-1 Lloyd-Max bits plus the QJL bit."""
-    return wl.Workload(name=f"quality-k{bits}", batch=1, h_q=h_kv, h_kv=h_kv, n_tokens=n, in_dtype="f32",
-                       key_mse_bits=bits - 1, value_kind="minmax", value_bits=2, scalar_dtype="f32",
-                       structure="iid", ring_cap=0, decode_steps=1, step_mode="none", seed=20270 + bits)
+def _key_workload(bits: float, h_kv: int, n: int) -> wl.Workload:
+    """TurboQuantProd(bits) keys: bits-1 Lloyd-Max bits plus the QJL bit; a
+    fractional width (2.5, 3.5) gives half of the rotated coordinates one more
+    Lloyd-Max bit."""
+    half = int(bits != int(bits))
+    return wl.Workload(name=f"quality-k{bits:g}", batch=1, h_q=h_kv, h_kv=h_kv, n_tokens=n, in_dtype="f32",
+                       key_mse_bits=int(bits) - 1, key_half=half, value_kind="minmax", value_bits=2,
+                       scalar_dtype="f32", structure="iid", ring_cap=0, decode_steps=1, step_mode="none",
+                       seed=20270 + int(2 * bits))
 
 
 def _gpu_dequantized_keys(w: wl.Workload, keys: np.ndarray) -> list:
@@ -104,7 +108,7 @@ def test_recall_at_k():
     say("[recall@k] N=4096, 64 queries, keys and queries 0.1 N(0, I)")
     say(f"  {'bits':>4} " + " ".join(f"{'k=' + str(k):>7}" for k in (1, 4, 8, 16, 32, 64)))
     rec = {}
-    for bits in (2, 3, 4):
+    for bits in (2, 2.5, 3, 3.5, 4):
         kd = _gpu_dequantized_keys(_key_workload(bits, 1, n), keys)[0]
         est = queries @ kd.T
         row = []
@@ -114,9 +118,12 @@ def test_recall_at_k():
             r = float(np.mean([len(set(t[i]) & set(e[i])) / k for i in range(nq)]))
             rec[(bits, k)] = r
             row.append(r)
-        say(f"  {bits:>4} " + " ".join(f"{r:>7.3f}" for r in row))
-    # more bits rank better, and every width is far above chance (8 / 4096)
+        say(f"  {bits:>4g} " + " ".join(f"{r:>7.3f}" for r in row))
+    # more bits rank better (a whole bit apart; half a bit apart the 64
+    # queries' noise can reorder neighbours), and every width is far above
+    # chance (8 / 4096)
     assert rec[(2, 8)] < rec[(3, 8)] < rec[(4, 8)]
+    assert rec[(2.5, 8)] < rec[(3.5, 8)]
     assert rec[(2, 8)] > 0.1
 
 
@@ -130,16 +137,21 @@ def test_inner_product_distortion_and_bias():
     y /= np.linalg.norm(y, axis=-1, keepdims=True)
     exact = y @ x[:, 0].T
     say("[distortion] unit keys and queries, d=128: E(<y,x~>-<y,x>)^2 against sqrt(3) pi^2 / (d 4^b)")
-    for bits in (2, 3, 4):
+    mses = []
+    for bits in (2, 2.5, 3, 3.5, 4):
         kd = _gpu_dequantized_keys(_key_workload(bits, 1, n), x)[0]
         err = y @ kd.T - exact
         mse = float(np.mean(err ** 2))
         bound = np.sqrt(3) * np.pi ** 2 / (D * 4.0 ** bits)
         se = float(np.std(err) / np.sqrt(err.size))
-        say(f"  b={bits}: mse {mse:.3e}, bound {bound:.3e}, ratio {mse / bound:.2f}; mean error {np.mean(err):+.2e} "
-            f"(4 SE = {4 * se:.1e})")
-        assert mse <= bound
+        say(f"  b={bits:g}: mse {mse:.3e}, bound {bound:.3e}, ratio {mse / bound:.2f}; mean error "
+            f"{np.mean(err):+.2e} (4 SE = {4 * se:.1e})")
+        if bits == int(bits):  # the bound is stated for whole widths
+            assert mse <= bound
         assert abs(float(np.mean(err))) < 4 * se + 1e-6
+        mses.append(mse)
+    # every half bit lowers the distortion
+    assert all(a > b for a, b in zip(mses, mses[1:])), mses
 
 
 def _cosine(out, ref):
