@@ -238,7 +238,9 @@ __global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
     for (int ct = 0; ct < 2; ++ct) {
       const float s2 = row_sum4(ss[ct]);
       nrm[ct] = sqrtf(s2);
-      inv[ct] = nrm[ct] > 0.f ? 1.0f / nrm[ct] : 0.f;
+      // a zero vector gets y = -0: its sign bit puts every coordinate in the
+      // lower cell of the middle threshold, as #{t < 0} does
+      inv[ct] = nrm[ct] > 0.f ? 1.0f / nrm[ct] : -0.0f;
     }
 
     // ---- GEMM 1: Y = Pi K^T (row tile rt = coordinates 16rt..16rt+15); bucketing.
