@@ -233,19 +233,23 @@ def _flip_mask(w, bk, kp, ref):
     return idx_g != ref.key.idx
 
 
-def slot_from_cache(w: wl.Workload, cache: tq.Cache, b: int, h: int, n: int) -> SlotCode:
-    """The codes of device cache slot (b, h), positions 0..n-1, read back into
-    the oracle's code records (so the oracle can decode a GPU-encoded cache)."""
-    kp = cache.k_planes[b, h, :n].cpu().numpy()
+def slot_from_cache(w: wl.Workload, cache: tq.Cache, b: int, h: int, n: int, start: int = 0) -> SlotCode:
+    """The codes of device cache slot (b, h), positions start..start+n-1, read
+    back into the oracle's code records (so the oracle can decode a
+    GPU-encoded cache)."""
+    end = start + n
+    kp = cache.k_planes[b, h, start:end].cpu().numpy()
     idx, qjl = read_key_planes(kp, w.d, w.key_mse_bits, bool(w.key_qjl), bool(w.key_half))
-    norm = cache.k_norm[b, h, :n].float().cpu().double().numpy()
-    rnorm = cache.k_rnorm[b, h, :n].float().cpu().double().numpy() if w.key_qjl else None
+    norm = cache.k_norm[b, h, start:end].float().cpu().double().numpy()
+    rnorm = cache.k_rnorm[b, h, start:end].float().cpu().double().numpy() if w.key_qjl else None
     key = oracle.KeyCode(idx=idx, qjl=qjl, norm=norm, rnorm=rnorm, y=None, z=None)
-    codes = read_value_planes(cache.v_planes[b, h, :(n + 31) // 32].cpu().numpy(), n, w)
+    blk0, blk1 = start // 32, (end + 31) // 32
+    words = cache.v_planes[b, h, blk0:blk1].cpu().numpy()
+    codes = read_value_planes(words, (blk1 - blk0) * 32, w)[start - 32 * blk0:end - 32 * blk0]
     if w.value_kind == "minmax":
-        meta = cache.v_meta[b, h, :n].cpu().numpy()
+        meta = cache.v_meta[b, h, start:end].cpu().numpy()
         val = oracle.ValueMinMax(code=codes, scale16=meta[..., 0].copy(), min16=meta[..., 1].copy(), ratio=None)
     else:
-        vn = cache.v_norm[b, h, :n].float().cpu().double().numpy()
+        vn = cache.v_norm[b, h, start:end].float().cpu().double().numpy()
         val = oracle.ValueMSE(idx=codes, norm=vn, y=None)
     return SlotCode(key, val)
