@@ -790,7 +790,14 @@ hipError_t launch_scan_mfma(const DecodeArgs& a, hipStream_t st, TimedLaunch tl)
 template <int NHT>
 hipError_t dispatch_mfma(const DecodeArgs& a, int kb, int qjl, int vmse, int vb, hipStream_t st,
                          TimedLaunch tl) {
-  if (!qjl) return hipErrorNotSupported;
+  if (!qjl) {  // keys without the QJL bit (the MSE-only quantizer)
+    if (a.key_half) return hipErrorNotSupported;
+    if (kb == 2 && !vmse && vb == 2) return launch_scan_mfma<2, false, false, 2, NHT>(a, st, tl);
+    if (kb == 3 && !vmse && vb == 2) return launch_scan_mfma<4, false, false, 2, NHT>(a, st, tl);
+    if (kb == 2 && vmse && vb == 3) return launch_scan_mfma<2, false, true, 4, NHT>(a, st, tl);
+    if (kb == 3 && vmse && vb == 3) return launch_scan_mfma<4, false, true, 4, NHT>(a, st, tl);
+    return hipErrorNotSupported;
+  }
   if (a.key_half) {  // kb counts the half plane: 1 + 1/2 or 2 + 1/2 MSE bits
     if (kb == 2 && !vmse && vb == 2) return launch_scan_mfma<2, true, false, 2, NHT, true>(a, st, tl);
     if (kb == 3 && !vmse && vb == 2) return launch_scan_mfma<4, true, false, 2, NHT, true>(a, st, tl);
@@ -818,10 +825,11 @@ size_t mfma_workspace_bytes(int batch, int h_q, int group) {
 hipError_t launch_decode_mfma(const DecodeArgs& a, int key_mse_bits, int key_qjl, int value_mse,
                               int value_bits, int key_planes, int value_planes, hipStream_t stream,
                               TimedLaunch tl) {
-  // covered: QJL keys with 2- or 3-bit indices, 2-bit min/max values in groups
-  // of 32 or 3-bit MSE values, antisymmetric codebooks, up to 8 query heads per
-  // KV head
-  if (!key_qjl || (key_mse_bits != 2 && key_mse_bits != 3)) return hipErrorNotSupported;
+  // covered: keys with 2- or 3-bit indices (or 1.5 / 2.5 with QJL), with or
+  // without the QJL bit, 2-bit min/max values in groups of 32 or 3-bit MSE
+  // values, antisymmetric codebooks, up to 8 query heads per KV head
+  if (key_mse_bits != 2 && key_mse_bits != 3) return hipErrorNotSupported;
+  if (!key_qjl && a.key_half) return hipErrorNotSupported;
   if (key_planes != (1 << (key_mse_bits - 1))) return hipErrorNotSupported;
   if (value_mse) {
     if (value_bits != 3 || value_planes != 4) return hipErrorNotSupported;
@@ -831,7 +839,7 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int key_mse_bits, int key_qjl
   if (a.group > 8) return hipErrorNotSupported;
   const int nht = a.group > 4 ? 2 : 1;
   const int pm = 1 << (key_mse_bits - 1);
-  const int npl = pm + 1;
+  const int npl = pm + (key_qjl ? 1 : 0);
   if (nht == 1)
     hipLaunchKernelGGL(qprep_mfma_kernel<4>, dim3(a.batch * a.h_kv), dim3(256), 0, stream, a, pm, npl, nht);
   else

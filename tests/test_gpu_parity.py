@@ -171,8 +171,21 @@ def test_decode_layouts_outside_the_mfma_path():
     base = SMALL["batched_small"].replace(batch=2, n_tokens=300)
     _decode_case(base.replace(key_mse_bits=1, value_bits=4, value_group=16), [300, 200], [2, 0], "k1 v4 g16")
     _decode_case(base.replace(key_mse_bits=4, value_bits=1, value_group=64), [300, 5], [0, 1], "k4 v1 g64")
-    _decode_case(base.replace(key_qjl=0), [300, 256], [1, 1], "no qjl")
     _decode_case(SMALL["long_small"].replace(value_bits=2, n_tokens=300), [300], [0], "mse v2")
+
+
+@pytest.mark.parametrize("path", ["mfma", "generic"])
+def test_decode_keys_without_qjl(path, monkeypatch):
+    """MSE-only keys (no QJL bit), 2 and 3 index bits, with min/max and MSE
+    values, on both scan paths."""
+    if path == "generic":
+        monkeypatch.setenv("TQ_DECODE_PATH", "generic")
+    base = SMALL["batched_small"].replace(batch=2, n_tokens=300, key_qjl=0)
+    _decode_case(base, [300, 256], [1, 1], f"no qjl, 2-bit keys ({path})")
+    _decode_case(base.replace(key_mse_bits=3), [300, 77], [0, 3], f"no qjl, 3-bit keys ({path})")
+    mse = SMALL["long_small"].replace(n_tokens=300, key_qjl=0)
+    _decode_case(mse, [300], [0], f"no qjl, MSE values ({path})")
+    _decode_case(mse.replace(key_mse_bits=2), [211], [0], f"no qjl, 2-bit keys, MSE values ({path})")
 
 
 def test_decode_empty_sequence_gives_zero():
