@@ -792,6 +792,8 @@ hipError_t dispatch_mfma(const DecodeArgs& a, int kb, int qjl, int vmse, int vb,
                          TimedLaunch tl) {
   if (!qjl) {  // keys without the QJL bit (the MSE-only quantizer)
     if (a.key_half) return hipErrorNotSupported;
+    if (kb == 1 && !vmse && vb == 2) return launch_scan_mfma<1, false, false, 2, NHT>(a, st, tl);
+    if (kb == 1 && vmse && vb == 3) return launch_scan_mfma<1, false, true, 4, NHT>(a, st, tl);
     if (kb == 2 && !vmse && vb == 2) return launch_scan_mfma<2, false, false, 2, NHT>(a, st, tl);
     if (kb == 3 && !vmse && vb == 2) return launch_scan_mfma<4, false, false, 2, NHT>(a, st, tl);
     if (kb == 2 && vmse && vb == 3) return launch_scan_mfma<2, false, true, 4, NHT>(a, st, tl);
@@ -805,6 +807,8 @@ hipError_t dispatch_mfma(const DecodeArgs& a, int kb, int qjl, int vmse, int vb,
     if (kb == 3 && vmse && vb == 3) return launch_scan_mfma<4, true, true, 4, NHT, true>(a, st, tl);
     return hipErrorNotSupported;
   }
+  if (kb == 1 && !vmse && vb == 2) return launch_scan_mfma<1, true, false, 2, NHT>(a, st, tl);
+  if (kb == 1 && vmse && vb == 3) return launch_scan_mfma<1, true, true, 4, NHT>(a, st, tl);
   if (kb == 2 && !vmse && vb == 2) return launch_scan_mfma<2, true, false, 2, NHT>(a, st, tl);
   if (kb == 3 && !vmse && vb == 2) return launch_scan_mfma<4, true, false, 2, NHT>(a, st, tl);
   if (kb == 2 && vmse && vb == 3) return launch_scan_mfma<2, true, true, 4, NHT>(a, st, tl);
@@ -825,10 +829,10 @@ size_t mfma_workspace_bytes(int batch, int h_q, int group) {
 hipError_t launch_decode_mfma(const DecodeArgs& a, int key_mse_bits, int key_qjl, int value_mse,
                               int value_bits, int key_planes, int value_planes, hipStream_t stream,
                               TimedLaunch tl) {
-  // covered: keys with 2- or 3-bit indices (or 1.5 / 2.5 with QJL), with or
-  // without the QJL bit, 2-bit min/max values in groups of 32 or 3-bit MSE
+  // covered: keys with 1-, 2- or 3-bit indices (or 1.5 / 2.5 with QJL), with
+  // or without the QJL bit, 2-bit min/max values in groups of 32 or 3-bit MSE
   // values, antisymmetric codebooks, up to 8 query heads per KV head
-  if (key_mse_bits != 2 && key_mse_bits != 3) return hipErrorNotSupported;
+  if (key_mse_bits < 1 || key_mse_bits > 3) return hipErrorNotSupported;
   if (!key_qjl && a.key_half) return hipErrorNotSupported;
   if (key_planes != (1 << (key_mse_bits - 1))) return hipErrorNotSupported;
   if (value_mse) {

@@ -59,8 +59,8 @@
  *  - K/V inputs are [batch][n][h_kv][d] row-major; queries [batch][h_q][d];
  *    the bf16 ring is [batch][ring_cap][h_kv][d] for K and for V.  Query head
  *    hq reads KV head hq / (h_q / h_kv).
- *  - Kernel paths.  Decode runs the int8-MFMA scan for keys of 2 or 3 index
- *    bits with or without the QJL bit (or 1.5 / 2.5 index bits with QJL), with
+ *  - Kernel paths.  Decode runs the int8-MFMA scan for keys of 1, 2 or 3
+ *    index bits with or without the QJL bit (or 1.5 / 2.5 with QJL), with
  *    2-bit min/max values in groups of 32 or 3-bit MSE values, else a VALU
  *    scan; environment variable
  *    TQ_DECODE_PATH=generic forces the VALU scan.  Encode of at most 4 new

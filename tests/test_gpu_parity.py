@@ -175,6 +175,19 @@ def test_decode_layouts_outside_the_mfma_path():
 
 
 @pytest.mark.parametrize("path", ["mfma", "generic"])
+def test_decode_one_bit_keys(path, monkeypatch):
+    """1-bit key indices (TurboQuantProd(2) and the 1-bit MSE-only keys), with
+    min/max and MSE values, on both scan paths."""
+    if path == "generic":
+        monkeypatch.setenv("TQ_DECODE_PATH", "generic")
+    base = SMALL["batched_small"].replace(batch=2, n_tokens=300, key_mse_bits=1)
+    _decode_case(base, [300, 190], [2, 0], f"1+1-bit keys ({path})")
+    _decode_case(base.replace(key_qjl=0), [300, 64], [0, 1], f"1-bit keys, no qjl ({path})")
+    mse = SMALL["long_small"].replace(n_tokens=300, key_mse_bits=1)
+    _decode_case(mse, [300], [0], f"1+1-bit keys, MSE values ({path})")
+
+
+@pytest.mark.parametrize("path", ["mfma", "generic"])
 def test_decode_keys_without_qjl(path, monkeypatch):
     """MSE-only keys (no QJL bit), 2 and 3 index bits, with min/max and MSE
     values, on both scan paths."""
