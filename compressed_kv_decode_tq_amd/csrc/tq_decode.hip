@@ -431,14 +431,14 @@ __global__ __launch_bounds__(kD) void combine_kernel(DecodeArgs a) {
     }
     A = o;
   }
-  // ring values (original space)
-  for (int j0 = 0; j0 < nr; j0 += 8) {
-    float v[8];
+  // ring values (original space), 32 loads in flight per round
+  for (int j0 = 0; j0 < nr; j0 += 32) {
+    float v[32];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < 32; ++u)
       v[u] = j0 + u < nr ? bf2f(a.ring_v[(((size_t)b * a.ring_cap + j0 + u) * a.h_kv + h) * kD + c]) : 0.f;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) A = fmaf(j0 + u < nr ? pr[j0 + u] : 0.f, v[u], A);
+    for (int u = 0; u < 32; ++u) A = fmaf(j0 + u < nr ? pr[j0 + u] : 0.f, v[u], A);
   }
   outp[c] = L > 0.f ? A / L : 0.f;
 }
