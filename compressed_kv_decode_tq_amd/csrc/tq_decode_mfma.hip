@@ -546,7 +546,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
     // row); alpha rescales the running sums.  p goes to LDS for the value MFMA,
     // for min/max values as p 2^c with c = ev - 2 min(n/4, 2): token 16ct + n
     // is in slot n/4 of its packed code word, whose bytes carry 4^min(n/4, 2)
-    const int c_p = VMSE ? 0 : ev_mm - ((n >> 2) < 2 ? 2 * (n >> 2) : 4);
+    // (4-bit codes: every slot is one whole code per byte, no scale)
+    const int c_p = VMSE ? 0 : (VB == 4 ? ev_mm : ev_mm - ((n >> 2) < 2 ? 2 * (n >> 2) : 4));
     float alpha[NHT];
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
@@ -573,7 +574,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
 
     // ---- values
     if (!VMSE) {
-      static_assert(VMSE || VB == 2, "min/max values on this path are 2-bit packed codes");
+      static_assert(VMSE || VB == 2 || VB == 4, "min/max values on this path are 2- or 4-bit packed codes");
       // Rows of the value MFMA are (head 4ht + n/4, group n%4) and this lane
       // supplies tokens 16g + 4k + r (k, r < 4): the tokens of the packed code
       // word g of the chunk, whose AND with 0x03 << 2k (k < 3), or with 0x30
@@ -621,7 +622,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
         // sum_t p_t min_t per (head, group), the slot scales 2^(ev - 2 min(k, 2))
         // undone: reduce over the four token quarters, then fetch (head g,
         // group gi) for the value layout
-        const float x = col_sum4(ldexpf(fmaf(Mk[0], 1.f, fmaf(Mk[1], 4.f, 16.f * (Mk[2] + Mk[3]))), -ev_mm));
+        const float x = VB == 4 ? col_sum4(ldexpf((Mk[0] + Mk[1]) + (Mk[2] + Mk[3]), -ev_mm))
+                                : col_sum4(ldexpf(fmaf(Mk[0], 1.f, fmaf(Mk[1], 4.f, 16.f * (Mk[2] + Mk[3]))), -ev_mm));
         float Mpv[NG];
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) Mpv[gi] = __shfl(x, 4 * g + gi);
@@ -645,8 +647,17 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) {
           const int gi = nt >> 1;  // group of channels 16nt..16nt+15
-          const uint32_t w = s_vw[g * (kD + kVwPad) + 16 * nt + n];
-          const u32x4 B = {w & 0x03030303u, w & 0x0c0c0c0cu, w & 0x30303030u, (w >> 2) & 0x30303030u};
+          u32x4 B;
+          if (VB == 4) {
+            // 4-bit codes: tokens 16g..16g+15 are the staged rows 2g and 2g+1
+            // (eight tokens each); token i of a word sits in byte i%4, nibble i/4
+            const uint32_t w0 = s_vw[(2 * g) * (kD + kVwPad) + 16 * nt + n];
+            const uint32_t w1 = s_vw[(2 * g + 1) * (kD + kVwPad) + 16 * nt + n];
+            B = u32x4{w0 & 0x0f0f0f0fu, (w0 >> 4) & 0x0f0f0f0fu, w1 & 0x0f0f0f0fu, (w1 >> 4) & 0x0f0f0f0fu};
+          } else {
+            const uint32_t w = s_vw[g * (kD + kVwPad) + 16 * nt + n];
+            B = u32x4{w & 0x03030303u, w & 0x0c0c0c0cu, w & 0x30303030u, (w >> 2) & 0x30303030u};
+          }
           // rows (head g, digit r) of group gi: element r is digit r's product
           const i32x4 C = mfma_i8(AG[gi], B, i32x4{0, 0, 0, 0});
           const float v = fmaf((float)((C[0] << 8) + C[1]), 65536.f, (float)((C[2] << 8) + C[3]));
@@ -793,24 +804,32 @@ hipError_t dispatch_mfma(const DecodeArgs& a, int kb, int qjl, int vmse, int vb,
   if (!qjl) {  // keys without the QJL bit (the MSE-only quantizer)
     if (a.key_half) return hipErrorNotSupported;
     if (kb == 1 && !vmse && vb == 2) return launch_scan_mfma<1, false, false, 2, NHT>(a, st, tl);
+    if (kb == 1 && !vmse && vb == 4) return launch_scan_mfma<1, false, false, 4, NHT>(a, st, tl);
     if (kb == 1 && vmse && vb == 3) return launch_scan_mfma<1, false, true, 4, NHT>(a, st, tl);
     if (kb == 2 && !vmse && vb == 2) return launch_scan_mfma<2, false, false, 2, NHT>(a, st, tl);
+    if (kb == 2 && !vmse && vb == 4) return launch_scan_mfma<2, false, false, 4, NHT>(a, st, tl);
     if (kb == 3 && !vmse && vb == 2) return launch_scan_mfma<4, false, false, 2, NHT>(a, st, tl);
+    if (kb == 3 && !vmse && vb == 4) return launch_scan_mfma<4, false, false, 4, NHT>(a, st, tl);
     if (kb == 2 && vmse && vb == 3) return launch_scan_mfma<2, false, true, 4, NHT>(a, st, tl);
     if (kb == 3 && vmse && vb == 3) return launch_scan_mfma<4, false, true, 4, NHT>(a, st, tl);
     return hipErrorNotSupported;
   }
   if (a.key_half) {  // kb counts the half plane: 1 + 1/2 or 2 + 1/2 MSE bits
     if (kb == 2 && !vmse && vb == 2) return launch_scan_mfma<2, true, false, 2, NHT, true>(a, st, tl);
+    if (kb == 2 && !vmse && vb == 4) return launch_scan_mfma<2, true, false, 4, NHT, true>(a, st, tl);
     if (kb == 3 && !vmse && vb == 2) return launch_scan_mfma<4, true, false, 2, NHT, true>(a, st, tl);
+    if (kb == 3 && !vmse && vb == 4) return launch_scan_mfma<4, true, false, 4, NHT, true>(a, st, tl);
     if (kb == 2 && vmse && vb == 3) return launch_scan_mfma<2, true, true, 4, NHT, true>(a, st, tl);
     if (kb == 3 && vmse && vb == 3) return launch_scan_mfma<4, true, true, 4, NHT, true>(a, st, tl);
     return hipErrorNotSupported;
   }
   if (kb == 1 && !vmse && vb == 2) return launch_scan_mfma<1, true, false, 2, NHT>(a, st, tl);
+  if (kb == 1 && !vmse && vb == 4) return launch_scan_mfma<1, true, false, 4, NHT>(a, st, tl);
   if (kb == 1 && vmse && vb == 3) return launch_scan_mfma<1, true, true, 4, NHT>(a, st, tl);
   if (kb == 2 && !vmse && vb == 2) return launch_scan_mfma<2, true, false, 2, NHT>(a, st, tl);
+  if (kb == 2 && !vmse && vb == 4) return launch_scan_mfma<2, true, false, 4, NHT>(a, st, tl);
   if (kb == 3 && !vmse && vb == 2) return launch_scan_mfma<4, true, false, 2, NHT>(a, st, tl);
+  if (kb == 3 && !vmse && vb == 4) return launch_scan_mfma<4, true, false, 4, NHT>(a, st, tl);
   if (kb == 2 && vmse && vb == 3) return launch_scan_mfma<2, true, true, 4, NHT>(a, st, tl);
   if (kb == 3 && vmse && vb == 3) return launch_scan_mfma<4, true, true, 4, NHT>(a, st, tl);
   return hipErrorNotSupported;
@@ -830,14 +849,14 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int key_mse_bits, int key_qjl
                               int value_bits, int key_planes, int value_planes, hipStream_t stream,
                               TimedLaunch tl) {
   // covered: keys with 1-, 2- or 3-bit indices (or 1.5 / 2.5 with QJL), with
-  // or without the QJL bit, 2-bit min/max values in groups of 32 or 3-bit MSE
-  // values, antisymmetric codebooks, up to 8 query heads per KV head
+  // or without the QJL bit, 2- or 4-bit min/max values in groups of 32 or
+  // 3-bit MSE values, antisymmetric codebooks, up to 8 query heads per KV head
   if (key_mse_bits < 1 || key_mse_bits > 3) return hipErrorNotSupported;
   if (!key_qjl && a.key_half) return hipErrorNotSupported;
   if (key_planes != (1 << (key_mse_bits - 1))) return hipErrorNotSupported;
   if (value_mse) {
     if (value_bits != 3 || value_planes != 4) return hipErrorNotSupported;
-  } else if (value_bits != 2 || a.value_group != 32) {
+  } else if ((value_bits != 2 && value_bits != 4) || a.value_group != 32) {
     return hipErrorNotSupported;
   }
   if (a.group > 8) return hipErrorNotSupported;

@@ -14,7 +14,7 @@ import oracle
 from compressed_kv_decode_tq_amd import tq
 from compressed_kv_decode_tq_amd import workloads as wl
 from tq_testlib import (OUT_RTOL, books, check_encode_slot, dequant_slot, encode_slot, key_plane_mismatches,
-                        layout_of, max_rel_err, read_value_planes, say, upload_slot)
+                        layout_of, max_rel_err, read_value_planes, say, slot_from_cache, upload_slot)
 
 pytestmark = pytest.mark.gpu
 
@@ -172,6 +172,53 @@ def test_decode_layouts_outside_the_mfma_path():
     _decode_case(base.replace(key_mse_bits=1, value_bits=4, value_group=16), [300, 200], [2, 0], "k1 v4 g16")
     _decode_case(base.replace(key_mse_bits=4, value_bits=1, value_group=64), [300, 5], [0, 1], "k4 v1 g64")
     _decode_case(SMALL["long_small"].replace(value_bits=2, n_tokens=300), [300], [0], "mse v2")
+
+
+@pytest.mark.parametrize("path", ["mfma", "generic"])
+def test_decode_four_bit_minmax_values(path, monkeypatch):
+    """4-bit min/max values in groups of 32 (packed, eight tokens per word),
+    with 2+1-, 3+1- and 3.5-bit keys, on both scan paths (the generic scan has
+    no half-bit keys)."""
+    if path == "generic":
+        monkeypatch.setenv("TQ_DECODE_PATH", "generic")
+    base = SMALL["batched_small"].replace(batch=2, n_tokens=300, value_bits=4)
+    _decode_case(base, [300, 133], [3, 0], f"4-bit values ({path})")
+    _decode_case(base.replace(key_mse_bits=3), [300, 64], [0, 2], f"3+1-bit keys, 4-bit values ({path})")
+    if path == "mfma":
+        _decode_case(base.replace(key_half=1), [257, 300], [1, 0], "3.5-bit keys, 4-bit values (mfma)")
+
+
+def test_four_bit_minmax_values_end_to_end():
+    """GPU encode of 4-bit min/max values (packed words) then GPU decode,
+    against the oracle decoding the GPU's codes."""
+    w = SMALL["batched_small"].replace(batch=2, n_tokens=320, value_bits=4)
+    bk = books(w)
+    pi, s, prm = _params(w)
+    k, v = wl.prefill_kv(w)
+    cache = tq.Cache(layout_of(w), w.batch, w.h_kv, 320, device=DEV)
+    tq.encode_kv(prm, k.to(DEV), v.to(DEV), [0] * w.batch, cache)
+    n_comp = [320, 201]
+    tot = np.zeros(3, dtype=np.int64)
+    for b in range(w.batch):
+        for h in range(w.h_kv):
+            ref = encode_slot(w, bk, pi, s, k[b, :, h].double().numpy(), v[b, :, h].double().numpy())
+            tot += check_encode_slot(w, bk, cache, b, h, ref, 0, w.n_tokens, f"4-bit values b{b} h{h}")
+    q = wl.query(w)
+    out = tq.decode_attn(prm, q.to(DEV), cache, n_comp)
+    torch.cuda.synchronize()
+    kd, vd = [], []
+    for b in range(w.batch):
+        kr, vr = [], []
+        for h in range(w.h_kv):
+            a_, c_ = dequant_slot(w, bk, pi, s, slot_from_cache(w, cache, b, h, n_comp[b]))
+            kr.append(a_)
+            vr.append(c_)
+        kd.append(kr)
+        vd.append(vr)
+    ref = oracle.decode_attention(q.double().numpy(), kd, vd)
+    err = max_rel_err(out.cpu().double().numpy(), ref)
+    say(f"[4-bit values end to end] codes match (excused {tot.tolist()}); decode max rel err {err.max():.2e}")
+    assert err.max() <= OUT_RTOL
 
 
 @pytest.mark.parametrize("path", ["mfma", "generic"])
