@@ -832,6 +832,8 @@ hipError_t dispatch_mfma(const DecodeArgs& a, int kb, int qjl, int vmse, int vb,
   if (kb == 3 && !vmse && vb == 4) return launch_scan_mfma<4, true, false, 4, NHT>(a, st, tl);
   if (kb == 2 && vmse && vb == 3) return launch_scan_mfma<2, true, true, 4, NHT>(a, st, tl);
   if (kb == 3 && vmse && vb == 3) return launch_scan_mfma<4, true, true, 4, NHT>(a, st, tl);
+  if (kb == 2 && vmse && vb == 2) return launch_scan_mfma<2, true, true, 2, NHT>(a, st, tl);
+  if (kb == 3 && vmse && vb == 2) return launch_scan_mfma<4, true, true, 2, NHT>(a, st, tl);
   return hipErrorNotSupported;
 }
 
@@ -850,12 +852,14 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int key_mse_bits, int key_qjl
                               TimedLaunch tl) {
   // covered: keys with 1-, 2- or 3-bit indices (or 1.5 / 2.5 with QJL), with
   // or without the QJL bit, 2- or 4-bit min/max values in groups of 32 or
-  // 3-bit MSE values, antisymmetric codebooks, up to 8 query heads per KV head
+  // 3-bit MSE values (2-bit MSE values with 2+1- and 3+1-bit keys),
+  // antisymmetric codebooks, up to 8 query heads per KV head
   if (key_mse_bits < 1 || key_mse_bits > 3) return hipErrorNotSupported;
   if (!key_qjl && a.key_half) return hipErrorNotSupported;
   if (key_planes != (1 << (key_mse_bits - 1))) return hipErrorNotSupported;
   if (value_mse) {
-    if (value_bits != 3 || value_planes != 4) return hipErrorNotSupported;
+    if ((value_bits != 2 && value_bits != 3) || value_planes != (1 << (value_bits - 1))) return hipErrorNotSupported;
+    if (value_bits == 2 && (!key_qjl || a.key_half || key_mse_bits < 2)) return hipErrorNotSupported;
   } else if ((value_bits != 2 && value_bits != 4) || a.value_group != 32) {
     return hipErrorNotSupported;
   }

@@ -61,8 +61,9 @@
  *    hq reads KV head hq / (h_q / h_kv).
  *  - Kernel paths.  Decode runs the int8-MFMA scan for keys of 1, 2 or 3
  *    index bits with or without the QJL bit (or 1.5 / 2.5 with QJL), with
- *    2- or 4-bit min/max values in groups of 32 or 3-bit MSE values, else a
- *    VALU scan; environment variable
+ *    2- or 4-bit min/max values in groups of 32 or 3-bit MSE values (and
+ *    2-bit MSE values with 2+1- or 3+1-bit keys), else a VALU scan;
+ *    environment variable
  *    TQ_DECODE_PATH=generic forces the VALU scan.  Encode of at most 4 new
  *    tokens per sequence runs a few-token fp32 kernel, else the MFMA rotation
  *    kernels; TQ_ENCODE_PATH=small or =mfma forces one.  All paths compute the

@@ -171,7 +171,18 @@ def test_decode_layouts_outside_the_mfma_path():
     base = SMALL["batched_small"].replace(batch=2, n_tokens=300)
     _decode_case(base.replace(key_mse_bits=1, value_bits=4, value_group=16), [300, 200], [2, 0], "k1 v4 g16")
     _decode_case(base.replace(key_mse_bits=4, value_bits=1, value_group=64), [300, 5], [0, 1], "k4 v1 g64")
-    _decode_case(SMALL["long_small"].replace(value_bits=2, n_tokens=300), [300], [0], "mse v2")
+    _decode_case(SMALL["long_small"].replace(value_bits=2, key_mse_bits=1, n_tokens=300), [300], [0], "k1 mse v2")
+
+
+@pytest.mark.parametrize("path", ["mfma", "generic"])
+def test_decode_two_bit_mse_values(path, monkeypatch):
+    """2-bit MSE values (two value planes) with 2+1- and 3+1-bit keys, on both
+    scan paths."""
+    if path == "generic":
+        monkeypatch.setenv("TQ_DECODE_PATH", "generic")
+    w = SMALL["long_small"].replace(value_bits=2, n_tokens=300)
+    _decode_case(w, [300], [0], f"3+1-bit keys, 2-bit MSE values ({path})")
+    _decode_case(w.replace(key_mse_bits=2, batch=2), [300, 97], [0, 0], f"2+1-bit keys, 2-bit MSE values ({path})")
 
 
 @pytest.mark.parametrize("path", ["mfma", "generic"])
