@@ -335,8 +335,12 @@ __device__ __forceinline__ float block2_max(float x, float* red2) {
 }
 
 // Merge of the split partials (m, l, acc) of one (sequence, query head) with
-// the exact ring tokens; MSE values are rotated back with Pi^T once.  Loads
-// are batched so the merge costs a few memory round trips, not one per split.
+// the exact ring tokens; MSE values are rotated back with Pi^T once.  Every
+// load that needs no earlier result (split headers, the first 16 splits' acc
+// words, the ring key row, the first 32 ring values) is issued before the
+// first use, so the merge costs about one memory round trip.
+constexpr int kCombinePre = 16;   // splits whose acc word is loaded up front
+constexpr int kRingPre = 32;      // ring values loaded up front
 template <bool VMSE>
 __global__ __launch_bounds__(kD) void combine_kernel(DecodeArgs a) {
   __shared__ float qv[kD];
@@ -351,17 +355,44 @@ __global__ __launch_bounds__(kD) void combine_kernel(DecodeArgs a) {
   int t, hq, hide_c, hide_r;
   virtual_head(a, h, gq, t, hq);
   const int c = threadIdx.x;
-  const size_t qoff = q_row(a, b, t, hq) * kD + c;
-  qv[c] = a.q_bf16 ? bf2f(reinterpret_cast<const uint16_t*>(a.q)[qoff]) : reinterpret_cast<const float*>(a.q)[qoff];
   hidden_keys(a, t, (int)a.n_ring.v[b], hide_c, hide_r);
   const int nr = (int)a.n_ring.v[b] - hide_r;  // ring tokens this query sees
   const int S = a.splits;
   const float* part0 = a.partial + ws_row(a, b, h, gq) * (kD + 2);
   const size_t sstride = (size_t)a.batch * rows * (kD + 2);
+  const size_t ring_row = (size_t)b * a.ring_cap * a.h_kv + h;  // ring token j: (ring_row + j h_kv) kD
 
-  // split headers (m, l): thread c takes splits c, c + 128, ...
-  float M = -INFINITY;
-  for (int sp = c; sp < S; sp += kD) {
+  // ---- loads
+  const size_t qoff = q_row(a, b, t, hq) * kD + c;
+  const float qc = a.q_bf16 ? bf2f(reinterpret_cast<const uint16_t*>(a.q)[qoff])
+                            : reinterpret_cast<const float*>(a.q)[qoff];
+  float hm = -INFINITY, hl = 0.f;  // header of split c (thread c < S)
+  if (c < S) {
+    hm = part0[(size_t)c * sstride];
+    hl = part0[(size_t)c * sstride + 1];
+  }
+  float pa[kCombinePre];
+#pragma unroll
+  for (int u = 0; u < kCombinePre; ++u) pa[u] = u < S ? part0[(size_t)u * sstride + 2 + c] : 0.f;
+  u32x4 kw[kD / 8];  // thread j's ring token key row (256 bytes)
+  if (c < nr) {
+    const u32x4* kr = reinterpret_cast<const u32x4*>(a.ring_k + (ring_row + (size_t)c * a.h_kv) * kD);
+#pragma unroll
+    for (int i = 0; i < kD / 8; ++i) kw[i] = kr[i];
+  }
+  float rv[kRingPre];
+#pragma unroll
+  for (int u = 0; u < kRingPre; ++u)
+    rv[u] = u < nr ? bf2f(a.ring_v[(ring_row + (size_t)u * a.h_kv) * kD + c]) : 0.f;
+
+  // ---- split headers (m, l): thread c takes splits c, c + 128, ...
+  qv[c] = qc;
+  float M = hm;
+  if (c < S) {
+    s_f[c] = hm;
+    s_l[c] = hl;
+  }
+  for (int sp = c + kD; sp < S; sp += kD) {
     const float* ph = part0 + (size_t)sp * sstride;
     const float m = ph[0], l = ph[1];
     s_f[sp] = m;
@@ -370,13 +401,9 @@ __global__ __launch_bounds__(kD) void combine_kernel(DecodeArgs a) {
   }
   __syncthreads();  // qv
 
-  // ring scores: thread j scores ring token j (its 256-byte key row in 16 loads)
+  // ring scores: thread j scores ring token j
   float sj = -INFINITY;
   if (c < nr) {
-    const u32x4* kr = reinterpret_cast<const u32x4*>(a.ring_k + (((size_t)b * a.ring_cap + c) * a.h_kv + h) * kD);
-    u32x4 kw[kD / 8];
-#pragma unroll
-    for (int i = 0; i < kD / 8; ++i) kw[i] = kr[i];
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < kD / 8; ++i)
@@ -406,9 +433,13 @@ __global__ __launch_bounds__(kD) void combine_kernel(DecodeArgs a) {
   pr[c] = pj;
   const float L = block2_sum(Lp + pj, red2);  // its barriers also publish s_f and pr
 
-  // channel c: sum over splits of f_s acc_s[c], eight partial loads in flight
+  // channel c: sum over splits of f_s acc_s[c]; splits past the first
+  // kCombinePre are loaded eight at a time
   float A = 0.f;
-  int sp = 0;
+#pragma unroll
+  for (int u = 0; u < kCombinePre; ++u)
+    if (u < S) A = fmaf(s_f[u], pa[u], A);
+  int sp = kCombinePre;
   for (; sp + 8 <= S; sp += 8) {
     float v[8];
 #pragma unroll
@@ -431,12 +462,15 @@ __global__ __launch_bounds__(kD) void combine_kernel(DecodeArgs a) {
     }
     A = o;
   }
-  // ring values (original space), 32 loads in flight per round
-  for (int j0 = 0; j0 < nr; j0 += 32) {
+  // ring values (original space): the first kRingPre are in registers, the
+  // rest come 32 loads at a time
+#pragma unroll
+  for (int u = 0; u < kRingPre; ++u) A = fmaf(u < nr ? pr[u] : 0.f, rv[u], A);
+  for (int j0 = kRingPre; j0 < nr; j0 += 32) {
     float v[32];
 #pragma unroll
     for (int u = 0; u < 32; ++u)
-      v[u] = j0 + u < nr ? bf2f(a.ring_v[(((size_t)b * a.ring_cap + j0 + u) * a.h_kv + h) * kD + c]) : 0.f;
+      v[u] = j0 + u < nr ? bf2f(a.ring_v[(ring_row + (size_t)(j0 + u) * a.h_kv) * kD + c]) : 0.f;
 #pragma unroll
     for (int u = 0; u < 32; ++u) A = fmaf(j0 + u < nr ? pr[j0 + u] : 0.f, v[u], A);
   }

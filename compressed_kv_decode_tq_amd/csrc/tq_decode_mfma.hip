@@ -105,15 +105,20 @@ __device__ __forceinline__ void digits128(int q, int d[4]) {
 // (g, n), 16 bytes: byte 4d + j holds digit n%4 of head 4ht + n/4 at
 // coordinate k = 32g + 8j + 4hf + d, pre-scaled by 2^-(k%8) (negated for
 // k%8 == 7).  Plane pl < PM multiplies w_pl * (Pi q); plane PM (QJL) 2 * (S q).
+// The two products are independent down to their digits: work-group (b h, 0)
+// makes the PM index planes from Pi q (and appends the ring token), (b h, 1)
+// the QJL plane from S q.
 template <int MAXG>
 __global__ __launch_bounds__(256) void qprep_mfma_kernel(DecodeArgs a, int pm, int npl, int nht) {
-  __shared__ float qv[kMaxGroup][kD];
-  __shared__ float qr[kMaxGroup][kD];
-  __shared__ float qs[kMaxGroup][kD];
-  __shared__ int e_mse[kMaxGroup], e_qjl[kMaxGroup];
+  constexpr int NQ = MAXG / 4;               // float4 groups of heads per coordinate
+  __shared__ floatx4 qt[kD][NQ];             // queries, coordinate-major: qt[j][gq/4][gq%4]
+  __shared__ float qx[kMaxGroup][kD];        // this part's product (Pi q or S q)
+  __shared__ float red[kMaxGroup][kD];       // upper-half partial sums of the product
+  __shared__ int e_head[kMaxGroup];
   const int b = blockIdx.x / a.h_kv, h = blockIdx.x % a.h_kv;
+  const int part = blockIdx.y;               // 0: Pi q, index planes; 1: S q, QJL plane
   const int G = a.group;
-  if (a.app_k && a.vbase == 0) {
+  if (part == 0 && a.app_k && a.vbase == 0) {
     // fused ring append: threads 0..127 write the key row, 128..255 the value
     // row of this (sequence, KV head), rounded to bf16 as the ring append does
     const int c = threadIdx.x & (kD - 1), which = threadIdx.x >> 7;
@@ -124,7 +129,19 @@ __global__ __launch_bounds__(256) void qprep_mfma_kernel(DecodeArgs a, int pm, i
     ring[dst] = a.app_bf16 ? reinterpret_cast<const uint16_t*>(in)[src]
                            : (uint16_t)f2bf(reinterpret_cast<const float*>(in)[src]);
   }
-  for (int i = threadIdx.x; i < kMaxGroup * kD; i += blockDim.x) {
+  // thread (hj, i): coordinates j of half hj of row i of the product; column
+  // j of the matrix is row j of its transpose, so consecutive threads read
+  // consecutive words.  The 64 matrix loads go out before the queries are
+  // staged, so both round trips overlap.
+  const int i_row = threadIdx.x & (kD - 1);
+  const int hj = threadIdx.x >> 7;
+  float w[kD / 2];
+  {
+    const float* mt = a.mat_t + (size_t)part * kD * kD + (size_t)(hj * (kD / 2)) * kD + i_row;
+#pragma unroll
+    for (int j = 0; j < kD / 2; ++j) w[j] = mt[(size_t)j * kD];
+  }
+  for (int i = threadIdx.x; i < MAXG * kD; i += blockDim.x) {
     const int gq = i / kD, c = i % kD;
     float x = 0.f;
     if (gq < G) {
@@ -133,98 +150,95 @@ __global__ __launch_bounds__(256) void qprep_mfma_kernel(DecodeArgs a, int pm, i
       const size_t off = q_row(a, b, t, hq) * kD + c;
       x = a.q_bf16 ? bf2f(reinterpret_cast<const uint16_t*>(a.q)[off]) : reinterpret_cast<const float*>(a.q)[off];
     }
-    qv[gq][c] = x;
+    reinterpret_cast<float*>(&qt[c][gq >> 2])[gq & 3] = x;
   }
   __syncthreads();
   {
-    // thread (which, i): row i of Pi q (which 0) or S q (which 1) for every
-    // head; column j of the matrix is row j of its transpose, so consecutive
-    // threads read consecutive words
-    const int i = threadIdx.x & (kD - 1);
-    const int which = threadIdx.x >> 7;
-    const float* mt = a.mat_t + (size_t)which * kD * kD + i;
-    // all 128 loads are issued before the first use: one memory round trip
-    float w[kD];
-#pragma unroll
-    for (int j = 0; j < kD; ++j) w[j] = mt[(size_t)j * kD];
-    __builtin_amdgcn_sched_barrier(0);  // no use moves above the loads
+    const int i = i_row;
     float acc[MAXG];
 #pragma unroll
     for (int gq = 0; gq < MAXG; ++gq) acc[gq] = 0.f;
 #pragma unroll
-    for (int j = 0; j < kD; ++j)
+    for (int j = 0; j < kD / 2; ++j)
 #pragma unroll
-      for (int gq = 0; gq < MAXG; ++gq) acc[gq] = fmaf(w[j], qv[gq][j], acc[gq]);
+      for (int u = 0; u < NQ; ++u) {
+        const floatx4 qj = qt[hj * (kD / 2) + j][u];
 #pragma unroll
-    for (int gq = 0; gq < MAXG; ++gq) (which == 0 ? qr : qs)[gq][i] = acc[gq];
+        for (int e = 0; e < 4; ++e) acc[4 * u + e] = fmaf(w[j], qj[e], acc[4 * u + e]);
+      }
+#pragma unroll
+    for (int gq = 0; gq < MAXG; ++gq) (hj ? red : qx)[gq][i] = acc[gq];
   }
   __syncthreads();
-  // per-head exponents and constants: one wave per head
+  for (int i = threadIdx.x; i < MAXG * kD; i += blockDim.x) qx[i / kD][i % kD] += red[i / kD][i % kD];
+  __syncthreads();
+  // per-head exponent and constants: one wave per head
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   for (int gq = wv; gq < MAXG; gq += 4) {
     // sr: sum of q_rot over the coordinates of the base table; srh over the
-    // half-bit coordinates (i mod 32 < 16) of the fractional layout
-    float mr = 0.f, ms = 0.f, sr = 0.f, srh = 0.f, ssum = 0.f;
+    // half-bit coordinates (i mod 32 < 16) of the fractional layout; for the
+    // QJL part, sr is sum(q_s)
+    float mx = 0.f, sr = 0.f, srh = 0.f;
     for (int c = lane; c < kD; c += 64) {
-      mr = fmaxf(mr, fabsf(qr[gq][c]));
-      ms = fmaxf(ms, fabsf(qs[gq][c]));
-      if (a.key_half && (c & 31) < 16)
-        srh += qr[gq][c];
+      const float x = qx[gq][c];
+      mx = fmaxf(mx, fabsf(x));
+      if (part == 0 && a.key_half && (c & 31) < 16)
+        srh += x;
       else
-        sr += qr[gq][c];
-      ssum += qs[gq][c];
+        sr += x;
     }
-    mr = wave_max(mr);
-    ms = wave_max(ms);
+    mx = wave_max(mx);
     sr = wave_sum(sr);
     srh = wave_sum(srh);
-    ssum = wave_sum(ssum);
-    float wmax = 0.f;
-    for (int p = 0; p < pm; ++p) wmax = fmaxf(wmax, fmaxf(fabsf(a.key_w[p]), fabsf(a.key_w_hi[p])));
-    int ex_r, ex_s;
-    frexpf(mr * wmax, &ex_r);  // |w_p q_rot| < 2^ex_r
-    frexpf(2.f * ms, &ex_s);
-    const int er = 26 - ex_r, es = 26 - ex_s;  // scaled values stay below 2^26
+    int ex;
+    if (part == 0) {
+      float wmax = 0.f;
+      for (int p = 0; p < pm; ++p) wmax = fmaxf(wmax, fmaxf(fabsf(a.key_w[p]), fabsf(a.key_w_hi[p])));
+      frexpf(mx * wmax, &ex);  // |w_p q_rot| < 2^ex
+    } else {
+      frexpf(2.f * mx, &ex);
+    }
+    const int e = 26 - ex;  // scaled values stay below 2^26
     if (lane == 0) {
-      e_mse[gq] = er;
-      e_qjl[gq] = es;
+      e_head[gq] = e;
       if (gq < G) {
         float* cst = a.qconst + ws_row(a, b, h, gq) * 4;
-        cst[0] = a.key_cst * sr + a.key_cst_hi * srh;  // constant part of <q_rot, c[idx]>
-        cst[1] = ldexpf(1.f, -er);   // digit scale of the MSE planes
-        cst[2] = ldexpf(1.f, -es);   // digit scale of the QJL plane
-        cst[3] = ssum;               // sum(q_s)
+        if (part == 0) {
+          cst[0] = a.key_cst * sr + a.key_cst_hi * srh;  // constant part of <q_rot, c[idx]>
+          cst[1] = ldexpf(1.f, -e);                      // digit scale of the MSE planes
+          if (npl == pm) cst[2] = cst[3] = 0.f;          // no QJL plane
+        } else {
+          cst[2] = ldexpf(1.f, -e);  // digit scale of the QJL plane
+          cst[3] = sr;               // sum(q_s)
+        }
       }
     }
   }
   __syncthreads();
-  const int ndw = nht * npl * 2 * 64 * 4;  // dwords of digit operands for this (sequence, KV head)
-  uint32_t* out = reinterpret_cast<uint32_t*>(a.qdig) + (size_t)(b * a.h_kv + h) * ndw;
+  // this part's planes: pl < pm (part 0) or pl == pm (part 1), for every head tile
+  const int ppl = part == 0 ? pm : 1;        // planes of this part
+  const int ndw = nht * ppl * 2 * 64 * 4;    // their digit dwords
+  uint32_t* out = reinterpret_cast<uint32_t*>(a.qdig) + (size_t)(b * a.h_kv + h) * (nht * npl * 2 * 64 * 4);
   for (int i = threadIdx.x; i < ndw; i += blockDim.x) {
     const int d = i & 3;
     const int ln = (i >> 2) & 63;
     const int hf = (i >> 8) & 1;
     const int rest = i >> 9;
-    const int pl = rest % npl, ht = rest / npl;
+    const int pp = rest % ppl, ht = rest / ppl;
+    const int pl = part == 0 ? pp : pm;
     const int g = ln >> 4, n = ln & 15;
     const int gq = 4 * ht + (n >> 2), L = n & 3;
     uint32_t word = 0;
     if (gq < G) {
+      const int e = e_head[gq];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int k = 32 * g + 8 * j + 4 * hf + d;
         const int s = k & 7;
-        float x;
-        int e;
-        if (pl < pm) {
-          // half-bit layout: per-coordinate table; key_w holds zeros past the
-          // base table's planes
-          x = (a.key_half && (k & 31) < 16 ? a.key_w_hi[pl] : a.key_w[pl]) * qr[gq][k];
-          e = e_mse[gq];
-        } else {
-          x = 2.f * qs[gq][k];
-          e = e_qjl[gq];
-        }
+        // half-bit layout: per-coordinate table; key_w holds zeros past the
+        // base table's planes
+        const float x = part == 0 ? (a.key_half && (k & 31) < 16 ? a.key_w_hi[pl] : a.key_w[pl]) * qx[gq][k]
+                                  : 2.f * qx[gq][k];
         const int q = (int)rintf(ldexpf(x, e - s));
         int dg[4];
         digits128(q, dg);
@@ -232,7 +246,7 @@ __global__ __launch_bounds__(256) void qprep_mfma_kernel(DecodeArgs a, int pm, i
         word |= (uint32_t)(v & 0xff) << (8 * j);
       }
     }
-    out[i] = word;
+    out[((((ht * npl + pl) * 2 + hf) * 64 + ln) << 2) + d] = word;
   }
 }
 
@@ -867,10 +881,11 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int key_mse_bits, int key_qjl
   const int nht = a.group > 4 ? 2 : 1;
   const int pm = 1 << (key_mse_bits - 1);
   const int npl = pm + (key_qjl ? 1 : 0);
+  const dim3 qgrid(a.batch * a.h_kv, key_qjl ? 2 : 1);
   if (nht == 1)
-    hipLaunchKernelGGL(qprep_mfma_kernel<4>, dim3(a.batch * a.h_kv), dim3(256), 0, stream, a, pm, npl, nht);
+    hipLaunchKernelGGL(qprep_mfma_kernel<4>, qgrid, dim3(256), 0, stream, a, pm, npl, nht);
   else
-    hipLaunchKernelGGL(qprep_mfma_kernel<8>, dim3(a.batch * a.h_kv), dim3(256), 0, stream, a, pm, npl, nht);
+    hipLaunchKernelGGL(qprep_mfma_kernel<8>, qgrid, dim3(256), 0, stream, a, pm, npl, nht);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = nht == 1 ? dispatch_mfma<1>(a, key_mse_bits, key_qjl, value_mse, value_bits, stream, tl)
