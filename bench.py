@@ -13,6 +13,9 @@ channels per KV head scaled x10, keys 2-bit Lloyd-Max + 1-bit QJL, values
 * value = effective HBM GB/s of the decode step (algorithmic bytes / time).
 * roofline = the split-scan kernel: compressed bytes per launch / its average
   duration, from HIP events recorded around that launch inside the timed steps.
+* cold = more steps, each timed alone right after a 1 GiB device write that
+  evicts the 256 MB MALL (the last-level cache), so no step reads a cache
+  that a previous step left in it.
 * cpu_baseline = the float64 oracle on a bounded sample, on the host cores.
 
 Prints ONE JSON line.
@@ -228,6 +231,9 @@ def main():
     ap.add_argument("--achievable-mib", type=int, default=1024,
                     help="after the timed steps, time a plain device copy of this many MiB (0: skip); "
                          "its read + write GB/s is reported as the achievable bandwidth")
+    ap.add_argument("--cold-steps", type=int, default=16,
+                    help="after the timed steps, this many more steps each timed alone (events around the "
+                         "call), each after a 1 GiB device write that evicts the 256 MB MALL; 0: skip")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU work: turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) "
                          "made with --copy-probe-mib into the decode scan's traffic summary under profiles/")
@@ -265,7 +271,7 @@ def main():
     prm = tq.Params(lay, pi, s, device=dev)
     k, v = wl.prefill_kv(w)
     k, v = k.to(dev), v.to(dev)
-    total_steps = args.warmup + args.steps
+    total_steps = args.warmup + args.steps + args.cold_steps
     nq = args.queries
     ring = w.ring_cap if w.step_mode == "ring" else 0
     if nq < 1 or (ring and nq > ring):
@@ -376,6 +382,33 @@ def main():
     scan_sorted = sorted(scan_ms)
     launch_spread = {"median": round(scan_sorted[len(scan_sorted) // 2], 5), "min": round(scan_sorted[0], 5),
                      "max": round(scan_sorted[-1], 5)}
+    cold = None
+    if args.cold_steps:
+        # cold steps: a write larger than the MALL before each, outside the
+        # events, so the compressed cache comes from HBM
+        if ring:
+            state["n_r"] = 0
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        cms, cby = [], []
+        for j in range(args.cold_steps):
+            flush.fill_(j & 0xff)
+            e0.record()
+            by, _ = step(args.warmup + args.steps + j)
+            e1.record()
+            torch.cuda.synchronize()
+            cms.append(e0.elapsed_time(e1))
+            cby.append(by)
+        del flush
+        torch.cuda.empty_cache()
+        order = sorted(range(len(cms)), key=lambda i: cms[i])
+        med = order[len(order) // 2]
+        cold = {"steps": args.cold_steps, "flush_mib": 1024,
+                "ms_per_step": {"median": round(cms[med], 5), "min": round(cms[order[0]], 5),
+                                "max": round(cms[order[-1]], 5)},
+                "gbs_at_median": round(cby[med] / (cms[med] * 1e-3) / 1e9, 2),
+                "note": "each step timed alone with events around the call, after a 1 GiB device write "
+                        "that evicts the 256 MB MALL"}
     copy_gbs = None
     if args.achievable_mib:
         # a plain device copy (read and write) on the same device: what HBM
@@ -419,6 +452,7 @@ def main():
                      "frac": round(scan_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "avg_launch_ms": round(scan_avg_ms, 5), "launch_ms": launch_spread,
                      "algorithmic_bytes_per_launch": int(scan_avg_bytes), "source_sha": sha},
+        "cold": cold,
         "achievable": None if copy_gbs is None else {
             "copy_gbs": round(copy_gbs, 1), "copy_mib": args.achievable_mib,
             "scan_over_copy": round(scan_gbs / copy_gbs, 4),

@@ -434,18 +434,18 @@ __global__ __launch_bounds__(kD) void combine_kernel(DecodeArgs a) {
   const float L = block2_sum(Lp + pj, red2);  // its barriers also publish s_f and pr
 
   // channel c: sum over splits of f_s acc_s[c]; splits past the first
-  // kCombinePre are loaded eight at a time
+  // kCombinePre are loaded sixteen at a time
   float A = 0.f;
 #pragma unroll
   for (int u = 0; u < kCombinePre; ++u)
     if (u < S) A = fmaf(s_f[u], pa[u], A);
   int sp = kCombinePre;
-  for (; sp + 8 <= S; sp += 8) {
-    float v[8];
+  for (; sp + 16 <= S; sp += 16) {
+    float v[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = part0[(size_t)(sp + u) * sstride + 2 + c];
+    for (int u = 0; u < 16; ++u) v[u] = part0[(size_t)(sp + u) * sstride + 2 + c];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) A = fmaf(s_f[sp + u], v[u], A);
+    for (int u = 0; u < 16; ++u) A = fmaf(s_f[sp + u], v[u], A);
   }
   for (; sp < S; ++sp) A = fmaf(s_f[sp], part0[(size_t)sp * sstride + 2 + c], A);
 
@@ -527,12 +527,14 @@ hipError_t dispatch_qjl(const DecodeArgs& a, int qjl, int vmse, int vb, hipStrea
 // Split of the token range for the decode grid, in whole 256-token rounds of
 // the four waves.  About kSplitTarget work-groups over the device; when that
 // makes splits shorter than kLongSplit tokens, they are lengthened towards
-// kLongSplit as long as at least kFloorGroups work-groups (eight per compute
-// unit) remain, so per-work-group set-up and merge stay small next to the scan
-// while a few long sequences still spread over every wave slot of the device
-// (8 sequence-heads of 131072 tokens: 512-token splits, 2048 work-groups).
+// kLongSplit as long as at least kFloorGroups work-groups (one round of three
+// per compute unit) remain, so per-work-group set-up and the combine's merge
+// stay small next to the scan while a few long sequences still fill every
+// compute unit (8 sequence-heads of 131072 tokens: 1536-token splits, 688
+// work-groups, against 512-token splits and 2048 work-groups for a floor of
+// eight per compute unit: 4% less time per step, most of it in the combine).
 constexpr int64_t kSplitTarget = 2048;
-constexpr int64_t kFloorGroups = 2048;
+constexpr int64_t kFloorGroups = 768;
 constexpr int64_t kLongSplit = 2048;
 constexpr int64_t kMinSplit = 256;
 
