@@ -228,8 +228,19 @@ int tq_encode_kv(const tq_layout* layout, const tq_params* params, const void* k
     // tile_start has kMaxSeqPerLaunch entries; the kernels stop their search at
     // `batch`, and num_tiles bounds the last sequence.
     a.num_tiles = (int32_t)tiles;
-    hipError_t e = tq::launch_encode_keys(a, bf16, layout->key_mse_bits, layout->key_qjl, layout->key_half, st,
-                                          take_timed(TQ_KERNEL_ENCODE_KEYS));
+    // few tokens with MSE values: keys and values in one launch, unless a
+    // caller asked to time one of the two kernels on its own
+    hipError_t e = hipErrorNotSupported;
+    if (layout->value_kind == TQ_V_MSE && !g_timed[TQ_KERNEL_ENCODE_KEYS].begin &&
+        !g_timed[TQ_KERNEL_ENCODE_VALUES].begin)
+      e = tq::launch_encode_small_kv(a, bf16, layout->key_mse_bits, layout->key_qjl, layout->key_half,
+                                     layout->value_bits, st);
+    if (e != hipErrorNotSupported) {
+      if (e != hipSuccess) return hip_fail(e, "encode launch");
+      continue;
+    }
+    e = tq::launch_encode_keys(a, bf16, layout->key_mse_bits, layout->key_qjl, layout->key_half, st,
+                               take_timed(TQ_KERNEL_ENCODE_KEYS));
     if (e != hipSuccess) return hip_fail(e, "encode keys launch");
     if (layout->value_kind == TQ_V_MSE)
       e = tq::launch_encode_values_mse(a, bf16, layout->value_bits, st, take_timed(TQ_KERNEL_ENCODE_VALUES));

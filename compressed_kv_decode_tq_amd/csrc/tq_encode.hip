@@ -505,7 +505,7 @@ __device__ __forceinline__ float block_sum128(float x, float* red) {
 // LDS staging of the matrices: for a handful of tokens that staging would
 // cost more than the products.
 template <bool IN_BF16, int MSE_BITS, bool QJL, bool VALUE, bool HALF>
-__global__ __launch_bounds__(kD) void encode_small_kernel(EncodeArgs a) {
+__device__ __forceinline__ void encode_small_body(EncodeArgs a) {
   static_assert(!(HALF && VALUE), "the half-bit layout is a key layout");
   constexpr int LV = 1 << MSE_BITS;
   __shared__ float xs[kD];
@@ -617,6 +617,22 @@ __global__ __launch_bounds__(kD) void encode_small_kernel(EncodeArgs a) {
     for (int p = 0; p < MSE_BITS; ++p)
       store_plane_word(a.v_planes + ((slot * nblk_cap + blk) * MSE_BITS + p) * kD + i, vw[p], vmask);
   }
+}
+
+template <bool IN_BF16, int MSE_BITS, bool QJL, bool VALUE, bool HALF>
+__global__ __launch_bounds__(kD) void encode_small_kernel(EncodeArgs a) {
+  encode_small_body<IN_BF16, MSE_BITS, QJL, VALUE, HALF>(a);
+}
+
+// Keys (QJL) and MSE values of the same few tokens in one launch: the two
+// codes share no data, so work-groups (tile, 0) encode the keys and (tile, 1)
+// the values, and the two run side by side instead of one after the other.
+template <bool IN_BF16, int KEY_BITS, int VAL_BITS>
+__global__ __launch_bounds__(kD) void encode_small_kv_kernel(EncodeArgs a) {
+  if (blockIdx.y == 0)
+    encode_small_body<IN_BF16, KEY_BITS, true, false, false>(a);
+  else
+    encode_small_body<IN_BF16, VAL_BITS, false, true, false>(a);
 }
 
 // Asymmetric min/max value code, one 32-token tile per wave: lane = (token,
@@ -840,6 +856,27 @@ hipError_t launch_encode_keys(const EncodeArgs& a, int in_bf16, int mse_bits, in
                : dispatch_rot_bits<true, false, false>(a, mse_bits, stream, tl);
   return qjl ? dispatch_rot_bits<false, true, false>(a, mse_bits, stream, tl)
              : dispatch_rot_bits<false, false, false>(a, mse_bits, stream, tl);
+}
+
+hipError_t launch_encode_small_kv(const EncodeArgs& a, int in_bf16, int key_mse_bits, int key_qjl, int key_half,
+                                  int value_bits, hipStream_t stream) {
+  if (a.num_tiles == 0) return hipSuccess;
+  if (!use_small_encode(a) || !key_qjl || key_half || key_mse_bits < 2 || key_mse_bits > 3 || value_bits < 2 ||
+      value_bits > 3)
+    return hipErrorNotSupported;
+  const dim3 grid(a.num_tiles, 2);
+  const int sel = (in_bf16 ? 4 : 0) + (key_mse_bits == 3 ? 2 : 0) + (value_bits == 3 ? 1 : 0);
+  switch (sel) {
+    case 0: hipLaunchKernelGGL((encode_small_kv_kernel<false, 2, 2>), grid, dim3(kD), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((encode_small_kv_kernel<false, 2, 3>), grid, dim3(kD), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((encode_small_kv_kernel<false, 3, 2>), grid, dim3(kD), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((encode_small_kv_kernel<false, 3, 3>), grid, dim3(kD), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((encode_small_kv_kernel<true, 2, 2>), grid, dim3(kD), 0, stream, a); break;
+    case 5: hipLaunchKernelGGL((encode_small_kv_kernel<true, 2, 3>), grid, dim3(kD), 0, stream, a); break;
+    case 6: hipLaunchKernelGGL((encode_small_kv_kernel<true, 3, 2>), grid, dim3(kD), 0, stream, a); break;
+    default: hipLaunchKernelGGL((encode_small_kv_kernel<true, 3, 3>), grid, dim3(kD), 0, stream, a); break;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_encode_values_mse(const EncodeArgs& a, int in_bf16, int bits, hipStream_t stream,

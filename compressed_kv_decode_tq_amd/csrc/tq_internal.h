@@ -178,6 +178,11 @@ hipError_t launch_prepare_params(const float* pi, const float* s, uint16_t* deri
                                  hipStream_t stream);
 hipError_t launch_encode_keys(const EncodeArgs& a, int in_bf16, int mse_bits, int qjl, int half,
                               hipStream_t stream, TimedLaunch t);
+// Few-token keys (QJL, 2 or 3 index bits) and MSE values (2 or 3 bits) of one
+// call in a single launch; hipErrorNotSupported for any other layout or for a
+// call the bulk kernels take.
+hipError_t launch_encode_small_kv(const EncodeArgs& a, int in_bf16, int key_mse_bits, int key_qjl, int key_half,
+                                  int value_bits, hipStream_t stream);
 hipError_t launch_encode_values_mse(const EncodeArgs& a, int in_bf16, int bits,
                                     hipStream_t stream, TimedLaunch t);
 hipError_t launch_encode_values_minmax(const EncodeArgs& a, int in_bf16, int bits,
