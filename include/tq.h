@@ -65,10 +65,11 @@
  *    2-bit MSE values with 2+1- or 3+1-bit keys), else a VALU scan;
  *    environment variable
  *    TQ_DECODE_PATH=generic forces the VALU scan.  Encode of at most 4 new
- *    tokens per sequence runs a few-token fp32 kernel, else the MFMA rotation
- *    kernels; TQ_ENCODE_PATH=small or =mfma forces one.  All paths compute the
- *    same codes up to the boundary window and the same outputs within
- *    rounding.
+ *    tokens per sequence runs a few-token fp32 kernel (keys and MSE values in
+ *    one launch for QJL keys of 2 or 3 index bits with 2- or 3-bit MSE
+ *    values), else the MFMA rotation kernels; TQ_ENCODE_PATH=small or =mfma
+ *    forces one.  All paths compute the same codes up to the boundary window
+ *    and the same outputs within rounding.
  */
 #ifndef TQ_H_
 #define TQ_H_
