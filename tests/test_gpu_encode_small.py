@@ -97,3 +97,43 @@ def test_whole_sequences_through_the_few_token_kernel(name, monkeypatch):
             tot += _check(w, bk, pi, s, cache, k, v, b, h, start, n, f"{name} forced b{b} h{h}")
     say(f"[few-token encode, forced] {name}: {n} tokens from position {start}; excused flips "
         f"MSE {tot[0]}, QJL {tot[1]}, values {tot[2]}")
+
+
+def _hip_events():
+    import ctypes
+    h = ctypes.CDLL("libamdhip64.so")
+    h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    a, b = ctypes.c_void_p(), ctypes.c_void_p()
+    assert h.hipEventCreate(ctypes.byref(a)) == 0 and h.hipEventCreate(ctypes.byref(b)) == 0
+    return h, a, b
+
+
+@pytest.mark.parametrize("name", ["3+1-bit keys, MSE values", "qwen layer, fp16 scalars"])
+def test_one_launch_and_two_launches_write_the_same_codes(name):
+    """Few-token calls with MSE values encode keys and values in one launch;
+    a call that asks to time the key kernel takes two launches instead.  Both
+    run the same per-token code, so the caches must agree bit for bit."""
+    w = CASES[name]
+    _, _, _, prm, k, v = _setup(w)
+    cap = ((w.n_tokens + 31) // 32) * 32
+    P = w.n_tokens - 6
+    caches = []
+    h, ea, eb = _hip_events()
+    for timed in (False, True):
+        cache = tq.Cache(layout_of(w), w.batch, w.h_kv, cap, device=DEV)
+        tq.encode_kv(prm, k[:, :P].contiguous().to(DEV), v[:, :P].contiguous().to(DEV), [0] * w.batch, cache)
+        for j in range(3):
+            pos = [P + j] * w.batch
+            if timed:
+                tq.time_next_launch(tq.TQ_KERNEL_ENCODE_KEYS, ea, eb)
+            tq.encode_kv(prm, k[:, P + j:P + j + 1].contiguous().to(DEV), v[:, P + j:P + j + 1].contiguous().to(DEV),
+                         pos, cache)
+        torch.cuda.synchronize()
+        caches.append(cache)
+    h.hipEventDestroy(ea)
+    h.hipEventDestroy(eb)
+    a, b = caches
+    for field in ("k_planes", "k_norm", "k_rnorm", "v_planes", "v_norm"):
+        assert torch.equal(getattr(a, field), getattr(b, field)), field
+    say(f"[few-token encode] {name}: one launch and two launches give identical caches")
