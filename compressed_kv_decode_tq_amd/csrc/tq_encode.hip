@@ -635,6 +635,44 @@ __global__ __launch_bounds__(kD) void encode_small_kv_kernel(EncodeArgs a) {
     encode_small_body<IN_BF16, VAL_BITS, false, true, false>(a);
 }
 
+// DPP move of a 32-bit value (all lanes active).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xf, 0xf, false);
+}
+
+// Bit offset of token i (0..15) in a packed 2-bit code word.
+__device__ __forceinline__ constexpr int packed2_offset(int i) { return 8 * (i & 3) + 2 * (i >> 2); }
+
+// 16 x 16 transpose of 2-bit fields inside each 16-lane row: on entry lane i
+// of the row holds in D[m] the fields (i, j) at packed2_offset(j); on exit
+// lane j holds the fields (i, j) at packed2_offset(i).  Stage k swaps lane
+// index bit k with field index bit k (field stride S_k): each lane keeps the
+// fields whose index bit k equals its own lane bit k and takes the others
+// from lane i ^ 2^k, rotated by S_k.  The partners come from quad
+// permutations, a half-row mirror then a quad reversal (lane i ^ 4), and a
+// rotation by 8 (lane i ^ 8); all four are their own inverses.
+__device__ __forceinline__ void transpose16_2bit(uint32_t (&D)[4], int li) {
+  constexpr uint32_t kM0[4] = {0x00ff00ffu, 0x0000ffffu, 0x33333333u, 0x0f0f0f0fu};
+  constexpr int kS[4] = {8, 16, 2, 4};
+  static_for<0, 4>([&](auto K) {
+    constexpr int k = decltype(K)::value;
+    const bool ak = (li >> k) & 1;
+    const uint32_t keep = ak ? (kM0[k] << kS[k]) : kM0[k];
+    const int sh = ak ? kS[k] : 32 - kS[k];  // rotate right by sh
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      uint32_t P;
+      if constexpr (k == 0) P = dpp_u32<0xb1>(D[m]);                 // quad_perm [1, 0, 3, 2]
+      else if constexpr (k == 1) P = dpp_u32<0x4e>(D[m]);            // quad_perm [2, 3, 0, 1]
+      else if constexpr (k == 2) P = dpp_u32<0x1b>(dpp_u32<0x141>(D[m]));  // half-row mirror, quad reversal
+      else P = dpp_u32<0x128>(D[m]);                                 // row rotation by 8
+      const uint32_t rot = __builtin_amdgcn_alignbit(P, P, sh);
+      D[m] = (D[m] & keep) | (rot & ~keep);
+    }
+  });
+}
+
 // Asymmetric min/max value code, one 32-token tile per wave: lane = (token,
 // half of the channels).  IEEE fp32 arithmetic in a fixed order so the codes
 // are reproducible bit for bit:
@@ -651,7 +689,9 @@ __global__ __launch_bounds__(256) void encode_minmax_kernel(EncodeArgs a) {
   const int nwaves = blockDim.x >> 6;
   // lane l (mod 32) encodes the token whose bit position in a plane word is
   // l mod 32, so a ballot over the wave is already the plane word
-  const int tok = vslot(lane & 31), half = lane >> 5;
+  // (2-bit codes: token = lane % 32 in order, and each 16-lane row builds its
+  // packed words by an in-register transpose instead)
+  const int tok = BITS == 2 ? (lane & 31) : vslot(lane & 31), half = lane >> 5;
   for (int tile = blockIdx.x * nwaves + wave; tile < a.num_tiles; tile += gridDim.x * nwaves) {
     int b, h;
     int64_t blk;
@@ -710,49 +750,71 @@ __global__ __launch_bounds__(256) void encode_minmax_kernel(EncodeArgs a) {
         *reinterpret_cast<uint32_t*>(m) = packed;
       }
     }
-    // token-transposed planes: ballot over the wave gives tokens 0..31 of
-    // channel e (low half) and of channel 64 + e (high half)
-    uint32_t w[BITS][2];
-#pragma unroll
-    for (int p = 0; p < BITS; ++p) w[p][0] = w[p][1] = 0u;
-    static_for<0, 64>([&](auto E) {
-      constexpr int e = decltype(E)::value;
-#pragma unroll
-      for (int p = 0; p < BITS; ++p) {
-        const uint64_t m = __ballot((code[e] >> p) & 1u);
-        // the ballot is wave-uniform: write its halves straight into lane e
-        w[p][0] = write_lane<e>(w[p][0], (uint32_t)m);
-        w[p][1] = write_lane<e>(w[p][1], (uint32_t)(m >> 32));
-      }
-    });
-    const uint32_t vmask = (uint32_t)__ballot(valid);  // bit l: lane l's token is written
     const int64_t nblk_cap = a.capacity >> 5;
-    uint32_t out[BITS][2], msk[BITS];
-    if constexpr (packed_value_codes(false, BITS)) {
-      // widths 2 and 4 are stored as packed codes
+    if constexpr (BITS == 2) {
+      // lane (half, h, i) holds token 16 h + i: its 64 codes go to D[m] with
+      // channel 16 m + j at the packed offset of token j, and the row
+      // transpose leaves channel 64 half + 16 m + i of word h in D[m]
+      const int li = lane & 15, hw = (lane >> 4) & 1;
+      uint32_t D[4] = {0u, 0u, 0u, 0u};
+      static_for<0, 64>([&](auto E) {
+        constexpr int e = decltype(E)::value;
+        D[e >> 4] |= code[e] << packed2_offset(e & 15);
+      });
+      transpose16_2bit(D, li);
+      // the word's valid tokens: OR of the row's own fields
+      uint32_t msk = valid ? 3u << packed2_offset(li) : 0u;
+      msk |= dpp_u32<0xb1>(msk);
+      msk |= dpp_u32<0x4e>(msk);
+      msk |= dpp_u32<0x124>(msk);
+      msk |= dpp_u32<0x128>(msk);
+      uint32_t* base = a.v_planes + ((slot * nblk_cap + blk) * BITS + hw) * kD + 64 * half + li;
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        uint32_t pl[BITS], pk[BITS];
-#pragma unroll
-        for (int p = 0; p < BITS; ++p) pl[p] = w[p][hf];
-        planes_to_packed<BITS>(pl, pk);
-#pragma unroll
-        for (int p = 0; p < BITS; ++p) out[p][hf] = pk[p];
-      }
-      mask_to_packed<BITS>(vmask, msk);
+      for (int m = 0; m < 4; ++m) store_plane_word(base + 16 * m, D[m], msk);
     } else {
+      // token-transposed planes: ballot over the wave gives tokens 0..31 of
+      // channel e (low half) and of channel 64 + e (high half)
+      uint32_t w[BITS][2];
+#pragma unroll
+      for (int p = 0; p < BITS; ++p) w[p][0] = w[p][1] = 0u;
+      static_for<0, 64>([&](auto E) {
+        constexpr int e = decltype(E)::value;
+#pragma unroll
+        for (int p = 0; p < BITS; ++p) {
+          const uint64_t m = __ballot((code[e] >> p) & 1u);
+          // the ballot is wave-uniform: write its halves straight into lane e
+          w[p][0] = write_lane<e>(w[p][0], (uint32_t)m);
+          w[p][1] = write_lane<e>(w[p][1], (uint32_t)(m >> 32));
+        }
+      });
+      const uint32_t vmask = (uint32_t)__ballot(valid);  // bit l: lane l's token is written
+      uint32_t out[BITS][2], msk[BITS];
+      if constexpr (packed_value_codes(false, BITS)) {
+        // widths 2 and 4 are stored as packed codes
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          uint32_t pl[BITS], pk[BITS];
+#pragma unroll
+          for (int p = 0; p < BITS; ++p) pl[p] = w[p][hf];
+          planes_to_packed<BITS>(pl, pk);
+#pragma unroll
+          for (int p = 0; p < BITS; ++p) out[p][hf] = pk[p];
+        }
+        mask_to_packed<BITS>(vmask, msk);
+      } else {
+#pragma unroll
+        for (int p = 0; p < BITS; ++p) {
+          out[p][0] = w[p][0];
+          out[p][1] = w[p][1];
+          msk[p] = vmask;
+        }
+      }
 #pragma unroll
       for (int p = 0; p < BITS; ++p) {
-        out[p][0] = w[p][0];
-        out[p][1] = w[p][1];
-        msk[p] = vmask;
+        uint32_t* base = a.v_planes + ((slot * nblk_cap + blk) * BITS + p) * kD;
+        store_plane_word(base + lane, out[p][0], msk[p]);
+        store_plane_word(base + 64 + lane, out[p][1], msk[p]);
       }
-    }
-#pragma unroll
-    for (int p = 0; p < BITS; ++p) {
-      uint32_t* base = a.v_planes + ((slot * nblk_cap + blk) * BITS + p) * kD;
-      store_plane_word(base + lane, out[p][0], msk[p]);
-      store_plane_word(base + 64 + lane, out[p][1], msk[p]);
     }
   }
 }
