@@ -63,6 +63,28 @@ def test_encode_parity(name):
     say(f"  excused flips: key MSE {tot[0]}, key QJL {tot[1]}, value MSE {tot[2]} of {n_coord} coordinates")
 
 
+@pytest.mark.parametrize("bits,group", [(1, 32), (2, 16), (2, 64), (3, 32), (4, 16), (4, 64)])
+def test_encode_minmax_widths_and_groups(bits, group):
+    """GPU min/max value codes for every width and group size, against the
+    oracle (codes bit-exact outside the window, fp16 delta and minimum exact),
+    with a ragged start so the first and last 32-token blocks are partial."""
+    w = SMALL["batched_small"].replace(batch=2, h_kv=2, h_q=8, n_tokens=150, value_bits=bits, value_group=group)
+    say(f"[encode min/max] {bits}-bit values, groups of {group}")
+    bk = books(w)
+    pi, s, prm = _params(w)
+    k, v = wl.prefill_kv(w)
+    start = 7
+    cache = tq.Cache(layout_of(w), w.batch, w.h_kv, 192, device=DEV)
+    tq.encode_kv(prm, k.to(DEV), v.to(DEV), [start] * w.batch, cache)
+    torch.cuda.synchronize()
+    tot = np.zeros(3, dtype=np.int64)
+    for b in range(w.batch):
+        for h in range(w.h_kv):
+            ref = encode_slot(w, bk, pi, s, k[b, :, h].double().numpy(), v[b, :, h].double().numpy())
+            tot += check_encode_slot(w, bk, cache, b, h, ref, start, w.n_tokens, f"{bits}b g{group} b{b} h{h}")
+    say(f"  excused value flips {tot[2]}")
+
+
 @pytest.mark.parametrize("value_kind", ["minmax", "mse"])
 def test_encode_ragged_positions_preserve_neighbours(value_kind):
     base = SMALL["batched_small"] if value_kind == "minmax" else SMALL["long_small"]
