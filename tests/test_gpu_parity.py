@@ -85,6 +85,30 @@ def test_encode_minmax_widths_and_groups(bits, group):
     say(f"  excused value flips {tot[2]}")
 
 
+@pytest.mark.parametrize("path", ["mfma", "small"])
+@pytest.mark.parametrize("kbits,qjl,vbits", [(1, 1, 1), (2, 0, 2), (3, 0, 4), (4, 1, 2), (4, 0, 3), (1, 0, 4)])
+def test_encode_key_and_mse_value_widths(kbits, qjl, vbits, path, monkeypatch):
+    """GPU key codes for every index width with and without the QJL bit, and
+    MSE value codes for every width, on the bulk (MFMA) and the few-token
+    kernels, against the oracle outside the boundary window."""
+    monkeypatch.setenv("TQ_ENCODE_PATH", path)
+    w = SMALL["long_small"].replace(batch=2, n_tokens=100, key_mse_bits=kbits, key_qjl=qjl, value_bits=vbits)
+    say(f"[encode widths] keys {kbits}{'+1' if qjl else ''}, MSE values {vbits} ({path})")
+    bk = books(w)
+    pi, s, prm = _params(w)
+    k, v = wl.prefill_kv(w)
+    start = 3
+    cache = tq.Cache(layout_of(w), w.batch, w.h_kv, 128, device=DEV)
+    tq.encode_kv(prm, k.to(DEV), v.to(DEV), [start] * w.batch, cache)
+    torch.cuda.synchronize()
+    tot = np.zeros(3, dtype=np.int64)
+    for b in range(w.batch):
+        for h in range(w.h_kv):
+            ref = encode_slot(w, bk, pi, s, k[b, :, h].double().numpy(), v[b, :, h].double().numpy())
+            tot += check_encode_slot(w, bk, cache, b, h, ref, start, w.n_tokens, f"k{kbits} q{qjl} v{vbits} b{b} h{h}")
+    say(f"  excused flips: key MSE {tot[0]}, key QJL {tot[1]}, value MSE {tot[2]}")
+
+
 @pytest.mark.parametrize("value_kind", ["minmax", "mse"])
 def test_encode_ragged_positions_preserve_neighbours(value_kind):
     base = SMALL["batched_small"] if value_kind == "minmax" else SMALL["long_small"]
