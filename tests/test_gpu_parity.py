@@ -305,6 +305,23 @@ def test_decode_keys_without_qjl(path, monkeypatch):
     _decode_case(mse.replace(key_mse_bits=2), [211], [0], f"no qjl, 2-bit keys, MSE values ({path})")
 
 
+@pytest.mark.parametrize("path", ["mfma", "generic"])
+@pytest.mark.parametrize("kbits,qjl,vkind,vbits,group", [
+    (4, 1, "minmax", 3, 32), (4, 0, "minmax", 1, 16), (3, 0, "minmax", 3, 64), (1, 1, "minmax", 1, 32),
+    (2, 1, "minmax", 2, 16), (2, 1, "minmax", 4, 64), (4, 1, "mse", 1, 32), (1, 0, "mse", 4, 32),
+    (3, 1, "mse", 2, 32), (4, 0, "mse", 4, 32)])
+def test_decode_layout_sweep(kbits, qjl, vkind, vbits, group, path, monkeypatch):
+    """Decode of oracle-encoded caches over key widths with and without QJL,
+    min/max widths and group sizes and MSE value widths, on both scan paths
+    (layouts the MFMA scan does not cover run on the generic scan either way)."""
+    if path == "generic":
+        monkeypatch.setenv("TQ_DECODE_PATH", "generic")
+    base = SMALL["batched_small"] if vkind == "minmax" else SMALL["long_small"]
+    w = base.replace(batch=2, n_tokens=260, key_mse_bits=kbits, key_qjl=qjl, value_bits=vbits, value_group=group)
+    nr = [2, 0] if w.ring_cap else [0, 0]
+    _decode_case(w, [260, 131], nr, f"k{kbits}{'+1' if qjl else ''} {vkind} v{vbits} g{group} ({path})")
+
+
 def test_decode_empty_sequence_gives_zero():
     w = SMALL["batched_small"].replace(batch=2, n_tokens=64)
     _decode_case(w, [0, 64], [0, 3], "empty")
