@@ -678,6 +678,31 @@ __device__ __forceinline__ void transpose16_2bit(uint32_t (&D)[4], int li) {
   });
 }
 
+// Bit offset of token i (0..7) in a packed 4-bit code word.
+__device__ __forceinline__ constexpr int packed4_offset(int i) { return 8 * (i & 3) + 4 * (i >> 2); }
+
+// The same transpose for 4-bit fields, 8 x 8 inside each 8-lane half-row
+// (three stages: lane i ^ 1, i ^ 2, i ^ 4).
+__device__ __forceinline__ void transpose8_4bit(uint32_t (&D)[8], int li) {
+  constexpr uint32_t kM0[3] = {0x00ff00ffu, 0x0000ffffu, 0x0f0f0f0fu};
+  constexpr int kS[3] = {8, 16, 4};
+  static_for<0, 3>([&](auto K) {
+    constexpr int k = decltype(K)::value;
+    const bool ak = (li >> k) & 1;
+    const uint32_t keep = ak ? (kM0[k] << kS[k]) : kM0[k];
+    const int sh = ak ? kS[k] : 32 - kS[k];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      uint32_t P;
+      if constexpr (k == 0) P = dpp_u32<0xb1>(D[m]);
+      else if constexpr (k == 1) P = dpp_u32<0x4e>(D[m]);
+      else P = dpp_u32<0x1b>(dpp_u32<0x141>(D[m]));
+      const uint32_t rot = __builtin_amdgcn_alignbit(P, P, sh);
+      D[m] = (D[m] & keep) | (rot & ~keep);
+    }
+  });
+}
+
 // Asymmetric min/max value code, one 32-token tile per wave: lane = (token,
 // half of the channels).  IEEE fp32 arithmetic in a fixed order so the codes
 // are reproducible bit for bit:
@@ -694,9 +719,9 @@ __global__ __launch_bounds__(256) void encode_minmax_kernel(EncodeArgs a) {
   const int nwaves = blockDim.x >> 6;
   // lane l (mod 32) encodes the token whose bit position in a plane word is
   // l mod 32, so a ballot over the wave is already the plane word
-  // (2-bit codes: token = lane % 32 in order, and each 16-lane row builds its
-  // packed words by an in-register transpose instead)
-  const int tok = BITS == 2 ? (lane & 31) : vslot(lane & 31), half = lane >> 5;
+  // (2- and 4-bit codes: token = lane % 32 in order, and each 16-lane row or
+  // 8-lane half-row builds its packed words by an in-register transpose)
+  const int tok = (BITS == 2 || BITS == 4) ? (lane & 31) : vslot(lane & 31), half = lane >> 5;
   for (int tile = blockIdx.x * nwaves + wave; tile < a.num_tiles; tile += gridDim.x * nwaves) {
     int b, h;
     int64_t blk;
@@ -776,6 +801,24 @@ __global__ __launch_bounds__(256) void encode_minmax_kernel(EncodeArgs a) {
       uint32_t* base = a.v_planes + ((slot * nblk_cap + blk) * BITS + hw) * kD + 64 * half + li;
 #pragma unroll
       for (int m = 0; m < 4; ++m) store_plane_word(base + 16 * m, D[m], msk);
+    } else if constexpr (BITS == 4) {
+      // lane (half, h, i) holds token 8 h + i: channel 8 m + j at the packed
+      // offset of token j in D[m]; the half-row transpose leaves channel
+      // 64 half + 8 m + i of word h in D[m]
+      const int li = lane & 7, hw = (lane >> 3) & 3;
+      uint32_t D[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+      static_for<0, 64>([&](auto E) {
+        constexpr int e = decltype(E)::value;
+        D[e >> 3] |= code[e] << packed4_offset(e & 7);
+      });
+      transpose8_4bit(D, li);
+      uint32_t msk = valid ? 15u << packed4_offset(li) : 0u;
+      msk |= dpp_u32<0xb1>(msk);
+      msk |= dpp_u32<0x4e>(msk);
+      msk |= dpp_u32<0x1b>(dpp_u32<0x141>(msk));
+      uint32_t* base = a.v_planes + ((slot * nblk_cap + blk) * BITS + hw) * kD + 64 * half + li;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) store_plane_word(base + 8 * m, D[m], msk);
     } else {
       // token-transposed planes: ballot over the wave gives tokens 0..31 of
       // channel e (low half) and of channel 64 + e (high half)
