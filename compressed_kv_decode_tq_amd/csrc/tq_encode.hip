@@ -74,16 +74,15 @@ __device__ __forceinline__ void tile_coords(const EncodeArgs& a, int tile, int& 
 }
 
 // Lane LANE of w0 and of w1 replaced by the two halves of the wave-uniform
-// 64-bit value m (two v_writelane, no lane masks).  m comes straight from a
-// VALU compare (a ballot), often in VCC, and v_writelane reads it as a scalar
-// operand: the compiler does not add the wait states that read needs after a
-// VALU write when the instruction is inline asm, so the asm brings its own
-// (s_nop 4: five wait states).  Without them lane 31 read a stale VCC.
+// 64-bit value m (a ballot), as a plain per-lane select: every lane compares
+// its own index, so no instruction reads a scalar that a VALU compare has just
+// written (the hazard an inline-asm v_writelane would need its own wait
+// states for).
 template <int LANE>
-__device__ __forceinline__ void write_lane2(uint32_t& w0, uint32_t& w1, uint64_t m) {
-  asm volatile("s_nop 4\n\tv_writelane_b32 %0, %2, %4\n\tv_writelane_b32 %1, %3, %4"
-               : "+v"(w0), "+v"(w1)
-               : "s"((uint32_t)m), "s"((uint32_t)(m >> 32)), "n"(LANE));
+__device__ __forceinline__ void write_lane2(uint32_t& w0, uint32_t& w1, uint64_t m, int lane) {
+  const bool mine = lane == LANE;
+  w0 = mine ? (uint32_t)m : w0;
+  w1 = mine ? (uint32_t)(m >> 32) : w1;
 }
 
 // f(std::integral_constant<int, I>{}) for I = B .. E-1, unrolled at compile time.
@@ -831,7 +830,7 @@ __global__ __launch_bounds__(256) void encode_minmax_kernel(EncodeArgs a) {
         for (int p = 0; p < BITS; ++p) {
           const uint64_t m = __ballot((code[e] >> p) & 1u);
           // the ballot is wave-uniform: write its halves straight into lane e
-          write_lane2<e>(w[p][0], w[p][1], m);
+          write_lane2<e>(w[p][0], w[p][1], m, lane);
         }
       });
       const uint32_t vmask = (uint32_t)__ballot(valid);  // bit l: lane l's token is written

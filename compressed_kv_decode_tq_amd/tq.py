@@ -171,6 +171,59 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+def _require(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_seq_list(name: str, xs, batch: int):
+    _require(xs is not None and len(xs) == batch, f"{name} must hold one entry per sequence ({batch})")
+
+
+def _check_device(cache: "Cache", **tensors):
+    dev = cache.k_planes.device
+    for name, t in tensors.items():
+        if t is not None:
+            _require(t.device == dev, f"{name} is on {t.device}, the cache on {dev}")
+
+
+def _check_ring(cache: "Cache", ring_k, ring_v, n_ring, d: int):
+    """Rings: both or neither; contiguous bf16 [B, R, H_kv, d] of one shape."""
+    if ring_k is None and ring_v is None:
+        return 0
+    _require(ring_k is not None and ring_v is not None, "ring_k and ring_v must be given together")
+    for name, r in (("ring_k", ring_k), ("ring_v", ring_v)):
+        _require(r.dtype == torch.bfloat16, f"{name} must be bf16")
+        _require(r.is_contiguous(), f"{name} must be contiguous (a slice of a ring has the wrong row stride)")
+        _require(r.dim() == 4 and r.shape[0] == cache.batch and r.shape[2] == cache.num_kv_heads
+                 and r.shape[3] == d and r.shape[1] > 0,
+                 f"{name} must be [{cache.batch}, R, {cache.num_kv_heads}, {d}], got {tuple(r.shape)}")
+    _require(ring_k.shape == ring_v.shape, "ring_k and ring_v must have the same shape")
+    _check_seq_list("n_ring", n_ring, cache.batch)
+    return int(ring_k.shape[1])
+
+
+def _check_decode(layout: Layout, q: torch.Tensor, cache: "Cache", n_compressed, out, workspace):
+    """Shapes, dtypes, contiguity and devices of a decode call, checked before
+    anything reaches the library (which trusts sizes it is given)."""
+    d = layout.head_dim
+    _require(q.dim() in (3, 4), "q must be [B, H_q, d] or [B, T, H_q, d]")
+    _require(q.dtype in (torch.float32, torch.bfloat16), "q must be fp32 or bf16")
+    _require(q.is_contiguous(), "q must be contiguous")
+    _require(q.shape[0] == cache.batch, f"q holds {q.shape[0]} sequences, the cache {cache.batch}")
+    _require(q.shape[-1] == d, f"q's last dimension {q.shape[-1]} is not head_dim {d}")
+    h_q = q.shape[-2]
+    _require(h_q > 0 and h_q % cache.num_kv_heads == 0,
+             f"h_q = {h_q} must be a positive multiple of num_kv_heads = {cache.num_kv_heads}")
+    _check_seq_list("n_compressed", n_compressed, cache.batch)
+    if out is not None:
+        _require(out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == tuple(q.shape),
+                 f"out must be contiguous fp32 of q's shape {tuple(q.shape)}")
+    if workspace is not None:
+        _require(workspace.dtype == torch.uint8 and workspace.is_contiguous(), "workspace must be contiguous uint8")
+    _check_device(cache, q=q, out=out, workspace=workspace)
+
+
 class Params:
     """Per-layer parameters on one device: Pi and S (fp32), the operands
     tq_prepare_params derives from them, and the codebook tables."""
@@ -251,6 +304,11 @@ def encode_kv(params: Params, k: torch.Tensor, v: torch.Tensor, dst_pos, cache: 
         raise ValueError("k and v must be contiguous")
     if k.shape[0] != cache.batch or k.shape[2] != cache.num_kv_heads:
         raise ValueError("k/v batch or head count does not match the cache")
+    _require(k.shape[3] == params.layout.head_dim, f"k's last dimension {k.shape[3]} is not head_dim "
+             f"{params.layout.head_dim}")
+    _require(k.dtype in (torch.float32, torch.bfloat16), "k and v must be fp32 or bf16")
+    _check_seq_list("dst_pos", dst_pos, cache.batch)
+    _check_device(cache, k=k, v=v)
     pos = (ctypes.c_int64 * cache.batch)(*[int(x) for x in dst_pos])
     lay, prm, cc = params.layout.c(), params.c(), cache.c()
     _check(lib().tq_encode_kv(ctypes.byref(lay), ctypes.byref(prm), _ptr(k), _ptr(v), _dtype_code(k),
@@ -261,11 +319,19 @@ def ring_append(k_new: torch.Tensor, v_new: torch.Tensor, ring_k: torch.Tensor, 
                 n_ring, stream=None):
     """Write one token per sequence (k_new, v_new: [B, 1, H_kv, d]) into the
     bf16 rings ([B, R, H_kv, d]) at positions n_ring[b]."""
+    _require(ring_k.dim() == 4, "rings must be [B, R, H_kv, d]")
     b, r, h, d = ring_k.shape
     if ring_k.dtype != torch.bfloat16 or ring_v.dtype != torch.bfloat16:
         raise ValueError("rings are bf16")
+    _require(ring_v.shape == ring_k.shape and ring_k.is_contiguous() and ring_v.is_contiguous(),
+             "ring_k and ring_v must be contiguous and of one shape")
     if tuple(k_new.shape) != (b, 1, h, d) or not k_new.is_contiguous() or not v_new.is_contiguous():
         raise ValueError("k_new/v_new must be contiguous [B, 1, H_kv, d]")
+    _require(v_new.shape == k_new.shape and v_new.dtype == k_new.dtype, "k_new and v_new must match")
+    _require(k_new.dtype in (torch.float32, torch.bfloat16), "k_new must be fp32 or bf16")
+    _check_seq_list("n_ring", n_ring, b)
+    for name, t in (("v_new", v_new), ("ring_k", ring_k), ("ring_v", ring_v)):
+        _require(t.device == k_new.device, f"{name} is not on k_new's device")
     nr = (ctypes.c_int32 * b)(*[int(x) for x in n_ring])
     _check(lib().tq_ring_append(_ptr(k_new), _ptr(v_new), _dtype_code(k_new), b, h, d,
                                 _ptr(ring_k), _ptr(ring_v), r, nr, _stream(stream)))
@@ -287,14 +353,17 @@ def decode_attn(params: Params, q: torch.Tensor, cache: Cache, n_compressed, rin
     several causal queries per sequence: q [B, T, H_q, d] -> out [B, T, H_q, d]
     (tq_decode_attn_multi)."""
     lay_py = params.layout
+    _check_decode(lay_py, q, cache, n_compressed, out, workspace)
+    ring_cap = _check_ring(cache, ring_k, ring_v, n_ring, lay_py.head_dim)
+    if ring_cap == 0 and n_ring is not None:
+        _check_seq_list("n_ring", n_ring, cache.batch)
+        _require(all(int(x) == 0 for x in n_ring), "n_ring must be 0 without ring buffers")
     multi = q.dim() == 4
     if multi:
         b, nq, h_q, d = q.shape
     else:
         b, h_q, d = q.shape
         nq = 1
-    if not q.is_contiguous():
-        raise ValueError("q must be contiguous")
     if scale is None:
         scale = 1.0 / float(np.sqrt(d))
     if out is None:
@@ -304,7 +373,6 @@ def decode_attn(params: Params, q: torch.Tensor, cache: Cache, n_compressed, rin
     need = decode_workspace_bytes(lay_py, b, h_q, cache.num_kv_heads, max_tokens, nq)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    ring_cap = 0 if ring_k is None else ring_k.shape[1]
     nr = (ctypes.c_int32 * b)(*([int(x) for x in n_ring] if n_ring is not None else [0] * b))
     lay, prm, cc = lay_py.c(), params.c(), cache.c()
     if multi:
@@ -329,12 +397,20 @@ def decode_attn_append(params: Params, q: torch.Tensor, cache: Cache, n_compress
     then q [B, H_q, d] attends over the compressed tokens and n_ring[b] + 1
     ring tokens.  n_ring holds the lengths before the append."""
     lay_py = params.layout
+    _require(q.dim() == 3, "q must be [B, H_q, d] (one query per sequence)")
+    _check_decode(lay_py, q, cache, n_compressed, out, workspace)
+    _require(ring_k is not None and ring_v is not None, "the fused append needs the ring buffers")
+    _check_ring(cache, ring_k, ring_v, n_ring, lay_py.head_dim)
     b, h_q, d = q.shape
     for t in (q, k_new, v_new, ring_k, ring_v):
         if not t.is_contiguous():
             raise ValueError("q, k_new, v_new and the ring buffers must be contiguous")
     if k_new.dtype != v_new.dtype:
         raise ValueError("k_new and v_new must have the same dtype")
+    _require(tuple(k_new.shape) == (b, 1, cache.num_kv_heads, d) and tuple(v_new.shape) == tuple(k_new.shape),
+             f"k_new and v_new must be [{b}, 1, {cache.num_kv_heads}, {d}]")
+    _require(k_new.dtype in (torch.float32, torch.bfloat16), "k_new and v_new must be fp32 or bf16")
+    _check_device(cache, k_new=k_new, v_new=v_new, ring_k=ring_k, ring_v=ring_v)
     if scale is None:
         scale = 1.0 / float(np.sqrt(d))
     if out is None:

@@ -29,13 +29,16 @@ Readings taken where the pages are silent:
   scalar dtype (fp32 or fp16, round-to-nearest-even); normalisation uses the
   unrounded norm, reconstruction the stored one.
 * Min/max values: groups of ``group`` consecutive channels of one token.  The
-  scale and zero are stored as fp16 and the codes are computed from the stored
-  fp16 values, all in IEEE fp32 arithmetic (the integer decision is taken in
-  the precision the kernel uses):
-      delta32 = fp32(fp32(max) - fp32(min)) / fp32(2^b - 1)
-      delta16 = fp16(delta32), min16 = fp16(min), inv = fp32(1 / delta16)
-      code    = clip(rint_half_even(fp32(fp32(v - min16) * inv)), 0, 2^b - 1)
+  scale and zero are stored as fp16; the scale is the group's range over the
+  2^b - 1 steps, formed in IEEE fp32 and then rounded to fp16, the zero is the
+  group's minimum rounded to fp16.  The code of each channel is the nearest
+  step from the STORED zero in units of the STORED scale, by plain division in
+  float64 with ties to even:
+      delta16 = fp16(fp32(fp32(max) - fp32(min)) / fp32(2^b - 1)), min16 = fp16(min)
+      code    = clip(rint_half_even((v - min16) / delta16), 0, 2^b - 1)
   with code 0 wherever delta16 == 0.  Reconstruction: min16 + code * delta16.
+  An implementation that forms the ratio in lower precision agrees with this
+  except where the ratio lies within its rounding error of a half-integer.
 """
 from __future__ import annotations
 
@@ -168,30 +171,31 @@ class ValueMinMax:
     code: np.ndarray  # (T, d) int
     scale16: np.ndarray  # (T, d/group) float16 delta
     min16: np.ndarray  # (T, d/group) float16 zero
-    ratio: np.ndarray  # (T, d) float32 (v - min16) * inv, before rounding
+    ratio: np.ndarray  # (T, d) float64 (v - min16) / delta16, before rounding (0 where delta16 == 0)
 
 
 def encode_values_minmax(v: np.ndarray, bits: int, group: int) -> ValueMinMax:
     """Asymmetric b-bit min/max code per group of ``group`` channels ([audit]
-    AUDIT 1 store arguments ``value_bits``, ``value_group_size``); IEEE fp32
-    arithmetic as stated in the module docstring."""
-    v32 = np.asarray(v).astype(np.float32)
-    t, d = v32.shape
+    AUDIT 1 store arguments ``value_bits``, ``value_group_size``), as stated
+    in the module docstring: fp16 scale and zero, then each code by float64
+    division against the stored fp16 values."""
+    v64 = np.asarray(v, dtype=np.float64)
+    t, d = v64.shape
     if d % group:
         raise ValueError("group must divide d")
-    g = v32.reshape(t, d // group, group)
-    mn = g.min(axis=-1)
-    mx = g.max(axis=-1)
-    levels = np.float32((1 << bits) - 1)
-    delta32 = (mx - mn) / levels
+    g = v64.reshape(t, d // group, group)
+    # scale and zero: the range is formed in fp32 (the inputs are fp32 or
+    # bf16, so their fp32 values are exact), then stored as fp16
+    mn32 = g.min(axis=-1).astype(np.float32)
+    mx32 = g.max(axis=-1).astype(np.float32)
+    levels = (1 << bits) - 1
+    delta32 = (mx32 - mn32) / np.float32(levels)
     scale16 = delta32.astype(np.float16)
-    min16 = mn.astype(np.float16)
-    s32 = scale16.astype(np.float32)
-    m32 = min16.astype(np.float32)
+    min16 = mn32.astype(np.float16)
+    s64 = scale16.astype(np.float64)[..., None]
+    m64 = min16.astype(np.float64)[..., None]
     with np.errstate(divide="ignore", invalid="ignore"):
-        inv = np.float32(1.0) / s32
-        ratio = (g - m32[..., None]) * inv[..., None]
-    ratio = np.where(s32[..., None] == 0, np.float32(0), ratio).astype(np.float32)
+        ratio = np.where(s64 > 0, (g - m64) / np.where(s64 > 0, s64, 1.0), 0.0)
     code = np.clip(np.rint(ratio), 0, levels).astype(np.int64)
     return ValueMinMax(code=code.reshape(t, d), scale16=scale16, min16=min16,
                        ratio=ratio.reshape(t, d))

@@ -87,3 +87,66 @@ def test_fused_append_against_oracle():
     err = max_rel_err(out.cpu().double().numpy(), ref)
     say(f"[fused append] against the oracle: max rel err {err.max():.2e} (bound {OUT_RTOL})")
     assert err.max() <= OUT_RTOL
+
+
+def _oracle_decode(w, bk, pi, s, cache, q, n_comp, rk, rv, n_ring):
+    """The oracle's attention over the GPU's own codes of every slot plus the
+    first n_ring[b] ring tokens."""
+    kd, vd = [], []
+    for b in range(w.batch):
+        kr, vr = [], []
+        for h in range(w.h_kv):
+            a_, c_ = dequant_slot(w, bk, pi, s, slot_from_cache(w, cache, b, h, n_comp[b]))
+            kr.append(a_)
+            vr.append(c_)
+        kd.append(kr)
+        vd.append(vr)
+    return oracle.decode_attention(q.cpu().double().numpy(), kd, vd, rk.cpu().double().numpy(),
+                                   rv.cpu().double().numpy(), list(n_ring))
+
+
+def test_ring_fill_flush_then_decode():
+    """The store's life cycle over one full ring (page "turboquant/audit_claims.py",
+    AUDIT 1: the most recent 128 tokens stay uncompressed in bf16): 128 fused
+    decode steps fill the ring, the full ring is flushed through tq_encode_kv
+    at each sequence's compressed length (ragged, not 32-aligned), and the next
+    step starts a new ring.  Checked against the oracle: decode outputs at
+    ring lengths 1, 64 and 128 and after the flush, and the flushed tokens'
+    codes against the oracle's encode of the same bf16 ring contents."""
+    from tq_testlib import check_encode_slot, encode_slot
+
+    w = wl.WORKLOADS[3].replace(batch=2, n_tokens=640, decode_steps=1)
+    n_comp = [640, 501]
+    bk = books(w)
+    pi, s = wl.params(w)
+    prm = tq.Params(layout_of(w), pi, s, device=DEV)
+    k, v = wl.prefill_kv(w)
+    cache = tq.Cache(layout_of(w), w.batch, w.h_kv, 800, device=DEV)
+    tq.encode_kv(prm, k.to(DEV), v.to(DEV), [0] * w.batch, cache)
+    # sequence 1 holds 501 compressed tokens: its positions 501.. are rewritten by the flush
+    rk = torch.zeros((w.batch, 128, w.h_kv, w.d), dtype=torch.bfloat16, device=DEV)
+    rv = torch.zeros_like(rk)
+    worst = 0.0
+    for i in range(129):
+        if i == 128:  # the ring is full: flush it, then the step appends to an empty ring
+            flushed_k, flushed_v = rk.clone(), rv.clone()
+            tq.encode_kv(prm, rk, rv, n_comp, cache)
+            torch.cuda.synchronize()
+            for b in range(w.batch):
+                for h in range(w.h_kv):
+                    ref = encode_slot(w, bk, pi, s, flushed_k[b, :, h].cpu().double().numpy(),
+                                      flushed_v[b, :, h].cpu().double().numpy())
+                    check_encode_slot(w, bk, cache, b, h, ref, n_comp[b], 128, f"flush b{b} h{h}")
+            n_comp = [n + 128 for n in n_comp]
+        n_r = i % 128
+        kn, vn = (x.to(DEV).contiguous() for x in wl.step_kv(w, i))
+        q = wl.query(w, i).to(DEV)
+        out = tq.decode_attn_append(prm, q, cache, n_comp, kn, vn, rk, rv, [n_r] * w.batch)
+        if i in (0, 63, 127, 128):
+            torch.cuda.synchronize()
+            ref = _oracle_decode(w, bk, pi, s, cache, q, n_comp, rk, rv, [n_r + 1] * w.batch)
+            err = float(max_rel_err(out.cpu().double().numpy(), ref).max())
+            worst = max(worst, err)
+            say(f"[ring flush] step {i}: compressed {n_comp}, ring {n_r + 1}, max rel err {err:.2e}")
+            assert err <= OUT_RTOL
+    say(f"[ring flush] worst {worst:.2e} (bound {OUT_RTOL})")

@@ -29,7 +29,7 @@ import torch
 import oracle
 from compressed_kv_decode_tq_amd import tq
 from compressed_kv_decode_tq_amd import workloads as wl
-from tq_testlib import (OUT_RTOL, books, check_encode_slot, dequant_slot, encode_slot, layout_of, max_rel_err,
+from tq_testlib import (gamma_report, OUT_RTOL, books, check_encode_slot, dequant_slot, encode_slot, layout_of, max_rel_err,
                         say, slot_from_cache)
 
 pytestmark = pytest.mark.gpu
@@ -92,6 +92,7 @@ def test_fullsize_batched_b32_hkv8_n32768():
         tot += check_encode_slot(w, bk, cache, b, h, ref, 0, w.n_tokens, f"b{b} h{h}")
     say(f"  encode: slots {slots} match outside the window; excused flips key MSE {tot[0]}, "
         f"key QJL {tot[1]} of {len(slots) * w.n_tokens * w.d} coordinates")
+    say("  " + gamma_report())
     del k, v
 
     # decode steps as bench.py runs them: one call appends the step token to
@@ -137,7 +138,8 @@ def test_fullsize_long_b1_hkv8_n131072():
         ref = encode_slot(w, bk, pi, s, k[b, :, h].double().numpy(), v[b, :, h].double().numpy())
         tot += check_encode_slot(w, bk, cache, b, h, ref, 0, w.n_tokens, f"b{b} h{h}")
     say(f"  encode: slots {slots} match outside the window; excused flips key MSE {tot[0]}, "
-        f"key QJL {tot[1]}, value MSE {tot[2]} of {len(slots) * w.n_tokens * w.d} coordinates")
+        f"key QJL {tot[1]}, value {tot[2]} of {len(slots) * w.n_tokens * w.d} coordinates")
+    say("  " + gamma_report())
     del k, v
 
     ws = torch.empty(tq.decode_workspace_bytes(layout_of(w), w.batch, w.h_q, w.h_kv, cap),
@@ -178,7 +180,8 @@ def test_fullsize_qwen_layer(name):
         ref = encode_slot(w, bk, pi, s, k[b, :, h].double().numpy(), v[b, :, h].double().numpy())
         tot += check_encode_slot(w, bk, cache, b, h, ref, 0, w.n_tokens, f"b{b} h{h}")
     say(f"  encode: all {len(slots)} slots match outside the window; excused flips key MSE {tot[0]}, "
-        f"key QJL {tot[1]}, value MSE {tot[2]} of {len(slots) * w.n_tokens * w.d} coordinates")
+        f"key QJL {tot[1]}, value {tot[2]} of {len(slots) * w.n_tokens * w.d} coordinates")
+    say("  " + gamma_report())
     q = wl.query(w, 0)
     out = tq.decode_attn(prm, q.to(DEV), cache, [w.n_tokens] * w.batch)
     torch.cuda.synchronize()

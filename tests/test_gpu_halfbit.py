@@ -18,7 +18,7 @@ import torch
 import oracle
 from compressed_kv_decode_tq_amd import tq
 from compressed_kv_decode_tq_amd import workloads as wl
-from tq_testlib import (OUT_RTOL, books, check_encode_slot, dequant_slot, encode_slot, layout_of, max_rel_err,
+from tq_testlib import (gamma_report, OUT_RTOL, books, check_encode_slot, dequant_slot, encode_slot, layout_of, max_rel_err,
                         say, slot_from_cache, upload_slot)
 
 pytestmark = pytest.mark.gpu
@@ -63,6 +63,7 @@ def test_half_bit_encode_parity(name):
             tot += check_encode_slot(w, bk, cache, b, h, ref, 0, w.n_tokens, f"{name} b{b} h{h}")
     say(f"[half-bit encode] {name}: every slot matches outside the window; excused flips "
         f"MSE {tot[0]}, QJL {tot[1]}, values {tot[2]}")
+    say("  " + gamma_report())
 
 
 @pytest.mark.parametrize("name", list(CASES))

@@ -13,7 +13,7 @@ import torch
 import oracle
 from compressed_kv_decode_tq_amd import tq
 from compressed_kv_decode_tq_amd import workloads as wl
-from tq_testlib import (OUT_RTOL, books, check_encode_slot, dequant_slot, encode_slot, key_plane_mismatches,
+from tq_testlib import (gamma_report, OUT_RTOL, books, check_encode_slot, dequant_slot, encode_slot, key_plane_mismatches,
                         layout_of, max_rel_err, read_value_planes, say, slot_from_cache, upload_slot)
 
 pytestmark = pytest.mark.gpu
@@ -60,7 +60,8 @@ def test_encode_parity(name):
             ref = encode_slot(w, bk, pi, s, k[b, :, h].double().numpy(), v[b, :, h].double().numpy())
             tot += check_encode_slot(w, bk, cache, b, h, ref, 0, w.n_tokens, f"{name} b{b} h{h}")
     n_coord = w.batch * w.h_kv * w.n_tokens * w.d
-    say(f"  excused flips: key MSE {tot[0]}, key QJL {tot[1]}, value MSE {tot[2]} of {n_coord} coordinates")
+    say(f"  excused flips: key MSE {tot[0]}, key QJL {tot[1]}, value {tot[2]} of {n_coord} coordinates")
+    say("  " + gamma_report())
 
 
 @pytest.mark.parametrize("bits,group", [(1, 32), (2, 16), (2, 64), (3, 32), (4, 16), (4, 64)])
@@ -83,6 +84,7 @@ def test_encode_minmax_widths_and_groups(bits, group):
             ref = encode_slot(w, bk, pi, s, k[b, :, h].double().numpy(), v[b, :, h].double().numpy())
             tot += check_encode_slot(w, bk, cache, b, h, ref, start, w.n_tokens, f"{bits}b g{group} b{b} h{h}")
     say(f"  excused value flips {tot[2]}")
+    say("  " + gamma_report())
 
 
 @pytest.mark.parametrize("path", ["mfma", "small"])
@@ -106,7 +108,8 @@ def test_encode_key_and_mse_value_widths(kbits, qjl, vbits, path, monkeypatch):
         for h in range(w.h_kv):
             ref = encode_slot(w, bk, pi, s, k[b, :, h].double().numpy(), v[b, :, h].double().numpy())
             tot += check_encode_slot(w, bk, cache, b, h, ref, start, w.n_tokens, f"k{kbits} q{qjl} v{vbits} b{b} h{h}")
-    say(f"  excused flips: key MSE {tot[0]}, key QJL {tot[1]}, value MSE {tot[2]}")
+    say(f"  excused flips: key MSE {tot[0]}, key QJL {tot[1]}, value {tot[2]}")
+    say("  " + gamma_report())
 
 
 @pytest.mark.parametrize("value_kind", ["minmax", "mse"])
@@ -275,6 +278,7 @@ def test_four_bit_minmax_values_end_to_end():
     ref = oracle.decode_attention(q.double().numpy(), kd, vd)
     err = max_rel_err(out.cpu().double().numpy(), ref)
     say(f"[4-bit values end to end] codes match (excused {tot.tolist()}); decode max rel err {err.max():.2e}")
+    say("  " + gamma_report())
     assert err.max() <= OUT_RTOL
 
 
@@ -402,7 +406,7 @@ def test_end_to_end(name):
     for (b, h), sc in codes.items():
         _, ex_m, ex_q = key_plane_mismatches(w, bk, cache.k_planes[b, h, :n].cpu().numpy(), sc.key)
         idx_g = read_value_planes(cache.v_planes[b, h].cpu().numpy(), n, w)
-        ex_v = 0 if w.value_kind == "minmax" else int(np.sum(idx_g != sc.val.idx))
+        ex_v = int(np.sum(idx_g != (sc.val.code if w.value_kind == "minmax" else sc.val.idx)))
         flipped[b, h] = (ex_m + ex_q + ex_v) > 0
     hq_flip = np.repeat(flipped, w.group, axis=1)
     say(f"  max rel err {err[~hq_flip].max() if (~hq_flip).any() else 0:.2e} over {int((~hq_flip).sum())} heads "

@@ -4,15 +4,23 @@ for attention, the GPU decode).
 This is a report with loose sanity bounds, not a parity test: parity against
 the oracle is in test_gpu_parity.py and test_gpu_fullsize.py.
 
-Protocols, following the pages:
+Protocols (the pages' claims give the questions; the experiments are this
+repository's own):
 
-- Needle retrieval (page "turboquant/audit_claims.py", AUDIT 2): 4096 noise
-  keys of scale sigma, one needle key of scale mu at position N/2, the query
-  equal to the needle.  A head succeeds when the needle has the largest
-  dequantized score.  The page reports 100 % retrieval down to SNR mu/sigma = 1.
-- Recall@k (same page, AUDIT 3): keys and queries 0.1 N(0, I), N = 4096,
-  64 queries.  Recall is the overlap of the top-k by quantized scores with the
-  exact top-k.  The page reports roughly 0.4-0.5 at k = 8 for 3 bits.
+- Retrieval by margin (the question of page "turboquant/audit_claims.py",
+  AUDIT 2: does a key the query points at stay the top score?): 8192
+  distractor keys uniform on the unit sphere, one target key at a random
+  position whose exact inner product with a unit query exceeds the largest
+  distractor's by a margin m, in units of the distractors' score standard
+  deviation 1/sqrt(d).  A trial succeeds when the target has the largest
+  quantized score; 16 trials per margin.  The page reports retrieval holding
+  down to an SNR of 1.
+- Nearest-key recall (the question of the same page's AUDIT 3, how well the
+  quantized scores rank keys): anisotropic keys (per-channel std drawn from
+  LogNormal(0, 1), as in the Qwen-shaped workload), N = 8192, 128 Gaussian
+  queries.  1-recall@k is the fraction of queries whose exact top-1 key is
+  among the k largest quantized scores; the median rank of that key is
+  reported too.
 - Inner-product distortion and bias (same page, AUDIT 5 and AUDIT 6): for
   unit keys and queries, E(<y, x~> - <y, x>)^2 stays below
   sqrt(3) pi^2 / (d 4^b), and the mean error is zero.
@@ -76,55 +84,65 @@ def _gpu_dequantized_keys(w: wl.Workload, keys: np.ndarray) -> list:
 
 
 @pytest.mark.timeout(300)
-def test_needle_retrieval():
-    rng = np.random.default_rng(7)
-    n, h_kv = 4096, 4
-    say("[needle retrieval] N=4096, 4 heads; needle key = query")
-    say(f"  {'SNR':>6} {'needle':>7} {'noise':>6} {'3-bit':>7} {'4-bit':>7}")
+def test_retrieval_by_margin():
+    rng = np.random.default_rng(17)
+    n, trials = 8192, 16
+    margins = (8, 6, 4, 3, 2, 1, 0)
+    say(f"[retrieval by margin] {n} unit-sphere distractors, target at a random position, "
+        f"{trials} trials per margin (margin in units of 1/sqrt(d))")
     rates = {}
-    for needle, noise in [(3.0, 0.02), (1.0, 0.1), (0.5, 0.1), (0.3, 0.1), (0.2, 0.1), (0.15, 0.1), (0.1, 0.1)]:
-        keys = rng.standard_normal((n, h_kv, D)) * noise
-        nk = rng.standard_normal((h_kv, D)) * needle
-        keys[n // 2] = nk
+    for bits in (3, 4):
+        w = _key_workload(bits, trials, n)
         row = []
-        for bits in (3, 4):
-            kd = _gpu_dequantized_keys(_key_workload(bits, h_kv, n), keys)
-            hits = sum(int(np.argmax(kd[h] @ nk[h]) == n // 2) for h in range(h_kv))
-            rates[(needle / noise, bits)] = hits / h_kv
-            row.append(hits / h_kv)
-        say(f"  {needle / noise:>6.1f} {needle:>7.2f} {noise:>6.2f} {row[0]:>7.0%} {row[1]:>7.0%}")
-    for snr in (150.0, 10.0):
-        for bits in (3, 4):
-            assert rates[(snr, bits)] == 1.0, (snr, bits)
+        for m in margins:
+            keys = rng.standard_normal((n, trials, D))
+            keys /= np.linalg.norm(keys, axis=-1, keepdims=True)
+            q = rng.standard_normal((trials, D))
+            q /= np.linalg.norm(q, axis=-1, keepdims=True)
+            pos = rng.integers(0, n, size=trials)
+            for t in range(trials):  # trial t is KV head t
+                c = min(float(np.max(keys[:, t] @ q[t])) + m / np.sqrt(D), 0.999)
+                u = rng.standard_normal(D)
+                u -= (u @ q[t]) * q[t]
+                u /= np.linalg.norm(u)
+                keys[pos[t], t] = c * q[t] + np.sqrt(1.0 - c * c) * u
+            kd = _gpu_dequantized_keys(w, keys)
+            hits = sum(int(np.argmax(kd[t] @ q[t]) == pos[t]) for t in range(trials))
+            rates[(bits, m)] = hits / trials
+            row.append(hits / trials)
+        say(f"  {bits}-bit keys: " + ", ".join(f"m={m}: {r:.0%}" for m, r in zip(margins, row)))
+    for bits in (3, 4):
+        for m in (8, 6, 4, 3):
+            assert rates[(bits, m)] == 1.0, (bits, m)
 
 
 @pytest.mark.timeout(300)
-def test_recall_at_k():
-    rng = np.random.default_rng(8)
-    n, nq = 4096, 64
-    keys = rng.standard_normal((n, 1, D)) * 0.1
-    queries = rng.standard_normal((nq, D)) * 0.1
-    true = queries @ keys[:, 0].T
-    say("[recall@k] N=4096, 64 queries, keys and queries 0.1 N(0, I)")
-    say(f"  {'bits':>4} " + " ".join(f"{'k=' + str(k):>7}" for k in (1, 4, 8, 16, 32, 64)))
-    rec = {}
+def test_nearest_key_recall():
+    rng = np.random.default_rng(18)
+    n, nq = 8192, 128
+    ks = (1, 4, 16, 64)
+    sig = np.exp(rng.standard_normal(D))
+    keys = rng.standard_normal((n, 1, D)) * sig
+    queries = rng.standard_normal((nq, D))
+    best = np.argmax(queries @ keys[:, 0].T, axis=1)
+    say(f"[nearest-key recall] N={n}, {nq} queries, keys with LogNormal(0,1) per-channel std")
+    say(f"  {'bits':>4} " + " ".join(f"{'@' + str(k):>6}" for k in ks) + "  median rank")
+    rec, med = {}, {}
     for bits in (2, 2.5, 3, 3.5, 4):
         kd = _gpu_dequantized_keys(_key_workload(bits, 1, n), keys)[0]
         est = queries @ kd.T
-        row = []
-        for k in (1, 4, 8, 16, 32, 64):
-            t = np.argsort(-true, axis=1)[:, :k]
-            e = np.argsort(-est, axis=1)[:, :k]
-            r = float(np.mean([len(set(t[i]) & set(e[i])) / k for i in range(nq)]))
-            rec[(bits, k)] = r
-            row.append(r)
-        say(f"  {bits:>4g} " + " ".join(f"{r:>7.3f}" for r in row))
-    # more bits rank better (a whole bit apart; half a bit apart the 64
-    # queries' noise can reorder neighbours), and every width is far above
-    # chance (8 / 4096)
-    assert rec[(2, 8)] < rec[(3, 8)] < rec[(4, 8)]
-    assert rec[(2.5, 8)] < rec[(3.5, 8)]
-    assert rec[(2, 8)] > 0.1
+        rank = np.array([int(np.sum(est[i] > est[i, best[i]])) for i in range(nq)])
+        med[bits] = float(np.median(rank))
+        for k in ks:
+            rec[(bits, k)] = float(np.mean(rank < k))
+        say(f"  {bits:>4g} " + " ".join(f"{rec[(bits, k)]:>6.3f}" for k in ks) + f"  {med[bits]:g}")
+    # whole bits rank strictly better; half a bit apart only the 2.5 / 3.5
+    # pair is far enough apart for 128 queries; every width is far above
+    # chance (16 / 8192)
+    assert rec[(2, 16)] < rec[(3, 16)] < rec[(4, 16)]
+    assert med[2] > med[3] > med[4]
+    assert rec[(2.5, 16)] < rec[(3.5, 16)]
+    assert rec[(2, 16)] > 0.2 and rec[(4, 64)] > 0.9
 
 
 @pytest.mark.timeout(300)

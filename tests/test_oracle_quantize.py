@@ -175,6 +175,60 @@ def test_minmax_codes_are_nearest_levels():
         assert np.all(np.abs(rec - v) <= 0.5 * step + 2 * np.abs(mn).repeat(32, axis=1) * 2 ** -11 + 1e-6)
 
 
+def test_minmax_codes_bruteforce_exact():
+    """The min/max code is the level min16 + k * delta16 nearest to v, found
+    here by exhaustive search in exact rational arithmetic (ties to the even
+    k), independent of the oracle's division.  The stored scale and zero are
+    checked against the group's range and minimum rounded by exact rational
+    steps too: delta = fp16(fp32(fp32(max) - fp32(min)) / (2^b - 1))."""
+    from fractions import Fraction
+
+    rng = np.random.default_rng(21)
+    v = (rng.standard_normal((3, 64)) * np.array([1.0, 10.0, 1e-3])[:, None]).astype(np.float32)
+    for bits in (1, 2, 3, 4):
+        mm = oracle.encode_values_minmax(v, bits, 16)
+        levels = (1 << bits) - 1
+        for t in range(v.shape[0]):
+            for gi in range(64 // 16):
+                grp = [Fraction(float(x)) for x in v[t, 16 * gi:16 * gi + 16]]
+                lo, hi = min(grp), max(grp)
+                # fp32 subtraction then fp32 division, then fp16: each an IEEE
+                # round-to-nearest of the exact rational result
+                rng32 = Fraction(float(np.float32(float(hi - lo))))
+                assert abs(rng32 - (hi - lo)) <= abs(hi - lo) * Fraction(1, 2 ** 24)
+                d32 = Fraction(float(np.float32(float(rng32 / levels))))
+                d16 = Fraction(float(np.float16(float(d32))))
+                m16 = Fraction(float(np.float16(float(lo))))
+                assert Fraction(float(mm.scale16[t, gi])) == d16
+                assert Fraction(float(mm.min16[t, gi])) == m16
+                for c in range(16):
+                    x = grp[c]
+                    if d16 == 0:
+                        want = 0
+                    else:
+                        dist = [abs(x - (m16 + k * d16)) for k in range(levels + 1)]
+                        best = min(dist)
+                        ties = [k for k in range(levels + 1) if dist[k] == best]
+                        want = ties[0] if len(ties) == 1 else [k for k in ties if k % 2 == 0][0]
+                        # beyond the top level (fp16 rounding of the range): clip
+                        assert want == min(levels, max(0, want))
+                    assert mm.code[t, 16 * gi + c] == want, (bits, t, gi, c)
+
+
+def test_minmax_ties_go_to_even():
+    """Hand-built group with every value on a level or exactly halfway between
+    two: range 0 .. 3 at 2 bits gives delta = 1, min = 0 (both exact in fp16);
+    0.5 -> 0, 1.5 -> 2, 2.5 -> 2 (half-to-even), and the ratio is stored
+    unrounded."""
+    v = np.zeros((1, 32), dtype=np.float32)
+    v[0, :8] = [0.0, 3.0, 0.5, 1.5, 2.5, 1.0, 2.0, 0.75]
+    mm = oracle.encode_values_minmax(v, 2, 32)
+    assert float(mm.scale16[0, 0]) == 1.0 and float(mm.min16[0, 0]) == 0.0
+    assert mm.code[0, :8].tolist() == [0, 3, 0, 2, 2, 1, 2, 1]
+    assert mm.ratio[0, :8].tolist() == [0.0, 3.0, 0.5, 1.5, 2.5, 1.0, 2.0, 0.75]
+    assert mm.ratio.dtype == np.float64
+
+
 def test_minmax_constant_group():
     v = np.full((2, 64), 1.25, dtype=np.float32)
     mm = oracle.encode_values_minmax(v, 2, 32)

@@ -16,6 +16,18 @@ from compressed_kv_decode_tq_amd import workloads as wl
 WINDOW = 1e-5          # codes may differ only where the oracle's coordinate is this close to a boundary
 OUT_RTOL = 2e-3        # max relative error of an attention output vector
 
+# Largest |gamma_gpu - gamma_oracle| seen by check_encode_slot (fp32 scalars),
+# reported by gamma_report().
+_GAMMA_ERR = {"max": 0.0, "tokens": 0}
+
+
+def gamma_report() -> str:
+    """Largest residual-norm error seen since the last report, then reset."""
+    r = (f"max |gamma - gamma_oracle| {_GAMMA_ERR['max']:.2e} over {_GAMMA_ERR['tokens']} tokens "
+         f"(bound {WINDOW:g} * sqrt(d))")
+    _GAMMA_ERR.update(max=0.0, tokens=0)
+    return r
+
 
 def say(*a):
     print(*a, flush=True)
@@ -179,7 +191,8 @@ def key_plane_mismatches(w: wl.Workload, bk: OracleBooks, gpu_planes: np.ndarray
 
 def check_encode_slot(w, bk, cache, b, h, ref, start, n, tag):
     """Compare the device cache slot (b, h) positions start..start+n-1 with the
-    oracle code `ref`; returns excused counts."""
+    oracle code `ref`; returns the excused counts (key MSE bits, key QJL bits,
+    value codes: MSE or min/max)."""
     kp = cache.k_planes[b, h, start:start + n].cpu().numpy()
     bad, ex_m, ex_q = key_plane_mismatches(w, bk, kp, ref.key)
     assert bad == 0, f"{tag}: {bad} key bits differ outside the {WINDOW} window"
@@ -198,22 +211,36 @@ def check_encode_slot(w, bk, cache, b, h, ref, start, n, tag):
             ulp = np.spacing(ref.key.rnorm.astype(np.float16)).astype(np.float64)
             assert np.all(np.abs(kr - ref.key.rnorm)[ok] <= ulp[ok] * 1.01), tag
         else:
-            # the rotation uses Pi = Pi_hi + Pi_lo in bf16 (each entry within
-            # 2^-18 |Pi_ij|), and fp32 inputs are split the same way, so
-            # |dr| <= 2 * 2^-18 * |Pi|_F = 2^-17 sqrt(d) bounds |d gamma|
-            bound = 2.0 ** -17 * np.sqrt(w.d)
-            assert np.all(np.abs(kr - ref.key.rnorm)[ok] <= bound), (tag, np.max(np.abs(kr - ref.key.rnorm)[ok]))
+            # The encode rule lets a rotated coordinate y_i move by up to WINDOW
+            # (a code may flip only that close to a boundary).  gamma is the norm
+            # of the residual y - c[idx] in rotated coordinates, so on a token with
+            # no flipped code such a perturbation moves it by at most
+            # |dy| <= WINDOW * sqrt(d) (triangle inequality).
+            bound = WINDOW * np.sqrt(w.d)
+            err = np.abs(kr - ref.key.rnorm)[ok]
+            if err.size:
+                _GAMMA_ERR["max"] = max(_GAMMA_ERR["max"], float(err.max()))
+                _GAMMA_ERR["tokens"] += int(err.size)
+            assert np.all(err <= bound), (tag, float(err.max()), bound)
     # values
     blk0 = start // 32
     nblk = (start + n + 31) // 32 - blk0
     words = cache.v_planes[b, h, blk0:blk0 + nblk].cpu().numpy()
     codes = read_value_planes(words, nblk * 32, w)[start - blk0 * 32: start - blk0 * 32 + n]
     if w.value_kind == "minmax":
-        assert np.array_equal(codes, ref.val.code), f"{tag}: min/max codes differ"
+        # a code may differ only where the oracle's ratio (v - min16) / delta16
+        # lies within WINDOW (in code units) of a rounding midpoint k + 1/2, and
+        # then only to the other neighbour of that midpoint
+        bad_v = codes != ref.val.code
+        r = ref.val.ratio
+        near = np.abs(r - np.floor(r) - 0.5) < WINDOW
+        assert np.sum(bad_v & ~near) == 0, \
+            f"{tag}: {int(np.sum(bad_v & ~near))} min/max codes differ outside the window"
+        assert np.all(np.abs(codes[bad_v] - ref.val.code[bad_v]) == 1), f"{tag}: min/max code off by more than 1"
+        ex_v = int(np.sum(bad_v))
         meta = cache.v_meta[b, h, start:start + n].cpu().numpy()
         assert np.array_equal(meta[..., 0].view(np.uint16), ref.val.scale16.view(np.uint16)), tag
         assert np.array_equal(meta[..., 1].view(np.uint16), ref.val.min16.view(np.uint16)), tag
-        ex_v = 0
     else:
         bad_v = codes != ref.val.idx
         near = np.min(np.abs(ref.val.y[..., None] - bk.v.thresholds[None, None, :]), axis=-1) < WINDOW
