@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtq.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["tq_api.cpp", "tq_codebook.cpp", "tq_encode.hip", "tq_decode.hip", "tq_decode_mfma.hip"]
+SOURCES = ["tq_api.cpp", "tq_codebook.cpp", "tq_encode.hip", "tq_decode.hip", "tq_decode_mfma.hip", "tq_noalloc.hip"]
 ARCH = os.environ.get("TQ_OFFLOAD_ARCH", "gfx950")
 # MFMA results land in ordinary VGPRs in the decode scan (no accumulator-register
 # copies: every result is consumed by VALU code right away)

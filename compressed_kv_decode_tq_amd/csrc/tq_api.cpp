@@ -311,7 +311,8 @@ int decode_attn_impl(const tq_layout* layout, const tq_params* params, const voi
                      int32_t num_q_heads, int32_t nq, const tq_cache* cache, const int64_t* n_compressed_host,
                      const void* ring_k, const void* ring_v, int32_t ring_cap, const int32_t* n_ring_host,
                      float softmax_scale, float* out, void* workspace, size_t workspace_bytes, void* stream,
-                     const void* k_new = nullptr, const void* v_new = nullptr, int32_t new_dtype = 0) {
+                     const void* k_new = nullptr, const void* v_new = nullptr, int32_t new_dtype = 0,
+                     bool noalloc = false) {
   g_err[0] = 0;
   const bool append = k_new != nullptr || v_new != nullptr;
   if (append) {
@@ -348,6 +349,14 @@ int decode_attn_impl(const tq_layout* layout, const tq_params* params, const voi
     max_tokens = std::max<int64_t>(max_tokens, n_compressed_host[b]);
   }
   const size_t need = decode_workspace_bytes_impl(layout, cache->batch, num_q_heads, h_kv, max_tokens, nq);
+  if (noalloc) {
+    // the static scratch: sizes beyond it are refused before the device is touched
+    if (need > TQ_NOALLOC_SCRATCH_BYTES)
+      return fail(TQ_ERR_WORKSPACE, "this call needs %zu bytes of workspace; the static scratch of "
+                  "tq_decode_attn_noalloc holds %zu", need, (size_t)TQ_NOALLOC_SCRATCH_BYTES);
+    hipError_t e = tq::noalloc_scratch(&workspace, &workspace_bytes);
+    if (e != hipSuccess) return hip_fail(e, "static decode scratch address");
+  }
   if (!workspace || workspace_bytes < need)
     return fail(TQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
 
@@ -493,6 +502,16 @@ int tq_decode_attn_append(const tq_layout* layout, const tq_params* params, cons
   return decode_attn_impl(layout, params, q, q_dtype, num_q_heads, 1, cache, n_compressed_host, ring_k, ring_v,
                           ring_cap, n_ring_host, softmax_scale, out, workspace, workspace_bytes, stream, k_new,
                           v_new, new_dtype);
+}
+
+int tq_decode_attn_noalloc(const tq_layout* layout, const tq_params* params, const void* q,
+                           int32_t q_dtype, int32_t num_q_heads, const tq_cache* cache,
+                           const int64_t* n_compressed_host, const void* ring_k, const void* ring_v,
+                           int32_t ring_cap, const int32_t* n_ring_host, float softmax_scale, float* out,
+                           void* stream) {
+  return decode_attn_impl(layout, params, q, q_dtype, num_q_heads, 1, cache, n_compressed_host, ring_k, ring_v,
+                          ring_cap, n_ring_host, softmax_scale, out, nullptr, 0, stream, nullptr, nullptr, 0,
+                          true);
 }
 
 int tq_decode_attn_multi(const tq_layout* layout, const tq_params* params, const void* q,

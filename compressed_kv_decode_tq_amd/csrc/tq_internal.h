@@ -202,6 +202,10 @@ size_t mfma_workspace_bytes(int batch, int h_q, int group);
 // The combine step shared by both decode paths.
 hipError_t launch_combine(const DecodeArgs& a, int value_mse, hipStream_t stream);
 
+// Device address and size of the static decode scratch on the current device
+// (tq_noalloc.hip); the address is looked up on the first call per device.
+hipError_t noalloc_scratch(void** ptr, size_t* bytes);
+
 // Decode work split used for the workspace size and the launch.
 void decode_split(int64_t max_tokens, int64_t units, int32_t* splits, int32_t* split_len);
 // Upper bound of decode_split's split count over all token counts <= max_tokens.

@@ -26,7 +26,7 @@ MAX_LEVELS = 16
 EXPORTS = ("tq_make_codebook", "tq_memory_bytes", "tq_params_derived_bytes", "tq_prepare_params",
            "tq_encode_kv", "tq_ring_append", "tq_decode_workspace_bytes", "tq_decode_attn",
            "tq_decode_workspace_bytes_multi", "tq_decode_attn_multi", "tq_decode_attn_append",
-           "tq_time_next_launch", "tq_last_error", "tq_version")
+           "tq_decode_attn_noalloc", "tq_time_next_launch", "tq_last_error", "tq_version")
 TQ_KERNEL_DECODE_SCAN, TQ_KERNEL_ENCODE_KEYS, TQ_KERNEL_ENCODE_VALUES = 0, 1, 2
 
 
@@ -98,6 +98,9 @@ def lib() -> ctypes.CDLL:
         L.tq_decode_attn_append.argtypes = [P(_Layout), P(_Params), vp, i32, i32, P(_Cache), P(i64), vp, vp, i32,
                                             vp, vp, i32, P(i32), ctypes.c_float, vp, vp, sz, vp]
         L.tq_decode_attn_append.restype = ctypes.c_int
+        L.tq_decode_attn_noalloc.argtypes = [P(_Layout), P(_Params), vp, i32, i32, P(_Cache), P(i64), vp, vp,
+                                             i32, P(i32), ctypes.c_float, vp, vp]
+        L.tq_decode_attn_noalloc.restype = ctypes.c_int
         L.tq_time_next_launch.argtypes = [i32, vp, vp]
         L.tq_time_next_launch.restype = ctypes.c_int
         L.tq_last_error.argtypes = []

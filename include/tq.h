@@ -26,7 +26,8 @@
  * Conventions for every entry point:
  *  - Pointers are DEVICE pointers unless the argument name ends in _host.
  *    Every buffer is owned by the caller; the library never allocates or
- *    frees device memory and keeps no state between calls.
+ *    frees device memory.  It keeps no state between calls, apart from the
+ *    static device scratch of tq_decode_attn_noalloc.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Device work is
  *    enqueued on it asynchronously; a device fault surfaces at the caller's
  *    next synchronisation.
@@ -266,6 +267,32 @@ int tq_decode_attn_multi(const tq_layout* layout, const tq_params* params, const
                          const int64_t* n_compressed_host, const void* ring_k, const void* ring_v,
                          int32_t ring_cap, const int32_t* n_ring_host, float softmax_scale, float* out,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Size of the static device scratch of tq_decode_attn_noalloc: 32 MiB, the
+ * workspace of up to 64 sequences per launch group with 32 KV heads of 8
+ * query heads each at any length. */
+#define TQ_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* Decode step that allocates nothing, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): tq_decode_attn without the workspace arguments.  The
+ * workspace lives in a static device array of TQ_NOALLOC_SCRATCH_BYTES bytes
+ * that each GPU holds from the library's first use on it until the process
+ * ends; the array's device address is looked up once per device, on the first
+ * call made with that device current.  Every call on a GPU shares that GPU's
+ * array and the array keeps the last call's contents: calls that overlap on
+ * one GPU (two streams, two host threads) race, so the caller serialises
+ * them.  Nothing needs clearing between calls: every workspace byte a call
+ * reads is written earlier in the same call.  q, out and every other argument
+ * as tq_decode_attn.  Errors as tq_decode_attn, plus TQ_ERR_WORKSPACE, with
+ * nothing launched, when the call needs more workspace than the scratch holds
+ * (tq_decode_workspace_bytes for its sizes above TQ_NOALLOC_SCRATCH_BYTES),
+ * and TQ_ERR_HIP when the scratch's address cannot be obtained. */
+int tq_decode_attn_noalloc(const tq_layout* layout, const tq_params* params, const void* q,
+                           int32_t q_dtype, int32_t num_q_heads, const tq_cache* cache,
+                           const int64_t* n_compressed_host, const void* ring_k, const void* ring_v,
+                           int32_t ring_cap, const int32_t* n_ring_host, float softmax_scale, float* out,
+                           void* stream);
 
 /* Measurement hook.  The next launch of `kernel` (TQ_KERNEL_*) made by the
  * calling thread records ev_begin just before it and ev_end just after it on
