@@ -116,6 +116,9 @@ def _check(rc: int):
         raise TqError(rc, lib().tq_last_error().decode())
 
 
+_LAYOUT_C: dict = {}  # Layout -> its C struct (a Layout is immutable)
+
+
 @dataclasses.dataclass(frozen=True)
 class Layout:
     head_dim: int = 128
@@ -128,8 +131,11 @@ class Layout:
     key_half: int = 0  # 1: half of the rotated coordinates get key_mse_bits + 1 bits
 
     def c(self) -> _Layout:
-        return _Layout(self.head_dim, self.key_mse_bits, self.key_qjl, self.value_kind,
-                       self.value_bits, self.value_group, self.scalar_dtype, self.key_half)
+        st = _LAYOUT_C.get(self)
+        if st is None:
+            st = _LAYOUT_C[self] = _Layout(self.head_dim, self.key_mse_bits, self.key_qjl, self.value_kind,
+                                           self.value_bits, self.value_group, self.scalar_dtype, self.key_half)
+        return st
 
     @property
     def key_planes(self) -> int:
@@ -174,6 +180,9 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
+_F32, _BF16, _U8 = torch.float32, torch.bfloat16, torch.uint8
+
+
 def _require(cond: bool, msg: str):
     if not cond:
         raise ValueError(msg)
@@ -194,6 +203,12 @@ def _check_ring(cache: "Cache", ring_k, ring_v, n_ring, d: int):
     """Rings: both or neither; contiguous bf16 [B, R, H_kv, d] of one shape."""
     if ring_k is None and ring_v is None:
         return 0
+    if (ring_k is not None and ring_v is not None and ring_k.dtype is _BF16 and ring_v.dtype is _BF16
+            and ring_k.dim() == 4 and ring_k.shape == ring_v.shape and ring_k.shape[0] == cache.batch
+            and ring_k.shape[2] == cache.num_kv_heads and ring_k.shape[3] == d and ring_k.shape[1] > 0
+            and ring_k.is_contiguous() and ring_v.is_contiguous() and n_ring is not None
+            and len(n_ring) == cache.batch):
+        return int(ring_k.shape[1])
     _require(ring_k is not None and ring_v is not None, "ring_k and ring_v must be given together")
     for name, r in (("ring_k", ring_k), ("ring_v", ring_v)):
         _require(r.dtype == torch.bfloat16, f"{name} must be bf16")
@@ -208,7 +223,22 @@ def _check_ring(cache: "Cache", ring_k, ring_v, n_ring, d: int):
 
 def _check_decode(layout: Layout, q: torch.Tensor, cache: "Cache", n_compressed, out, workspace):
     """Shapes, dtypes, contiguity and devices of a decode call, checked before
-    anything reaches the library (which trusts sizes it is given)."""
+    anything reaches the library (which trusts sizes it is given).  The common
+    case is one expression; anything off goes through the detailed checks,
+    which name the problem."""
+    sh = q.shape
+    dev = cache.k_planes.device
+    if (len(sh) in (3, 4) and sh[0] == cache.batch and sh[-1] == layout.head_dim and sh[-2] > 0
+            and sh[-2] % cache.num_kv_heads == 0 and (q.dtype is _F32 or q.dtype is _BF16) and q.device == dev
+            and q.is_contiguous() and len(n_compressed) == cache.batch
+            and (out is None or (out.dtype is _F32 and out.shape == sh and out.device == dev and out.is_contiguous()))
+            and (workspace is None or (workspace.dtype is _U8 and workspace.device == dev
+                                       and workspace.is_contiguous()))):
+        return
+    _check_decode_detail(layout, q, cache, n_compressed, out, workspace)
+
+
+def _check_decode_detail(layout: Layout, q: torch.Tensor, cache: "Cache", n_compressed, out, workspace):
     d = layout.head_dim
     _require(q.dim() in (3, 4), "q must be [B, H_q, d] or [B, T, H_q, d]")
     _require(q.dtype in (torch.float32, torch.bfloat16), "q must be fp32 or bf16")
@@ -253,6 +283,11 @@ class Params:
             self.v_centroids = self.v_thresholds = np.zeros(0, dtype=np.float32)
 
     def c(self) -> _Params:
+        """The C struct; built on first use (a Params is not changed after
+        construction)."""
+        p = self.__dict__.get("_cstruct")
+        if p is not None:
+            return p
         p = _Params()
         p.pi, p.s, p.derived = _ptr(self.pi), _ptr(self.s), _ptr(self.derived)
         for i, x in enumerate(self.k_centroids):
@@ -267,6 +302,7 @@ class Params:
             p.k_centroids_hi[i] = float(x)
         for i, x in enumerate(self.k_thresholds_hi):
             p.k_thresholds_hi[i] = float(x)
+        self._cstruct = p
         return p
 
 
@@ -294,8 +330,13 @@ class Cache:
             self.v_norm = torch.zeros(shp, dtype=sd, device=device)
 
     def c(self) -> _Cache:
-        return _Cache(_ptr(self.k_planes), _ptr(self.k_norm), _ptr(self.k_rnorm), _ptr(self.v_planes),
-                      _ptr(self.v_meta), _ptr(self.v_norm), self.batch, self.num_kv_heads, self.capacity)
+        """The C struct; built on first use (the tensors are fixed at construction)."""
+        st = self.__dict__.get("_cstruct")
+        if st is None:
+            st = self._cstruct = _Cache(_ptr(self.k_planes), _ptr(self.k_norm), _ptr(self.k_rnorm),
+                                        _ptr(self.v_planes), _ptr(self.v_meta), _ptr(self.v_norm), self.batch,
+                                        self.num_kv_heads, self.capacity)
+        return st
 
 
 def encode_kv(params: Params, k: torch.Tensor, v: torch.Tensor, dst_pos, cache: Cache, stream=None):
@@ -371,12 +412,11 @@ def decode_attn(params: Params, q: torch.Tensor, cache: Cache, n_compressed, rin
         scale = 1.0 / float(np.sqrt(d))
     if out is None:
         out = torch.empty(tuple(q.shape), dtype=torch.float32, device=q.device)
-    nc = (ctypes.c_int64 * b)(*[int(x) for x in n_compressed])
-    max_tokens = max(int(x) for x in n_compressed)
-    need = decode_workspace_bytes(lay_py, b, h_q, cache.num_kv_heads, max_tokens, nq)
-    if workspace is None:
+    nc = (ctypes.c_int64 * b)(*n_compressed)
+    if workspace is None:  # (a given workspace is checked against the need by the library)
+        need = decode_workspace_bytes(lay_py, b, h_q, cache.num_kv_heads, max(n_compressed), nq)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    nr = (ctypes.c_int32 * b)(*([int(x) for x in n_ring] if n_ring is not None else [0] * b))
+    nr = (ctypes.c_int32 * b)(*(n_ring if n_ring is not None else [0] * b))
     lay, prm, cc = lay_py.c(), params.c(), cache.c()
     if multi:
         _check(lib().tq_decode_attn_multi(ctypes.byref(lay), ctypes.byref(prm), _ptr(q), _dtype_code(q), h_q, nq,
@@ -418,12 +458,11 @@ def decode_attn_append(params: Params, q: torch.Tensor, cache: Cache, n_compress
         scale = 1.0 / float(np.sqrt(d))
     if out is None:
         out = torch.empty(tuple(q.shape), dtype=torch.float32, device=q.device)
-    nc = (ctypes.c_int64 * b)(*[int(x) for x in n_compressed])
-    max_tokens = max(int(x) for x in n_compressed)
-    need = decode_workspace_bytes(lay_py, b, h_q, cache.num_kv_heads, max_tokens)
-    if workspace is None:
+    nc = (ctypes.c_int64 * b)(*n_compressed)
+    if workspace is None:  # (a given workspace is checked against the need by the library)
+        need = decode_workspace_bytes(lay_py, b, h_q, cache.num_kv_heads, max(n_compressed))
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    nr = (ctypes.c_int32 * b)(*[int(x) for x in n_ring])
+    nr = (ctypes.c_int32 * b)(*n_ring)
     lay, prm, cc = lay_py.c(), params.c(), cache.c()
     _check(lib().tq_decode_attn_append(ctypes.byref(lay), ctypes.byref(prm), _ptr(q), _dtype_code(q), h_q,
                                        ctypes.byref(cc), nc, _ptr(k_new), _ptr(v_new), _dtype_code(k_new),
