@@ -11,6 +11,7 @@
 //   o     = sum_j p_j v~_j / sum_j p_j over compressed and ring tokens, where
 //           v~_j = min_j + delta_j code_j (min/max values) or, for MSE values,
 //           the accumulation runs in rotated space and Pi^T is applied once.
+#include "tq_combine.h"
 #include "tq_common.h"
 #include "tq_internal.h"
 
@@ -311,170 +312,18 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(DecodeArgs a) {
   }
 }
 
-// Combine: work-group per (sequence, query head), thread per channel.
-// Largest split count the combine kernel stages in LDS (decode_max_splits never
-// exceeds 2048 work-groups' worth of splits of one (sequence, KV head)).
+// Combine as its own kernel: work-group per (sequence, KV head, virtual head),
+// thread per channel.  Largest split count it stages in LDS (decode_max_splits
+// never exceeds 2048 work-groups' worth of splits of one slot).
 constexpr int kMaxCombineSplits = 2048;
 
-// Sum / max over a 128-thread block (two waves), result in every thread.
-__device__ __forceinline__ float block2_sum(float x, float* red2) {
-  x = wave_sum(x);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red2[w] = x;
-  __syncthreads();
-  return red2[0] + red2[1];
-}
-__device__ __forceinline__ float block2_max(float x, float* red2) {
-  x = wave_max(x);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red2[w] = x;
-  __syncthreads();
-  return fmaxf(red2[0], red2[1]);
-}
-
-// Merge of the split partials (m, l, acc) of one (sequence, query head) with
-// the exact ring tokens; MSE values are rotated back with Pi^T once.  Every
-// load that needs no earlier result (split headers, the first 16 splits' acc
-// words, the ring key row, the first 32 ring values) is issued before the
-// first use, so the merge costs about one memory round trip.
-constexpr int kCombinePre = 16;   // splits whose acc word is loaded up front
-constexpr int kRingPre = 32;      // ring values loaded up front
 template <bool VMSE>
 __global__ __launch_bounds__(kD) void combine_kernel(DecodeArgs a) {
-  __shared__ float qv[kD];
-  __shared__ float s_f[kMaxCombineSplits];  // per split: m, then its merge factor
-  __shared__ float s_l[kMaxCombineSplits];
-  __shared__ float pr[kD];                  // ring probabilities (ring_cap <= 128 per pass)
-  __shared__ float arot[kD];
-  __shared__ float red2[2];
-  // block = (sequence, KV head, virtual head of the launch)
+  __shared__ CombineLds<kMaxCombineSplits> lds;
   const int rows = a.h_kv * a.group;
   const int b = blockIdx.x / rows, h = (blockIdx.x % rows) / a.group, gq = blockIdx.x % a.group;
-  int t, hq, hide_c, hide_r;
-  virtual_head(a, h, gq, t, hq);
-  const int c = threadIdx.x;
-  hidden_keys(a, t, (int)a.n_ring.v[b], hide_c, hide_r);
-  const int nr = (int)a.n_ring.v[b] - hide_r;  // ring tokens this query sees
-  const int S = a.splits;
-  const float* part0 = a.partial + ws_row(a, b, h, gq) * (kD + 2);
-  const size_t sstride = (size_t)a.batch * rows * (kD + 2);
-  const size_t ring_row = (size_t)b * a.ring_cap * a.h_kv + h;  // ring token j: (ring_row + j h_kv) kD
-
-  // ---- loads
-  const size_t qoff = q_row(a, b, t, hq) * kD + c;
-  const float qc = a.q_bf16 ? bf2f(reinterpret_cast<const uint16_t*>(a.q)[qoff])
-                            : reinterpret_cast<const float*>(a.q)[qoff];
-  float hm = -INFINITY, hl = 0.f;  // header of split c (thread c < S)
-  if (c < S) {
-    hm = part0[(size_t)c * sstride];
-    hl = part0[(size_t)c * sstride + 1];
-  }
-  float pa[kCombinePre];
-#pragma unroll
-  for (int u = 0; u < kCombinePre; ++u) pa[u] = u < S ? part0[(size_t)u * sstride + 2 + c] : 0.f;
-  u32x4 kw[kD / 8];  // thread j's ring token key row (256 bytes)
-  if (c < nr) {
-    const u32x4* kr = reinterpret_cast<const u32x4*>(a.ring_k + (ring_row + (size_t)c * a.h_kv) * kD);
-#pragma unroll
-    for (int i = 0; i < kD / 8; ++i) kw[i] = kr[i];
-  }
-  float rv[kRingPre];
-#pragma unroll
-  for (int u = 0; u < kRingPre; ++u)
-    rv[u] = u < nr ? bf2f(a.ring_v[(ring_row + (size_t)u * a.h_kv) * kD + c]) : 0.f;
-
-  // ---- split headers (m, l): thread c takes splits c, c + 128, ...
-  qv[c] = qc;
-  float M = hm;
-  if (c < S) {
-    s_f[c] = hm;
-    s_l[c] = hl;
-  }
-  for (int sp = c + kD; sp < S; sp += kD) {
-    const float* ph = part0 + (size_t)sp * sstride;
-    const float m = ph[0], l = ph[1];
-    s_f[sp] = m;
-    s_l[sp] = l;
-    M = fmaxf(M, m);
-  }
-  __syncthreads();  // qv
-
-  // ring scores: thread j scores ring token j
-  float sj = -INFINITY;
-  if (c < nr) {
-    float acc = 0.f;
-#pragma unroll
-    for (int i = 0; i < kD / 8; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc = fmaf(qv[8 * i + 2 * e], bf2f(kw[i][e] & 0xffffu), acc);
-        acc = fmaf(qv[8 * i + 2 * e + 1], bf2f(kw[i][e] >> 16), acc);
-      }
-    sj = a.scale * acc;
-  }
-  M = block2_max(fmaxf(M, sj), red2);
-  float* outp = a.out + q_row(a, b, t, hq) * kD;
-  if (M == -INFINITY) {  // no token at all
-    outp[c] = 0.f;
-    return;
-  }
-
-  // merge factors of the splits and of the ring tokens; L in one block sum
-  float Lp = 0.f;
-  for (int sp = c; sp < S; sp += kD) {
-    const float m = s_f[sp];
-    const float f = m == -INFINITY ? 0.f : __expf(m - M);
-    s_f[sp] = f;
-    Lp = fmaf(f, s_l[sp], Lp);
-  }
-  const float pj = c < nr ? __expf(sj - M) : 0.f;
-  pr[c] = pj;
-  const float L = block2_sum(Lp + pj, red2);  // its barriers also publish s_f and pr
-
-  // channel c: sum over splits of f_s acc_s[c]; splits past the first
-  // kCombinePre are loaded sixteen at a time
-  float A = 0.f;
-#pragma unroll
-  for (int u = 0; u < kCombinePre; ++u)
-    if (u < S) A = fmaf(s_f[u], pa[u], A);
-  int sp = kCombinePre;
-  for (; sp + 16 <= S; sp += 16) {
-    float v[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) v[u] = part0[(size_t)(sp + u) * sstride + 2 + c];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) A = fmaf(s_f[sp + u], v[u], A);
-  }
-  for (; sp < S; ++sp) A = fmaf(s_f[sp], part0[(size_t)sp * sstride + 2 + c], A);
-
-  if (VMSE) {  // accumulated in rotated space: apply Pi^T once (column c of Pi)
-    arot[c] = A;
-    __syncthreads();
-    float o = 0.f;
-    for (int i0 = 0; i0 < kD; i0 += 16) {
-      float w[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) w[u] = a.pi[(size_t)(i0 + u) * kD + c];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) o = fmaf(w[u], arot[i0 + u], o);
-    }
-    A = o;
-  }
-  // ring values (original space): the first kRingPre are in registers, the
-  // rest come 32 loads at a time
-#pragma unroll
-  for (int u = 0; u < kRingPre; ++u) A = fmaf(u < nr ? pr[u] : 0.f, rv[u], A);
-  for (int j0 = kRingPre; j0 < nr; j0 += 32) {
-    float v[32];
-#pragma unroll
-    for (int u = 0; u < 32; ++u)
-      v[u] = j0 + u < nr ? bf2f(a.ring_v[(ring_row + (size_t)(j0 + u) * a.h_kv) * kD + c]) : 0.f;
-#pragma unroll
-    for (int u = 0; u < 32; ++u) A = fmaf(j0 + u < nr ? pr[j0 + u] : 0.f, v[u], A);
-  }
-  outp[c] = L > 0.f ? A / L : 0.f;
+  combine_unit<VMSE, kMaxCombineSplits>(a, b, h, gq, true, lds, a.partial + ws_row(a, b, h, gq) * (kD + 2),
+                                        (size_t)a.batch * a.h_kv * a.group * (kD + 2));
 }
 
 __global__ void ring_append_kernel(const void* k_new, const void* v_new, int in_bf16, int h_kv,

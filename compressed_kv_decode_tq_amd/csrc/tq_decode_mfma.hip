@@ -25,6 +25,11 @@
 //   exactly the 16 tokens its digit row needs for the value MFMA, so no data
 //   moves between the two.
 // * A byte holding 2^7 reads as -128 in int8; the matching digits are negated.
+#include <algorithm>
+#include <climits>
+#include <cstdlib>
+#include <cstring>
+
 #include "tq_common.h"
 #include "tq_internal.h"
 
@@ -108,43 +113,106 @@ __device__ __forceinline__ void digits128(int q, int d[4]) {
 // The two products are independent down to their digits: work-group (b h, 0)
 // makes the PM index planes from Pi q (and appends the ring token), (b h, 1)
 // the QJL plane from S q.
-template <int MAXG>
-__global__ __launch_bounds__(256) void qprep_mfma_kernel(DecodeArgs a, int pm, int npl, int nht) {
-  constexpr int NQ = MAXG / 4;               // float4 groups of heads per coordinate
-  __shared__ floatx4 qt[kD][NQ];             // queries, coordinate-major: qt[j][gq/4][gq%4]
-  __shared__ float qx[kMaxGroup][kD];        // this part's product (Pi q or S q)
-  __shared__ float red[kMaxGroup][kD];       // upper-half partial sums of the product
-  __shared__ int e_head[kMaxGroup];
-  const int b = blockIdx.x / a.h_kv, h = blockIdx.x % a.h_kv;
-  const int part = blockIdx.y;               // 0: Pi q, index planes; 1: S q, QJL plane
-  const int G = a.group;
-  if (part == 0 && a.app_k && a.vbase == 0) {
-    // fused ring append: threads 0..127 write the key row, 128..255 the value
-    // row of this (sequence, KV head), rounded to bf16 as the ring append does
-    const int c = threadIdx.x & (kD - 1), which = threadIdx.x >> 7;
-    const size_t src = ((size_t)b * a.h_kv + h) * kD + c;
-    const size_t dst = (((size_t)b * a.ring_cap + a.n_ring.v[b] - 1) * a.h_kv + h) * kD + c;
-    const void* in = which ? a.app_v : a.app_k;
-    uint16_t* ring = which ? a.app_ring_v : a.app_ring_k;
-    ring[dst] = a.app_bf16 ? reinterpret_cast<const uint16_t*>(in)[src]
-                           : (uint16_t)f2bf(reinterpret_cast<const float*>(in)[src]);
-  }
-  // thread (hj, i): coordinates j of half hj of row i of the product; column
-  // j of the matrix is row j of its transpose, so consecutive threads read
-  // consecutive words.  The 64 matrix loads go out before the queries are
-  // staged, so both round trips overlap.
-  const int i_row = threadIdx.x & (kD - 1);
-  const int hj = threadIdx.x >> 7;
-  float w[kD / 2];
-  {
-    const float* mt = a.mat_t + (size_t)part * kD * kD + (size_t)(hj * (kD / 2)) * kD + i_row;
+// Digit operands of the score planes [pl0, pl1) of one slot, for every head
+// tile.  x_at(pl, gq, k) is the value plane pl multiplies at coordinate k for
+// head gq (w_pl (Pi q)_k or 2 (S q)_k), e_at(pl, gq) its fixed-point exponent.
+// One work item is (head tile, plane, half, lane group, head of the tile,
+// byte offset d): it rounds the four coordinates k = 32g + 8j + 4hf + d
+// (j < 4) once, splits each into its four base-128 digits and writes the four
+// digit dwords of that head (digit rows L = 0..3).
+template <class XAt, class EAt>
+__device__ __forceinline__ void emit_digits(int tid, int nthreads, int pl0, int pl1, int npl, int nht, int G,
+                                            XAt x_at, EAt e_at, uint32_t* dig) {
+  const int np = pl1 - pl0;
+  const int items = nht * np * 2 * 4 * 4 * 4;
+  for (int it = tid; it < items; it += nthreads) {
+    const int d = it & 3, hh = (it >> 2) & 3, g = (it >> 4) & 3, hf = (it >> 6) & 1;
+    const int rest = it >> 7;
+    const int pl = pl0 + rest % np, ht = rest / np;
+    const int gq = 4 * ht + hh;
+    uint32_t word[4] = {0u, 0u, 0u, 0u};
+    if (gq < G) {
+      const int e = e_at(pl, gq);
 #pragma unroll
-    for (int j = 0; j < kD / 2; ++j) w[j] = mt[(size_t)j * kD];
+      for (int j = 0; j < 4; ++j) {
+        const int k = 32 * g + 8 * j + 4 * hf + d;
+        const int s = k & 7;
+        const int q = (int)rintf(ldexpf(x_at(pl, gq, k), e - s));
+        int dg[4];
+        digits128(q, dg);
+#pragma unroll
+        for (int L = 0; L < 4; ++L) word[L] |= (uint32_t)((s == 7 ? -dg[L] : dg[L]) & 0xff) << (8 * j);
+      }
+    }
+#pragma unroll
+    for (int L = 0; L < 4; ++L) {
+      const int ln = 16 * g + 4 * hh + L;
+      dig[((((ht * npl + pl) * 2 + hf) * 64 + ln) << 2) + d] = word[L];
+    }
   }
-  for (int i = threadIdx.x; i < MAXG * kD; i += blockDim.x) {
+}
+
+// Per-head fixed-point exponent and score constants of one product (part 0:
+// Pi q, part 1: S q) of one head, on one wave.
+__device__ __forceinline__ int head_constants(const DecodeArgs& a, const float* x, int part, int lane, int pm,
+                                              int npl, float* cst) {
+  // sr: sum over the coordinates of the base table; srh over the half-bit
+  // coordinates (i mod 32 < 16) of the fractional layout; for the QJL part,
+  // sr is sum(q_s)
+  float mx = 0.f, sr = 0.f, srh = 0.f;
+  for (int c = lane; c < kD; c += 64) {
+    const float v = x[c];
+    mx = fmaxf(mx, fabsf(v));
+    if (part == 0 && a.key_half && (c & 31) < 16)
+      srh += v;
+    else
+      sr += v;
+  }
+  mx = wave_max(mx);
+  sr = wave_sum(sr);
+  srh = wave_sum(srh);
+  int ex;
+  if (part == 0) {
+    float wmax = 0.f;
+    for (int p = 0; p < pm; ++p) wmax = fmaxf(wmax, fmaxf(fabsf(a.key_w[p]), fabsf(a.key_w_hi[p])));
+    frexpf(mx * wmax, &ex);  // |w_p q_rot| < 2^ex
+  } else {
+    frexpf(2.f * mx, &ex);
+  }
+  const int e = 26 - ex;  // scaled values stay below 2^26
+  if (lane == 0 && cst) {
+    if (part == 0) {
+      cst[0] = a.key_cst * sr + a.key_cst_hi * srh;  // constant part of <q_rot, c[idx]>
+      cst[1] = ldexpf(1.f, -e);                      // digit scale of the MSE planes
+      if (npl == pm) cst[2] = cst[3] = 0.f;          // no QJL plane
+    } else {
+      cst[2] = ldexpf(1.f, -e);  // digit scale of the QJL plane
+      cst[3] = sr;               // sum(q_s)
+    }
+  }
+  return e;
+}
+
+// The step's ring token of slot (b, h), rounded to bf16 (256 threads: the
+// first 128 write the key row, the others the value row).
+__device__ __forceinline__ void append_ring_token(const DecodeArgs& a, int b, int h, int tid) {
+  const int c = tid & (kD - 1), which = tid >> 7;
+  const size_t src = ((size_t)b * a.h_kv + h) * kD + c;
+  const size_t dst = (((size_t)b * a.ring_cap + a.n_ring.v[b] - 1) * a.h_kv + h) * kD + c;
+  const void* in = which ? a.app_v : a.app_k;
+  uint16_t* ring = which ? a.app_ring_v : a.app_ring_k;
+  ring[dst] = a.app_bf16 ? reinterpret_cast<const uint16_t*>(in)[src]
+                         : (uint16_t)f2bf(reinterpret_cast<const float*>(in)[src]);
+}
+
+// Queries of the slot's virtual heads into LDS, coordinate-major: qt[j][gq/4][gq%4].
+template <int MAXG>
+__device__ __forceinline__ void stage_queries(const DecodeArgs& a, int b, int h, int tid, int nthreads,
+                                              floatx4 (*qt)[MAXG / 4]) {
+  for (int i = tid; i < MAXG * kD; i += nthreads) {
     const int gq = i / kD, c = i % kD;
     float x = 0.f;
-    if (gq < G) {
+    if (gq < a.group) {
       int t, hq;
       virtual_head(a, h, gq, t, hq);
       const size_t off = q_row(a, b, t, hq) * kD + c;
@@ -152,106 +220,150 @@ __global__ __launch_bounds__(256) void qprep_mfma_kernel(DecodeArgs a, int pm, i
     }
     reinterpret_cast<float*>(&qt[c][gq >> 2])[gq & 3] = x;
   }
+}
+
+// Row i of the product's matrix (Pi for part 0, S for part 1, row-major),
+// columns [j0, j0 + NJ), in 16-byte words: one batch of loads.
+template <int NJ>
+__device__ __forceinline__ void load_row(const DecodeArgs& a, int part, int i, int j0, floatx4 (&m)[NJ / 4]) {
+  const floatx4* row = reinterpret_cast<const floatx4*>((part == 0 ? a.pi : a.s) + (size_t)i * kD + j0);
+#pragma unroll
+  for (int u = 0; u < NJ / 4; ++u) m[u] = row[u];
+}
+
+// Coordinate i of the product for the MAXG heads from that row and the staged
+// queries.
+template <int MAXG, int NJ>
+__device__ __forceinline__ void row_times_queries(const floatx4 (&m)[NJ / 4], int j0, const floatx4 (*qt)[MAXG / 4],
+                                                  float (&acc)[MAXG]) {
+#pragma unroll
+  for (int gq = 0; gq < MAXG; ++gq) acc[gq] = 0.f;
+#pragma unroll
+  for (int u = 0; u < NJ / 4; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int v = 0; v < MAXG / 4; ++v) {
+        const floatx4 qj = qt[j0 + 4 * u + e][v];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) acc[4 * v + f] = fmaf(m[u][e], qj[f], acc[4 * v + f]);
+      }
+}
+
+// LDS of one q-prep part (256 threads).
+template <int MAXG>
+struct QprepLds {
+  floatx4 qt[kD][MAXG / 4];  // queries, coordinate-major
+  float qx[kMaxGroup][kD];   // this part's product (Pi q or S q)
+  float red[kMaxGroup][kD];  // upper-half partial sums of the product
+  int e_head[kMaxGroup];
+};
+
+// One q-prep part of slot (b, h) on 256 threads: part 0 makes the
+// index-plane digits from Pi q (and appends the ring token), part 1 the QJL
+// digits from S q.  Thread (hj, i) forms coordinate i over the half hj of the
+// columns.  Digits go to dig (the slot's nht * npl * 2 * 64 * 4 dwords),
+// per-head constants to cst_base ([group][4]).
+template <int MAXG>
+__device__ __forceinline__ void qprep_part(const DecodeArgs& a, int b, int h, int part, int tid, QprepLds<MAXG>& L,
+                                           uint32_t* dig, float* cst_base, int pm, int npl, int nht) {
+  const int G = a.group;
+  if (part == 0 && a.app_k && a.vbase == 0) append_ring_token(a, b, h, tid);
+  const int i = tid & (kD - 1), hj = tid >> 7;
+  floatx4 m[kD / 8];
+  load_row<kD / 2>(a, part, i, hj * (kD / 2), m);  // in flight while the queries are staged
+  stage_queries<MAXG>(a, b, h, tid, 256, L.qt);
   __syncthreads();
   {
-    const int i = i_row;
     float acc[MAXG];
+    row_times_queries<MAXG, kD / 2>(m, hj * (kD / 2), L.qt, acc);
 #pragma unroll
-    for (int gq = 0; gq < MAXG; ++gq) acc[gq] = 0.f;
-#pragma unroll
-    for (int j = 0; j < kD / 2; ++j)
-#pragma unroll
-      for (int u = 0; u < NQ; ++u) {
-        const floatx4 qj = qt[hj * (kD / 2) + j][u];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[4 * u + e] = fmaf(w[j], qj[e], acc[4 * u + e]);
-      }
-#pragma unroll
-    for (int gq = 0; gq < MAXG; ++gq) (hj ? red : qx)[gq][i] = acc[gq];
+    for (int gq = 0; gq < MAXG; ++gq) (hj ? L.red : L.qx)[gq][i] = acc[gq];
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < MAXG * kD; i += blockDim.x) qx[i / kD][i % kD] += red[i / kD][i % kD];
+  for (int j = tid; j < MAXG * kD; j += 256) L.qx[j / kD][j % kD] += L.red[j / kD][j % kD];
   __syncthreads();
-  // per-head exponent and constants: one wave per head
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = tid & 63, wv = tid >> 6;
   for (int gq = wv; gq < MAXG; gq += 4) {
-    // sr: sum of q_rot over the coordinates of the base table; srh over the
-    // half-bit coordinates (i mod 32 < 16) of the fractional layout; for the
-    // QJL part, sr is sum(q_s)
-    float mx = 0.f, sr = 0.f, srh = 0.f;
-    for (int c = lane; c < kD; c += 64) {
-      const float x = qx[gq][c];
-      mx = fmaxf(mx, fabsf(x));
-      if (part == 0 && a.key_half && (c & 31) < 16)
-        srh += x;
-      else
-        sr += x;
-    }
-    mx = wave_max(mx);
-    sr = wave_sum(sr);
-    srh = wave_sum(srh);
-    int ex;
-    if (part == 0) {
-      float wmax = 0.f;
-      for (int p = 0; p < pm; ++p) wmax = fmaxf(wmax, fmaxf(fabsf(a.key_w[p]), fabsf(a.key_w_hi[p])));
-      frexpf(mx * wmax, &ex);  // |w_p q_rot| < 2^ex
-    } else {
-      frexpf(2.f * mx, &ex);
-    }
-    const int e = 26 - ex;  // scaled values stay below 2^26
-    if (lane == 0) {
-      e_head[gq] = e;
-      if (gq < G) {
-        float* cst = a.qconst + ws_row(a, b, h, gq) * 4;
-        if (part == 0) {
-          cst[0] = a.key_cst * sr + a.key_cst_hi * srh;  // constant part of <q_rot, c[idx]>
-          cst[1] = ldexpf(1.f, -e);                      // digit scale of the MSE planes
-          if (npl == pm) cst[2] = cst[3] = 0.f;          // no QJL plane
-        } else {
-          cst[2] = ldexpf(1.f, -e);  // digit scale of the QJL plane
-          cst[3] = sr;               // sum(q_s)
-        }
-      }
-    }
+    const int e = head_constants(a, L.qx[gq], part, lane, pm, npl, gq < G ? cst_base + gq * 4 : nullptr);
+    if (lane == 0) L.e_head[gq] = e;
   }
   __syncthreads();
-  // this part's planes: pl < pm (part 0) or pl == pm (part 1), for every head tile
-  const int ppl = part == 0 ? pm : 1;        // planes of this part
-  const int ndw = nht * ppl * 2 * 64 * 4;    // their digit dwords
-  uint32_t* out = reinterpret_cast<uint32_t*>(a.qdig) + (size_t)(b * a.h_kv + h) * (nht * npl * 2 * 64 * 4);
-  for (int i = threadIdx.x; i < ndw; i += blockDim.x) {
-    const int d = i & 3;
-    const int ln = (i >> 2) & 63;
-    const int hf = (i >> 8) & 1;
-    const int rest = i >> 9;
-    const int pp = rest % ppl, ht = rest / ppl;
-    const int pl = part == 0 ? pp : pm;
-    const int g = ln >> 4, n = ln & 15;
-    const int gq = 4 * ht + (n >> 2), L = n & 3;
-    uint32_t word = 0;
-    if (gq < G) {
-      const int e = e_head[gq];
+  const int pl0 = part == 0 ? 0 : pm, pl1 = part == 0 ? pm : pm + 1;
+  emit_digits(
+      tid, 256, pl0, pl1, npl, nht, G,
+      [&](int pl, int gq, int k) {
+        return part == 0 ? (a.key_half && (k & 31) < 16 ? a.key_w_hi[pl] : a.key_w[pl]) * L.qx[gq][k]
+                         : 2.f * L.qx[gq][k];
+      },
+      [&](int, int gq) { return L.e_head[gq]; }, dig);
+}
+
+// LDS of the folded q-prep (both products).
+template <int MAXG>
+struct QprepBothLds {
+  floatx4 qt[kD][MAXG / 4];     // queries, coordinate-major
+  float qx[2][kMaxGroup][kD];   // Pi q and S q
+  int e_head[2][kMaxGroup];
+};
+
+// Both q-prep products of slot (b, h) inside a 256-thread scan work-group:
+// thread (p, i) forms coordinate i of product p over all columns; the digits
+// and constants go to LDS.  append: also write the step's ring token.
+template <int MAXG>
+__device__ __forceinline__ void qprep_both(const DecodeArgs& a, int b, int h, int tid, bool append,
+                                           QprepBothLds<MAXG>& L, uint32_t* dig, float* cst_base, int pm, int npl,
+                                           int nht) {
+  const int nparts = npl > pm ? 2 : 1;
+  const int G = a.group;
+  if (append && a.app_k && a.vbase == 0) append_ring_token(a, b, h, tid);
+  const int i = tid & (kD - 1), part = tid >> 7;
+  // the row in two halves, so the loads in flight stay within the scan's
+  // register budget; the first half is in flight while the queries are staged
+  floatx4 m[kD / 8];
+  if (part < nparts) load_row<kD / 2>(a, part, i, 0, m);
+  stage_queries<MAXG>(a, b, h, tid, 256, L.qt);
+  __syncthreads();
+  if (part < nparts) {
+    float acc[MAXG], acc2[MAXG];
+    row_times_queries<MAXG, kD / 2>(m, 0, L.qt, acc);
+    load_row<kD / 2>(a, part, i, kD / 2, m);
+    row_times_queries<MAXG, kD / 2>(m, kD / 2, L.qt, acc2);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int k = 32 * g + 8 * j + 4 * hf + d;
-        const int s = k & 7;
-        // half-bit layout: per-coordinate table; key_w holds zeros past the
-        // base table's planes
-        const float x = part == 0 ? (a.key_half && (k & 31) < 16 ? a.key_w_hi[pl] : a.key_w[pl]) * qx[gq][k]
-                                  : 2.f * qx[gq][k];
-        const int q = (int)rintf(ldexpf(x, e - s));
-        int dg[4];
-        digits128(q, dg);
-        const int v = s == 7 ? -dg[L] : dg[L];
-        word |= (uint32_t)(v & 0xff) << (8 * j);
-      }
-    }
-    out[((((ht * npl + pl) * 2 + hf) * 64 + ln) << 2) + d] = word;
+    for (int gq = 0; gq < MAXG; ++gq) L.qx[part][gq][i] = acc[gq] + acc2[gq];
   }
+  __syncthreads();
+  const int lane = tid & 63, wv = tid >> 6;
+  for (int task = wv; task < nparts * MAXG; task += 4) {
+    const int pp = task / MAXG, gq = task % MAXG;
+    const int e = head_constants(a, L.qx[pp][gq], pp, lane, pm, npl, gq < G ? cst_base + gq * 4 : nullptr);
+    if (lane == 0) L.e_head[pp][gq] = e;
+  }
+  __syncthreads();
+  emit_digits(
+      tid, 256, 0, npl, npl, nht, G,
+      [&](int pl, int gq, int k) {
+        return pl < pm ? (a.key_half && (k & 31) < 16 ? a.key_w_hi[pl] : a.key_w[pl]) * L.qx[0][gq][k]
+                       : 2.f * L.qx[1][gq][k];
+      },
+      [&](int pl, int gq) { return L.e_head[pl < pm ? 0 : 1][gq]; }, dig);
+  __syncthreads();
+}
+
+// Separate q-prep kernel of the split scan: work-group (b h, part).
+template <int MAXG>
+__global__ __launch_bounds__(256) void qprep_mfma_kernel(DecodeArgs a, int pm, int npl, int nht) {
+  __shared__ QprepLds<MAXG> lds;
+  const int b = blockIdx.x / a.h_kv, h = blockIdx.x % a.h_kv;
+  uint32_t* dig = reinterpret_cast<uint32_t*>(a.qdig) + (size_t)(b * a.h_kv + h) * (nht * npl * 2 * 64 * 4);
+  qprep_part<MAXG>(a, b, h, (int)blockIdx.y, (int)threadIdx.x, lds, dig, a.qconst + ws_row(a, b, h, 0) * 4, pm,
+                   npl, nht);
 }
 
 template <int PM, bool QJL, bool VMSE, int PVB, int NHT, bool HALF = false>
 __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
+  constexpr int NW = 4;            // waves of the work-group
+  constexpr int kRound = 64 * NW;  // tokens the waves take per round of chunks
   constexpr int KB = PM == 1 ? 1 : (PM == 2 ? 2 : 3);  // stored key index planes
   constexpr int KP = KB + (QJL ? 1 : 0);               // stored key planes
   // HALF: index plane KB - 1 is the half plane (16-bit chunk per lane group)
@@ -273,7 +385,12 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
   constexpr int kStage = kStageMeta + kStageNg + kStageVw + kStageP + kStageTr;
   constexpr int kMerge = NHEAD * (kD + 2);
   constexpr int kStride = kStage > kMerge ? kStage : kMerge;
-  __shared__ __attribute__((aligned(16))) uint32_t smem[4 * kStride];
+  // q-prep folded into the work-group: its LDS and the digits it makes, in
+  // the space the chunk staging uses afterwards
+  constexpr int kQpDw = (int)((sizeof(QprepBothLds<4 * NHT>) + 15) / 16 * 4);
+  constexpr int kQpAll = kQpDw + NHT * NPL * 2 * 64 * 4 + 4 * NHEAD;
+  constexpr int kSmem = NW * kStride > kQpAll ? NW * kStride : kQpAll;
+  __shared__ __attribute__((aligned(16))) uint32_t smem[kSmem];
 
   // the wave index is uniform: reading it from the first lane keeps the chunk
   // loop, its bounds and the full/partial chunk test in scalar registers
@@ -292,10 +409,23 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
   float* s_p = reinterpret_cast<float*>(s_vw + kStageVw);
   uint32_t* s_tr = s_vw + kStageVw + kStageP;
 
-  // query digit operands and per-head constants (score layout: head 4ht + n/4)
+  // query digit operands and per-head constants (score layout: head 4ht + n/4):
+  // made by the q-prep kernel, or here first when q-prep is folded into the
+  // scan (in LDS that the chunk staging reuses afterwards)
+  const u32x4* dig_src = reinterpret_cast<const u32x4*>(a.qdig) + (size_t)sh * NHT * NPL * 2 * 64;
+  const float* cst_src = a.qconst + ws_row(a, b, h, 0) * 4;
+  if (a.qfold) {
+    QprepBothLds<4 * NHT>* ql = reinterpret_cast<QprepBothLds<4 * NHT>*>(smem);
+    uint32_t* dig = smem + kQpDw;
+    float* cstl = reinterpret_cast<float*>(dig + NHT * NPL * 2 * 64 * 4);
+    // the ring token is written once per slot: by its first split
+    qprep_both<4 * NHT>(a, b, h, threadIdx.x, blockIdx.x == 0, *ql, dig, cstl, PM, NPL, NHT);
+    dig_src = reinterpret_cast<const u32x4*>(dig);
+    cst_src = cstl;
+  }
   u32x4 qb[NHT][NPL][2];
   {
-    const u32x4* src = reinterpret_cast<const u32x4*>(a.qdig) + (size_t)sh * NHT * NPL * 2 * 64;
+    const u32x4* src = dig_src;
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht)
 #pragma unroll
@@ -311,7 +441,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
   for (int ht = 0; ht < NHT; ++ht) {
     const int hq = 4 * ht + g;
     if (hq < G) {
-      const floatx4 cs = *reinterpret_cast<const floatx4*>(a.qconst + ws_row(a, b, h, hq) * 4);
+      const floatx4 cs = *reinterpret_cast<const floatx4*>(cst_src + hq * 4);
       c0[ht] = cs[0];
       k1[ht] = cs[1];
       k2[ht] = cs[2];
@@ -322,6 +452,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
     k1h[ht] = 16384.f * k1[ht];
     k2h[ht] = 16384.f * k2[ht];
   }
+  if (a.qfold) __syncthreads();  // every wave holds its digits before the staging overwrites them
   const float u_scale = a.scale * 1.4426950409f;  // exp(x) = exp2(x log2 e)
   // Several causal queries per sequence: the compressed tokens each head of
   // this lane sees (lim) and the fewest any head of the launch sees (lim_min,
@@ -359,7 +490,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
   }
 
   // Chunk loads are issued one chunk ahead: the registers below hold chunk
-  // c0t + 256 of this wave while chunk c0t is being computed.
+  // c0t + kRound of this wave while chunk c0t is being computed.
   uint32_t pX[4][KP];       // key plane words: token 16ct + n, plane word g
   float pNrm = 0.f, pGam = 0.f;
   u32x4 pMeta = u32x4{0u, 0u, 0u, 0u};
@@ -389,7 +520,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
     return a.scalar_f16 ? __half2float(*reinterpret_cast<const __half*>(p)) : *reinterpret_cast<const float*>(p);
   };
   auto load_chunk = [&](int it, bool keys, bool rest) {
-    const int64_t c = first + (int64_t)it * 256;
+    const int64_t c = first + (int64_t)it * kRound;
     const int rem_c = (int)(t_end - c < 64 ? t_end - c : 64);
     const uint8_t* xk = kp + c * (int64_t)rec;
     const char* xn = reinterpret_cast<const char*>(a.k_norm) + (int64_t)(sidx0 + c) * ssz;
@@ -460,7 +591,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
   if (first < t_end) load_chunk(0, true, true);
 
   int it = 0;
-  for (int64_t c0t = first; c0t < t_end; c0t += 256, ++it) {
+  for (int64_t c0t = first; c0t < t_end; c0t += kRound, ++it) {
     const int rem = (int)(t_end - c0t < 64 ? t_end - c0t : 64);  // valid tokens of this chunk
     // ---- stage this chunk's per-token data and value words in LDS; the
     // value-weight exponent comes from the largest delta (min/max values) or
@@ -490,7 +621,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
       }
     }
     uint32_t(&X)[4][KP] = pX;  // the key words are reloaded once the scores are done
-    if (c0t + 256 < t_end) load_chunk(it + 1, false, true);
+    if (c0t + kRound < t_end) load_chunk(it + 1, false, true);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
@@ -554,7 +685,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
         for (int ct = 0; ct < 4; ++ct) sc[ht][ct] = c0t + 16 * ct + n < lim[ht] ? sc[ht][ct] : -INFINITY;
     }
 
-    if (c0t + 256 < t_end) load_chunk(it + 1, true, false);
+    if (c0t + kRound < t_end) load_chunk(it + 1, true, false);
 
     // ---- online softmax in log2 units over the 16 lanes of a head (one DPP
     // row); alpha rescales the running sums.  p goes to LDS for the value MFMA,
@@ -782,11 +913,11 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
     const int hh = i / kD, c = i % kD;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, base[w * kStride + hh * (kD + 2)]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, base[w * kStride + hh * (kD + 2)]);
     float L = 0.f, Acc = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < NW; ++w) {
         const float mw = base[w * kStride + hh * (kD + 2)];
         const float f = mw == -INFINITY ? 0.f : __expf(mw - M);
         L += f * base[w * kStride + hh * (kD + 2) + 1];
@@ -861,7 +992,19 @@ size_t mfma_workspace_bytes(int batch, int h_q, int group) {
   return dig + cst + 256;
 }
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, int key_mse_bits, int key_qjl, int value_mse,
+// The split scan makes its query digits in every work-group (no q-prep
+// kernel, no launch gap) when the whole grid runs in one round of three
+// work-groups per compute unit, so the redundant work is done side by side
+// at the start; larger grids keep the q-prep kernel.  TQ_DECODE_QFOLD=1 or =0
+// forces one of the two.
+bool qfold_mode(const DecodeArgs& a) {
+  const char* env = std::getenv("TQ_DECODE_QFOLD");
+  if (env && std::strcmp(env, "1") == 0) return true;
+  if (env && std::strcmp(env, "0") == 0) return false;
+  return (int64_t)a.splits * a.batch * a.h_kv <= 3 * (int64_t)device_cu_count();
+}
+
+hipError_t launch_decode_mfma(const DecodeArgs& a_in, int key_mse_bits, int key_qjl, int value_mse,
                               int value_bits, int key_planes, int value_planes, hipStream_t stream,
                               TimedLaunch tl) {
   // covered: keys with 1-, 2- or 3-bit indices (or 1.5 / 2.5 with QJL), with
@@ -869,23 +1012,27 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int key_mse_bits, int key_qjl
   // 3-bit MSE values (2-bit MSE values with 2+1- and 3+1-bit keys),
   // antisymmetric codebooks, up to 8 query heads per KV head
   if (key_mse_bits < 1 || key_mse_bits > 3) return hipErrorNotSupported;
-  if (!key_qjl && a.key_half) return hipErrorNotSupported;
+  if (!key_qjl && a_in.key_half) return hipErrorNotSupported;
   if (key_planes != (1 << (key_mse_bits - 1))) return hipErrorNotSupported;
   if (value_mse) {
     if ((value_bits != 2 && value_bits != 3) || value_planes != (1 << (value_bits - 1))) return hipErrorNotSupported;
-    if (value_bits == 2 && (!key_qjl || a.key_half || key_mse_bits < 2)) return hipErrorNotSupported;
-  } else if ((value_bits != 2 && value_bits != 4) || a.value_group != 32) {
+    if (value_bits == 2 && (!key_qjl || a_in.key_half || key_mse_bits < 2)) return hipErrorNotSupported;
+  } else if ((value_bits != 2 && value_bits != 4) || a_in.value_group != 32) {
     return hipErrorNotSupported;
   }
-  if (a.group > 8) return hipErrorNotSupported;
-  const int nht = a.group > 4 ? 2 : 1;
+  if (a_in.group > 8) return hipErrorNotSupported;
+  const int nht = a_in.group > 4 ? 2 : 1;
+  DecodeArgs a = a_in;
+  a.qfold = qfold_mode(a);
   const int pm = 1 << (key_mse_bits - 1);
   const int npl = pm + (key_qjl ? 1 : 0);
   const dim3 qgrid(a.batch * a.h_kv, key_qjl ? 2 : 1);
-  if (nht == 1)
-    hipLaunchKernelGGL(qprep_mfma_kernel<4>, qgrid, dim3(256), 0, stream, a, pm, npl, nht);
-  else
-    hipLaunchKernelGGL(qprep_mfma_kernel<8>, qgrid, dim3(256), 0, stream, a, pm, npl, nht);
+  if (!a.qfold) {
+    if (nht == 1)
+      hipLaunchKernelGGL(qprep_mfma_kernel<4>, qgrid, dim3(256), 0, stream, a, pm, npl, nht);
+    else
+      hipLaunchKernelGGL(qprep_mfma_kernel<8>, qgrid, dim3(256), 0, stream, a, pm, npl, nht);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = nht == 1 ? dispatch_mfma<1>(a, key_mse_bits, key_qjl, value_mse, value_bits, stream, tl)

@@ -122,6 +122,9 @@ struct DecodeArgs {
   float val_cst;
   int8_t* qdig;           // workspace: query digit operands of the MFMA scan
   float* qconst;          // workspace: [batch][h_kv][group][4] per-head score constants
+  // 1: every split work-group of the MFMA scan makes its slot's query digits
+  // itself (no q-prep kernel); used when the whole grid runs in one round
+  int32_t qfold;
   SeqValues n_comp;
   SeqValues n_ring;
   // Fused ring append (single query): the new token of sequence b and KV head

@@ -12,7 +12,7 @@ import torch
 import oracle
 from compressed_kv_decode_tq_amd import tq
 from compressed_kv_decode_tq_amd import workloads as wl
-from tq_testlib import OUT_RTOL, books, dequant_slot, layout_of, max_rel_err, say, slot_from_cache
+from tq_testlib import DECODE_PATHS, set_decode_path, OUT_RTOL, books, dequant_slot, layout_of, max_rel_err, say, slot_from_cache
 
 pytestmark = pytest.mark.gpu
 
@@ -41,11 +41,10 @@ def _setup(w, n_comp, n_ring, new_dtype):
     return prm, cache, ring_k, ring_v, kn, vn, q
 
 
-@pytest.mark.parametrize("path", ["mfma", "generic"])
+@pytest.mark.parametrize("path", DECODE_PATHS)
 @pytest.mark.parametrize("new_dtype", [torch.bfloat16, torch.float32])
 def test_fused_append_equals_append_then_decode(path, new_dtype, monkeypatch):
-    if path == "generic":
-        monkeypatch.setenv("TQ_DECODE_PATH", "generic")
+    set_decode_path(monkeypatch, path)
     w = wl.WORKLOADS[1].replace(batch=3, n_tokens=700)
     n_comp = [700, 333, 64]
     n_ring = [0, 17, 127]  # empty ring, ragged, the last free slot
@@ -150,3 +149,4 @@ def test_ring_fill_flush_then_decode():
             say(f"[ring flush] step {i}: compressed {n_comp}, ring {n_r + 1}, max rel err {err:.2e}")
             assert err <= OUT_RTOL
     say(f"[ring flush] worst {worst:.2e} (bound {OUT_RTOL})")
+

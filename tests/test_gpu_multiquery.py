@@ -19,7 +19,7 @@ import torch
 import oracle
 from compressed_kv_decode_tq_amd import tq
 from compressed_kv_decode_tq_amd import workloads as wl
-from tq_testlib import OUT_RTOL, books, dequant_slot, encode_slot, layout_of, max_rel_err, say, upload_slot
+from tq_testlib import DECODE_PATHS, set_decode_path, OUT_RTOL, books, dequant_slot, encode_slot, layout_of, max_rel_err, say, upload_slot
 
 pytestmark = pytest.mark.gpu
 
@@ -77,10 +77,9 @@ def _multi_case(w, nq, n_comp, n_ring, tag):
     return got
 
 
-@pytest.mark.parametrize("path", ["mfma", "generic"])
+@pytest.mark.parametrize("path", DECODE_PATHS)
 def test_multi_query_two_queries_one_pass(path, monkeypatch):
-    if path == "generic":
-        monkeypatch.setenv("TQ_DECODE_PATH", "generic")
+    set_decode_path(monkeypatch, path)
     w = wl.WORKLOADS[1].replace(batch=2, n_tokens=700)
     _multi_case(w, 2, [700, 513], [3, 1], f"gqa4 ({path})")
 

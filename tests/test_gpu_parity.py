@@ -13,7 +13,7 @@ import torch
 import oracle
 from compressed_kv_decode_tq_amd import tq
 from compressed_kv_decode_tq_amd import workloads as wl
-from tq_testlib import (gamma_report, OUT_RTOL, books, check_encode_slot, dequant_slot, encode_slot, key_plane_mismatches,
+from tq_testlib import (DECODE_PATHS, set_decode_path, gamma_report, OUT_RTOL, books, check_encode_slot, dequant_slot, encode_slot, key_plane_mismatches,
                         layout_of, max_rel_err, read_value_planes, say, slot_from_cache, upload_slot)
 
 pytestmark = pytest.mark.gpu
@@ -196,13 +196,12 @@ def _decode_case(w, n_comp, n_ring, tag, steps_kv=None):
     return got
 
 
-@pytest.mark.parametrize("path", ["mfma", "generic"])
+@pytest.mark.parametrize("path", DECODE_PATHS)
 @pytest.mark.parametrize("name", list(SMALL))
 def test_decode_parity(name, path, monkeypatch):
     """Both decode paths: the int8-MFMA bit-plane scan (taken for symmetric
     codebooks) and the generic scan (forced with TQ_DECODE_PATH=generic)."""
-    if path == "generic":
-        monkeypatch.setenv("TQ_DECODE_PATH", "generic")
+    set_decode_path(monkeypatch, path)
     w = SMALL[name]
     nr = [1] * w.batch if w.ring_cap else [0] * w.batch
     _decode_case(w, [w.n_tokens] * w.batch, nr, f"{name} ({path})")
@@ -223,24 +222,22 @@ def test_decode_layouts_outside_the_mfma_path():
     _decode_case(SMALL["long_small"].replace(value_bits=2, key_mse_bits=1, n_tokens=300), [300], [0], "k1 mse v2")
 
 
-@pytest.mark.parametrize("path", ["mfma", "generic"])
+@pytest.mark.parametrize("path", DECODE_PATHS)
 def test_decode_two_bit_mse_values(path, monkeypatch):
     """2-bit MSE values (two value planes) with 2+1- and 3+1-bit keys, on both
     scan paths."""
-    if path == "generic":
-        monkeypatch.setenv("TQ_DECODE_PATH", "generic")
+    set_decode_path(monkeypatch, path)
     w = SMALL["long_small"].replace(value_bits=2, n_tokens=300)
     _decode_case(w, [300], [0], f"3+1-bit keys, 2-bit MSE values ({path})")
     _decode_case(w.replace(key_mse_bits=2, batch=2), [300, 97], [0, 0], f"2+1-bit keys, 2-bit MSE values ({path})")
 
 
-@pytest.mark.parametrize("path", ["mfma", "generic"])
+@pytest.mark.parametrize("path", DECODE_PATHS)
 def test_decode_four_bit_minmax_values(path, monkeypatch):
     """4-bit min/max values in groups of 32 (packed, eight tokens per word),
     with 2+1-, 3+1- and 3.5-bit keys, on both scan paths (the generic scan has
     no half-bit keys)."""
-    if path == "generic":
-        monkeypatch.setenv("TQ_DECODE_PATH", "generic")
+    set_decode_path(monkeypatch, path)
     base = SMALL["batched_small"].replace(batch=2, n_tokens=300, value_bits=4)
     _decode_case(base, [300, 133], [3, 0], f"4-bit values ({path})")
     _decode_case(base.replace(key_mse_bits=3), [300, 64], [0, 2], f"3+1-bit keys, 4-bit values ({path})")
@@ -282,12 +279,11 @@ def test_four_bit_minmax_values_end_to_end():
     assert err.max() <= OUT_RTOL
 
 
-@pytest.mark.parametrize("path", ["mfma", "generic"])
+@pytest.mark.parametrize("path", DECODE_PATHS)
 def test_decode_one_bit_keys(path, monkeypatch):
     """1-bit key indices (TurboQuantProd(2) and the 1-bit MSE-only keys), with
     min/max and MSE values, on both scan paths."""
-    if path == "generic":
-        monkeypatch.setenv("TQ_DECODE_PATH", "generic")
+    set_decode_path(monkeypatch, path)
     base = SMALL["batched_small"].replace(batch=2, n_tokens=300, key_mse_bits=1)
     _decode_case(base, [300, 190], [2, 0], f"1+1-bit keys ({path})")
     _decode_case(base.replace(key_qjl=0), [300, 64], [0, 1], f"1-bit keys, no qjl ({path})")
@@ -295,12 +291,11 @@ def test_decode_one_bit_keys(path, monkeypatch):
     _decode_case(mse, [300], [0], f"1+1-bit keys, MSE values ({path})")
 
 
-@pytest.mark.parametrize("path", ["mfma", "generic"])
+@pytest.mark.parametrize("path", DECODE_PATHS)
 def test_decode_keys_without_qjl(path, monkeypatch):
     """MSE-only keys (no QJL bit), 2 and 3 index bits, with min/max and MSE
     values, on both scan paths."""
-    if path == "generic":
-        monkeypatch.setenv("TQ_DECODE_PATH", "generic")
+    set_decode_path(monkeypatch, path)
     base = SMALL["batched_small"].replace(batch=2, n_tokens=300, key_qjl=0)
     _decode_case(base, [300, 256], [1, 1], f"no qjl, 2-bit keys ({path})")
     _decode_case(base.replace(key_mse_bits=3), [300, 77], [0, 3], f"no qjl, 3-bit keys ({path})")
@@ -309,7 +304,7 @@ def test_decode_keys_without_qjl(path, monkeypatch):
     _decode_case(mse.replace(key_mse_bits=2), [211], [0], f"no qjl, 2-bit keys, MSE values ({path})")
 
 
-@pytest.mark.parametrize("path", ["mfma", "generic"])
+@pytest.mark.parametrize("path", DECODE_PATHS)
 @pytest.mark.parametrize("kbits,qjl,vkind,vbits,group", [
     (4, 1, "minmax", 3, 32), (4, 0, "minmax", 1, 16), (3, 0, "minmax", 3, 64), (1, 1, "minmax", 1, 32),
     (2, 1, "minmax", 2, 16), (2, 1, "minmax", 4, 64), (4, 1, "mse", 1, 32), (1, 0, "mse", 4, 32),
@@ -318,8 +313,7 @@ def test_decode_layout_sweep(kbits, qjl, vkind, vbits, group, path, monkeypatch)
     """Decode of oracle-encoded caches over key widths with and without QJL,
     min/max widths and group sizes and MSE value widths, on both scan paths
     (layouts the MFMA scan does not cover run on the generic scan either way)."""
-    if path == "generic":
-        monkeypatch.setenv("TQ_DECODE_PATH", "generic")
+    set_decode_path(monkeypatch, path)
     base = SMALL["batched_small"] if vkind == "minmax" else SMALL["long_small"]
     w = base.replace(batch=2, n_tokens=260, key_mse_bits=kbits, key_qjl=qjl, value_bits=vbits, value_group=group)
     nr = [2, 0] if w.ring_cap else [0, 0]
