@@ -12,7 +12,8 @@ channels per KV head scaled x10, keys 2-bit Lloyd-Max + 1-bit QJL, values
   W untimed warm-up steps, then K timed steps (ring lengths 1..K).
 * value = effective HBM GB/s of the decode step (algorithmic bytes / time).
 * roofline = the split-scan kernel: compressed bytes per launch / its average
-  duration, from HIP events recorded around that launch inside the timed steps.
+  duration, from HIP events recorded around that launch on every 4th of the
+  timed steps (--time-every).
 * cold = more steps, each timed alone right after a 1 GiB device write that
   evicts the 256 MB MALL (the last-level cache), so no step reads a cache
   that a previous step left in it.
@@ -231,6 +232,10 @@ def main():
     ap.add_argument("--achievable-mib", type=int, default=1024,
                     help="after the timed steps, time a plain device copy of this many MiB (0: skip); "
                          "its read + write GB/s is reported as the achievable bandwidth")
+    ap.add_argument("--time-every", type=int, default=4,
+                    help="record the timing events around the decode scan on every k-th timed step: each event "
+                         "pair is a pair of packets in the stream that delays the next kernel, so timing every "
+                         "step would slow the steps being measured")
     ap.add_argument("--cold-steps", type=int, default=16,
                     help="after the timed steps, this many more steps each timed alone (events around the "
                          "call), each after a 1 GiB device write that evicts the 256 MB MALL; 0: skip")
@@ -361,18 +366,21 @@ def main():
     torch.cuda.synchronize()
     if ring:  # the timed steps start from an empty ring
         state["n_r"] = 0
-    ev = Events(args.steps)
+    every = max(1, args.time_every)
+    timed = list(range(0, args.steps, every))  # steps whose scan launch is timed
+    ev = Events(len(timed))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     tot_bytes = 0
     scan_bytes = []
     for j in range(args.steps):
-        by, sb = step(args.warmup + j, ev.pairs[j])
+        by, sb = step(args.warmup + j, ev.pairs[j // every] if j % every == 0 else None)
         tot_bytes += by
-        scan_bytes.append(sb)
+        if j % every == 0:
+            scan_bytes.append(sb)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    scan_ms = [ev.ms(j) for j in range(args.steps)]
+    scan_ms = [ev.ms(i) for i in range(len(timed))]
     ev.close()
     ms_per_step = wall / args.steps * 1e3
     gbs = tot_bytes / wall / 1e9
@@ -451,6 +459,7 @@ def main():
                      "achieved": round(scan_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(scan_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "avg_launch_ms": round(scan_avg_ms, 5), "launch_ms": launch_spread,
+                     "timed_launches": f"{len(scan_ms)} of {args.steps} (every {every})",
                      "algorithmic_bytes_per_launch": int(scan_avg_bytes), "source_sha": sha},
         "cold": cold,
         "achievable": None if copy_gbs is None else {

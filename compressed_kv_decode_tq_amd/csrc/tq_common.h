@@ -129,16 +129,34 @@ inline int device_cu_count() {
   return cached[dev];
 }
 
+// Reductions over the wave, the result in every lane, in registers only (no
+// LDS round trip): DPP steps within each 16-lane row, then the gfx950
+// cross-row lane swaps combine the four rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
+  x = fmaxf(x, dpp_f<0xB1>(x));   // quad_perm 1,0,3,2
+  x = fmaxf(x, dpp_f<0x4E>(x));   // quad_perm 2,3,0,1
+  x = fmaxf(x, dpp_f<0x124>(x));  // row_ror 4
+  x = fmaxf(x, dpp_f<0x128>(x));  // row_ror 8
+  auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+  auto u = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(u[0]), __uint_as_float(u[1]));
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+  x += dpp_f<0xB1>(x);
+  x += dpp_f<0x4E>(x);
+  x += dpp_f<0x124>(x);
+  x += dpp_f<0x128>(x);
+  auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(t[0]) + __uint_as_float(t[1]);
+  auto u = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(u[0]) + __uint_as_float(u[1]);
 }
 
 }  // namespace tq

@@ -342,12 +342,9 @@ __global__ void ring_append_kernel(const void* k_new, const void* v_new, int in_
 
 template <int KB, bool QJL, bool VMSE, int VB>
 hipError_t launch_scan(const DecodeArgs& a, hipStream_t st, TimedLaunch tl) {
-  if (tl.begin) (void)hipEventRecord(tl.begin, st);
-  hipLaunchKernelGGL((scan_kernel<KB, QJL, VMSE, VB>), dim3(a.splits, a.batch * a.h_kv),
-                     dim3(kScanThreads), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (tl.end) (void)hipEventRecord(tl.end, st);
-  return e;
+  launch_maybe_timed(scan_kernel<KB, QJL, VMSE, VB>, dim3(a.splits, a.batch * a.h_kv), dim3(kScanThreads), st, tl,
+                     a);
+  return hipGetLastError();
 }
 
 template <int KB, bool QJL, bool VMSE>

@@ -299,57 +299,6 @@ __device__ __forceinline__ void qprep_part(const DecodeArgs& a, int b, int h, in
       [&](int, int gq) { return L.e_head[gq]; }, dig);
 }
 
-// LDS of the folded q-prep (both products).
-template <int MAXG>
-struct QprepBothLds {
-  floatx4 qt[kD][MAXG / 4];     // queries, coordinate-major
-  float qx[2][kMaxGroup][kD];   // Pi q and S q
-  int e_head[2][kMaxGroup];
-};
-
-// Both q-prep products of slot (b, h) inside a 256-thread scan work-group:
-// thread (p, i) forms coordinate i of product p over all columns; the digits
-// and constants go to LDS.  append: also write the step's ring token.
-template <int MAXG>
-__device__ __forceinline__ void qprep_both(const DecodeArgs& a, int b, int h, int tid, bool append,
-                                           QprepBothLds<MAXG>& L, uint32_t* dig, float* cst_base, int pm, int npl,
-                                           int nht) {
-  const int nparts = npl > pm ? 2 : 1;
-  const int G = a.group;
-  if (append && a.app_k && a.vbase == 0) append_ring_token(a, b, h, tid);
-  const int i = tid & (kD - 1), part = tid >> 7;
-  // the row in two halves, so the loads in flight stay within the scan's
-  // register budget; the first half is in flight while the queries are staged
-  floatx4 m[kD / 8];
-  if (part < nparts) load_row<kD / 2>(a, part, i, 0, m);
-  stage_queries<MAXG>(a, b, h, tid, 256, L.qt);
-  __syncthreads();
-  if (part < nparts) {
-    float acc[MAXG], acc2[MAXG];
-    row_times_queries<MAXG, kD / 2>(m, 0, L.qt, acc);
-    load_row<kD / 2>(a, part, i, kD / 2, m);
-    row_times_queries<MAXG, kD / 2>(m, kD / 2, L.qt, acc2);
-#pragma unroll
-    for (int gq = 0; gq < MAXG; ++gq) L.qx[part][gq][i] = acc[gq] + acc2[gq];
-  }
-  __syncthreads();
-  const int lane = tid & 63, wv = tid >> 6;
-  for (int task = wv; task < nparts * MAXG; task += 4) {
-    const int pp = task / MAXG, gq = task % MAXG;
-    const int e = head_constants(a, L.qx[pp][gq], pp, lane, pm, npl, gq < G ? cst_base + gq * 4 : nullptr);
-    if (lane == 0) L.e_head[pp][gq] = e;
-  }
-  __syncthreads();
-  emit_digits(
-      tid, 256, 0, npl, npl, nht, G,
-      [&](int pl, int gq, int k) {
-        return pl < pm ? (a.key_half && (k & 31) < 16 ? a.key_w_hi[pl] : a.key_w[pl]) * L.qx[0][gq][k]
-                       : 2.f * L.qx[1][gq][k];
-      },
-      [&](int pl, int gq) { return L.e_head[pl < pm ? 0 : 1][gq]; }, dig);
-  __syncthreads();
-}
-
 // Separate q-prep kernel of the split scan: work-group (b h, part).
 template <int MAXG>
 __global__ __launch_bounds__(256) void qprep_mfma_kernel(DecodeArgs a, int pm, int npl, int nht) {
@@ -385,12 +334,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
   constexpr int kStage = kStageMeta + kStageNg + kStageVw + kStageP + kStageTr;
   constexpr int kMerge = NHEAD * (kD + 2);
   constexpr int kStride = kStage > kMerge ? kStage : kMerge;
-  // q-prep folded into the work-group: its LDS and the digits it makes, in
-  // the space the chunk staging uses afterwards
-  constexpr int kQpDw = (int)((sizeof(QprepBothLds<4 * NHT>) + 15) / 16 * 4);
-  constexpr int kQpAll = kQpDw + NHT * NPL * 2 * 64 * 4 + 4 * NHEAD;
-  constexpr int kSmem = NW * kStride > kQpAll ? NW * kStride : kQpAll;
-  __shared__ __attribute__((aligned(16))) uint32_t smem[kSmem];
+  __shared__ __attribute__((aligned(16))) uint32_t smem[NW * kStride];
 
   // the wave index is uniform: reading it from the first lane keeps the chunk
   // loop, its bounds and the full/partial chunk test in scalar registers
@@ -409,20 +353,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
   float* s_p = reinterpret_cast<float*>(s_vw + kStageVw);
   uint32_t* s_tr = s_vw + kStageVw + kStageP;
 
-  // query digit operands and per-head constants (score layout: head 4ht + n/4):
-  // made by the q-prep kernel, or here first when q-prep is folded into the
-  // scan (in LDS that the chunk staging reuses afterwards)
+  // query digit operands and per-head constants (score layout: head 4ht + n/4)
   const u32x4* dig_src = reinterpret_cast<const u32x4*>(a.qdig) + (size_t)sh * NHT * NPL * 2 * 64;
   const float* cst_src = a.qconst + ws_row(a, b, h, 0) * 4;
-  if (a.qfold) {
-    QprepBothLds<4 * NHT>* ql = reinterpret_cast<QprepBothLds<4 * NHT>*>(smem);
-    uint32_t* dig = smem + kQpDw;
-    float* cstl = reinterpret_cast<float*>(dig + NHT * NPL * 2 * 64 * 4);
-    // the ring token is written once per slot: by its first split
-    qprep_both<4 * NHT>(a, b, h, threadIdx.x, blockIdx.x == 0, *ql, dig, cstl, PM, NPL, NHT);
-    dig_src = reinterpret_cast<const u32x4*>(dig);
-    cst_src = cstl;
-  }
   u32x4 qb[NHT][NPL][2];
   {
     const u32x4* src = dig_src;
@@ -452,7 +385,6 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
     k1h[ht] = 16384.f * k1[ht];
     k2h[ht] = 16384.f * k2[ht];
   }
-  if (a.qfold) __syncthreads();  // every wave holds its digits before the staging overwrites them
   const float u_scale = a.scale * 1.4426950409f;  // exp(x) = exp2(x log2 e)
   // Several causal queries per sequence: the compressed tokens each head of
   // this lane sees (lim) and the fewest any head of the launch sees (lim_min,
@@ -935,12 +867,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
 
 template <int PM, bool QJL, bool VMSE, int PVB, int NHT, bool HALF = false>
 hipError_t launch_scan_mfma(const DecodeArgs& a, hipStream_t st, TimedLaunch tl) {
-  if (tl.begin) (void)hipEventRecord(tl.begin, st);
-  hipLaunchKernelGGL((scan_mfma_kernel<PM, QJL, VMSE, PVB, NHT, HALF>), dim3(a.splits, a.batch * a.h_kv),
-                     dim3(kScanThreads), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (tl.end) (void)hipEventRecord(tl.end, st);
-  return e;
+  launch_maybe_timed(scan_mfma_kernel<PM, QJL, VMSE, PVB, NHT, HALF>, dim3(a.splits, a.batch * a.h_kv),
+                     dim3(kScanThreads), st, tl, a);
+  return hipGetLastError();
 }
 
 template <int NHT>
@@ -992,18 +921,6 @@ size_t mfma_workspace_bytes(int batch, int h_q, int group) {
   return dig + cst + 256;
 }
 
-// The split scan makes its query digits in every work-group (no q-prep
-// kernel, no launch gap) when the whole grid runs in one round of three
-// work-groups per compute unit, so the redundant work is done side by side
-// at the start; larger grids keep the q-prep kernel.  TQ_DECODE_QFOLD=1 or =0
-// forces one of the two.
-bool qfold_mode(const DecodeArgs& a) {
-  const char* env = std::getenv("TQ_DECODE_QFOLD");
-  if (env && std::strcmp(env, "1") == 0) return true;
-  if (env && std::strcmp(env, "0") == 0) return false;
-  return (int64_t)a.splits * a.batch * a.h_kv <= 3 * (int64_t)device_cu_count();
-}
-
 hipError_t launch_decode_mfma(const DecodeArgs& a_in, int key_mse_bits, int key_qjl, int value_mse,
                               int value_bits, int key_planes, int value_planes, hipStream_t stream,
                               TimedLaunch tl) {
@@ -1022,17 +939,14 @@ hipError_t launch_decode_mfma(const DecodeArgs& a_in, int key_mse_bits, int key_
   }
   if (a_in.group > 8) return hipErrorNotSupported;
   const int nht = a_in.group > 4 ? 2 : 1;
-  DecodeArgs a = a_in;
-  a.qfold = qfold_mode(a);
+  const DecodeArgs& a = a_in;
   const int pm = 1 << (key_mse_bits - 1);
   const int npl = pm + (key_qjl ? 1 : 0);
   const dim3 qgrid(a.batch * a.h_kv, key_qjl ? 2 : 1);
-  if (!a.qfold) {
-    if (nht == 1)
-      hipLaunchKernelGGL(qprep_mfma_kernel<4>, qgrid, dim3(256), 0, stream, a, pm, npl, nht);
-    else
-      hipLaunchKernelGGL(qprep_mfma_kernel<8>, qgrid, dim3(256), 0, stream, a, pm, npl, nht);
-  }
+  if (nht == 1)
+    hipLaunchKernelGGL(qprep_mfma_kernel<4>, qgrid, dim3(256), 0, stream, a, pm, npl, nht);
+  else
+    hipLaunchKernelGGL(qprep_mfma_kernel<8>, qgrid, dim3(256), 0, stream, a, pm, npl, nht);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = nht == 1 ? dispatch_mfma<1>(a, key_mse_bits, key_qjl, value_mse, value_bits, stream, tl)

@@ -122,9 +122,6 @@ struct DecodeArgs {
   float val_cst;
   int8_t* qdig;           // workspace: query digit operands of the MFMA scan
   float* qconst;          // workspace: [batch][h_kv][group][4] per-head score constants
-  // 1: every split work-group of the MFMA scan makes its slot's query digits
-  // itself (no q-prep kernel); used when the whole grid runs in one round
-  int32_t qfold;
   SeqValues n_comp;
   SeqValues n_ring;
   // Fused ring append (single query): the new token of sequence b and KV head
@@ -174,6 +171,15 @@ struct TimedLaunch {
   hipEvent_t begin = nullptr;
   hipEvent_t end = nullptr;
 };
+
+// Launch of a kernel that may be timed: the events are recorded on the launch
+// stream just before and just after it.
+template <typename F, typename... Args>
+inline void launch_maybe_timed(F kernel, dim3 grid, dim3 block, hipStream_t st, TimedLaunch tl, Args... args) {
+  if (tl.begin) (void)hipEventRecord(tl.begin, st);
+  hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+  if (tl.end) (void)hipEventRecord(tl.end, st);
+}
 
 // Launchers (defined in the .hip files).  Each returns hipSuccess or the
 // launch error.

@@ -18,7 +18,7 @@ import torch
 import oracle
 from compressed_kv_decode_tq_amd import tq
 from compressed_kv_decode_tq_amd import workloads as wl
-from tq_testlib import (set_decode_path, gamma_report, OUT_RTOL, books, check_encode_slot, dequant_slot, encode_slot, layout_of, max_rel_err,
+from tq_testlib import (gamma_report, OUT_RTOL, books, check_encode_slot, dequant_slot, encode_slot, layout_of, max_rel_err,
                         say, slot_from_cache, upload_slot)
 
 pytestmark = pytest.mark.gpu
@@ -67,9 +67,7 @@ def test_half_bit_encode_parity(name):
 
 
 @pytest.mark.parametrize("name", list(CASES))
-@pytest.mark.parametrize("path", ["mfma", "fold"])
-def test_half_bit_decode_parity(name, path, monkeypatch):
-    set_decode_path(monkeypatch, path)
+def test_half_bit_decode_parity(name):
     w = CASES[name]
     bk, pi, s, prm, k, v = _setup(w)
     n_comp = [w.n_tokens - 37 * b for b in range(w.batch)]
@@ -91,7 +89,7 @@ def test_half_bit_decode_parity(name, path, monkeypatch):
     torch.cuda.synchronize()
     ref = oracle.decode_attention(q.double().numpy(), kd, vd)
     err = max_rel_err(out.cpu().double().numpy(), ref)
-    say(f"[half-bit decode] {name} ({path}): max rel err {err.max():.2e} (bound {OUT_RTOL})")
+    say(f"[half-bit decode] {name}: max rel err {err.max():.2e} (bound {OUT_RTOL})")
     assert err.max() <= OUT_RTOL
 
 

@@ -29,10 +29,9 @@ def gamma_report() -> str:
     return r
 
 
-#: Decode paths the parity tests run: the MFMA split scan with its q-prep and
-#: combine kernels ("mfma"), the same with the query digits made inside every
-#: scan work-group ("fold"), and the VALU scan ("generic").
-DECODE_PATHS = ["mfma", "fold", "generic"]
+#: Decode paths the parity tests run: the MFMA scan ("mfma") and the VALU
+#: scan ("generic").
+DECODE_PATHS = ["mfma", "generic"]
 
 
 def set_decode_path(monkeypatch, path: str):
@@ -41,7 +40,6 @@ def set_decode_path(monkeypatch, path: str):
         monkeypatch.setenv("TQ_DECODE_PATH", "generic")
     else:
         monkeypatch.delenv("TQ_DECODE_PATH", raising=False)
-        monkeypatch.setenv("TQ_DECODE_QFOLD", "1" if path == "fold" else "0")
 
 
 def say(*a):
