@@ -74,9 +74,12 @@ class Events:
 
 
 def _source_sha(*names):
+    """Hash of the named kernel sources and of the build script (which holds
+    their compiler flags): a traffic figure taken on other code is not used."""
     h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(ROOT, "compressed_kv_decode_tq_amd", "csrc", n), "rb") as f:
+    paths = [os.path.join(ROOT, "compressed_kv_decode_tq_amd", "csrc", n) for n in names]
+    for path in paths + [os.path.join(ROOT, "compressed_kv_decode_tq_amd", "build.py")]:
+        with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -157,6 +160,20 @@ def pmc_summary(args):
     print(json.dumps(summary, indent=1))
 
 
+def _cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or the platform's
+    processor string."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(w, seconds_budget: float = 25.0):
     """Time the float64 oracle (encode, then dequantize-then-attend decode) on a
     bounded sample: sequence 0, every KV head, its first n tokens."""
@@ -204,9 +221,13 @@ def cpu_baseline(w, seconds_budget: float = 25.0):
         value_bits=w.value_bits, value_group=w.value_group, scalar_dtype=w.scalar_dtype,
         key_half=w.key_half))["total"]
     nbytes = per_th * w.h_kv * n * seqs
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    pools = threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in pools] + [1])
     return {
         "value": round(nbytes / t_dec / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "cpu_model": _cpu_model(),
+        "blas": [{"library": i.get("internal_api"), "threads": i.get("num_threads")} for i in pools
+                 if i.get("user_api") == "blas"],
         "sample": f"{seqs} of {w.batch} sequences, all {w.h_kv} KV heads, {n} tokens each: float64 encode "
                   f"({t_enc:.2f} s) and one dequantize-then-attend decode step for their {w.h_q} query heads "
                   f"({t_dec:.2f} s); value = compressed bytes of the sample / decode time",

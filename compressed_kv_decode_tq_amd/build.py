@@ -17,11 +17,15 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtq.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["tq_api.cpp", "tq_codebook.cpp", "tq_encode.hip", "tq_decode.hip", "tq_decode_mfma.hip", "tq_noalloc.hip"]
+SOURCES = ["tq_api.cpp", "tq_codebook.cpp", "tq_plan.cpp", "tq_encode.hip", "tq_decode.hip", "tq_decode_mfma.hip", "tq_noalloc.hip"]
 ARCH = os.environ.get("TQ_OFFLOAD_ARCH", "gfx950")
 # MFMA results land in ordinary VGPRs in the decode scan (no accumulator-register
-# copies: every result is consumed by VALU code right away)
-SOURCE_FLAGS = {"tq_decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# copies: every result is consumed by VALU code right away).  The decode scan
+# also runs with the IEEE mode bit clear and no NaN operands assumed: its
+# maxima then need no quieting of their inputs, so a DPP row move folds into
+# the max (the file's kernels read their indices through the hardware
+# builtins, so no device-library call is left behind by the mode change).
+SOURCE_FLAGS = {"tq_decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mno-amdgpu-ieee", "-fno-honor-nans"]}
 
 
 def _hipcc() -> str:

@@ -60,9 +60,11 @@ double moment_anti(double x, int d) {
 
 int make_codebook(int d, int bits, double* cent, double* thr) {
   const int levels = 1 << bits;
-  // start from equal-width cells over +-3 standard deviations (std = 1/sqrt(d))
+  // start from equal-width cells over +-3 standard deviations (std = 1/sqrt(d)),
+  // kept inside the support [-1, 1]: for d < 10 three deviations reach past it,
+  // and a midpoint beyond +-1 has no defined cell integral
   std::vector<double> c(levels), cn(levels), e(levels + 1);
-  const double span = 3.0 / std::sqrt(static_cast<double>(d));
+  const double span = std::fmin(3.0 / std::sqrt(static_cast<double>(d)), 1.0);
   for (int k = 0; k < levels; ++k) c[k] = -span + span * (2.0 * k + 1.0) / levels;
   for (int it = 0; it < 200000; ++it) {
     e[0] = -1.0;

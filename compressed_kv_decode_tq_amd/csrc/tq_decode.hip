@@ -370,48 +370,6 @@ hipError_t dispatch_qjl(const DecodeArgs& a, int qjl, int vmse, int vb, hipStrea
 
 }  // namespace
 
-// Split of the token range for the decode grid, in whole 256-token rounds of
-// the four waves.  About kSplitTarget work-groups over the device; when that
-// makes splits shorter than kLongSplit tokens, they are lengthened towards
-// kLongSplit as long as at least kFloorGroups work-groups (one round of three
-// per compute unit) remain, so per-work-group set-up and the combine's merge
-// stay small next to the scan while a few long sequences still fill every
-// compute unit (8 sequence-heads of 131072 tokens: 1536-token splits, 688
-// work-groups, against 512-token splits and 2048 work-groups for a floor of
-// eight per compute unit: 4% less time per step, most of it in the combine).
-constexpr int64_t kSplitTarget = 2048;
-constexpr int64_t kFloorGroups = 768;
-constexpr int64_t kLongSplit = 2048;
-constexpr int64_t kMinSplit = 256;
-
-void decode_split(int64_t max_tokens, int64_t units, int32_t* splits, int32_t* split_len) {
-  if (units < 1) units = 1;
-  int64_t want = (kSplitTarget + units - 1) / units;
-  if (want < 1) want = 1;
-  int64_t len = (max_tokens + want - 1) / want;
-  int64_t floor_len = (max_tokens * units + kFloorGroups - 1) / kFloorGroups;  // keeps >= kFloorGroups groups
-  if (floor_len > kLongSplit) floor_len = kLongSplit;
-  if (len < floor_len) len = floor_len;
-  len = ((len + 255) / 256) * 256;
-  if (len < kMinSplit) len = kMinSplit;
-  int64_t n = (max_tokens + len - 1) / len;
-  if (n < 1) n = 1;
-  *splits = (int32_t)n;
-  *split_len = (int32_t)len;
-}
-
-// The split count of decode_split for any token count up to max_tokens is at
-// most this bound (len >= n / want gives at most `want` splits, len >= kMinSplit
-// at most ceil(max_tokens / kMinSplit)); the bound never decreases as
-// max_tokens grows, so a workspace sized for a capacity fits every shorter call.
-int32_t decode_max_splits(int64_t max_tokens, int64_t units) {
-  int64_t want = units > 0 ? (kSplitTarget + units - 1) / units : 1;
-  if (want < 1) want = 1;
-  int64_t by_len = (max_tokens + kMinSplit - 1) / kMinSplit;
-  int64_t n = want < by_len ? want : by_len;
-  return (int32_t)(n < 1 ? 1 : n);
-}
-
 hipError_t launch_decode(const DecodeArgs& a, int key_mse_bits, int key_qjl, int value_mse,
                          int value_bits, hipStream_t stream, TimedLaunch tl) {
   hipLaunchKernelGGL(qprep_kernel, dim3(a.batch * a.h_kv), dim3(256), 0, stream, a);

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])
-@pytest.mark.parametrize("d", [16, 128])
+@pytest.mark.parametrize("d", [3, 4, 5, 8, 16, 128])
 def test_codebook_matches_oracle(d, bits):
     c, t = tq.make_codebook(d, bits)
     ref = oracle.lloyd_max(d, bits)
@@ -39,7 +39,9 @@ def test_codebook_matches_oracle(d, bits):
     ulp_c = np.spacing(np.abs(ref.centroids).astype(np.float32))
     assert np.all(np.abs(c.astype(np.float64) - ref.centroids) <= ulp_c)
     ulp_t = np.spacing(np.maximum(np.abs(ref.thresholds), 1e-30).astype(np.float32))
-    assert np.all(np.abs(t.astype(np.float64) - ref.thresholds) <= np.maximum(ulp_t, 1e-15))
+    # the oracle does not impose symmetry, so its middle threshold is zero only to
+    # its iteration tolerance (a few 1e-15); near zero the bound is absolute
+    assert np.all(np.abs(t.astype(np.float64) - ref.thresholds) <= np.maximum(ulp_t, 1e-13))
     # exact symmetry of the table
     assert np.array_equal(c, -c[::-1])
 
