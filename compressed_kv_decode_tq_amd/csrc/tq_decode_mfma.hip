@@ -303,9 +303,9 @@ __device__ __forceinline__ void qprep_part(const DecodeArgs& a, int b, int h, in
 template <int MAXG>
 __global__ __launch_bounds__(256) void qprep_mfma_kernel(DecodeArgs a, int pm, int npl, int nht) {
   __shared__ QprepLds<MAXG> lds;
-  const int b = blockIdx.x / a.h_kv, h = blockIdx.x % a.h_kv;
+  const int b = __builtin_amdgcn_workgroup_id_x() / a.h_kv, h = __builtin_amdgcn_workgroup_id_x() % a.h_kv;
   uint32_t* dig = reinterpret_cast<uint32_t*>(a.qdig) + (size_t)(b * a.h_kv + h) * (nht * npl * 2 * 64 * 4);
-  qprep_part<MAXG>(a, b, h, (int)blockIdx.y, (int)threadIdx.x, lds, dig, a.qconst + ws_row(a, b, h, 0) * 4, pm,
+  qprep_part<MAXG>(a, b, h, (int)__builtin_amdgcn_workgroup_id_y(), (int)__builtin_amdgcn_workitem_id_x(), lds, dig, a.qconst + ws_row(a, b, h, 0) * 4, pm,
                    npl, nht);
 }
 
@@ -338,13 +338,13 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
 
   // the wave index is uniform: reading it from the first lane keeps the chunk
   // loop, its bounds and the full/partial chunk test in scalar registers
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = __builtin_amdgcn_workitem_id_x() & 63, wave = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_workitem_id_x() >> 6);
   const int g = lane >> 4, n = lane & 15;
-  const int sh = blockIdx.y;
+  const int sh = __builtin_amdgcn_workgroup_id_y();
   const int b = sh / a.h_kv, h = sh % a.h_kv;
   const int G = a.group;
   const int64_t n_c = a.n_comp.v[b];
-  const int64_t t_begin = (int64_t)blockIdx.x * a.split_len;
+  const int64_t t_begin = (int64_t)__builtin_amdgcn_workgroup_id_x() * a.split_len;
   const int64_t t_end = t_begin + a.split_len < n_c ? t_begin + a.split_len : n_c;
 
   uint32_t* s_meta = smem + wave * kStride;
@@ -442,14 +442,22 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
     if (HALF && sp == KP - 1) return sp * (kD / 8) - kD / 16;
     return sp * (kD / 8);
   };
-  auto key_word = [&](const uint8_t* p) -> uint32_t { return *reinterpret_cast<const uint32_t*>(p); };
-  auto key_half_word = [&](const uint8_t* p) -> uint32_t { return *reinterpret_cast<const uint16_t*>(p); };
+  // The compressed cache is read once per step: its loads are non-temporal
+  // (streamed past the caches instead of displacing the query digits and the
+  // per-head constants every work-group reuses).
+  auto key_word = [&](const uint8_t* p) -> uint32_t {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+  };
+  auto key_half_word = [&](const uint8_t* p) -> uint32_t {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
+  };
   const uint32_t s_lane = lane * (uint32_t)ssz;       // token `lane`'s scalar
   const uint32_t m_lane = VMSE ? s_lane : lane * (uint32_t)(NG * 4);
   const uint32_t v_lane = lane * 16u;                 // four value words per lane
   auto scalar_at = [&](const void* base, uint32_t off) -> float {
     const char* p = reinterpret_cast<const char*>(base) + off;
-    return a.scalar_f16 ? __half2float(*reinterpret_cast<const __half*>(p)) : *reinterpret_cast<const float*>(p);
+    return a.scalar_f16 ? __half2float(__ushort_as_half(__builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p))))
+                        : __builtin_nontemporal_load(reinterpret_cast<const float*>(p));
   };
   auto load_chunk = [&](int it, bool keys, bool rest) {
     const int64_t c = first + (int64_t)it * kRound;
@@ -473,18 +481,18 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
       if (VMSE)
         pMeta[0] = __float_as_uint(scalar_at(xm, m_lane));
       else
-        pMeta = *reinterpret_cast<const u32x4*>(xm + m_lane);
+        pMeta = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xm + m_lane));
 #pragma unroll
-      for (int i = 0; i < VB; ++i) pVw[i] = *reinterpret_cast<const u32x4*>(xv + v_lane + i * 1024);
+      for (int i = 0; i < VB; ++i) pVw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xv + v_lane + i * 1024));
     } else if (rem_c == 64) {  // full chunk: no per-lane guards
       pNrm = scalar_at(xn, s_lane);
       if (QJL) pGam = scalar_at(xg, s_lane);
       if (VMSE)
         pMeta[0] = __float_as_uint(scalar_at(xm, m_lane));
       else
-        pMeta = *reinterpret_cast<const u32x4*>(xm + m_lane);
+        pMeta = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xm + m_lane));
 #pragma unroll
-      for (int i = 0; i < VB; ++i) pVw[i] = *reinterpret_cast<const u32x4*>(xv + v_lane + i * 1024);
+      for (int i = 0; i < VB; ++i) pVw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xv + v_lane + i * 1024));
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
@@ -611,6 +619,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
       }
     }
     if (c0t + 64 > lim_min) {  // tail of the compressed part under a causal query
+      // (a wave-uniform branch, kept a branch: the per-lane selects below run
+      // only in the chunks that need them)
+      asm volatile("" ::: "memory");
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht)
 #pragma unroll
@@ -721,24 +732,27 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi)
           AG[gi] = *reinterpret_cast<const u32x4*>(s_tr + 4 * ((n & 3) * 64 + ((lane & ~3) | (gi ^ (n & 3)))));
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-          const int gi = nt >> 1;  // group of channels 16nt..16nt+15
-          u32x4 B;
+        auto value_operand = [&](int nt) -> u32x4 {
           if (VB == 4) {
             // 4-bit codes: tokens 16g..16g+15 are the staged rows 2g and 2g+1
             // (eight tokens each); token i of a word sits in byte i%4, nibble i/4
             const uint32_t w0 = s_vw[(2 * g) * (kD + kVwPad) + 16 * nt + n];
             const uint32_t w1 = s_vw[(2 * g + 1) * (kD + kVwPad) + 16 * nt + n];
-            B = u32x4{w0 & 0x0f0f0f0fu, (w0 >> 4) & 0x0f0f0f0fu, w1 & 0x0f0f0f0fu, (w1 >> 4) & 0x0f0f0f0fu};
-          } else {
-            const uint32_t w = s_vw[g * (kD + kVwPad) + 16 * nt + n];
-            B = u32x4{w & 0x03030303u, w & 0x0c0c0c0cu, w & 0x30303030u, (w >> 2) & 0x30303030u};
+            return u32x4{w0 & 0x0f0f0f0fu, (w0 >> 4) & 0x0f0f0f0fu, w1 & 0x0f0f0f0fu, (w1 >> 4) & 0x0f0f0f0fu};
           }
-          // rows (head g, digit r) of group gi: element r is digit r's product
-          const i32x4 C = mfma_i8(AG[gi], B, i32x4{0, 0, 0, 0});
+          const uint32_t w = s_vw[g * (kD + kVwPad) + 16 * nt + n];
+          return u32x4{w & 0x03030303u, w & 0x0c0c0c0cu, w & 0x30303030u, (w >> 2) & 0x30303030u};
+        };
+        // rows (head g, digit r) of group nt/2 (channels 16nt..16nt+15):
+        // element r is digit r's product.  The MFMA of tile nt + 1 is issued
+        // before the result of tile nt is read, so its latency overlaps.
+        i32x4 Cn = mfma_i8(AG[0], value_operand(0), i32x4{0, 0, 0, 0});
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+          const i32x4 C = Cn;
+          if (nt + 1 < 8) Cn = mfma_i8(AG[(nt + 1) >> 1], value_operand(nt + 1), i32x4{0, 0, 0, 0});
           const float v = fmaf((float)((C[0] << 8) + C[1]), 65536.f, (float)((C[2] << 8) + C[3]));
-          acc[ht][nt] = fmaf(acc[ht][nt], alpha_pv[ht], fmaf(v, inv_sv, Mpv[gi]));
+          acc[ht][nt] = fmaf(acc[ht][nt], alpha_pv[ht], fmaf(v, inv_sv, Mpv[nt >> 1]));
         }
       }
     } else {
@@ -841,7 +855,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
   }
   __syncthreads();
   const float* base = reinterpret_cast<const float*>(smem);
-  for (int i = threadIdx.x; i < G * kD; i += blockDim.x) {
+  for (int i = __builtin_amdgcn_workitem_id_x(); i < G * kD; i += kScanThreads) {
     const int hh = i / kD, c = i % kD;
     float M = -INFINITY;
 #pragma unroll
@@ -856,7 +870,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
         Acc += f * base[w * kStride + hh * (kD + 2) + 2 + c];
       }
     }
-    float* part = a.partial + ((size_t)blockIdx.x * a.batch * a.h_kv * G + ws_row(a, b, h, hh)) * (kD + 2);
+    float* part = a.partial + ((size_t)__builtin_amdgcn_workgroup_id_x() * a.batch * a.h_kv * G + ws_row(a, b, h, hh)) * (kD + 2);
     if (c == 0) {
       part[0] = M;
       part[1] = L;
@@ -912,14 +926,6 @@ hipError_t dispatch_mfma(const DecodeArgs& a, int kb, int qjl, int vmse, int vb,
 }
 
 }  // namespace
-
-size_t mfma_workspace_bytes(int batch, int h_q, int group) {
-  const int nht = (group + 3) / 4;
-  const int h_kv = h_q / group;
-  const size_t dig = (size_t)batch * h_kv * nht * 5 * 2 * 64 * 16;  // up to 5 score planes
-  const size_t cst = (size_t)batch * h_q * 4 * 4;
-  return dig + cst + 256;
-}
 
 hipError_t launch_decode_mfma(const DecodeArgs& a_in, int key_mse_bits, int key_qjl, int value_mse,
                               int value_bits, int key_planes, int value_planes, hipStream_t stream,

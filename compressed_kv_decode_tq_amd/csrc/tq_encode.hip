@@ -25,6 +25,8 @@
 namespace tq {
 namespace {
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 // LDS holds each bf16 matrix as 128 rows of 16 16-byte chunks; chunk c of row r
 // sits in slot c ^ 8*((c >> 1) & 1) ^ (r & 15).  The MFMA operand reads (lane
 // (g, tc) takes chunk 4ks + g of row 16rt + tc) then fall on distinct banks
@@ -105,7 +107,6 @@ __device__ __forceinline__ void store_plane_word(uint32_t* p, uint32_t w, uint32
 
 // Two fp32 values rounded to bf16 (nearest even), packed low | high << 16.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
@@ -703,10 +704,31 @@ __device__ __forceinline__ void transpose8_4bit(uint32_t (&D)[8], int li) {
 }
 
 // Asymmetric min/max value code, one 32-token tile per wave: lane = (token,
-// half of the channels).  IEEE fp32 arithmetic in a fixed order so the codes
-// are reproducible bit for bit:
+// half of the channels).  The stored scale and zero are exact functions of the
+// group (correctly rounded fp32 division, then fp16):
 //   delta = fp16(fp32(max - min) / (2^b - 1)), zero = fp16(min)
 //   code  = clamp(rint(fp32(v - zero) * fp32(1 / delta)), 0, 2^b - 1), 0 if delta == 0
+// in IEEE fp32 with every step correctly rounded.  The rounding to an integer
+// (ties to even) is the addition of 1.5 * 2^23, which leaves the code, biased by
+// that number's bit pattern, in the low bits of the sum; an integer clamp to
+// [bias, bias + 2^b - 1] then saturates quotients outside the code range, of
+// any size and sign.  A quotient that is exactly a midpoint k + 1/2 in fp32 (it
+// happens: the inputs are bf16 or fp16 numbers) rounds to even, as the plain
+// definition does.
+constexpr float kRoundBias = 12582912.0f;  // 1.5 * 2^23: adding it rounds to an integer
+constexpr int kBiasBits = 0x4B400000;       // its bit pattern, the code 0 after the addition
+
+// Sum over the fields of a packed word (field j at bit 8 (j % 4) + W (j / 4),
+// N fields of width W) of the bias each biased code carries, modulo 2^32:
+// subtracting it from the sum of the shifted biased codes leaves the codes,
+// since their fields do not overlap.
+template <int N, int W>
+constexpr uint32_t packed_bias() {
+  uint32_t c = 0u;
+  for (int j = 0; j < N; ++j) c += (uint32_t)kBiasBits << (8 * (j & 3) + W * (j >> 2));
+  return c;
+}
+
 template <bool IN_BF16, int BITS, int GS>
 __global__ __launch_bounds__(256) void encode_minmax_kernel(EncodeArgs a) {
   constexpr int L = (1 << BITS) - 1;
@@ -730,13 +752,15 @@ __global__ __launch_bounds__(256) void encode_minmax_kernel(EncodeArgs a) {
     const int64_t dp = blk * 32 + tok;
     const int64_t t = dp - pos;
     const bool valid = t >= 0 && t < a.n_new;
+    // the row of a token outside the written range is clamped to a real one:
+    // the load stays in bounds, and neither its codes nor its scales are stored
     const int64_t row = ((int64_t)b * a.n_new + (valid ? t : 0)) * a.h_kv + h;
     float x[64];
     if (IN_BF16) {
       const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.v) + row * kD + 64 * half);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const u32x4 w = valid ? p[i] : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 w = p[i];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           x[8 * i + 2 * e] = bf2f(w[e] & 0xffffu);
@@ -747,7 +771,7 @@ __global__ __launch_bounds__(256) void encode_minmax_kernel(EncodeArgs a) {
       const floatx4* p = reinterpret_cast<const floatx4*>(reinterpret_cast<const float*>(a.v) + row * kD + 64 * half);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const floatx4 w = valid ? p[i] : floatx4{0.f, 0.f, 0.f, 0.f};
+        const floatx4 w = p[i];
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[4 * i + e] = w[e];
       }
@@ -765,12 +789,15 @@ __global__ __launch_bounds__(256) void encode_minmax_kernel(EncodeArgs a) {
       const __half d16 = __float2half_rn(__fdiv_rn(__fsub_rn(mx, mn), (float)L));
       const __half z16 = __float2half_rn(mn);
       const float d32 = __half2float(d16), z32 = __half2float(z16);
+      // delta == 0 (a constant group): a zero factor leaves every code at 0
       const float invd = d32 != 0.f ? __fdiv_rn(1.0f, d32) : 0.f;
 #pragma unroll
       for (int e = 0; e < GS; ++e) {
-        float r = rintf(__fmul_rn(__fsub_rn(x[gi * GS + e], z32), invd));
-        r = fminf(fmaxf(r, 0.f), (float)L);
-        code[gi * GS + e] = d32 != 0.f ? (uint32_t)r : 0u;
+        // the product is rounded before the addition (no fused multiply-add)
+#pragma clang fp contract(off)
+        const float q = (x[gi * GS + e] - z32) * invd;
+        const float f = q + kRoundBias;
+        code[gi * GS + e] = (uint32_t)min(max(__float_as_int(f), kBiasBits), kBiasBits + L);  // biased code
       }
       if (valid) {
         const int grp = half * NG + gi;
@@ -785,11 +812,14 @@ __global__ __launch_bounds__(256) void encode_minmax_kernel(EncodeArgs a) {
       // channel 16 m + j at the packed offset of token j, and the row
       // transpose leaves channel 64 half + 16 m + i of word h in D[m]
       const int li = lane & 15, hw = (lane >> 4) & 1;
+      constexpr uint32_t kBias = packed_bias<16, 2>();
       uint32_t D[4] = {0u, 0u, 0u, 0u};
       static_for<0, 64>([&](auto E) {
         constexpr int e = decltype(E)::value;
-        D[e >> 4] |= code[e] << packed2_offset(e & 15);
+        D[e >> 4] += code[e] << packed2_offset(e & 15);
       });
+#pragma unroll
+      for (int m = 0; m < 4; ++m) D[m] -= kBias;
       transpose16_2bit(D, li);
       // the word's valid tokens: OR of the row's own fields
       uint32_t msk = valid ? 3u << packed2_offset(li) : 0u;
@@ -805,11 +835,14 @@ __global__ __launch_bounds__(256) void encode_minmax_kernel(EncodeArgs a) {
       // offset of token j in D[m]; the half-row transpose leaves channel
       // 64 half + 8 m + i of word h in D[m]
       const int li = lane & 7, hw = (lane >> 3) & 3;
+      constexpr uint32_t kBias = packed_bias<8, 4>();
       uint32_t D[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
       static_for<0, 64>([&](auto E) {
         constexpr int e = decltype(E)::value;
-        D[e >> 3] |= code[e] << packed4_offset(e & 7);
+        D[e >> 3] += code[e] << packed4_offset(e & 7);
       });
+#pragma unroll
+      for (int m = 0; m < 8; ++m) D[m] -= kBias;
       transpose8_4bit(D, li);
       uint32_t msk = valid ? 15u << packed4_offset(li) : 0u;
       msk |= dpp_u32<0xb1>(msk);
@@ -824,6 +857,8 @@ __global__ __launch_bounds__(256) void encode_minmax_kernel(EncodeArgs a) {
       uint32_t w[BITS][2];
 #pragma unroll
       for (int p = 0; p < BITS; ++p) w[p][0] = w[p][1] = 0u;
+#pragma unroll
+      for (int e = 0; e < 64; ++e) code[e] -= (uint32_t)kBiasBits;
       static_for<0, 64>([&](auto E) {
         constexpr int e = decltype(E)::value;
 #pragma unroll
