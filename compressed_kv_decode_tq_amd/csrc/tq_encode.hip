@@ -204,8 +204,9 @@ __global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
           // token: the load stays in bounds and holds finite values.  MFMA
           // output columns depend only on their own input column, and such
           // columns are never stored, so they need no masking.
-          kin[ct][ks] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(src) + row[ct] * kD +
-                                                        32 * ks + 8 * g);
+          // (inputs are read once: non-temporal loads)
+          kin[ct][ks] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+              reinterpret_cast<const uint16_t*>(src) + row[ct] * kD + 32 * ks + 8 * g));
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
@@ -222,10 +223,11 @@ __global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
       for (int ct = 0; ct < 2; ++ct) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const float* fp = reinterpret_cast<const float*>(src) + row[ct] * kD + 32 * ks + 8 * g;
-          float f[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) f[e] = fp[e];  // clamped row: in bounds, finite, never stored
+          const floatx4* fp = reinterpret_cast<const floatx4*>(reinterpret_cast<const float*>(src) + row[ct] * kD +
+                                                               32 * ks + 8 * g);
+          // clamped row: in bounds, finite, never stored; read once (non-temporal)
+          const floatx4 f0 = __builtin_nontemporal_load(fp), f1 = __builtin_nontemporal_load(fp + 1);
+          const float f[8] = {f0[0], f0[1], f0[2], f0[3], f1[0], f1[1], f1[2], f1[3]};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const uint32_t hp = pack_bf16x2(f[2 * e], f[2 * e + 1]);
