@@ -1,5 +1,5 @@
-// Decode on the int8 matrix cores of gfx950: the compressed scan as integer
-// MFMAs over the stored bit planes.
+// Decode on the matrix cores of gfx950: the compressed scan as MFMAs over the
+// stored bit planes.
 //
 // What is computed (page "03. Results & Benchmarks", "Latency Benchmarks":
 // scores, QJL correction, online softmax and value accumulation in one pass;
@@ -13,18 +13,20 @@
 //   so <q_rot, c[idx]> = cst sum(q_rot) + sum_p w_p <q_rot, plane_p>, and the
 //   QJL term is <q_s, 2 bit - 1> = 2 <q_s, bit> - sum(q_s).  Every score term is
 //   a 0/1-vector times a query vector.
-// * Those products run as v_mfma_i32_16x16x64_i8: one operand is the bit plane
-//   itself (a byte per bit, taken from a 32-bit plane word with ONE AND against
-//   0x01010101 << s, so the byte holds 2^s), the other the query in fixed point
-//   split into four signed base-128 digits (one digit per MFMA row/column),
-//   pre-scaled by 2^-s to cancel the byte's 2^s.  Integer sums are exact; the
-//   fixed point keeps 20+ significant bits of every query coordinate.
-// * The value sum sum_t p_t v~_t runs the same way with the roles swapped: the
-//   weights p_t delta_t (min/max) or p_t |v_t| (MSE values) in fixed-point
-//   digits, times the value bit planes.  The score MFMA leaves each lane holding
-//   exactly the 16 tokens its digit row needs for the value MFMA, so no data
-//   moves between the two.
-// * A byte holding 2^7 reads as -128 in int8; the matching digits are negated.
+// * Those products run as v_mfma_scale_f32_16x16x128_f8f6f4: the B operand is
+//   the bit plane itself as fp4 numbers (a 32-bit plane word becomes the 32
+//   nibbles of one lane with one AND per dword, each nibble 0 or a power of
+//   two), the A operand the query as four fp8 digits of a float expansion (one
+//   digit per MFMA row), whose per-row scales undo the digits' exponents.  One
+//   MFMA covers all 128 coordinates of a plane; sums are fp32, and the four
+//   digits keep about 16 significant bits of every query coordinate.
+// * The value sum sum_t p_t v~_t runs as v_mfma_i32_16x16x64_i8 with the roles
+//   swapped: the weights p_t delta_t (min/max) or p_t |v_t| (MSE values) in
+//   fixed-point digits, times the value bit planes (bytes holding 2^s, from
+//   one AND against 0x01010101 << s; a byte holding 2^7 reads as -128, so the
+//   matching digits are negated).  Integer sums are exact.  The score MFMA
+//   leaves each lane holding exactly the 16 tokens its digit row needs for the
+//   value MFMA, so no data moves between the two.
 #include <algorithm>
 #include <climits>
 #include <cstdlib>
@@ -44,6 +46,40 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ i32x4 mfma_i8(u32x4 a, u32x4 b, i32x4 c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b),
                                                c, 0, 0, 0);
+}
+
+// Bytes of a plane word: byte j of the result is bit (8j + s) of w, scaled by 2^s
+// (operand bytes of the MSE-value MFMAs).
+__device__ __forceinline__ uint32_t plane_bytes(uint32_t w, int s) { return w & (0x01010101u << s); }
+
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+// Score MFMA: A = fp8 (e4m3) query digits, B = fp4 (e2m1) key bits, 16x16x128,
+// fp32 accumulation.  sa: the scale of this lane's A row (E8M0, byte 0); B is
+// unscaled.
+__device__ __forceinline__ floatx4 mfma_f8f4(const i32x8& a, const i32x8& b, floatx4 c, int sa) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, sa, 0, 0x7F7F7F7F);
+}
+
+// fp4 operand of one 32-bit key plane word: nibble j of dword v' holds bit
+// 4j + v' of the word as an e2m1 number (bits 0, 1, 2 in place: 0.5, 1, 2; bit 3
+// moved down to bit 2: 2), so the 32 coordinates of the word fill the 32
+// nibbles with one AND (two for bit 3) per dword.  The query digits carry the
+// inverse weights 2, 1, 1/2, 1/2.
+__device__ __forceinline__ i32x8 fp4_bits(uint32_t w) {
+  return i32x8{(int)(w & 0x11111111u), (int)(w & 0x22222222u), (int)(w & 0x44444444u),
+               (int)((w >> 1) & 0x44444444u), 0, 0, 0, 0};
+}
+
+// Coordinate (within the head) and the log2 of the inverse nibble weight of the
+// A element at lane group g, dword v, byte b of the score MFMA: the MFMA pairs
+// that element with nibble j' = 4 (v % 2) + b of dword v' = 2 (g % 2) + (v / 2) % 2
+// of lane group g' = 2 (v / 4) + g / 2 of the B operand, which holds coordinate
+// 32 g' + 4 j' + v'.
+__device__ __forceinline__ int score_coordinate(int g, int v, int b, int& wexp) {
+  const int gp = 2 * (v >> 2) + (g >> 1), vp = 2 * (g & 1) + ((v >> 1) & 1), jp = 4 * (v & 1) + b;
+  wexp = vp == 0 ? 1 : (vp == 1 ? 0 : -1);
+  return 32 * gp + 4 * jp + vp;
 }
 
 // Sum over the 4 lanes of a quad (xor 1, then xor 2) with DPP.
@@ -92,67 +128,54 @@ __device__ __forceinline__ float col_sum4(float x) {
   return __uint_as_float(u[0]) + __uint_as_float(u[1]);
 }
 
-// Bytes of a plane word: byte j of the result is bit (8j + s) of w, scaled by 2^s.
-__device__ __forceinline__ uint32_t plane_bytes(uint32_t w, int s) { return w & (0x01010101u << s); }
 
-// Signed base-128 digits of q (|q| < 2^27), most significant first.
-__device__ __forceinline__ void digits128(int q, int d[4]) {
-#pragma unroll
-  for (int L = 3; L >= 1; --L) {
-    const int r = ((q + 64) & 127) - 64;
-    d[L] = r;
-    q = (q - r) >> 7;
-  }
-  d[0] = q;
-}
-
-// Query digits: for head tile ht, score plane pl, contraction half hf and lane
-// (g, n), 16 bytes: byte 4d + j holds digit n%4 of head 4ht + n/4 at
-// coordinate k = 32g + 8j + 4hf + d, pre-scaled by 2^-(k%8) (negated for
-// k%8 == 7).  Plane pl < PM multiplies w_pl * (Pi q); plane PM (QJL) 2 * (S q).
-// The two products are independent down to their digits: work-group (b h, 0)
-// makes the PM index planes from Pi q (and appends the ring token), (b h, 1)
-// the QJL plane from S q.
-// Digit operands of the score planes [pl0, pl1) of one slot, for every head
-// tile.  x_at(pl, gq, k) is the value plane pl multiplies at coordinate k for
-// head gq (w_pl (Pi q)_k or 2 (S q)_k), e_at(pl, gq) its fixed-point exponent.
-// One work item is (head tile, plane, half, lane group, head of the tile,
-// byte offset d): it rounds the four coordinates k = 32g + 8j + 4hf + d
-// (j < 4) once, splits each into its four base-128 digits and writes the four
-// digit dwords of that head (digit rows L = 0..3).
-template <class XAt, class EAt>
+// Query digits of the score MFMAs.  For head tile ht, score plane pl and A
+// lane (g, m), m = 4 hh + L: 32 fp8 bytes, byte b of dword v holding digit L of
+// the value x of head 4 ht + hh at the coordinate that element meets in the
+// MFMA (score_coordinate), times 2^sigma / (nibble weight).  Plane pl < PM
+// multiplies w_pl * (Pi q); plane PM (QJL) 2 * (S q).  The four digits are a
+// float expansion: d0 = fp8(y), d1 = fp8(16 (y - d0)), ... (each rounded to
+// nearest), so y = d0 + d1/16 + d2/256 + d3/4096 to about 2^-16 relative; the
+// MFMA's row scale 2^(-sigma - 4L) undoes the scaling, so the four digit rows
+// of a head sum to sum_c x_c bit_c.  The two products are independent down to
+// their digits: work-group (b h, 0) makes the PM index planes from Pi q (and
+// appends the ring token), (b h, 1) the QJL plane from S q.
+// One work item is (head tile, plane, lane group, head of the tile, dword): it
+// expands the four coordinates of that dword once and writes the dword of
+// each of the four digit rows.  x_at(pl, gq, k) is the value plane pl
+// multiplies at coordinate k for head gq, s_at(pl, gq) its exponent sigma.
+template <class XAt, class SAt>
 __device__ __forceinline__ void emit_digits(int tid, int nthreads, int pl0, int pl1, int npl, int nht, int G,
-                                            XAt x_at, EAt e_at, uint32_t* dig) {
+                                            XAt x_at, SAt s_at, uint32_t* dig) {
   const int np = pl1 - pl0;
-  const int items = nht * np * 2 * 4 * 4 * 4;
+  const int items = nht * np * 4 * 4 * 8;
   for (int it = tid; it < items; it += nthreads) {
-    const int d = it & 3, hh = (it >> 2) & 3, g = (it >> 4) & 3, hf = (it >> 6) & 1;
+    const int v = it & 7, hh = (it >> 3) & 3, g = (it >> 5) & 3;
     const int rest = it >> 7;
     const int pl = pl0 + rest % np, ht = rest / np;
     const int gq = 4 * ht + hh;
     uint32_t word[4] = {0u, 0u, 0u, 0u};
     if (gq < G) {
-      const int e = e_at(pl, gq);
+      const int sg = s_at(pl, gq);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int k = 32 * g + 8 * j + 4 * hf + d;
-        const int s = k & 7;
-        const int q = (int)rintf(ldexpf(x_at(pl, gq, k), e - s));
-        int dg[4];
-        digits128(q, dg);
+      for (int b = 0; b < 4; ++b) {
+        int wexp;
+        const int k = score_coordinate(g, v, b, wexp);
+        float y = ldexpf(x_at(pl, gq, k), sg + wexp);  // |y| < 2^8, inside fp8's range
 #pragma unroll
-        for (int L = 0; L < 4; ++L) word[L] |= (uint32_t)((s == 7 ? -dg[L] : dg[L]) & 0xff) << (8 * j);
+        for (int L = 0; L < 4; ++L) {
+          const uint32_t d = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.f, 0, false) & 0xffu;
+          word[L] |= d << (8 * b);
+          y = (y - __builtin_amdgcn_cvt_f32_fp8((int)d, 0)) * 16.f;  // exact remainder, next digit
+        }
       }
     }
 #pragma unroll
-    for (int L = 0; L < 4; ++L) {
-      const int ln = 16 * g + 4 * hh + L;
-      dig[((((ht * npl + pl) * 2 + hf) * 64 + ln) << 2) + d] = word[L];
-    }
+    for (int L = 0; L < 4; ++L) dig[(((ht * npl + pl) * 64 + 16 * g + 4 * hh + L) << 3) + v] = word[L];
   }
 }
 
-// Per-head fixed-point exponent and score constants of one product (part 0:
+// Per-head digit exponent sigma and score constants of one product (part 0:
 // Pi q, part 1: S q) of one head, on one wave.
 __device__ __forceinline__ int head_constants(const DecodeArgs& a, const float* x, int part, int lane, int pm,
                                               int npl, float* cst) {
@@ -179,15 +202,19 @@ __device__ __forceinline__ int head_constants(const DecodeArgs& a, const float* 
   } else {
     frexpf(2.f * mx, &ex);
   }
-  const int e = 26 - ex;  // scaled values stay below 2^26
+  // sigma: the scaled values |x| 2^sigma stay below 2^7 (2^8 after the inverse
+  // nibble weight), inside fp8's range of 448; clipped so the row scales
+  // 127 - sigma - 4L stay valid E8M0 exponents
+  int e = 7 - ex;
+  e = e < -100 ? -100 : (e > 100 ? 100 : e);
   if (lane == 0 && cst) {
     if (part == 0) {
       cst[0] = a.key_cst * sr + a.key_cst_hi * srh;  // constant part of <q_rot, c[idx]>
-      cst[1] = ldexpf(1.f, -e);                      // digit scale of the MSE planes
+      cst[1] = (float)e;                             // sigma of the MSE planes
       if (npl == pm) cst[2] = cst[3] = 0.f;          // no QJL plane
     } else {
-      cst[2] = ldexpf(1.f, -e);  // digit scale of the QJL plane
-      cst[3] = sr;               // sum(q_s)
+      cst[2] = (float)e;  // sigma of the QJL plane
+      cst[3] = sr;        // sum(q_s)
     }
   }
   return e;
@@ -353,37 +380,45 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
   float* s_p = reinterpret_cast<float*>(s_vw + kStageVw);
   uint32_t* s_tr = s_vw + kStageVw + kStageP;
 
-  // query digit operands and per-head constants (score layout: head 4ht + n/4)
-  const u32x4* dig_src = reinterpret_cast<const u32x4*>(a.qdig) + (size_t)sh * NHT * NPL * 2 * 64;
+  // query digit operands and per-head constants.  A rows: lane (g, n) supplies
+  // row n = (head 4ht + n/4, digit n%4) of the score MFMAs, with the row scale
+  // 2^(-sigma - 4 (n%4)) of that head and product; outputs: lane (g, n) holds
+  // head 4ht + g's four digit rows for token 16ct + n.
+  const u32x4* dig_src = reinterpret_cast<const u32x4*>(a.qdig) + (size_t)sh * NHT * NPL * 64 * 2;
   const float* cst_src = a.qconst + ws_row(a, b, h, 0) * 4;
-  u32x4 qb[NHT][NPL][2];
+  i32x8 qa[NHT][NPL];
   {
     const u32x4* src = dig_src;
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht)
 #pragma unroll
-      for (int pl = 0; pl < NPL; ++pl)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) qb[ht][pl][hf] = src[((ht * NPL + pl) * 2 + hf) * 64 + lane];
+      for (int pl = 0; pl < NPL; ++pl) {
+        const u32x4 lo = src[((ht * NPL + pl) * 64 + lane) * 2], hi = src[((ht * NPL + pl) * 64 + lane) * 2 + 1];
+        qa[ht][pl] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
   }
-  // score of (head, token) in log2 units: u (K1 Dm + c0) + w (K2 Ds - c3), where
-  // u = tau log2(e) n, w = u kappa gamma and Dm, Ds are the digit-combined
-  // integer dot products; lane (g, n) scores head 4ht + g
-  float k1[NHT], k2[NHT], c0[NHT], c3[NHT], k1h[NHT], k2h[NHT];
+  int sc_m[NHT], sc_s[NHT];  // E8M0 row scales of the index planes and of the QJL plane
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht) {
+    const int hq = 4 * ht + (n >> 2);
+    const floatx4 cs = hq < G ? *reinterpret_cast<const floatx4*>(cst_src + hq * 4) : floatx4{0.f, 0.f, 0.f, 0.f};
+    sc_m[ht] = 0x7F7F7F00 | (127 - (int)cs[1] - 4 * (n & 3));
+    sc_s[ht] = 0x7F7F7F00 | (127 - (int)cs[2] - 4 * (n & 3));
+  }
+  // score of (head, token) in log2 units: u (Sm + c0) + w (Ss - c3), where
+  // u = tau log2(e) n, w = u kappa gamma and Sm, Ss are the digit rows' sums;
+  // lane (g, n) scores head 4ht + g
+  float c0[NHT], c3[NHT];
 #pragma unroll
   for (int ht = 0; ht < NHT; ++ht) {
     const int hq = 4 * ht + g;
     if (hq < G) {
       const floatx4 cs = *reinterpret_cast<const floatx4*>(cst_src + hq * 4);
       c0[ht] = cs[0];
-      k1[ht] = cs[1];
-      k2[ht] = cs[2];
       c3[ht] = cs[3];
     } else {
-      c0[ht] = k1[ht] = k2[ht] = c3[ht] = 0.f;
+      c0[ht] = c3[ht] = 0.f;
     }
-    k1h[ht] = 16384.f * k1[ht];
-    k2h[ht] = 16384.f * k2[ht];
   }
   const float u_scale = a.scale * 1.4426950409f;  // exp(x) = exp2(x log2 e)
   // Several causal queries per sequence: the compressed tokens each head of
@@ -567,8 +602,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 
     // ---- scores (log2 units).  The query digits are the A operand and the
-    // key bits the B operand, so lane (g, n) receives, for token 16ct + n and
-    // head 4ht + g, all four digit partial sums (accumulator element r = digit r).
+    // key bits the B operand (fp4, one MFMA per plane covers all 128
+    // coordinates), so lane (g, n) receives, for token 16ct + n and head 4ht + g,
+    // all four digit rows (accumulator element r = digit r), already scaled.
     float sc[NHT][4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
@@ -579,42 +615,31 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
         P[2 % PM] = X[ct][2 % KP];
         P[3 % PM] = X[ct][0] ^ X[ct][1 % KP] ^ X[ct][2 % KP];
       }
-      i32x4 am[NHT], as[NHT];
+      // the constants enter through the accumulators (element 0: digit row 0)
+      floatx4 cm[NHT], cq[NHT];
 #pragma unroll
-      for (int ht = 0; ht < NHT; ++ht) am[ht] = as[ht] = i32x4{0, 0, 0, 0};
+      for (int ht = 0; ht < NHT; ++ht) {
+        cm[ht] = floatx4{c0[ht], 0.f, 0.f, 0.f};
+        cq[ht] = floatx4{-c3[ht], 0.f, 0.f, 0.f};
+      }
 #pragma unroll
       for (int pl = 0; pl < PM; ++pl) {
+        const i32x8 Bk = fp4_bits(P[pl]);
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const u32x4 Bk = {plane_bytes(P[pl], 4 * hf), plane_bytes(P[pl], 4 * hf + 1),
-                            plane_bytes(P[pl], 4 * hf + 2), plane_bytes(P[pl], 4 * hf + 3)};
-#pragma unroll
-          for (int ht = 0; ht < NHT; ++ht) am[ht] = mfma_i8(qb[ht][pl][hf], Bk, am[ht]);
-        }
+        for (int ht = 0; ht < NHT; ++ht) cm[ht] = mfma_f8f4(qa[ht][pl], Bk, cm[ht], sc_m[ht]);
       }
       if (QJL) {
-        const uint32_t Ps = X[ct][KP - 1];
+        const i32x8 Bk = fp4_bits(X[ct][KP - 1]);
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const u32x4 Bk = {plane_bytes(Ps, 4 * hf), plane_bytes(Ps, 4 * hf + 1), plane_bytes(Ps, 4 * hf + 2),
-                            plane_bytes(Ps, 4 * hf + 3)};
-#pragma unroll
-          for (int ht = 0; ht < NHT; ++ht) as[ht] = mfma_i8(qb[ht][NPL - 1][hf], Bk, as[ht]);
-        }
+        for (int ht = 0; ht < NHT; ++ht) cq[ht] = mfma_f8f4(qa[ht][NPL - 1], Bk, cq[ht], sc_s[ht]);
       }
       const int u = 16 * ct + n;  // token inside the chunk
       const floatx4 ng = *reinterpret_cast<const floatx4*>(s_ng + 4 * u);
       const float ut = ng[0], wt = ng[1];
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) {
-        // digits carry 2^21, 2^14, 2^7, 1: two exact integer halves, each
-        // scaled in float (the 2^14 of the upper half is folded into k1h, k2h)
-        const float dmh = (float)((am[ht][0] << 7) + am[ht][1]), dml = (float)((am[ht][2] << 7) + am[ht][3]);
-        float sv = fmaf(ut, fmaf(dmh, k1h[ht], fmaf(dml, k1[ht], c0[ht])), ng[2]);
-        if (QJL) {
-          const float dsh = (float)((as[ht][0] << 7) + as[ht][1]), dsl = (float)((as[ht][2] << 7) + as[ht][3]);
-          sv = fmaf(wt, fmaf(dsh, k2h[ht], fmaf(dsl, k2[ht], -c3[ht])), sv);
-        }
+        float sv = fmaf(ut, (cm[ht][0] + cm[ht][1]) + (cm[ht][2] + cm[ht][3]), ng[2]);
+        if (QJL) sv = fmaf(wt, (cq[ht][0] + cq[ht][1]) + (cq[ht][2] + cq[ht][3]), sv);
         sc[ht][ct] = sv;
       }
     }
