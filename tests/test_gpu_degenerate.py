@@ -107,3 +107,45 @@ def test_degenerate_tokens(name):
         f"decode max rel err {err.max():.2e}")
     assert np.all(np.isfinite(out.cpu().numpy()))
     assert err.max() <= OUT_RTOL
+
+
+QUERY_SCALES = (0.0, 1e-6, 1.0, 4.0, 16.0, 64.0)
+
+
+@pytest.mark.parametrize("path", ["mfma", "generic"])
+@pytest.mark.parametrize("name", ["2+1-bit keys, min/max values", "3+1-bit keys, MSE values", "qwen layer, fp16 scalars"])
+def test_query_scales(name, path, monkeypatch):
+    """Queries over nine decades of magnitude, one scale per query head: a
+    zero query (uniform attention), 1e-6 (nearly uniform) and 1 .. 64 times a
+    unit Gaussian (ever more peaked softmax, where the score precision of the
+    query's digit expansion decides the output).  Decode of the GPU's codes
+    against the oracle, on both scan paths."""
+    from tq_testlib import set_decode_path
+    set_decode_path(monkeypatch, path)
+    w = CASES[name].replace(n_tokens=96)
+    bk = books(w)
+    pi, s = wl.params(w)
+    prm = tq.Params(layout_of(w), pi, s, device=DEV)
+    k, v = wl.prefill_kv(w)
+    cache = tq.Cache(layout_of(w), 1, w.h_kv, 96, device=DEV)
+    tq.encode_kv(prm, k.to(DEV), v.to(DEV), [0], cache)
+    torch.cuda.synchronize()
+    kd, vd = [[]], [[]]
+    for h in range(w.h_kv):
+        a_, c_ = dequant_slot(w, bk, pi, s, slot_from_cache(w, cache, 0, h, w.n_tokens))
+        kd[0].append(a_)
+        vd[0].append(c_)
+    rng = np.random.default_rng(11)
+    q = rng.standard_normal((1, w.h_q, w.d))
+    for hq in range(w.h_q):
+        q[0, hq] *= QUERY_SCALES[hq % len(QUERY_SCALES)]
+    qt = torch.from_numpy(q).to(w.torch_dtype)
+    out = tq.decode_attn(prm, qt.to(DEV), cache, [w.n_tokens])
+    torch.cuda.synchronize()
+    ref = oracle.decode_attention(qt.double().numpy(), kd, vd)
+    err = max_rel_err(out.cpu().double().numpy(), ref)
+    per_scale = {sc: float(err[0, [hq for hq in range(w.h_q) if hq % len(QUERY_SCALES) == i]].max())
+                 for i, sc in enumerate(QUERY_SCALES) if i < w.h_q}
+    say(f"[query scales] {name} ({path}): " + ", ".join(f"{sc:g}: {e:.1e}" for sc, e in per_scale.items()))
+    assert np.all(np.isfinite(out.cpu().numpy()))
+    assert err.max() <= OUT_RTOL
