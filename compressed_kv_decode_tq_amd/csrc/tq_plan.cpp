@@ -6,15 +6,18 @@
 
 namespace tq {
 
-// Split of the token range for the decode grid, in whole 256-token rounds of
-// the four waves.  About kSplitTarget work-groups over the device; when that
-// makes splits shorter than kLongSplit tokens, they are lengthened towards
-// kLongSplit as long as at least kFloorGroups work-groups (one round of three
-// per compute unit) remain, so per-work-group set-up and the combine's merge
-// stay small next to the scan while a few long sequences still fill every
-// compute unit (8 sequence-heads of 131072 tokens: 1536-token splits, 688
-// work-groups, against 512-token splits and 2048 work-groups for a floor of
-// eight per compute unit: 4% less time per step, most of it in the combine).
+// Split of the token range for the decode grid, in whole 64-token chunks
+// (the waves of a work-group take the chunks of its split in turn).  About
+// kSplitTarget work-groups over the device; when that makes splits shorter than
+// kLongSplit tokens, they are lengthened towards kLongSplit as long as at least
+// kFloorGroups work-groups (one round of three per compute unit) remain, so
+// per-work-group set-up and the combine's merge stay small next to the scan
+// while a few long sequences still fill every compute unit.  8 sequence-heads
+// of 131072 tokens: 1408-token splits, 752 work-groups (about three per compute
+// unit), against 1536-token splits and 688 work-groups with whole 256-token
+// rounds (5% less scan time) and 512-token splits and 2048 work-groups for a
+// floor of eight per compute unit (4% more time per step, most of it in the
+// combine).
 constexpr int64_t kSplitTarget = 2048;
 constexpr int64_t kFloorGroups = 768;
 constexpr int64_t kLongSplit = 2048;
@@ -28,7 +31,7 @@ void decode_split(int64_t max_tokens, int64_t units, int32_t* splits, int32_t* s
   int64_t floor_len = (max_tokens * units + kFloorGroups - 1) / kFloorGroups;  // keeps >= kFloorGroups groups
   if (floor_len > kLongSplit) floor_len = kLongSplit;
   if (len < floor_len) len = floor_len;
-  len = ((len + 255) / 256) * 256;
+  len = ((len + 63) / 64) * 64;
   if (len < kMinSplit) len = kMinSplit;
   int64_t n = (max_tokens + len - 1) / len;
   if (n < 1) n = 1;
