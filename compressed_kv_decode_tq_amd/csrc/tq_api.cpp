@@ -201,7 +201,7 @@ int tq_encode_kv(const tq_layout* layout, const tq_params* params, const void* k
     const size_t in_off = (size_t)b0 * n_new * h_kv * tq::kD * esz;
     a.k = (const char*)k + in_off;
     a.v = (const char*)v + in_off;
-    a.k_planes = cache->k_planes + seq_off(b0, h_kv, cap, kpb);
+    a.k_planes = cache->k_planes + seq_off(b0, h_kv, tq::key_slot_tokens(cap), kpb);
     a.k_norm = (char*)cache->k_norm + seq_off(b0, h_kv, cap, sz);
     a.k_rnorm = cache->k_rnorm ? (char*)cache->k_rnorm + seq_off(b0, h_kv, cap, sz) : nullptr;
     a.v_planes = (uint32_t*)((char*)cache->v_planes + seq_off(b0, h_kv, cap, (size_t)layout->value_bits * tq::kD / 8));
@@ -380,7 +380,7 @@ int decode_attn_impl(const tq_layout* layout, const tq_params* params, const voi
     const size_t new_off = (size_t)b0 * h_kv * tq::kD * (new_dtype == TQ_F32 ? 4 : 2);
     tq::decode_split(max_tokens, (int64_t)std::min(cache->batch, tq::kMaxSeqPerLaunch) * h_kv, &a.splits, &a.split_len);
     a.q = (const char*)q + (size_t)b0 * nq * num_q_heads * tq::kD * qsz;
-    a.k_planes = cache->k_planes + seq_off(b0, h_kv, cap, kpb);
+    a.k_planes = cache->k_planes + seq_off(b0, h_kv, tq::key_slot_tokens(cap), kpb);
     a.k_norm = (const char*)cache->k_norm + seq_off(b0, h_kv, cap, sz);
     a.k_rnorm = cache->k_rnorm ? (const char*)cache->k_rnorm + seq_off(b0, h_kv, cap, sz) : nullptr;
     a.v_planes = (const uint32_t*)((const char*)cache->v_planes + seq_off(b0, h_kv, cap, (size_t)layout->value_bits * tq::kD / 8));

@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(DecodeArgs a) {
   __syncthreads();
 
   const size_t rec = (size_t)KP * (kD / 8);
-  const uint8_t* kp = a.k_planes + (size_t)sh * a.capacity * rec;
+  const uint8_t* kp = a.k_planes + (size_t)sh * key_slot_tokens(a.capacity) * rec;
   const size_t sidx0 = (size_t)sh * a.capacity;
   const int ngrp = kD / a.value_group;
   const uint32_t* vp = a.v_planes + (size_t)sh * (a.capacity >> 5) * VB * kD;
@@ -131,11 +131,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(DecodeArgs a) {
       float n = 0.f, gam = 0.f;
       if (valid) {
 #pragma unroll
-        for (int p = 0; p < KP; ++p) {
-          const u32x4 x = *reinterpret_cast<const u32x4*>(kp + tok * rec + p * 16);
+        for (int p = 0; p < KP; ++p)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[p][e] = x[e];
-        }
+          for (int e = 0; e < 4; ++e) w[p][e] = *reinterpret_cast<const uint32_t*>(kp + key_word_offset(tok, rec, p * 16, e, 4));
         n = load_scalar(a.k_norm, sidx0 + tok, a.scalar_f16);
         if (QJL) gam = load_scalar(a.k_rnorm, sidx0 + tok, a.scalar_f16);
       } else {

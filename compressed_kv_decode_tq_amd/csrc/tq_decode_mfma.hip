@@ -62,23 +62,34 @@ __device__ __forceinline__ floatx4 mfma_f8f4(const i32x8& a, const i32x8& b, flo
 }
 
 // fp4 operand of one 32-bit key plane word: nibble j of dword v' holds bit
-// 4j + v' of the word as an e2m1 number (bits 0, 1, 2 in place: 0.5, 1, 2; bit 3
-// moved down to bit 2: 2), so the 32 coordinates of the word fill the 32
-// nibbles with one AND (two for bit 3) per dword.  The query digits carry the
-// inverse weights 2, 1, 1/2, 1/2.
-__device__ __forceinline__ i32x8 fp4_bits(uint32_t w) {
+// 4j + v' of the word as an e2m1 number.  Bits 0, 1 and 2 stay in place (0.5,
+// 1, 2: one AND per dword).  Bit 3 of a nibble is e2m1's sign, so dword 3
+// keeps it there and sets bit 0 (one AND-OR): the nibble reads +0.5 for a clear
+// bit and -0.5 for a set one, i.e. 0.5 - bit.  The query digits carry the
+// inverse weights 2, 1, 1/2 and -1; the -1 digits' constant offset
+// -0.5 sum(x) over the coordinates of dword 3 (those = 3 mod 4) is taken back
+// in the per-head constants.
+// k88, k11: 0x88888888 and 0x11111111 held in registers (fp4_masks), so the
+// AND-OR is one three-operand instruction rather than two with literals.
+__device__ __forceinline__ i32x8 fp4_bits(uint32_t w, uint32_t k88, uint32_t k11) {
   return i32x8{(int)(w & 0x11111111u), (int)(w & 0x22222222u), (int)(w & 0x44444444u),
-               (int)((w >> 1) & 0x44444444u), 0, 0, 0, 0};
+               (int)((w & k88) | k11), 0, 0, 0, 0};
+}
+__device__ __forceinline__ void fp4_masks(uint32_t& k88, uint32_t& k11) {
+  k88 = 0x88888888u;
+  k11 = 0x11111111u;
+  asm("" : "+s"(k88), "+v"(k11));  // no instruction: only hides the constants from folding
 }
 
-// Coordinate (within the head) and the log2 of the inverse nibble weight of the
-// A element at lane group g, dword v, byte b of the score MFMA: the MFMA pairs
-// that element with nibble j' = 4 (v % 2) + b of dword v' = 2 (g % 2) + (v / 2) % 2
-// of lane group g' = 2 (v / 4) + g / 2 of the B operand, which holds coordinate
-// 32 g' + 4 j' + v'.
-__device__ __forceinline__ int score_coordinate(int g, int v, int b, int& wexp) {
+// Coordinate (within the head), log2 of the magnitude of the inverse nibble
+// weight, and its sign, of the A element at lane group g, dword v, byte b of
+// the score MFMA: the MFMA pairs that element with nibble j' = 4 (v % 2) + b of
+// dword v' = 2 (g % 2) + (v / 2) % 2 of lane group g' = 2 (v / 4) + g / 2 of the
+// B operand, which holds coordinate 32 g' + 4 j' + v' (so v' = coordinate mod 4).
+__device__ __forceinline__ int score_coordinate(int g, int v, int b, int& wexp, bool& neg) {
   const int gp = 2 * (v >> 2) + (g >> 1), vp = 2 * (g & 1) + ((v >> 1) & 1), jp = 4 * (v & 1) + b;
-  wexp = vp == 0 ? 1 : (vp == 1 ? 0 : -1);
+  wexp = vp == 0 ? 1 : (vp == 1 ? 0 : (vp == 2 ? -1 : 0));
+  neg = vp == 3;
   return 32 * gp + 4 * jp + vp;
 }
 
@@ -137,7 +148,8 @@ __device__ __forceinline__ float col_sum4(float x) {
 // float expansion: d0 = fp8(y), d1 = fp8(16 (y - d0)), ... (each rounded to
 // nearest), so y = d0 + d1/16 + d2/256 + d3/4096 to about 2^-16 relative; the
 // MFMA's row scale 2^(-sigma - 4L) undoes the scaling, so the four digit rows
-// of a head sum to sum_c x_c bit_c.  The two products are independent down to
+// of a head sum to sum_c x_c bit_c - 0.5 sum_{c = 3 mod 4} x_c (the offset of
+// fp4_bits' dword 3, added back through the head constants).  The two products are independent down to
 // their digits: work-group (b h, 0) makes the PM index planes from Pi q (and
 // appends the ring token), (b h, 1) the QJL plane from S q.
 // One work item is (head tile, plane, lane group, head of the tile, dword): it
@@ -160,8 +172,10 @@ __device__ __forceinline__ void emit_digits(int tid, int nthreads, int pl0, int 
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         int wexp;
-        const int k = score_coordinate(g, v, b, wexp);
-        float y = ldexpf(x_at(pl, gq, k), sg + wexp);  // |y| < 2^8, inside fp8's range
+        bool neg;
+        const int k = score_coordinate(g, v, b, wexp, neg);
+        const float xk = x_at(pl, gq, k);
+        float y = ldexpf(neg ? -xk : xk, sg + wexp);  // |y| < 2^8, inside fp8's range
 #pragma unroll
         for (int L = 0; L < 4; ++L) {
           const uint32_t d = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.f, 0, false) & 0xffu;
@@ -181,19 +195,26 @@ __device__ __forceinline__ int head_constants(const DecodeArgs& a, const float* 
                                               int npl, float* cst) {
   // sr: sum over the coordinates of the base table; srh over the half-bit
   // coordinates (i mod 32 < 16) of the fractional layout; for the QJL part,
-  // sr is sum(q_s)
-  float mx = 0.f, sr = 0.f, srh = 0.f;
+  // sr is sum(q_s).  s3, s3h: the same sums over the coordinates = 3 mod 4
+  // only (the nibbles that carry 0.5 - bit).
+  float mx = 0.f, sr = 0.f, srh = 0.f, s3 = 0.f, s3h = 0.f;
   for (int c = lane; c < kD; c += 64) {
     const float v = x[c];
+    const float v3 = (c & 3) == 3 ? v : 0.f;
     mx = fmaxf(mx, fabsf(v));
-    if (part == 0 && a.key_half && (c & 31) < 16)
+    if (part == 0 && a.key_half && (c & 31) < 16) {
       srh += v;
-    else
+      s3h += v3;
+    } else {
       sr += v;
+      s3 += v3;
+    }
   }
   mx = wave_max(mx);
   sr = wave_sum(sr);
   srh = wave_sum(srh);
+  s3 = wave_sum(s3);
+  s3h = wave_sum(s3h);
   int ex;
   if (part == 0) {
     float wmax = 0.f;
@@ -209,12 +230,21 @@ __device__ __forceinline__ int head_constants(const DecodeArgs& a, const float* 
   e = e < -100 ? -100 : (e > 100 ? 100 : e);
   if (lane == 0 && cst) {
     if (part == 0) {
-      cst[0] = a.key_cst * sr + a.key_cst_hi * srh;  // constant part of <q_rot, c[idx]>
-      cst[1] = (float)e;                             // sigma of the MSE planes
-      if (npl == pm) cst[2] = cst[3] = 0.f;          // no QJL plane
+      // constant part of <q_rot, c[idx]>, plus the dword-3 offsets of the PM
+      // planes: 0.5 sum_p sum_{c = 3 mod 4} w_p(c) q_rot(c)
+      float w = 0.f, wh = 0.f;
+      for (int p = 0; p < pm; ++p) {
+        w += a.key_w[p];
+        wh += a.key_w_hi[p];
+      }
+      cst[0] = a.key_cst * sr + a.key_cst_hi * srh + 0.5f * (s3 * w + (a.key_half ? s3h * wh : 0.f));
+      cst[1] = (float)e;                     // sigma of the MSE planes
+      if (npl == pm) cst[2] = cst[3] = 0.f;  // no QJL plane
     } else {
       cst[2] = (float)e;  // sigma of the QJL plane
-      cst[3] = sr;        // sum(q_s)
+      // sum(q_s), less the dword-3 offset of the QJL plane (whose x is 2 q_s):
+      // the scan adds -cst[3]
+      cst[3] = sr - s3;
     }
   }
   return e;
@@ -421,6 +451,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
     }
   }
   const float u_scale = a.scale * 1.4426950409f;  // exp(x) = exp2(x log2 e)
+  uint32_t k88, k11;
+  fp4_masks(k88, k11);
   // Several causal queries per sequence: the compressed tokens each head of
   // this lane sees (lim) and the fewest any head of the launch sees (lim_min,
   // wave-uniform); chunks that end at or below lim_min need no per-head mask.
@@ -440,26 +472,37 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
     lim_min = n_c - hide_c;
   }
 
-  // key record: full planes of 16 bytes; with HALF the last index plane has 8
+  // key record: full planes of 16 bytes; with HALF the last index plane has 8.
+  // The slot's key planes are stored in blocks of 64 tokens (key_word_offset):
+  // a chunk is one block, each of its planes one contiguous region.
   const size_t rec = (size_t)KP * (kD / 8) - (HALF ? kD / 16 : 0);
-  const uint8_t* kp = a.k_planes + (size_t)sh * a.capacity * rec;
+  const uint8_t* kp = a.k_planes + (size_t)sh * key_slot_tokens(a.capacity) * rec;
   const size_t sidx0 = (size_t)sh * a.capacity;
   const uint32_t* vp = a.v_planes + (size_t)sh * (a.capacity >> 5) * VB * kD;
 
-  // running max (log2 units) starts at a finite floor so exp2(-inf - m) is 0, never NaN
-  float m_run[NHT], l_part[NHT], acc[NHT][8];
+  // Running max m_run (log2 units; starts at a finite floor so exp2(-inf - m)
+  // is 0, never NaN) and the reference m_ref of the running sums l_part and
+  // acc, which hold sum_t 2^(s_t - m_ref) (...).  p is formed against m_run
+  // (so p <= 1 for the value digits) and added with the factor
+  // 2^(m_run - m_ref) >= 1; the sums are rescaled to a new reference only when
+  // m_run has moved more than kLazyRescale above m_ref (fp32 has the range),
+  // so a chunk normally adds to the sums with one fused multiply-add each.
+  constexpr float kLazyRescale = 32.f;
+  float m_run[NHT], m_ref[NHT], l_part[NHT], acc[NHT][8];
 #pragma unroll
   for (int ht = 0; ht < NHT; ++ht) {
-    m_run[ht] = -1e30f;
+    m_run[ht] = m_ref[ht] = -1e30f;
     l_part[ht] = 0.f;
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) acc[ht][nt] = 0.f;
   }
 
   // Chunk loads are issued one chunk ahead: the registers below hold chunk
-  // c0t + kRound of this wave while chunk c0t is being computed.
+  // c0t + kRound of this wave while chunk c0t is being computed.  Scalars
+  // are kept as loaded (fp16 or fp32 bits) and converted when staged, so no
+  // load has to complete before the chunk that uses it.
   uint32_t pX[4][KP];       // key plane words: token 16ct + n, plane word g
-  float pNrm = 0.f, pGam = 0.f;
+  uint32_t pNrm = 0u, pGam = 0u;
   u32x4 pMeta = u32x4{0u, 0u, 0u, 0u};
   u32x4 pVw[VB];
   const int64_t first = t_begin + 64 * wave;
@@ -467,112 +510,93 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
   // Addresses are a wave-uniform chunk base (scalar registers) plus a 32-bit
   // per-lane byte offset, so the loads take the scalar-base form and no
   // 64-bit per-lane pointers stay live across the loop.
-  const uint32_t k_lane = n * (uint32_t)rec + 4 * g;  // word g of token n's plane records
-  // byte offset of stored plane sp inside a record, for lane group g: full
-  // planes at 16 sp + 4g; the half plane's 16-bit chunk g (its coordinates
-  // 32g..32g+15) at 16 (KB - 1) + 2g; the QJL plane 8 bytes earlier than a
-  // full-plane record would put it
-  auto key_off = [&](int sp) -> int {
-    if (HALF && sp == KB - 1) return (KB - 1) * (kD / 8) - 2 * g;  // k_lane adds 4g
-    if (HALF && sp == KP - 1) return sp * (kD / 8) - kD / 16;
-    return sp * (kD / 8);
-  };
-  // The compressed cache is read once per step: its loads are non-temporal
-  // (streamed past the caches instead of displacing the query digits and the
-  // per-head constants every work-group reuses).
-  auto key_word = [&](const uint8_t* p) -> uint32_t {
-    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
-  };
-  auto key_half_word = [&](const uint8_t* p) -> uint32_t {
-    return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
-  };
+  // Region of stored plane sp in a key block: 64 times the plane's offset in
+  // the record (full planes at 16 sp, the half plane at 16 (KB - 1), the QJL
+  // plane after it); lane (g, n) reads words 4 (4n + g) .. + 3 of it, its
+  // four column tiles' word g (16-bit words in the half plane).
+  auto key_region = [&](int sp) -> int { return 64 * ((HALF && sp == KP - 1) ? sp * (kD / 8) - kD / 16 : sp * (kD / 8)); };
+  const uint32_t k_lane = (4 * n + g) * 16u, k_lane_half = (4 * n + g) * 8u;
   const uint32_t s_lane = lane * (uint32_t)ssz;       // token `lane`'s scalar
   const uint32_t m_lane = VMSE ? s_lane : lane * (uint32_t)(NG * 4);
   const uint32_t v_lane = lane * 16u;                 // four value words per lane
-  auto scalar_at = [&](const void* base, uint32_t off) -> float {
+  // The compressed cache is read once per step: its loads are non-temporal
+  // (streamed past the caches instead of displacing the query digits and the
+  // per-head constants every work-group reuses).
+  auto scalar_bits = [&](const void* base, uint32_t off) -> uint32_t {
     const char* p = reinterpret_cast<const char*>(base) + off;
-    return a.scalar_f16 ? __half2float(__ushort_as_half(__builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p))))
-                        : __builtin_nontemporal_load(reinterpret_cast<const float*>(p));
+    return a.scalar_f16 ? (uint32_t)__builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p))
+                        : __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
   };
-  auto load_chunk = [&](int it, bool keys, bool rest) {
-    const int64_t c = first + (int64_t)it * kRound;
+  auto scalar_value = [&](uint32_t bits) -> float {
+    return a.scalar_f16 ? __half2float(__ushort_as_half((unsigned short)bits)) : __uint_as_float(bits);
+  };
+  // The keys of a chunk: a whole 64-token block, read without per-lane guards
+  // even for a partial chunk (the block is allocated; tokens past the end get
+  // a -inf score from the staged mask, and fp4 bits are always finite).
+  auto load_keys = [&](int64_t c) {
+    const uint8_t* xk = kp + (c >> 6) * (int64_t)(64 * rec);
+#pragma unroll
+    for (int sp = 0; sp < KP; ++sp) {
+      if (HALF && sp == KB - 1) {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(xk + key_region(sp) + k_lane_half));
+        pX[0][sp] = v[0] & 0xffffu;
+        pX[1][sp] = v[0] >> 16;
+        pX[2][sp] = v[1] & 0xffffu;
+        pX[3][sp] = v[1] >> 16;
+      } else {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xk + key_region(sp) + k_lane));
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) pX[ct][sp] = v[ct];
+      }
+    }
+  };
+  // The per-token data and value words of a chunk (guarded past its end).
+  auto load_rest = [&](int64_t c) {
     const int rem_c = (int)(t_end - c < 64 ? t_end - c : 64);
-    const uint8_t* xk = kp + c * (int64_t)rec;
     const char* xn = reinterpret_cast<const char*>(a.k_norm) + (int64_t)(sidx0 + c) * ssz;
     const char* xg = QJL ? reinterpret_cast<const char*>(a.k_rnorm) + (int64_t)(sidx0 + c) * ssz : nullptr;
     const char* xm = VMSE ? reinterpret_cast<const char*>(a.v_norm) + (int64_t)(sidx0 + c) * ssz
                           : reinterpret_cast<const char*>(a.v_meta) + (int64_t)(sidx0 + c) * (NG * 4);
     const char* xv = reinterpret_cast<const char*>(vp + (c >> 5) * VB * kD);
-    if (rem_c == 64 && !rest) {
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-        for (int sp = 0; sp < KP; ++sp)
-          pX[ct][sp] = (HALF && sp == KB - 1) ? key_half_word(xk + k_lane + 16 * ct * rec + key_off(sp))
-                                               : key_word(xk + k_lane + 16 * ct * rec + key_off(sp));
-    } else if (rem_c == 64 && !keys) {
-      pNrm = scalar_at(xn, s_lane);
-      if (QJL) pGam = scalar_at(xg, s_lane);
+    if (rem_c == 64) {  // full chunk: no per-lane guards
+      pNrm = scalar_bits(xn, s_lane);
+      if (QJL) pGam = scalar_bits(xg, s_lane);
       if (VMSE)
-        pMeta[0] = __float_as_uint(scalar_at(xm, m_lane));
+        pMeta[0] = scalar_bits(xm, m_lane);
       else
         pMeta = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xm + m_lane));
 #pragma unroll
       for (int i = 0; i < VB; ++i) pVw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xv + v_lane + i * 1024));
-    } else if (rem_c == 64) {  // full chunk: no per-lane guards
-      pNrm = scalar_at(xn, s_lane);
-      if (QJL) pGam = scalar_at(xg, s_lane);
-      if (VMSE)
-        pMeta[0] = __float_as_uint(scalar_at(xm, m_lane));
-      else
-        pMeta = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xm + m_lane));
-#pragma unroll
-      for (int i = 0; i < VB; ++i) pVw[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xv + v_lane + i * 1024));
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-        for (int sp = 0; sp < KP; ++sp)
-          pX[ct][sp] = (HALF && sp == KB - 1) ? key_half_word(xk + k_lane + 16 * ct * rec + key_off(sp))
-                                               : key_word(xk + k_lane + 16 * ct * rec + key_off(sp));
     } else {
       const bool valid = lane < rem_c;
-      if (rest) {
-        pNrm = valid ? scalar_at(xn, s_lane) : 0.f;
-        pGam = (QJL && valid) ? scalar_at(xg, s_lane) : 0.f;
-        if (VMSE)
-          pMeta[0] = valid ? __float_as_uint(scalar_at(xm, m_lane)) : 0u;
-        else
-          pMeta = valid ? *reinterpret_cast<const u32x4*>(xm + m_lane) : u32x4{0u, 0u, 0u, 0u};
+      pNrm = valid ? scalar_bits(xn, s_lane) : 0u;
+      pGam = (QJL && valid) ? scalar_bits(xg, s_lane) : 0u;
+      if (VMSE)
+        pMeta[0] = valid ? scalar_bits(xm, m_lane) : 0u;
+      else
+        pMeta = valid ? *reinterpret_cast<const u32x4*>(xm + m_lane) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int i = 0; i < VB; ++i) {
-          const int idx = (i * 64 + lane) * 4;  // dword index inside [2][VB][128]
-          pVw[i] = (idx < VB * kD || rem_c > 32) ? *reinterpret_cast<const u32x4*>(xv + v_lane + i * 1024)
-                                                 : u32x4{0u, 0u, 0u, 0u};
-        }
-      }
-      if (keys) {
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          const bool v2 = 16 * ct + n < rem_c;
-#pragma unroll
-          for (int sp = 0; sp < KP; ++sp)
-            pX[ct][sp] = !v2 ? 0u
-                         : (HALF && sp == KB - 1) ? key_half_word(xk + k_lane + 16 * ct * rec + key_off(sp))
-                                                  : key_word(xk + k_lane + 16 * ct * rec + key_off(sp));
-        }
+      for (int i = 0; i < VB; ++i) {
+        const int idx = (i * 64 + lane) * 4;  // dword index inside [2][VB][128]
+        pVw[i] = (idx < VB * kD || rem_c > 32) ? *reinterpret_cast<const u32x4*>(xv + v_lane + i * 1024)
+                                               : u32x4{0u, 0u, 0u, 0u};
       }
     }
   };
-  if (first < t_end) load_chunk(0, true, true);
+  if (first < t_end) {
+    load_rest(first);
+    load_keys(first);
+  }
 
-  int it = 0;
-  for (int64_t c0t = first; c0t < t_end; c0t += kRound, ++it) {
+  for (int64_t c0t = first; c0t < t_end; c0t += kRound) {
     const int rem = (int)(t_end - c0t < 64 ? t_end - c0t : 64);  // valid tokens of this chunk
     // ---- stage this chunk's per-token data and value words in LDS; the
     // value-weight exponent comes from the largest delta (min/max values) or
     // |v| (MSE values) of the chunk, as bits (non-negative: integer order is
     // float order)
-    const uint32_t mb_lane = VMSE ? pMeta[0]
+    const float vnorm = VMSE ? scalar_value(pMeta[0]) : 0.f;  // |v| (MSE values)
+    const uint32_t mb_lane = VMSE ? __float_as_uint(vnorm)
                                   : max(max(pMeta[0] & 0x7fffu, pMeta[1] & 0x7fffu),
                                         max(pMeta[2] & 0x7fffu, pMeta[3] & 0x7fffu));
     // min/max values: the exponent of the value weights is known before the
@@ -582,11 +606,11 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
     __builtin_amdgcn_wave_barrier();
     {
       // per token: u, w and an additive mask (-inf past the end of the chunk)
-      const float u = u_scale * pNrm;
+      const float u = u_scale * scalar_value(pNrm);
       *reinterpret_cast<floatx4*>(s_ng + 4 * lane) =
-          floatx4{u, QJL ? u * kQjlScale * pGam : 0.f, lane < rem ? 0.f : -INFINITY, 0.f};
+          floatx4{u, QJL ? u * kQjlScale * scalar_value(pGam) : 0.f, lane < rem ? 0.f : -INFINITY, 0.f};
       if (VMSE)
-        s_meta[lane * NG] = pMeta[0];
+        s_meta[lane * NG] = __float_as_uint(vnorm);
       else
         *reinterpret_cast<u32x4*>(s_meta + lane * NG + kMetaPad * (lane >> 4)) = pMeta;
 #pragma unroll
@@ -596,7 +620,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
       }
     }
     uint32_t(&X)[4][KP] = pX;  // the key words are reloaded once the scores are done
-    if (c0t + kRound < t_end) load_chunk(it + 1, false, true);
+    if (c0t + kRound < t_end) load_rest(c0t + kRound);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
@@ -624,12 +648,12 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
       }
 #pragma unroll
       for (int pl = 0; pl < PM; ++pl) {
-        const i32x8 Bk = fp4_bits(P[pl]);
+        const i32x8 Bk = fp4_bits(P[pl], k88, k11);
 #pragma unroll
         for (int ht = 0; ht < NHT; ++ht) cm[ht] = mfma_f8f4(qa[ht][pl], Bk, cm[ht], sc_m[ht]);
       }
       if (QJL) {
-        const i32x8 Bk = fp4_bits(X[ct][KP - 1]);
+        const i32x8 Bk = fp4_bits(X[ct][KP - 1], k88, k11);
 #pragma unroll
         for (int ht = 0; ht < NHT; ++ht) cq[ht] = mfma_f8f4(qa[ht][NPL - 1], Bk, cq[ht], sc_s[ht]);
       }
@@ -653,37 +677,50 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
         for (int ct = 0; ct < 4; ++ct) sc[ht][ct] = c0t + 16 * ct + n < lim[ht] ? sc[ht][ct] : -INFINITY;
     }
 
-    if (c0t + kRound < t_end) load_chunk(it + 1, true, false);
+    if (c0t + kRound < t_end) load_keys(c0t + kRound);
 
     // ---- online softmax in log2 units over the 16 lanes of a head (one DPP
-    // row); alpha rescales the running sums.  p goes to LDS for the value MFMA,
+    // row), with the lazily rescaled sums above.  p goes to LDS for the value MFMA,
     // for min/max values as p 2^c with c = ev - 2 min(n/4, 2): token 16ct + n
     // is in slot n/4 of its packed code word, whose bytes carry 4^min(n/4, 2)
     // (4-bit codes: every slot is one whole code per byte, no scale)
     const int c_p = VMSE ? 0 : (VB == 4 ? ev_mm : ev_mm - ((n >> 2) < 2 ? 2 * (n >> 2) : 4));
-    float alpha[NHT];
+    float lsum[NHT];
+    bool far = false;
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
       const float mloc = row_max16(fmaxf(fmaxf(sc[ht][0], sc[ht][1]), fmaxf(sc[ht][2], sc[ht][3])));
       const float m_new = fmaxf(m_run[ht], mloc);
-      alpha[ht] = __builtin_amdgcn_exp2f(m_run[ht] - m_new);
       m_run[ht] = m_new;
+      far |= m_new - m_ref[ht] > kLazyRescale;
       const float m_p = m_new - (float)c_p;
-      float lsum = 0.f;
+      lsum[ht] = 0.f;
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
         const float e = __builtin_amdgcn_exp2f(sc[ht][ct] - m_p);  // 0 for tokens past the end
         s_p[(4 * ht + g) * 64 + 16 * ct + n] = e;
-        lsum += e;
+        lsum[ht] += e;
       }
-      l_part[ht] = fmaf(l_part[ht], alpha[ht], VMSE ? lsum : ldexpf(lsum, -c_p));
+    }
+    if (__builtin_amdgcn_ballot_w64(far)) {  // wave-uniform: a new reference for every lane
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) {
+        const float f = __builtin_amdgcn_exp2f(m_ref[ht] - m_run[ht]);
+        l_part[ht] *= f;
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) acc[ht][nt] *= f;
+        m_ref[ht] = m_run[ht];
+      }
+    }
+    float beta[NHT];  // 2^(m_run - m_ref) of the accumulator rows: head 4ht + g
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      beta[ht] = __builtin_amdgcn_exp2f(m_run[ht] - m_ref[ht]);
+      l_part[ht] = fmaf(VMSE ? lsum[ht] : ldexpf(lsum[ht], -c_p), beta[ht], l_part[ht]);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    float alpha_pv[NHT];
-#pragma unroll
-    for (int ht = 0; ht < NHT; ++ht) alpha_pv[ht] = alpha[ht];  // accumulator rows: head 4ht + g
 
     // ---- values
     if (!VMSE) {
@@ -777,7 +814,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
           const i32x4 C = Cn;
           if (nt + 1 < 8) Cn = mfma_i8(AG[(nt + 1) >> 1], value_operand(nt + 1), i32x4{0, 0, 0, 0});
           const float v = fmaf((float)((C[0] << 8) + C[1]), 65536.f, (float)((C[2] << 8) + C[3]));
-          acc[ht][nt] = fmaf(acc[ht][nt], alpha_pv[ht], fmaf(v, inv_sv, Mpv[nt >> 1]));
+          acc[ht][nt] = fmaf(fmaf(v, inv_sv, Mpv[nt >> 1]), beta[ht], acc[ht][nt]);
         }
       }
     } else {
@@ -856,7 +893,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
         }
 #pragma unroll
         for (int ht = 0; ht < NHT; ++ht)
-          acc[ht][nt] = fmaf(acc[ht][nt], alpha_pv[ht], fmaf(vs[ht], inv_sv, a.val_cst * PNpv[ht]));
+          acc[ht][nt] = fmaf(fmaf(vs[ht], inv_sv, a.val_cst * PNpv[ht]), beta[ht], acc[ht][nt]);
       }
     }
   }
@@ -866,13 +903,14 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
   float lsum[NHT];
 #pragma unroll
   for (int ht = 0; ht < NHT; ++ht) lsum[ht] = row_sum16(l_part[ht]);  // the 16 lanes of head 4ht + g
+  // (the sums are relative to m_ref, which is therefore the partial's max)
   __syncthreads();
   float* mrg = reinterpret_cast<float*>(smem) + wave * kStride;
 #pragma unroll
   for (int ht = 0; ht < NHT; ++ht) {
     if (n == 0) {
       const int hh = 4 * ht + g;
-      mrg[hh * (kD + 2)] = lsum[ht] > 0.f ? m_run[ht] * 0.6931471806f : -INFINITY;
+      mrg[hh * (kD + 2)] = lsum[ht] > 0.f ? m_ref[ht] * 0.6931471806f : -INFINITY;
       mrg[hh * (kD + 2) + 1] = lsum[ht];
     }
 #pragma unroll

@@ -469,13 +469,16 @@ __global__ __launch_bounds__(kEncThreads) void encode_rot_kernel(EncodeArgs a) {
         // then rows g and g^1: row g ends with word g
         const auto sf = __builtin_amdgcn_permlane16_swap(ka, kb, false, false);
         const uint32_t fin = sf[0] | sf[1];
-        uint8_t* recp = a.k_planes + (slot * a.capacity + dpos[ct]) * rec;
+        uint8_t* kslot = a.k_planes + slot * key_slot_tokens(a.capacity) * rec;
         if (valid[ct]) {
           if (HALF && p == MSE_BITS)  // coordinates 32g..32g+15: the low half of the word
-            *reinterpret_cast<uint16_t*>(recp + MSE_BITS * (kD / 8) + 2 * g) = (uint16_t)fin;
+            *reinterpret_cast<uint16_t*>(kslot + key_word_offset(dpos[ct], rec, MSE_BITS * (kD / 8), g, 2)) =
+                (uint16_t)fin;
           else
-            *reinterpret_cast<uint32_t*>(recp + (p < MSE_BITS ? p * (kD / 8) : MSE_BITS * (kD / 8) + (HALF ? kD / 16 : 0)) +
-                                         4 * g) = fin;
+            *reinterpret_cast<uint32_t*>(
+                kslot + key_word_offset(dpos[ct], rec,
+                                        p < MSE_BITS ? p * (kD / 8) : MSE_BITS * (kD / 8) + (HALF ? kD / 16 : 0), g,
+                                        4)) = fin;
         }
       }
     }
@@ -588,28 +591,30 @@ __device__ __forceinline__ void encode_small_body(EncodeArgs a) {
     }
     // plane words by ballot: wave wv holds coordinates 64 wv .. 64 wv + 63,
     // the words 2 wv and 2 wv + 1 of every plane
-    uint8_t* recp = a.k_planes + (slot * a.capacity + dp) * rec;
+    uint8_t* kslot = a.k_planes + slot * key_slot_tokens(a.capacity) * rec;
 #pragma unroll
     for (int p = 0; p < MSE_BITS; ++p) {
       const uint64_t m = __ballot((idx >> p) & 1);
       if (lane == 0) {
-        *reinterpret_cast<uint32_t*>(recp + p * (kD / 8) + 8 * wv) = (uint32_t)m;
-        *reinterpret_cast<uint32_t*>(recp + p * (kD / 8) + 8 * wv + 4) = (uint32_t)(m >> 32);
+        *reinterpret_cast<uint32_t*>(kslot + key_word_offset(dp, rec, p * (kD / 8), 2 * wv, 4)) = (uint32_t)m;
+        *reinterpret_cast<uint32_t*>(kslot + key_word_offset(dp, rec, p * (kD / 8), 2 * wv + 1, 4)) = (uint32_t)(m >> 32);
       }
     }
     if (HALF) {  // the extra bit of the half-bit coordinates: the low 16 bits of each word
       const uint64_t m = __ballot(hi && ((idx >> MSE_BITS) & 1));
       if (lane == 0) {
-        *reinterpret_cast<uint16_t*>(recp + MSE_BITS * (kD / 8) + 4 * wv) = (uint16_t)(m & 0xffffu);
-        *reinterpret_cast<uint16_t*>(recp + MSE_BITS * (kD / 8) + 4 * wv + 2) = (uint16_t)((m >> 32) & 0xffffu);
+        *reinterpret_cast<uint16_t*>(kslot + key_word_offset(dp, rec, MSE_BITS * (kD / 8), 2 * wv, 2)) =
+            (uint16_t)(m & 0xffffu);
+        *reinterpret_cast<uint16_t*>(kslot + key_word_offset(dp, rec, MSE_BITS * (kD / 8), 2 * wv + 1, 2)) =
+            (uint16_t)((m >> 32) & 0xffffu);
       }
     }
     if (QJL) {
       const uint64_t m = __ballot(zbit);
       const int off = MSE_BITS * (kD / 8) + (HALF ? kD / 16 : 0);
       if (lane == 0) {
-        *reinterpret_cast<uint32_t*>(recp + off + 8 * wv) = (uint32_t)m;
-        *reinterpret_cast<uint32_t*>(recp + off + 8 * wv + 4) = (uint32_t)(m >> 32);
+        *reinterpret_cast<uint32_t*>(kslot + key_word_offset(dp, rec, off, 2 * wv, 4)) = (uint32_t)m;
+        *reinterpret_cast<uint32_t*>(kslot + key_word_offset(dp, rec, off, 2 * wv + 1, 4)) = (uint32_t)(m >> 32);
       }
     }
     if (i == 0) {

@@ -35,6 +35,20 @@ inline size_t key_record_bytes(int mse_bits, int qjl, int half) {
   return (size_t)(mse_bits + qjl) * (kD / 8) + (size_t)half * (kD / 16);
 }
 
+// Key planes are stored in blocks of 64 token positions; a slot holds
+// ceil(capacity / 64) blocks.  Inside a block every plane of the record (at
+// byte offset o of the record: full planes of 16 bytes, the half plane of 8)
+// takes 64 times its size from byte 64 o, and word w of token u = 16 c + n
+// (c < 4, n < 16) of the block (coordinates 32 w .. 32 w + 31: 4 bytes, 2 in
+// the half plane) sits at word index 4 (4 n + w) + c of that region.  The
+// decode scan's lane (w, n) then finds the words of its four 16-token column
+// tiles side by side, and a wave reads each plane of a 64-token chunk as one
+// contiguous block.
+__host__ __device__ constexpr int64_t key_slot_tokens(int64_t capacity) { return (capacity + 63) / 64 * 64; }
+__host__ __device__ constexpr size_t key_word_offset(int64_t t, size_t rec, size_t plane_off, int w, int wbytes) {
+  return (size_t)(t >> 6) * 64 * rec + plane_off * 64 + (size_t)((((int)(t & 15) << 2) + w) * 4 + (int)((t >> 4) & 3)) * wbytes;
+}
+
 // Column of S' that the encode kernel's second GEMM meets at contraction index
 // k.  The first GEMM leaves, in lane group g of a 16x16x32 MFMA, the rotated
 // coordinates 16*rt + 4*g + r (row tile rt, accumulator r); the kernel feeds

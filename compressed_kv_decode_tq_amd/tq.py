@@ -316,7 +316,8 @@ class Cache:
         self.layout, self.batch, self.num_kv_heads, self.capacity = layout, batch, num_kv_heads, capacity
         sd = layout.scalar_torch_dtype
         shp = (batch, num_kv_heads, capacity)
-        self.k_planes = torch.zeros(*shp, layout.key_planes * d // 8 + layout.key_half * d // 16,
+        rec = layout.key_planes * d // 8 + layout.key_half * d // 16
+        self.k_planes = torch.zeros(batch, num_kv_heads, (capacity + 63) // 64, 64 * rec,
                                     dtype=torch.uint8, device=device)
         self.k_norm = torch.zeros(shp, dtype=sd, device=device)
         self.k_rnorm = torch.zeros(shp, dtype=sd, device=device) if layout.key_qjl else None

@@ -37,14 +37,20 @@
  *    describes the most recent failure of the calling thread.
  *  - Layout of the compressed cache, per (sequence b, KV head h) slot of
  *    `capacity` token positions (capacity a multiple of 32):
- *      k_planes  uint8 [batch][h_kv][capacity][record], record =
- *                (key_mse_bits + key_qjl)*d/8 + key_half*d/16 bytes: plane
- *                p < key_mse_bits holds bit p of each coordinate's Lloyd-Max
- *                index (coordinate i is bit i%8 of byte i/8); with key_half
- *                a half plane of d/16 bytes follows, bit key_mse_bits of the
- *                index of coordinate i (i mod 32 < 16) at bit position
- *                16*(i/32) + i%32; then the QJL sign bits (1 = non-negative)
- *                in the full-plane order.
+ *      k_planes  uint8 [batch][h_kv][ceil(capacity/64)][64*record]: token
+ *                records of record = (key_mse_bits + key_qjl)*d/8 +
+ *                key_half*d/16 bytes: plane p < key_mse_bits holds bit p of
+ *                each coordinate's Lloyd-Max index (coordinate i is bit i%8
+ *                of byte i/8); with key_half a half plane of d/16 bytes
+ *                follows, bit key_mse_bits of the index of coordinate i
+ *                (i mod 32 < 16) at bit position 16*(i/32) + i%32; then the
+ *                QJL sign bits (1 = non-negative) in the full-plane order.
+ *                The records are stored in blocks of 64 token positions,
+ *                interleaved by words: the plane at byte offset o of the
+ *                record, s bytes long, fills bytes [64*o, 64*(o+s)) of the
+ *                block, and its word w (4 bytes; 2 in the half plane) of the
+ *                token at position 64*j + 16*c + n (c < 4, n < 16) is word
+ *                4*(4*n + w) + c of that range in block j.
  *      k_norm    [batch][h_kv][capacity] scalar_dtype   |k|
  *      k_rnorm   [batch][h_kv][capacity] scalar_dtype   |r| (QJL keys only)
  *      v_planes  uint32 [batch][h_kv][capacity/32][value_bits][d].  Bit

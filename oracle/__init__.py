@@ -41,4 +41,5 @@ from .layout import (  # noqa: F401
     Layout, pack_key_planes, unpack_key_planes, pack_value_planes, unpack_value_planes,
     pack_value_codes, unpack_value_codes, pack_value_words, unpack_value_words, value_words_packed,
     memory_bytes, bytes_per_token_head, half_plane_position,
+    key_record_planes, key_block_positions, key_records_to_blocks, key_blocks_to_records,
 )

@@ -7,7 +7,7 @@ can be compared bit for bit.
 
 Per (sequence, KV head) slot of ``capacity`` tokens:
 
-* key planes   uint8  [capacity][record], record = key_mse_bits full planes
+* key planes   one record per token, record = key_mse_bits full planes
   (d/8 bytes each), then with the half-bit layout one half plane (d/16 bytes),
   then the QJL plane (d/8 bytes) when key_qjl.  Full plane p holds bit p of
   every coordinate's Lloyd-Max index, coordinate i in bit i % 8 of byte
@@ -15,6 +15,11 @@ Per (sequence, KV head) slot of ``capacity`` tokens:
   the half-bit coordinates (i mod 32 < 16), coordinate i at bit position
   h = 16 (i // 32) + i mod 32 (bit h % 8 of byte h // 8).  The QJL plane
   holds the sign bits (1 = non-negative) in the full-plane order.
+  Stored as uint8 [ceil(capacity/64)][64 * record]: blocks of 64 token
+  positions, interleaved by words.  The plane at record byte offset o (s bytes)
+  fills bytes 64 o .. 64 (o + s) - 1 of its block, and its word w (4 bytes, 2
+  in the half plane) of token 64 j + 16 c + n (c < 4, n < 16) is word
+  4 (4 n + w) + c of that range (key_records_to_blocks).
 * key norm, key residual norm   [capacity] fp32 or fp16.
 * value words uint32 [capacity/32][value_bits][d], in one of two forms:
   - bit planes (MSE values, and min/max values of width 1 or 3): word (blk, p,
@@ -114,6 +119,55 @@ def pack_key_planes(idx: np.ndarray, qjl: np.ndarray | None, mse_bits: int, half
         planes.append(np.asarray(qjl, dtype=np.uint8) & 1)
     bits = np.concatenate(planes, axis=1)  # (T, record bits)
     return np.packbits(bits, axis=1, bitorder="little")
+
+
+def key_record_planes(d: int, mse_bits: int, qjl: bool, half: bool = False) -> list[tuple[int, int, int]]:
+    """(byte offset, bytes, word bytes) of every plane of a key record."""
+    planes = [(p * d // 8, d // 8, 4) for p in range(mse_bits)]
+    off = mse_bits * d // 8
+    if half:
+        planes.append((off, d // 16, 2))
+        off += d // 16
+    if qjl:
+        planes.append((off, d // 8, 4))
+    return planes
+
+
+def key_block_positions(d: int, mse_bits: int, qjl: bool, half: bool = False) -> np.ndarray:
+    """(64, record) array: the byte of a 64-token storage block that holds
+    byte j of the record of token u (u < 64) of the block."""
+    planes = key_record_planes(d, mse_bits, qjl, half)
+    rec = sum(size for _, size, _ in planes)
+    pos = np.zeros((64, rec), dtype=np.int64)
+    for u in range(64):
+        c, n = u // 16, u % 16
+        for off, size, wb in planes:
+            for w in range(size // wb):
+                for byte in range(wb):
+                    pos[u, off + w * wb + byte] = 64 * off + (4 * (4 * n + w) + c) * wb + byte
+    return pos
+
+
+def key_records_to_blocks(records: np.ndarray, d: int, mse_bits: int, qjl: bool, half: bool = False) -> np.ndarray:
+    """(..., T, record) token records, T a multiple of 64 -> (..., T/64, 64 record) storage blocks."""
+    records = np.asarray(records, dtype=np.uint8)
+    *lead, t, rec = records.shape
+    assert t % 64 == 0
+    pos = key_block_positions(d, mse_bits, qjl, half)
+    blocks = np.zeros((*lead, t // 64, 64 * rec), dtype=np.uint8)
+    src = records.reshape(*lead, t // 64, 64, rec)
+    blocks[..., pos] = src  # pos is (64, rec): scatter every token byte of every block
+    return blocks
+
+
+def key_blocks_to_records(blocks: np.ndarray, d: int, mse_bits: int, qjl: bool, half: bool = False) -> np.ndarray:
+    """Inverse of key_records_to_blocks: (..., B, 64 record) -> (..., 64 B, record)."""
+    blocks = np.asarray(blocks, dtype=np.uint8)
+    *lead, nb, width = blocks.shape
+    pos = key_block_positions(d, mse_bits, qjl, half)
+    rec = pos.shape[1]
+    assert width == 64 * rec
+    return blocks[..., pos].reshape(*lead, nb * 64, rec)
 
 
 def unpack_key_planes(packed: np.ndarray, d: int, mse_bits: int, qjl: bool, half: bool = False):

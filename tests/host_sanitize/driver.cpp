@@ -61,7 +61,7 @@ struct HostCache {
   tq_cache c;
   HostCache(const tq_layout& l, int batch, int h_kv, int64_t cap) {
     const size_t slots = (size_t)batch * h_kv * cap;
-    kp = Buf(slots * key_rec(l));
+    kp = Buf((size_t)batch * h_kv * ((cap + 63) / 64 * 64) * key_rec(l));  // whole 64-token blocks
     kn = Buf(slots * ssz(l));
     if (l.key_qjl) kr = Buf(slots * ssz(l));
     vp = Buf(slots * (size_t)l.value_bits * 16);

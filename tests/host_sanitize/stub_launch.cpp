@@ -41,7 +41,7 @@ size_t key_rec(int mse_bits, int qjl, int half) { return tq::key_record_bytes(ms
 // Cache extents of `slots` (sequence, head) slots of `cap` tokens.
 void touch_cache_keys(const uint8_t* planes, const void* norm, const void* rnorm, size_t slots, int64_t cap,
                       size_t kpb, int qjl, size_t ssz) {
-  touch(planes, slots * cap * kpb);
+  touch(planes, slots * (size_t)tq::key_slot_tokens(cap) * kpb);  // whole 64-token key blocks
   touch(norm, slots * cap * ssz);
   if (qjl) touch(rnorm, slots * cap * ssz);
 }

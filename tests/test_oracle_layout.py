@@ -32,6 +32,38 @@ def test_key_planes_round_trip_and_bit_positions():
     assert np.array_equal(p, expect)
 
 
+def test_key_block_storage_positions():
+    """Records in 64-token blocks, interleaved by words: the plane at record
+    offset o fills block bytes 64 o .. 64 (o + size) - 1, and word w of token
+    16 c + n of the block is word 4 (4 n + w) + c there (include/tq.h)."""
+    for mse_bits, qjl, half in ((2, True, False), (1, True, True), (2, True, True), (3, False, False)):
+        pos = oracle.key_block_positions(128, mse_bits, qjl, half)
+        rec = pos.shape[1]
+        assert rec == (mse_bits + qjl) * 16 + half * 8
+        assert sorted(pos.ravel().tolist()) == list(range(64 * rec))  # a permutation of the block
+        rng = np.random.default_rng(mse_bits + 10 * half)
+        recs = rng.integers(0, 256, size=(3, 128, rec), dtype=np.uint8)
+        blocks = oracle.key_records_to_blocks(recs, 128, mse_bits, qjl, half)
+        assert blocks.shape == (3, 2, 64 * rec)
+        assert np.array_equal(oracle.key_blocks_to_records(blocks, 128, mse_bits, qjl, half), recs)
+    # worked examples, 2-bit index + QJL (record 48 bytes: planes at 0, 16, 32)
+    pos = oracle.key_block_positions(128, 2, True)
+    # token 37 = 16*2 + 5 (c = 2, n = 5), plane 1 (offset 16), record byte 16 + 9:
+    # word w = 9 // 4 = 2, byte 1 of it -> 64*16 + (4*(4*5 + 2) + 2)*4 + 1
+    assert pos[37, 25] == 1024 + (4 * 22 + 2) * 4 + 1
+    # token 0, QJL plane byte 0 -> 64*32
+    assert pos[0, 32] == 2048
+    # token 63 = 16*3 + 15, plane 0, last byte (word 3, byte 3): 0 + (4*63 + 3)*4 + 3 = 1023
+    assert pos[63, 15] == 1023
+    # half-bit layout, 2 + 1/2 index bits + QJL (record 16+16+8+16 = 56): the
+    # half plane at offset 32 has 2-byte words; token 17 = 16 + 1 (c = 1, n = 1),
+    # half-plane record byte 32 + 5 (word 2, byte 1) -> 64*32 + (4*(4 + 2) + 1)*2 + 1;
+    # the QJL plane at offset 40
+    pos = oracle.key_block_positions(128, 2, True, True)
+    assert pos[17, 37] == 2048 + (4 * 6 + 1) * 2 + 1
+    assert pos[0, 40] == 64 * 40
+
+
 def test_value_planes_round_trip_and_bit_positions():
     rng = np.random.default_rng(1)
     for bits in (1, 2, 3, 4):

@@ -108,6 +108,22 @@ def _f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().double().numpy()
 
 
+def key_records(w: wl.Workload, blocks: torch.Tensor | np.ndarray) -> np.ndarray:
+    """The token records ([..., 64 B, record]) of key-plane storage blocks
+    ([..., B, 64 record], e.g. cache.k_planes[b, h])."""
+    if isinstance(blocks, torch.Tensor):
+        blocks = blocks.cpu().numpy()
+    return oracle.key_blocks_to_records(blocks, w.d, w.key_mse_bits, bool(w.key_qjl), bool(w.key_half))
+
+
+def put_key_records(cache: tq.Cache, w: wl.Workload, b: int, h: int, start: int, records: np.ndarray):
+    """Write token records at positions start .. start + T - 1 of slot (b, h)."""
+    allrec = key_records(w, cache.k_planes[b, h])
+    allrec[start:start + records.shape[0]] = records
+    blocks = oracle.key_records_to_blocks(allrec, w.d, w.key_mse_bits, bool(w.key_qjl), bool(w.key_half))
+    cache.k_planes[b, h] = torch.from_numpy(blocks).to(cache.k_planes.device)
+
+
 def upload_slot(cache: tq.Cache, w: wl.Workload, b: int, h: int, sc: SlotCode, start: int = 0):
     """Write the oracle-packed codes of one slot into the device cache at
     positions start .. start + T - 1 (start a multiple of 32)."""
@@ -115,7 +131,7 @@ def upload_slot(cache: tq.Cache, w: wl.Workload, b: int, h: int, sc: SlotCode, s
     t = sc.key.idx.shape[0]
     dev = cache.k_planes.device
     kp = oracle.pack_key_planes(sc.key.idx, sc.key.qjl if w.key_qjl else None, w.key_mse_bits, half=bool(w.key_half))
-    cache.k_planes[b, h, start:start + t] = torch.from_numpy(kp).to(dev)
+    put_key_records(cache, w, b, h, start, kp)
     sd = np.float32 if w.scalar_dtype == "f32" else np.float16
     cache.k_norm[b, h, start:start + t] = torch.from_numpy(sc.key.norm.astype(sd)).to(dev)
     if w.key_qjl:
@@ -206,7 +222,7 @@ def check_encode_slot(w, bk, cache, b, h, ref, start, n, tag):
     """Compare the device cache slot (b, h) positions start..start+n-1 with the
     oracle code `ref`; returns the excused counts (key MSE bits, key QJL bits,
     value codes: MSE or min/max)."""
-    kp = cache.k_planes[b, h, start:start + n].cpu().numpy()
+    kp = key_records(w, cache.k_planes[b, h])[start:start + n]
     bad, ex_m, ex_q = key_plane_mismatches(w, bk, kp, ref.key)
     assert bad == 0, f"{tag}: {bad} key bits differ outside the {WINDOW} window"
     flip = np.any(_flip_mask(w, bk, kp, ref), axis=1)
@@ -278,7 +294,7 @@ def slot_from_cache(w: wl.Workload, cache: tq.Cache, b: int, h: int, n: int, sta
     back into the oracle's code records (so the oracle can decode a
     GPU-encoded cache)."""
     end = start + n
-    kp = cache.k_planes[b, h, start:end].cpu().numpy()
+    kp = key_records(w, cache.k_planes[b, h])[start:end]
     idx, qjl = read_key_planes(kp, w.d, w.key_mse_bits, bool(w.key_qjl), bool(w.key_half))
     norm = cache.k_norm[b, h, start:end].float().cpu().double().numpy()
     rnorm = cache.k_rnorm[b, h, start:end].float().cpu().double().numpy() if w.key_qjl else None
