@@ -489,10 +489,15 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
   // so a chunk normally adds to the sums with one fused multiply-add each.
   constexpr float kLazyRescale = 32.f;
   float m_run[NHT], m_ref[NHT], l_part[NHT], acc[NHT][8];
+  // min/max values: sum_t p_t min_t against m_ref, kept in the weight layout
+  // (lane (g, n): head 4ht + n/4, group n%4, the lane's quarter of the
+  // tokens) and added to the channel sums once, after the last chunk
+  float macc[NHT];
 #pragma unroll
   for (int ht = 0; ht < NHT; ++ht) {
     m_run[ht] = m_ref[ht] = -1e30f;
     l_part[ht] = 0.f;
+    macc[ht] = 0.f;
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) acc[ht][nt] = 0.f;
   }
@@ -602,7 +607,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
     // min/max values: the exponent of the value weights is known before the
     // softmax, so p is produced already scaled (see the value section)
     const int ev_mm = VMSE ? 0 : 44 - (int)(wave_max_u32_uniform(mb_lane) >> 10);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     {
       // per token: u, w and an additive mask (-inf past the end of the chunk)
@@ -621,9 +626,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
     }
     uint32_t(&X)[4][KP] = pX;  // the key words are reloaded once the scores are done
     if (c0t + kRound < t_end) load_rest(c0t + kRound);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     // ---- scores (log2 units).  The query digits are the A operand and the
     // key bits the B operand (fp4, one MFMA per plane covers all 128
@@ -702,13 +707,21 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
         lsum[ht] += e;
       }
     }
-    if (__builtin_amdgcn_ballot_w64(far)) {  // wave-uniform: a new reference for every lane
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(far) != 0, 0)) {  // wave-uniform: a new reference for every lane
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) {
         const float f = __builtin_amdgcn_exp2f(m_ref[ht] - m_run[ht]);
         l_part[ht] *= f;
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) acc[ht][nt] *= f;
+        if (!VMSE) {  // the factor of head 4ht + n/4 (DPP row n/4), through scalar registers
+          const float f0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), 0));
+          const float f1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), 16));
+          const float f2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), 32));
+          const float f3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), 48));
+          const int q = n >> 2;
+          macc[ht] *= q == 0 ? f0 : (q == 1 ? f1 : (q == 2 ? f2 : f3));
+        }
         m_ref[ht] = m_run[ht];
       }
     }
@@ -718,9 +731,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
       beta[ht] = __builtin_amdgcn_exp2f(m_run[ht] - m_ref[ht]);
       l_part[ht] = fmaf(VMSE ? lsum[ht] : ldexpf(lsum[ht], -c_p), beta[ht], l_part[ht]);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     // ---- values
     if (!VMSE) {
@@ -756,7 +769,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
             const float mn = __half2float(__ushort_as_half((unsigned short)(mm >> 16)));
             const float pe = pv[k][r];
             const int W = (int)fmaf(pe, dl, 0.5f);  // non-negative: rounds to nearest
-            V[r] = ((uint32_t)W + 0x00808080u) ^ 0x00808080u;  // bytes = signed base-256 digits
+            // signed base-256 digits are the bytes of (W + 0x808080) ^ 0x808080;
+            // the XOR of the three low bytes is applied after the transpose
+            V[r] = (uint32_t)W + 0x00808080u;
             Mk[k] = fmaf(pe, mn, Mk[k]);
           }
           // 4x4 byte transpose: digit plane d holds byte d of the four tokens
@@ -764,32 +779,30 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
           const uint32_t t01hi = __builtin_amdgcn_perm(V[1], V[0], 0x07030602u);
           const uint32_t t23lo = __builtin_amdgcn_perm(V[3], V[2], 0x05010400u);
           const uint32_t t23hi = __builtin_amdgcn_perm(V[3], V[2], 0x07030602u);
-          A[3][k] = __builtin_amdgcn_perm(t23lo, t01lo, 0x05040100u);  // least significant digit
-          A[2][k] = __builtin_amdgcn_perm(t23lo, t01lo, 0x07060302u);
-          A[1][k] = __builtin_amdgcn_perm(t23hi, t01hi, 0x05040100u);
+          A[3][k] = __builtin_amdgcn_perm(t23lo, t01lo, 0x05040100u) ^ 0x80808080u;  // least significant digit
+          A[2][k] = __builtin_amdgcn_perm(t23lo, t01lo, 0x07060302u) ^ 0x80808080u;
+          A[1][k] = __builtin_amdgcn_perm(t23hi, t01hi, 0x05040100u) ^ 0x80808080u;
           A[0][k] = __builtin_amdgcn_perm(t23hi, t01hi, 0x07060302u);  // most significant digit
         }
-        // sum_t p_t min_t per (head, group), the slot scales 2^(ev - 2 min(k, 2))
-        // undone: reduce over the four token quarters, then fetch (head g,
-        // group gi) for the value layout
-        const float x = VB == 4 ? col_sum4(ldexpf((Mk[0] + Mk[1]) + (Mk[2] + Mk[3]), -ev_mm))
-                                : col_sum4(ldexpf(fmaf(Mk[0], 1.f, fmaf(Mk[1], 4.f, 16.f * (Mk[2] + Mk[3]))), -ev_mm));
-        float Mpv[NG];
-#pragma unroll
-        for (int gi = 0; gi < NG; ++gi) Mpv[gi] = __shfl(x, 4 * g + gi);
+        // this lane's part of sum_t p_t min_t for (head 4ht + n/4, group n%4),
+        // the slot scales 2^(ev - 2 min(k, 2)) undone, added against m_ref with
+        // that head's factor 2^(m_run - m_ref) (held by DPP row n/4)
+        const float mk = VB == 4 ? (Mk[0] + Mk[1]) + (Mk[2] + Mk[3])
+                                 : fmaf(Mk[0], 1.f, fmaf(Mk[1], 4.f, 16.f * (Mk[2] + Mk[3])));
+        macc[ht] = fmaf(mk, inv_sv * __shfl(beta[ht], 16 * (n >> 2) + n), macc[ht]);
         // Exchange the digit blocks inside each quad of lanes: lane (g, 4h + G)
         // holds digit d of row (head h, group G) in A[d]; the value MFMA of
         // group G takes rows (head h, digit d) from lane (g, 4h + d), so one
         // MFMA per channel tile yields all four digits of its own group.  Block
         // d of lane L sits at slot d * 64 + (L ^ d): writes and reads both
         // cover all banks once per 16 lanes.
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int d = 0; d < 4; ++d) *reinterpret_cast<u32x4*>(s_tr + 4 * (d * 64 + (lane ^ d))) = A[d];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         u32x4 AG[NG];
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi)
@@ -808,13 +821,14 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
         // rows (head g, digit r) of group nt/2 (channels 16nt..16nt+15):
         // element r is digit r's product.  The MFMA of tile nt + 1 is issued
         // before the result of tile nt is read, so its latency overlaps.
+        const float s_acc = inv_sv * beta[ht];  // weight scale and reference factor of head 4ht + g
         i32x4 Cn = mfma_i8(AG[0], value_operand(0), i32x4{0, 0, 0, 0});
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) {
           const i32x4 C = Cn;
           if (nt + 1 < 8) Cn = mfma_i8(AG[(nt + 1) >> 1], value_operand(nt + 1), i32x4{0, 0, 0, 0});
           const float v = fmaf((float)((C[0] << 8) + C[1]), 65536.f, (float)((C[2] << 8) + C[3]));
-          acc[ht][nt] = fmaf(fmaf(v, inv_sv, Mpv[nt >> 1]), beta[ht], acc[ht][nt]);
+          acc[ht][nt] = fmaf(v, s_acc, acc[ht][nt]);
         }
       }
     } else {
@@ -895,6 +909,17 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
         for (int ht = 0; ht < NHT; ++ht)
           acc[ht][nt] = fmaf(fmaf(vs[ht], inv_sv, a.val_cst * PNpv[ht]), beta[ht], acc[ht][nt]);
       }
+    }
+  }
+
+  if (!VMSE) {
+    // the min terms: reduce over the four token quarters, then fetch (head g,
+    // group gi) into the channel layout
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      const float x = col_sum4(macc[ht]);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) acc[ht][nt] += __shfl(x, 4 * g + (nt >> 1));
     }
   }
 
