@@ -279,32 +279,32 @@ __device__ __forceinline__ void stage_queries(const DecodeArgs& a, int b, int h,
   }
 }
 
-// Row i of the product's matrix (Pi for part 0, S for part 1, row-major),
-// columns [j0, j0 + NJ), in 16-byte words: one batch of loads.
+// Row i of the product's matrix (Pi for part 0, S for part 1), columns
+// [j0, j0 + NJ), read from the transposed copies (Pi^T, S^T) so that the
+// threads of a wave, which take consecutive rows, read consecutive words: one
+// batch of coalesced loads.
 template <int NJ>
-__device__ __forceinline__ void load_row(const DecodeArgs& a, int part, int i, int j0, floatx4 (&m)[NJ / 4]) {
-  const floatx4* row = reinterpret_cast<const floatx4*>((part == 0 ? a.pi : a.s) + (size_t)i * kD + j0);
+__device__ __forceinline__ void load_row(const DecodeArgs& a, int part, int i, int j0, float (&m)[NJ]) {
+  const float* col = a.mat_t + ((size_t)part * kD + j0) * kD + i;  // M^T[j][i] = M[i][j]
 #pragma unroll
-  for (int u = 0; u < NJ / 4; ++u) m[u] = row[u];
+  for (int u = 0; u < NJ; ++u) m[u] = col[(size_t)u * kD];
 }
 
 // Coordinate i of the product for the MAXG heads from that row and the staged
 // queries.
 template <int MAXG, int NJ>
-__device__ __forceinline__ void row_times_queries(const floatx4 (&m)[NJ / 4], int j0, const floatx4 (*qt)[MAXG / 4],
+__device__ __forceinline__ void row_times_queries(const float (&m)[NJ], int j0, const floatx4 (*qt)[MAXG / 4],
                                                   float (&acc)[MAXG]) {
 #pragma unroll
   for (int gq = 0; gq < MAXG; ++gq) acc[gq] = 0.f;
 #pragma unroll
-  for (int u = 0; u < NJ / 4; ++u)
+  for (int u = 0; u < NJ; ++u)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+    for (int v = 0; v < MAXG / 4; ++v) {
+      const floatx4 qj = qt[j0 + u][v];
 #pragma unroll
-      for (int v = 0; v < MAXG / 4; ++v) {
-        const floatx4 qj = qt[j0 + 4 * u + e][v];
-#pragma unroll
-        for (int f = 0; f < 4; ++f) acc[4 * v + f] = fmaf(m[u][e], qj[f], acc[4 * v + f]);
-      }
+      for (int f = 0; f < 4; ++f) acc[4 * v + f] = fmaf(m[u], qj[f], acc[4 * v + f]);
+    }
 }
 
 // LDS of one q-prep part (256 threads).
@@ -327,7 +327,7 @@ __device__ __forceinline__ void qprep_part(const DecodeArgs& a, int b, int h, in
   const int G = a.group;
   if (part == 0 && a.app_k && a.vbase == 0) append_ring_token(a, b, h, tid);
   const int i = tid & (kD - 1), hj = tid >> 7;
-  floatx4 m[kD / 8];
+  float m[kD / 2];
   load_row<kD / 2>(a, part, i, hj * (kD / 2), m);  // in flight while the queries are staged
   stage_queries<MAXG>(a, b, h, tid, 256, L.qt);
   __syncthreads();
