@@ -4,9 +4,12 @@
 // audit_claims.py", AUDIT 1: the recent tokens kept uncompressed in a bf16
 // ring, attended exactly).
 //
-// A combine unit is 128 threads, thread c owning output channel c.  Every
-// barrier below is a whole-work-group barrier executed unconditionally (a unit
-// with no head to combine still takes part in the barriers).
+// A combine unit is one work-group of 512 threads.  Thread (qq, c) = (tid / 128,
+// tid % 128) owns output channel c for quarter qq of the splits, of the ring
+// tokens and (MSE values) of the rows of Pi; the four quarters meet in LDS.
+// Ring token j is scored by the four threads 4j .. 4j + 3 (32 channels each,
+// one DPP quad sum), so its key row is read as one contiguous 256-byte block.
+// Every barrier below is a whole-work-group barrier executed unconditionally.
 #pragma once
 
 #include "tq_common.h"
@@ -14,6 +17,8 @@
 
 namespace tq {
 
+constexpr int kCombineThreads = 512;
+constexpr int kCombineQuarters = kCombineThreads / kD;
 
 // LDS of one combine unit for at most MAXS splits.
 template <int MAXS>
@@ -21,104 +26,105 @@ struct CombineLds {
   float qv[kD];
   float s_f[MAXS];  // per split: m, then its merge factor
   float s_l[MAXS];
-  float pr[kD];     // ring probabilities (ring_cap <= 128 per pass)
+  float pr[kMaxRing];                // ring probabilities
+  float part[kCombineQuarters][kD];  // per-quarter channel sums
   float arot[kD];
-  float red[2];
+  float red[kCombineThreads / 64];
 };
 
-// Max / sum over the two waves of a unit, result in every thread of the unit.
+// Sum over the 4 lanes of a quad (xor 1, then xor 2) with DPP.
+__device__ __forceinline__ float combine_quad_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, true));
+  return x;
+}
+
+// Max / sum over the work-group's waves, result in every thread.
 __device__ __forceinline__ float unit_max(float x, float* red) {
   x = wave_max(x);
+  __syncthreads();  // red is free again
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[(threadIdx.x >> 6) & 1] = x;
-  __syncthreads();
-  return fmaxf(red[0], red[1]);
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kCombineThreads / 64; ++w) r = fmaxf(r, red[w]);
+  return r;
 }
 __device__ __forceinline__ float unit_sum(float x, float* red) {
   x = wave_sum(x);
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[(threadIdx.x >> 6) & 1] = x;
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
   __syncthreads();
-  return red[0] + red[1];
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kCombineThreads / 64; ++w) r += red[w];
+  return r;
 }
 
 // Merge of the split partials (m, l, acc) of virtual head gq of slot (b, h),
-// split s at part0 + s * sstride (global memory, or LDS for one split), with
-// the exact ring tokens; MSE values (VMSE) are rotated back with Pi^T
-// once.  Writes out[.][c].  Every load that needs no earlier result (split
-// headers, the first kCombinePre splits' acc words, the ring key row, the
-// first kRingPre ring values) is issued before its first use, so the merge
-// costs about one memory round trip.  `active` false: no head for this unit,
-// barriers only.  a.splits <= MAXS.
+// split s at part0 + s * sstride, with the exact ring tokens; MSE values (VMSE)
+// are rotated back with Pi^T once.  Writes out[.][c].  The loads that need no
+// earlier result (split headers, each quarter's first kPre split words, the
+// ring key rows, each quarter's first kRingPre ring values) are issued before
+// their first use.  a.splits <= MAXS; at most kMaxRing ring tokens.
 template <bool VMSE, int MAXS>
-__device__ __forceinline__ void combine_unit(const DecodeArgs& a, int b, int h, int gq, bool active,
-                                             CombineLds<MAXS>& L, const float* part0, size_t sstride) {
-  constexpr int kCombinePre = 16;  // splits whose accumulator word is loaded up front
-  constexpr int kRingPre = 32;     // ring values loaded up front
-  const int c = threadIdx.x & (kD - 1);
-  int t = 0, hq = 0, nr = 0, S = 0;
-  if (active) {
-    int hide_c, hide_r;
-    virtual_head(a, h, gq, t, hq);
-    hidden_keys(a, t, (int)a.n_ring.v[b], hide_c, hide_r);
-    nr = (int)a.n_ring.v[b] - hide_r;  // ring tokens this query sees
-    S = a.splits;
-  }
+__device__ __forceinline__ void combine_unit(const DecodeArgs& a, int b, int h, int gq, CombineLds<MAXS>& L,
+                                             const float* part0, size_t sstride) {
+  constexpr int Q = kCombineQuarters;
+  constexpr int kPre = 8;      // split accumulator words per thread loaded up front
+  constexpr int kRingPre = 8;  // ring values per thread loaded up front
+  constexpr int kBatch = 8;    // loads per later round
+  const int tid = threadIdx.x, c = tid & (kD - 1), qq = tid / kD;
+  int t, hq, hide_c, hide_r;
+  virtual_head(a, h, gq, t, hq);
+  hidden_keys(a, t, (int)a.n_ring.v[b], hide_c, hide_r);
+  const int nr = (int)a.n_ring.v[b] - hide_r;  // ring tokens this query sees
+  const int S = a.splits;
   const size_t ring_row = (size_t)b * a.ring_cap * a.h_kv + h;  // ring token j: (ring_row + j h_kv) kD
 
   // ---- loads
-  float qc = 0.f;
-  if (active) {
+  if (tid < kD) {
     const size_t qoff = q_row(a, b, t, hq) * kD + c;
-    qc = a.q_bf16 ? bf2f(reinterpret_cast<const uint16_t*>(a.q)[qoff]) : reinterpret_cast<const float*>(a.q)[qoff];
+    L.qv[c] = a.q_bf16 ? bf2f(reinterpret_cast<const uint16_t*>(a.q)[qoff]) : reinterpret_cast<const float*>(a.q)[qoff];
   }
-  float hm = -INFINITY, hl = 0.f;  // header of split c (thread c < S)
-  if (c < S) {
-    hm = part0[(size_t)c * sstride];
-    hl = part0[(size_t)c * sstride + 1];
-  }
-  float pa[kCombinePre];
-#pragma unroll
-  for (int u = 0; u < kCombinePre; ++u) pa[u] = u < S ? part0[(size_t)u * sstride + 2 + c] : 0.f;
-  u32x4 kw[kD / 8];  // thread j's ring token key row (256 bytes)
-  if (c < nr) {
-    const u32x4* kr = reinterpret_cast<const u32x4*>(a.ring_k + (ring_row + (size_t)c * a.h_kv) * kD);
-#pragma unroll
-    for (int i = 0; i < kD / 8; ++i) kw[i] = kr[i];
-  }
-  float rv[kRingPre];
-#pragma unroll
-  for (int u = 0; u < kRingPre; ++u)
-    rv[u] = u < nr ? bf2f(a.ring_v[(ring_row + (size_t)u * a.h_kv) * kD + c]) : 0.f;
-
-  // ---- split headers (m, l): thread c takes splits c, c + 128, ...
-  L.qv[c] = qc;
-  float M = hm;
-  if (c < S) {
-    L.s_f[c] = hm;
-    L.s_l[c] = hl;
-  }
-  for (int sp = c + kD; sp < S; sp += kD) {
-    const float* ph = part0 + (size_t)sp * sstride;
-    const float m = ph[0], l = ph[1];
+  float M = -INFINITY;  // split headers: thread tid takes splits tid, tid + 512, ...
+  for (int sp = tid; sp < S; sp += kCombineThreads) {
+    const float m = part0[(size_t)sp * sstride], l = part0[(size_t)sp * sstride + 1];
     L.s_f[sp] = m;
     L.s_l[sp] = l;
     M = fmaxf(M, m);
   }
-  __syncthreads();  // qv
+  float pa[kPre];  // quarter qq: splits qq, qq + 4, ...
+#pragma unroll
+  for (int u = 0; u < kPre; ++u) pa[u] = qq + Q * u < S ? part0[(size_t)(qq + Q * u) * sstride + 2 + c] : 0.f;
+  const int rj = tid >> 2, rq = tid & 3;  // ring token scored, and its channel quarter
+  u32x4 kw[4];
+  if (rj < nr) {
+    const u32x4* kr = reinterpret_cast<const u32x4*>(a.ring_k + (ring_row + (size_t)rj * a.h_kv) * kD + 32 * rq);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kw[i] = kr[i];
+  }
+  float rv[kRingPre];  // quarter qq: ring tokens qq, qq + 4, ...
+#pragma unroll
+  for (int u = 0; u < kRingPre; ++u)
+    rv[u] = qq + Q * u < nr ? bf2f(a.ring_v[(ring_row + (size_t)(qq + Q * u) * a.h_kv) * kD + c]) : 0.f;
+  __syncthreads();  // qv, split headers
 
-  // ring scores: thread j scores ring token j
+  // ---- ring scores
   float sj = -INFINITY;
-  if (c < nr) {
+  {
     float acc = 0.f;
+    if (rj < nr) {
 #pragma unroll
-    for (int i = 0; i < kD / 8; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc = fmaf(L.qv[8 * i + 2 * e], bf2f(kw[i][e] & 0xffffu), acc);
-        acc = fmaf(L.qv[8 * i + 2 * e + 1], bf2f(kw[i][e] >> 16), acc);
-      }
-    sj = a.scale * acc;
+        for (int e = 0; e < 4; ++e) {
+          acc = fmaf(L.qv[32 * rq + 8 * i + 2 * e], bf2f(kw[i][e] & 0xffffu), acc);
+          acc = fmaf(L.qv[32 * rq + 8 * i + 2 * e + 1], bf2f(kw[i][e] >> 16), acc);
+        }
+    }
+    acc = combine_quad_sum(acc);  // the token's four threads are one quad of a wave
+    if (rj < nr) sj = a.scale * acc;
   }
   M = unit_max(fmaxf(M, sj), L.red);
   const bool any = M != -INFINITY;  // uniform over the unit; false: no token at all
@@ -126,69 +132,79 @@ __device__ __forceinline__ void combine_unit(const DecodeArgs& a, int b, int h, 
   // merge factors of the splits and of the ring tokens; L in one unit sum
   float Lp = 0.f;
   if (any) {
-    for (int sp = c; sp < S; sp += kD) {
+    for (int sp = tid; sp < S; sp += kCombineThreads) {
       const float m = L.s_f[sp];
       const float f = m == -INFINITY ? 0.f : __expf(m - M);
       L.s_f[sp] = f;
       Lp = fmaf(f, L.s_l[sp], Lp);
     }
   }
-  const float pj = (any && c < nr) ? __expf(sj - M) : 0.f;
-  L.pr[c] = pj;
-  const float Lsum = unit_sum(Lp + pj, L.red);  // its barriers also publish s_f and pr
+  const float pj = (any && rj < nr) ? __expf(sj - M) : 0.f;
+  if (rq == 0) L.pr[rj] = pj;  // rj < 128 = kMaxRing
+  const float Lsum = unit_sum(Lp + (rq == 0 ? pj : 0.f), L.red);  // its barriers also publish s_f and pr
 
-  // channel c: sum over splits of f_s acc_s[c]; splits past the first
-  // kCombinePre are loaded sixteen at a time
+  // ---- channel c, quarter qq of the splits
   float A = 0.f;
   if (any) {
 #pragma unroll
-    for (int u = 0; u < kCombinePre; ++u)
-      if (u < S) A = fmaf(L.s_f[u], pa[u], A);
-    constexpr int kBatch = 16;  // split accumulator words per round of loads
-    int sp = kCombinePre;
+    for (int u = 0; u < kPre; ++u)
+      if (qq + Q * u < S) A = fmaf(L.s_f[qq + Q * u], pa[u], A);
+    int u0 = kPre;
 #pragma unroll 1
-    for (; sp + kBatch <= S; sp += kBatch) {
+    for (; qq + Q * (u0 + kBatch - 1) < S; u0 += kBatch) {
       float v[kBatch];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) v[u] = part0[(size_t)(sp + u) * sstride + 2 + c];
+      for (int u = 0; u < kBatch; ++u) v[u] = part0[(size_t)(qq + Q * (u0 + u)) * sstride + 2 + c];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) A = fmaf(L.s_f[sp + u], v[u], A);
+      for (int u = 0; u < kBatch; ++u) A = fmaf(L.s_f[qq + Q * (u0 + u)], v[u], A);
     }
-    for (; sp < S; ++sp) A = fmaf(L.s_f[sp], part0[(size_t)sp * sstride + 2 + c], A);
+    for (int sp = qq + Q * u0; sp < S; sp += Q) A = fmaf(L.s_f[sp], part0[(size_t)sp * sstride + 2 + c], A);
   }
-  if (VMSE) {  // accumulated in rotated space: apply Pi^T once (column c of Pi)
-    L.arot[c] = A;
+  if (VMSE) {  // accumulated in rotated space: apply Pi^T once (column c of Pi, rows of quarter qq)
+    L.part[qq][c] = A;
     __syncthreads();
+    if (tid < kD) L.arot[c] = (L.part[0][c] + L.part[1][c]) + (L.part[2][c] + L.part[3][c]);
+    __syncthreads();  // arot written, part read: part is free again
+    float o = 0.f;
     if (any) {
-      float o = 0.f;
-#pragma unroll 1
-      for (int i0 = 0; i0 < kD; i0 += 16) {
+#pragma unroll
+      for (int i0 = 0; i0 < kD / Q; i0 += 16) {
         float w[16];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) w[u] = a.pi[(size_t)(i0 + u) * kD + c];
+        for (int u = 0; u < 16; ++u) w[u] = a.pi[(size_t)((kD / Q) * qq + i0 + u) * kD + c];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) o = fmaf(w[u], L.arot[i0 + u], o);
+        for (int u = 0; u < 16; ++u) o = fmaf(w[u], L.arot[(kD / Q) * qq + i0 + u], o);
       }
-      A = o;
     }
+    A = o;
   }
   if (any) {
-    // ring values (original space): the first kRingPre are in registers, the
-    // rest come 32 loads at a time
+    // ring values (original space), quarter qq of the ring tokens: the first
+    // kRingPre are in registers, the rest come kBatch loads at a time
 #pragma unroll
-    for (int u = 0; u < kRingPre; ++u) A = fmaf(u < nr ? L.pr[u] : 0.f, rv[u], A);
-    constexpr int kRingBatch = 32;  // ring values per round of loads
+    for (int u = 0; u < kRingPre; ++u)
+      if (qq + Q * u < nr) A = fmaf(L.pr[qq + Q * u], rv[u], A);
 #pragma unroll 1
-    for (int j0 = kRingPre; j0 < nr; j0 += kRingBatch) {
-      float v[kRingBatch];
+    for (int u0 = kRingPre; qq + Q * u0 < nr; u0 += kBatch) {
+      float v[kBatch];
 #pragma unroll
-      for (int u = 0; u < kRingBatch; ++u)
-        v[u] = j0 + u < nr ? bf2f(a.ring_v[(ring_row + (size_t)(j0 + u) * a.h_kv) * kD + c]) : 0.f;
+      for (int u = 0; u < kBatch; ++u) {
+        const int j = qq + Q * (u0 + u);
+        v[u] = j < nr ? bf2f(a.ring_v[(ring_row + (size_t)j * a.h_kv) * kD + c]) : 0.f;
+      }
 #pragma unroll
-      for (int u = 0; u < kRingBatch; ++u) A = fmaf(j0 + u < nr ? L.pr[j0 + u] : 0.f, v[u], A);
+      for (int u = 0; u < kBatch; ++u) {
+        const int j = qq + Q * (u0 + u);
+        if (j < nr) A = fmaf(L.pr[j], v[u], A);
+      }
     }
   }
-  if (active) a.out[q_row(a, b, t, hq) * kD + c] = (any && Lsum > 0.f) ? A / Lsum : 0.f;
+  L.part[qq][c] = A;
+  __syncthreads();
+  if (tid < kD) {
+    const float tot = (L.part[0][c] + L.part[1][c]) + (L.part[2][c] + L.part[3][c]);
+    a.out[q_row(a, b, t, hq) * kD + c] = (any && Lsum > 0.f) ? tot / Lsum : 0.f;
+  }
 }
 
 }  // namespace tq

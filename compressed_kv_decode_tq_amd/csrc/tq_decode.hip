@@ -310,17 +310,17 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(DecodeArgs a) {
   }
 }
 
-// Combine as its own kernel: work-group per (sequence, KV head, virtual head),
-// thread per channel.  Largest split count it stages in LDS (decode_max_splits
+// Combine as its own kernel: work-group of kCombineThreads per (sequence, KV
+// head, virtual head).  Largest split count it stages in LDS (decode_max_splits
 // never exceeds 2048 work-groups' worth of splits of one slot).
 constexpr int kMaxCombineSplits = 2048;
 
 template <bool VMSE>
-__global__ __launch_bounds__(kD) void combine_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeArgs a) {
   __shared__ CombineLds<kMaxCombineSplits> lds;
   const int rows = a.h_kv * a.group;
   const int b = blockIdx.x / rows, h = (blockIdx.x % rows) / a.group, gq = blockIdx.x % a.group;
-  combine_unit<VMSE, kMaxCombineSplits>(a, b, h, gq, true, lds, a.partial + ws_row(a, b, h, gq) * (kD + 2),
+  combine_unit<VMSE, kMaxCombineSplits>(a, b, h, gq, lds, a.partial + ws_row(a, b, h, gq) * (kD + 2),
                                         (size_t)a.batch * a.h_kv * a.group * (kD + 2));
 }
 
@@ -386,9 +386,9 @@ hipError_t launch_decode(const DecodeArgs& a, int key_mse_bits, int key_qjl, int
 
 hipError_t launch_combine(const DecodeArgs& a, int value_mse, hipStream_t stream) {
   if (value_mse)
-    hipLaunchKernelGGL(combine_kernel<true>, dim3(a.batch * a.h_kv * a.group), dim3(kD), 0, stream, a);
+    hipLaunchKernelGGL(combine_kernel<true>, dim3(a.batch * a.h_kv * a.group), dim3(kCombineThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(combine_kernel<false>, dim3(a.batch * a.h_kv * a.group), dim3(kD), 0, stream, a);
+    hipLaunchKernelGGL(combine_kernel<false>, dim3(a.batch * a.h_kv * a.group), dim3(kCombineThreads), 0, stream, a);
   return hipGetLastError();
 }
 
