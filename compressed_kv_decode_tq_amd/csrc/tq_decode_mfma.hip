@@ -387,7 +387,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
   constexpr int kStageNg = 64 * 4;              // floats: per token u = tau log2e n, w = u kappa gamma, mask
   constexpr int kStageVw = 2 * VB * kD + 2 * VB * kVwPad;  // dwords
   constexpr int kStageP = NHEAD * 64;           // floats: p of (head, token) for the value MFMA
-  constexpr int kStageTr = VMSE ? 0 : 64 * 16;  // dwords: value-weight digit blocks, exchanged between lanes
+  constexpr int kStageTr = VMSE ? 64 * 4 : 64 * 16;  // dwords: value-weight digit blocks, exchanged between lanes
   constexpr int kStage = kStageMeta + kStageNg + kStageVw + kStageP + kStageTr;
   constexpr int kMerge = NHEAD * (kD + 2);
   constexpr int kStride = kStage > kMerge ? kStage : kMerge;
@@ -489,9 +489,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
   // so a chunk normally adds to the sums with one fused multiply-add each.
   constexpr float kLazyRescale = 32.f;
   float m_run[NHT], m_ref[NHT], l_part[NHT], acc[NHT][8];
-  // min/max values: sum_t p_t min_t against m_ref, kept in the weight layout
-  // (lane (g, n): head 4ht + n/4, group n%4, the lane's quarter of the
-  // tokens) and added to the channel sums once, after the last chunk
+  // sum_t p_t min_t (min/max values) or sum_t p_t |v_t| (MSE values) against
+  // m_ref, kept in the weight layout (lane (g, n): head 4ht + n/4 and its own
+  // share of the tokens, of group n%4 for min/max values) and added to the
+  // channel sums once, after the last chunk
   float macc[NHT];
 #pragma unroll
   for (int ht = 0; ht < NHT; ++ht) {
@@ -714,7 +715,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
         l_part[ht] *= f;
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) acc[ht][nt] *= f;
-        if (!VMSE) {  // the factor of head 4ht + n/4 (DPP row n/4), through scalar registers
+        {  // macc: the factor of head 4ht + n/4 (DPP row n/4), through scalar registers
           const float f0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), 0));
           const float f1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), 16));
           const float f2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f), 32));
@@ -832,51 +833,62 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
         }
       }
     } else {
-      // this lane's 16 tokens in the bit-plane order: 16ct + 4g + r
-      floatx4 pv[NHT][4];
-#pragma unroll
-      for (int ht = 0; ht < NHT; ++ht)
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-          pv[ht][ct] = *reinterpret_cast<const floatx4*>(s_p + (4 * ht + (n >> 2)) * 64 + 16 * ct + 4 * g);
-      // MSE values: weights p_t |v_t| (same for every value plane), rows (head,
-      // digit); accumulated in rotated space
-      const int mydig_shift = 7 * (3 - (n & 3));
+      // MSE values: weights W = p_t |v_t| (the same for every value plane),
+      // accumulated in rotated space.  Rows of the value MFMA are (head, digit);
+      // its K slot (dword c, byte r) holds token 16c + 4g + r, whose value bit
+      // sits at bit s = 4 (c % 2) + g of its byte (bit-plane order), so W enters
+      // as W 2^(ev - s) and a byte holding 2^7 reads as -128 (W negated there).
+      // Lane (g, 4h + c) forms W for head 4ht + h and the four tokens 16c + 4g + r
+      // only (no lane repeats another's), as signed base-256 digits; a quad
+      // exchange through LDS then gives lane (g, 4h + d) digit d of all sixteen.
       const uint32_t mb = wave_max_u32_uniform(mb_lane);
       int ex;
       frexpf(__uint_as_float(mb), &ex);
-      const int ev = 26 - ex;
+      const int ev = 30 - ex;  // |W 2^ev| < 2^30
       const float inv_sv = ldexpf(1.f, -ev);
+      const int cq = n & 3, s_tok = 4 * (cq & 1) + g;
+      const float sc = s_tok == 7 ? -ldexpf(1.f, ev - 7) : ldexpf(1.f, ev - s_tok);
+      const float half = s_tok == 7 ? -0.5f : 0.5f;  // rounds |W| to nearest
+      float nvs[4], nvr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        nvr[r] = __uint_as_float(s_meta[(16 * cq + 4 * g + r) * NG]);
+        nvs[r] = nvr[r] * sc;
+      }
       u32x4 A[NHT];
-      float PN[NHT];
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) {
-        A[ht] = u32x4{0u, 0u, 0u, 0u};
-        PN[ht] = 0.f;
-      }
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const int s_tok = 4 * (ct & 1) + g;
-        const float sc = ldexpf(1.f, ev - s_tok);
+        const floatx4 pq = *reinterpret_cast<const floatx4*>(s_p + (4 * ht + (n >> 2)) * 64 + 16 * cq + 4 * g);
+        uint32_t V[4];
+        float pn = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int u = 16 * ct + 4 * g + r;
-          const float nv = __uint_as_float(s_meta[u * NG]);
-#pragma unroll
-          for (int ht = 0; ht < NHT; ++ht) {
-            const uint32_t W = (uint32_t)fmaf(pv[ht][ct][r], nv * sc, 0.5f);
-            int dg = (int)((W >> mydig_shift) & 127u);
-            if (s_tok == 7) dg = -dg;
-            A[ht][ct] |= (uint32_t)(dg & 0xff) << (8 * r);
-            PN[ht] = fmaf(pv[ht][ct][r], nv, PN[ht]);
-          }
+          V[r] = (uint32_t)(int)fmaf(pq[r], nvs[r], half) + 0x00808080u;
+          pn = fmaf(pq[r], nvr[r], pn);
         }
-      }
-      float PNpv[NHT];
+        // this lane's part of sum_t p_t |v_t| for head 4ht + n/4, against m_ref
+        macc[ht] = fmaf(pn, __shfl(beta[ht], 16 * (n >> 2) + n), macc[ht]);
+        // 4x4 byte transpose: D[d] holds digit d of the four tokens
+        uint32_t D[4];
+        const uint32_t t01lo = __builtin_amdgcn_perm(V[1], V[0], 0x05010400u);
+        const uint32_t t01hi = __builtin_amdgcn_perm(V[1], V[0], 0x07030602u);
+        const uint32_t t23lo = __builtin_amdgcn_perm(V[3], V[2], 0x05010400u);
+        const uint32_t t23hi = __builtin_amdgcn_perm(V[3], V[2], 0x07030602u);
+        D[3] = __builtin_amdgcn_perm(t23lo, t01lo, 0x05040100u) ^ 0x80808080u;  // least significant digit
+        D[2] = __builtin_amdgcn_perm(t23lo, t01lo, 0x07060302u) ^ 0x80808080u;
+        D[1] = __builtin_amdgcn_perm(t23hi, t01hi, 0x05040100u) ^ 0x80808080u;
+        D[0] = __builtin_amdgcn_perm(t23hi, t01hi, 0x07060302u);  // most significant digit
+        // quad exchange: digit d of lane L at slot 64 d + (L ^ d); lane (g, 4h + d)
+        // reads dword c from lane (g, 4h + c)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int ht = 0; ht < NHT; ++ht) {
-        const float x = col_sum4(PN[ht]);
-        PNpv[ht] = __shfl(x, 4 * g);
+        for (int d = 0; d < 4; ++d) s_tr[64 * d + (lane ^ d)] = D[d];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int c = 0; c < 4; ++c) A[ht][c] = s_tr[64 * cq + (((lane & ~3) | c) ^ cq)];
       }
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
@@ -889,25 +901,28 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
         for (int d = 0; d < 4; ++d)
 #pragma unroll
           for (int pv = 0; pv < VB; ++pv) Wd[d][pv] = s_vw[((d >> 1) * VB + pv) * kD + ch];
+        u32x4 Bp[VB];
 #pragma unroll
         for (int pl = 0; pl < PVB; ++pl) {
           u32x4 B;
 #pragma unroll
           for (int d = 0; d < 4; ++d) {
-            const uint32_t w = pl < VB ? Wd[d][pl % VB] : (Wd[d][0] ^ Wd[d][1 % VB] ^ Wd[d][2 % VB]);
-            B[d] = plane_bytes(w, 4 * (d & 1) + g);
+            if (pl < VB) {
+              B[d] = plane_bytes(Wd[d][pl % VB], 4 * (d & 1) + g);
+              Bp[pl % VB][d] = B[d];
+            } else {  // the parity plane: the AND distributes over the XOR
+              B[d] = Bp[0][d] ^ Bp[1 % VB][d] ^ Bp[2 % VB][d];
+            }
           }
 #pragma unroll
           for (int ht = 0; ht < NHT; ++ht) {
             const i32x4 C = mfma_i8(A[ht], B, i32x4{0, 0, 0, 0});
-            const int hi = (C[0] << 7) + C[1], lo = (C[2] << 7) + C[3];
-            const float v = fmaf((float)hi, 16384.f, (float)lo);
+            const float v = fmaf((float)((C[0] << 8) + C[1]), 65536.f, (float)((C[2] << 8) + C[3]));
             vs[ht] = fmaf(v, a.val_w[pl], vs[ht]);
           }
         }
 #pragma unroll
-        for (int ht = 0; ht < NHT; ++ht)
-          acc[ht][nt] = fmaf(fmaf(vs[ht], inv_sv, a.val_cst * PNpv[ht]), beta[ht], acc[ht][nt]);
+        for (int ht = 0; ht < NHT; ++ht) acc[ht][nt] = fmaf(vs[ht], inv_sv * beta[ht], acc[ht][nt]);
       }
     }
   }
@@ -920,6 +935,15 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
       const float x = col_sum4(macc[ht]);
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) acc[ht][nt] += __shfl(x, 4 * g + (nt >> 1));
+    }
+  } else {
+    // the constant of the value codebook times sum_t p_t |v_t|: reduce over the
+    // sixteen lanes of each head, then fetch head g
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      const float x = __shfl(quad_sum(col_sum4(macc[ht])), 4 * g);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) acc[ht][nt] = fmaf(a.val_cst, x, acc[ht][nt]);
     }
   }
 
