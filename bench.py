@@ -14,9 +14,9 @@ channels per KV head scaled x10, keys 2-bit Lloyd-Max + 1-bit QJL, values
 * roofline = the split-scan kernel: compressed bytes per launch / its average
   duration, from HIP events recorded around that launch on every 4th of the
   timed steps (--time-every).
-* cold = more steps, each timed alone right after a 1 GiB device write that
+* cold = more steps, each timed alone right after a 1 GiB device read that
   evicts the 256 MB MALL (the last-level cache), so no step reads a cache
-  that a previous step left in it.
+  that a previous step left in it; the scan launch of each is timed too.
 * cpu_baseline = the float64 oracle on a bounded sample, on the host cores.
 
 Prints ONE JSON line.
@@ -413,31 +413,44 @@ def main():
                      "max": round(scan_sorted[-1], 5)}
     cold = None
     if args.cold_steps:
-        # cold steps: a write larger than the MALL before each, outside the
-        # events, so the compressed cache comes from HBM
+        # cold steps: a read of 1 GiB (four times the MALL) before each,
+        # outside the events, so the compressed cache comes from HBM; a read
+        # leaves clean lines behind, so the step does not also pay for writing
+        # back someone else's dirty data
         if ring:
             state["n_r"] = 0
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        cms, cby = [], []
+        cev = Events(args.cold_steps)  # the scan launch of every cold step
+        cms, cby, csb = [], [], []
         for j in range(args.cold_steps):
-            flush.fill_(j & 0xff)
+            flushed = flush.amax()  # reads all of it; the result stays on the device
             e0.record()
-            by, _ = step(args.warmup + args.steps + j)
+            by, sb = step(args.warmup + args.steps + j, cev.pairs[j])
             e1.record()
             torch.cuda.synchronize()
             cms.append(e0.elapsed_time(e1))
             cby.append(by)
-        del flush
+            csb.append(sb)
+        cscan = [cev.ms(i) for i in range(args.cold_steps)]
+        cev.close()
+        del flush, flushed
         torch.cuda.empty_cache()
         order = sorted(range(len(cms)), key=lambda i: cms[i])
         med = order[len(order) // 2]
+        sorder = sorted(range(len(cscan)), key=lambda i: cscan[i])
+        smed = sorder[len(sorder) // 2]
+        cold_scan_gbs = csb[smed] / (cscan[smed] * 1e-3) / 1e9
         cold = {"steps": args.cold_steps, "flush_mib": 1024,
                 "ms_per_step": {"median": round(cms[med], 5), "min": round(cms[order[0]], 5),
                                 "max": round(cms[order[-1]], 5)},
                 "gbs_at_median": round(cby[med] / (cms[med] * 1e-3) / 1e9, 2),
-                "note": "each step timed alone with events around the call, after a 1 GiB device write "
-                        "that evicts the 256 MB MALL"}
+                "scan_ms": {"median": round(cscan[smed], 5), "min": round(cscan[sorder[0]], 5),
+                            "max": round(cscan[sorder[-1]], 5)},
+                "scan_gbs_at_median": round(cold_scan_gbs, 1),
+                "scan_frac_at_median": round(cold_scan_gbs / HBM_PEAK_GBS, 4),
+                "note": "each step timed alone with events around the call, after a 1 GiB device read "
+                        "that evicts the 256 MB MALL; scan_ms: the scan launch of the same steps"}
     copy_gbs = None
     if args.achievable_mib:
         # a plain device copy (read and write) on the same device: what HBM
