@@ -152,29 +152,28 @@ __device__ __forceinline__ float col_sum4(float x) {
 // fp4_bits' dword 3, added back through the head constants).  The two products are independent down to
 // their digits: work-group (b h, 0) makes the PM index planes from Pi q (and
 // appends the ring token), (b h, 1) the QJL plane from S q.
-// One work item is (head tile, plane, lane group, head of the tile, dword): it
-// expands the four coordinates of that dword once and writes the dword of
-// each of the four digit rows.  x_at(pl, gq, k) is the value plane pl
-// multiplies at coordinate k for head gq, s_at(pl, gq) its exponent sigma.
+// One work item is (plane, lane group, head of the tile, dword) of head tile
+// ht: it expands the four coordinates of that dword once and writes the dword
+// of each of the four digit rows.  x_at(pl, hh, k) is the value plane pl
+// multiplies at coordinate k for head 4 ht + hh, s_at(pl, hh) its exponent sigma.
 template <class XAt, class SAt>
-__device__ __forceinline__ void emit_digits(int tid, int nthreads, int pl0, int pl1, int npl, int nht, int G,
+__device__ __forceinline__ void emit_digits(int tid, int nthreads, int pl0, int pl1, int npl, int ht, int G,
                                             XAt x_at, SAt s_at, uint32_t* dig) {
   const int np = pl1 - pl0;
-  const int items = nht * np * 4 * 4 * 8;
+  const int items = np * 4 * 4 * 8;
   for (int it = tid; it < items; it += nthreads) {
     const int v = it & 7, hh = (it >> 3) & 3, g = (it >> 5) & 3;
-    const int rest = it >> 7;
-    const int pl = pl0 + rest % np, ht = rest / np;
+    const int pl = pl0 + (it >> 7);
     const int gq = 4 * ht + hh;
     uint32_t word[4] = {0u, 0u, 0u, 0u};
     if (gq < G) {
-      const int sg = s_at(pl, gq);
+      const int sg = s_at(pl, hh);
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         int wexp;
         bool neg;
         const int k = score_coordinate(g, v, b, wexp, neg);
-        const float xk = x_at(pl, gq, k);
+        const float xk = x_at(pl, hh, k);
         float y = ldexpf(neg ? -xk : xk, sg + wexp);  // |y| < 2^8, inside fp8's range
 #pragma unroll
         for (int L = 0; L < 4; ++L) {
@@ -262,16 +261,17 @@ __device__ __forceinline__ void append_ring_token(const DecodeArgs& a, int b, in
                          : (uint16_t)f2bf(reinterpret_cast<const float*>(in)[src]);
 }
 
-// Queries of the slot's virtual heads into LDS, coordinate-major: qt[j][gq/4][gq%4].
+// Queries of virtual heads hoff .. hoff + MAXG - 1 of the slot into LDS,
+// coordinate-major: qt[j][gq/4][gq%4] for head hoff + gq.
 template <int MAXG>
-__device__ __forceinline__ void stage_queries(const DecodeArgs& a, int b, int h, int tid, int nthreads,
+__device__ __forceinline__ void stage_queries(const DecodeArgs& a, int b, int h, int hoff, int tid, int nthreads,
                                               floatx4 (*qt)[MAXG / 4]) {
   for (int i = tid; i < MAXG * kD; i += nthreads) {
     const int gq = i / kD, c = i % kD;
     float x = 0.f;
-    if (gq < a.group) {
+    if (hoff + gq < a.group) {
       int t, hq;
-      virtual_head(a, h, gq, t, hq);
+      virtual_head(a, h, hoff + gq, t, hq);
       const size_t off = q_row(a, b, t, hq) * kD + c;
       x = a.q_bf16 ? bf2f(reinterpret_cast<const uint16_t*>(a.q)[off]) : reinterpret_cast<const float*>(a.q)[off];
     }
@@ -311,25 +311,27 @@ __device__ __forceinline__ void row_times_queries(const float (&m)[NJ], int j0, 
 template <int MAXG>
 struct QprepLds {
   floatx4 qt[kD][MAXG / 4];  // queries, coordinate-major
-  float qx[kMaxGroup][kD];   // this part's product (Pi q or S q)
-  float red[kMaxGroup][kD];  // upper-half partial sums of the product
-  int e_head[kMaxGroup];
+  float qx[MAXG][kD];   // this part's product (Pi q or S q)
+  float red[MAXG][kD];  // upper-half partial sums of the product
+  int e_head[MAXG];
 };
 
-// One q-prep part of slot (b, h) on 256 threads: part 0 makes the
-// index-plane digits from Pi q (and appends the ring token), part 1 the QJL
-// digits from S q.  Thread (hj, i) forms coordinate i over the half hj of the
-// columns.  Digits go to dig (the slot's nht * npl * 2 * 64 * 4 dwords),
-// per-head constants to cst_base ([group][4]).
+// One q-prep part of head tile ht (heads 4 ht .. 4 ht + 3) of slot (b, h) on
+// 256 threads: part 0 makes the index-plane digits from Pi q (and, for tile 0,
+// appends the ring token), part 1 the QJL digits from S q.  Thread (hj, i)
+// forms coordinate i over the half hj of the columns.  Digits go to dig (the
+// slot's nht * npl * 2 * 64 * 4 dwords), per-head constants to cst_base
+// ([group][4]).
 template <int MAXG>
-__device__ __forceinline__ void qprep_part(const DecodeArgs& a, int b, int h, int part, int tid, QprepLds<MAXG>& L,
-                                           uint32_t* dig, float* cst_base, int pm, int npl, int nht) {
-  const int G = a.group;
-  if (part == 0 && a.app_k && a.vbase == 0) append_ring_token(a, b, h, tid);
+__device__ __forceinline__ void qprep_part(const DecodeArgs& a, int b, int h, int part, int ht, int tid,
+                                           QprepLds<MAXG>& L, uint32_t* dig, float* cst_base, int pm, int npl) {
+  static_assert(MAXG == 4, "one head tile per work-group");
+  const int G = a.group, hoff = 4 * ht;
+  if (part == 0 && ht == 0 && a.app_k && a.vbase == 0) append_ring_token(a, b, h, tid);
   const int i = tid & (kD - 1), hj = tid >> 7;
   float m[kD / 2];
   load_row<kD / 2>(a, part, i, hj * (kD / 2), m);  // in flight while the queries are staged
-  stage_queries<MAXG>(a, b, h, tid, 256, L.qt);
+  stage_queries<MAXG>(a, b, h, hoff, tid, 256, L.qt);
   __syncthreads();
   {
     float acc[MAXG];
@@ -342,28 +344,27 @@ __device__ __forceinline__ void qprep_part(const DecodeArgs& a, int b, int h, in
   __syncthreads();
   const int lane = tid & 63, wv = tid >> 6;
   for (int gq = wv; gq < MAXG; gq += 4) {
-    const int e = head_constants(a, L.qx[gq], part, lane, pm, npl, gq < G ? cst_base + gq * 4 : nullptr);
+    const int e = head_constants(a, L.qx[gq], part, lane, pm, npl, hoff + gq < G ? cst_base + (hoff + gq) * 4 : nullptr);
     if (lane == 0) L.e_head[gq] = e;
   }
   __syncthreads();
   const int pl0 = part == 0 ? 0 : pm, pl1 = part == 0 ? pm : pm + 1;
   emit_digits(
-      tid, 256, pl0, pl1, npl, nht, G,
-      [&](int pl, int gq, int k) {
-        return part == 0 ? (a.key_half && (k & 31) < 16 ? a.key_w_hi[pl] : a.key_w[pl]) * L.qx[gq][k]
-                         : 2.f * L.qx[gq][k];
+      tid, 256, pl0, pl1, npl, ht, G,
+      [&](int pl, int hh, int k) {
+        return part == 0 ? (a.key_half && (k & 31) < 16 ? a.key_w_hi[pl] : a.key_w[pl]) * L.qx[hh][k]
+                         : 2.f * L.qx[hh][k];
       },
-      [&](int, int gq) { return L.e_head[gq]; }, dig);
+      [&](int, int hh) { return L.e_head[hh]; }, dig);
 }
 
-// Separate q-prep kernel of the split scan: work-group (b h, part).
-template <int MAXG>
+// Separate q-prep kernel of the split scan: work-group (b h, part, head tile).
 __global__ __launch_bounds__(256) void qprep_mfma_kernel(DecodeArgs a, int pm, int npl, int nht) {
-  __shared__ QprepLds<MAXG> lds;
+  __shared__ QprepLds<4> lds;
   const int b = __builtin_amdgcn_workgroup_id_x() / a.h_kv, h = __builtin_amdgcn_workgroup_id_x() % a.h_kv;
   uint32_t* dig = reinterpret_cast<uint32_t*>(a.qdig) + (size_t)(b * a.h_kv + h) * (nht * npl * 2 * 64 * 4);
-  qprep_part<MAXG>(a, b, h, (int)__builtin_amdgcn_workgroup_id_y(), (int)__builtin_amdgcn_workitem_id_x(), lds, dig, a.qconst + ws_row(a, b, h, 0) * 4, pm,
-                   npl, nht);
+  qprep_part<4>(a, b, h, (int)__builtin_amdgcn_workgroup_id_y(), (int)__builtin_amdgcn_workgroup_id_z(),
+                (int)__builtin_amdgcn_workitem_id_x(), lds, dig, a.qconst + ws_row(a, b, h, 0) * 4, pm, npl);
 }
 
 template <int PM, bool QJL, bool VMSE, int PVB, int NHT, bool HALF = false>
@@ -1060,11 +1061,8 @@ hipError_t launch_decode_mfma(const DecodeArgs& a_in, int key_mse_bits, int key_
   const DecodeArgs& a = a_in;
   const int pm = 1 << (key_mse_bits - 1);
   const int npl = pm + (key_qjl ? 1 : 0);
-  const dim3 qgrid(a.batch * a.h_kv, key_qjl ? 2 : 1);
-  if (nht == 1)
-    hipLaunchKernelGGL(qprep_mfma_kernel<4>, qgrid, dim3(256), 0, stream, a, pm, npl, nht);
-  else
-    hipLaunchKernelGGL(qprep_mfma_kernel<8>, qgrid, dim3(256), 0, stream, a, pm, npl, nht);
+  const dim3 qgrid(a.batch * a.h_kv, key_qjl ? 2 : 1, nht);
+  hipLaunchKernelGGL(qprep_mfma_kernel, qgrid, dim3(256), 0, stream, a, pm, npl, nht);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = nht == 1 ? dispatch_mfma<1>(a, key_mse_bits, key_qjl, value_mse, value_bits, stream, tl)
