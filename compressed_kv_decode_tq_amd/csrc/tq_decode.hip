@@ -311,9 +311,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(DecodeArgs a) {
 }
 
 // Combine as its own kernel: work-group of kCombineThreads per (sequence, KV
-// head, virtual head).  Largest split count it stages in LDS (decode_max_splits
-// never exceeds 2048 work-groups' worth of splits of one slot).
-constexpr int kMaxCombineSplits = 2048;
+// head, virtual head).  Largest split count it stages in LDS (decode_split
+// never splits a slot into more than kSplitTarget parts).
+constexpr int kMaxCombineSplits = (int)kSplitTarget;
 
 template <bool VMSE>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeArgs a) {

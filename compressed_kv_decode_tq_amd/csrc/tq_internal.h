@@ -229,6 +229,9 @@ hipError_t launch_combine(const DecodeArgs& a, int value_mse, hipStream_t stream
 // (tq_noalloc.hip); the address is looked up on the first call per device.
 hipError_t noalloc_scratch(void** ptr, size_t* bytes);
 
+// Work-groups a decode launch aims at (three per compute unit); no slot is
+// ever split into more than this many parts.
+constexpr int64_t kSplitTarget = 768;
 // Decode work split used for the workspace size and the launch.
 void decode_split(int64_t max_tokens, int64_t units, int32_t* splits, int32_t* split_len);
 // Upper bound of decode_split's split count over all token counts <= max_tokens.

@@ -8,17 +8,19 @@ namespace tq {
 
 // Split of the token range for the decode grid, in whole 64-token chunks
 // (the waves of a work-group take the chunks of its split in turn).  About
-// kSplitTarget work-groups over the device; when that makes splits shorter than
-// kLongSplit tokens, they are lengthened towards kLongSplit as long as at least
-// kFloorGroups work-groups (one round of three per compute unit) remain, so
-// per-work-group set-up and the combine's merge stay small next to the scan
-// while a few long sequences still fill every compute unit.  8 sequence-heads
-// of 131072 tokens: 1408-token splits, 752 work-groups (about three per compute
-// unit), against 1536-token splits and 688 work-groups with whole 256-token
-// rounds (5% less scan time) and 512-token splits and 2048 work-groups for a
-// floor of eight per compute unit (4% more time per step, most of it in the
-// combine).
-constexpr int64_t kSplitTarget = 2048;
+// kSplitTarget work-groups over the device: 768 is three per compute unit, one
+// round at the scan's three waves per SIMD, so no second, partly filled round
+// of work-groups trails the first (32 sequences of 8 KV heads at 32768 tokens:
+// 3 splits of 10944 tokens per sequence-head, 166 against 167-170 us for 8
+// splits and 2048 work-groups, 171-175 us for 1024).  When that makes splits
+// shorter than kLongSplit tokens, they are lengthened towards kLongSplit as long
+// as at least kFloorGroups work-groups remain, so per-work-group set-up and the
+// combine's merge stay small next to the scan while a few long sequences still
+// fill every compute unit.  8 sequence-heads of 131072 tokens: 1408-token
+// splits, 752 work-groups (about three per compute unit), against 1536-token
+// splits and 688 work-groups with whole 256-token rounds (5% less scan time)
+// and 512-token splits and 2048 work-groups for a floor of eight per compute
+// unit (4% more time per step, most of it in the combine).
 constexpr int64_t kFloorGroups = 768;
 constexpr int64_t kLongSplit = 2048;
 constexpr int64_t kMinSplit = 256;
