@@ -82,17 +82,21 @@ __device__ __forceinline__ void combine_unit(const DecodeArgs& a, int b, int h, 
   const int S = a.splits;
   const size_t ring_row = (size_t)b * a.ring_cap * a.h_kv + h;  // ring token j: (ring_row + j h_kv) kD
 
-  // ---- loads
-  if (tid < kD) {
-    const size_t qoff = q_row(a, b, t, hq) * kD + c;
-    L.qv[c] = a.q_bf16 ? bf2f(reinterpret_cast<const uint16_t*>(a.q)[qoff]) : reinterpret_cast<const float*>(a.q)[qoff];
-  }
-  float M = -INFINITY;  // split headers: thread tid takes splits tid, tid + 512, ...
-  for (int sp = tid; sp < S; sp += kCombineThreads) {
-    const float m = part0[(size_t)sp * sstride], l = part0[(size_t)sp * sstride + 1];
-    L.s_f[sp] = m;
-    L.s_l[sp] = l;
-    M = fmaxf(M, m);
+  // ---- loads, all issued before the first is used: raw bits, converted where
+  // they are used, so no conversion waits on a load while later loads are
+  // still to be issued
+  const size_t qoff = q_row(a, b, t, hq) * kD + c;
+  uint32_t qraw = 0u;
+  if (tid < kD)
+    qraw = a.q_bf16 ? (uint32_t)reinterpret_cast<const uint16_t*>(a.q)[qoff]
+                    : reinterpret_cast<const uint32_t*>(a.q)[qoff];
+  constexpr int kHdr = (MAXS + kCombineThreads - 1) / kCombineThreads;  // split headers per thread
+  float hm[kHdr], hl[kHdr];  // thread tid takes splits tid, tid + 512, ...
+#pragma unroll
+  for (int u = 0; u < kHdr; ++u) {
+    const int sp = tid + kCombineThreads * u;
+    hm[u] = sp < S ? part0[(size_t)sp * sstride] : -INFINITY;
+    hl[u] = sp < S ? part0[(size_t)sp * sstride + 1] : 0.f;
   }
   float pa[kPre];  // quarter qq: splits qq, qq + 4, ...
 #pragma unroll
@@ -104,10 +108,26 @@ __device__ __forceinline__ void combine_unit(const DecodeArgs& a, int b, int h, 
 #pragma unroll
     for (int i = 0; i < 4; ++i) kw[i] = kr[i];
   }
-  float rv[kRingPre];  // quarter qq: ring tokens qq, qq + 4, ...
+  // quarter qq: ring tokens qq, qq + 4, ... (bf16 bits), read from tokens
+  // clamped to the last one seen (the extra values are never used) by the
+  // waves whose quarter has a token at all (the quarter is uniform over a wave)
+  uint32_t rv[kRingPre] = {};
+  if (__builtin_amdgcn_readfirstlane(qq) < nr) {
 #pragma unroll
-  for (int u = 0; u < kRingPre; ++u)
-    rv[u] = qq + Q * u < nr ? bf2f(a.ring_v[(ring_row + (size_t)(qq + Q * u) * a.h_kv) * kD + c]) : 0.f;
+    for (int u = 0; u < kRingPre; ++u)
+      rv[u] = a.ring_v[(ring_row + (size_t)min(qq + Q * u, nr - 1) * a.h_kv) * kD + c];
+  }
+  if (tid < kD) L.qv[c] = a.q_bf16 ? bf2f(qraw) : __uint_as_float(qraw);
+  float M = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < kHdr; ++u) {
+    const int sp = tid + kCombineThreads * u;
+    if (sp < S) {
+      L.s_f[sp] = hm[u];
+      L.s_l[sp] = hl[u];
+    }
+    M = fmaxf(M, hm[u]);
+  }
   __syncthreads();  // qv, split headers
 
   // ---- ring scores
@@ -183,19 +203,19 @@ __device__ __forceinline__ void combine_unit(const DecodeArgs& a, int b, int h, 
     // kRingPre are in registers, the rest come kBatch loads at a time
 #pragma unroll
     for (int u = 0; u < kRingPre; ++u)
-      if (qq + Q * u < nr) A = fmaf(L.pr[qq + Q * u], rv[u], A);
+      if (qq + Q * u < nr) A = fmaf(L.pr[qq + Q * u], bf2f(rv[u]), A);
 #pragma unroll 1
     for (int u0 = kRingPre; qq + Q * u0 < nr; u0 += kBatch) {
-      float v[kBatch];
+      uint32_t v[kBatch];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
-        const int j = qq + Q * (u0 + u);
-        v[u] = j < nr ? bf2f(a.ring_v[(ring_row + (size_t)j * a.h_kv) * kD + c]) : 0.f;
+        const int j = min(qq + Q * (u0 + u), nr - 1);
+        v[u] = a.ring_v[(ring_row + (size_t)j * a.h_kv) * kD + c];
       }
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         const int j = qq + Q * (u0 + u);
-        if (j < nr) A = fmaf(L.pr[j], v[u], A);
+        if (j < nr) A = fmaf(L.pr[j], bf2f(v[u]), A);
       }
     }
   }

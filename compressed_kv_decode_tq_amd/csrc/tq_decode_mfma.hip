@@ -250,32 +250,60 @@ __device__ __forceinline__ int head_constants(const DecodeArgs& a, const float* 
 }
 
 // The step's ring token of slot (b, h), rounded to bf16 (256 threads: the
-// first 128 write the key row, the others the value row).
-__device__ __forceinline__ void append_ring_token(const DecodeArgs& a, int b, int h, int tid) {
-  const int c = tid & (kD - 1), which = tid >> 7;
+// first 128 take the key row, the others the value row): ring_token_load reads
+// this thread's element (as stored: bf16 or fp32 bits) and its ring position,
+// ring_token_store writes it to the ring, so the reads can be issued with the
+// work-group's other loads and the write left to the end.
+struct RingToken {
+  uint32_t raw;
+  uint16_t* dst;  // its ring element
+};
+__device__ __forceinline__ RingToken ring_token_load(const DecodeArgs& a, int b, int h, int tid) {
+  // which row is uniform over a wave (128 threads per row): the pointer choice
+  // stays in scalar registers
+  const int c = tid & (kD - 1), which = __builtin_amdgcn_readfirstlane(tid >> 7);
   const size_t src = ((size_t)b * a.h_kv + h) * kD + c;
-  const size_t dst = (((size_t)b * a.ring_cap + a.n_ring.v[b] - 1) * a.h_kv + h) * kD + c;
   const void* in = which ? a.app_v : a.app_k;
-  uint16_t* ring = which ? a.app_ring_v : a.app_ring_k;
-  ring[dst] = a.app_bf16 ? reinterpret_cast<const uint16_t*>(in)[src]
-                         : (uint16_t)f2bf(reinterpret_cast<const float*>(in)[src]);
+  RingToken r;
+  r.raw = a.app_bf16 ? (uint32_t)reinterpret_cast<const uint16_t*>(in)[src]
+                     : reinterpret_cast<const uint32_t*>(in)[src];
+  r.dst = (which ? a.app_ring_v : a.app_ring_k) + (((size_t)b * a.ring_cap + a.n_ring.v[b] - 1) * a.h_kv + h) * kD + c;
+  return r;
+}
+__device__ __forceinline__ void ring_token_store(const DecodeArgs& a, const RingToken& r) {
+  *r.dst = a.app_bf16 ? (uint16_t)r.raw : (uint16_t)f2bf(__uint_as_float(r.raw));
 }
 
-// Queries of virtual heads hoff .. hoff + MAXG - 1 of the slot into LDS,
-// coordinate-major: qt[j][gq/4][gq%4] for head hoff + gq.
 template <int MAXG>
-__device__ __forceinline__ void stage_queries(const DecodeArgs& a, int b, int h, int hoff, int tid, int nthreads,
-                                              floatx4 (*qt)[MAXG / 4]) {
-  for (int i = tid; i < MAXG * kD; i += nthreads) {
-    const int gq = i / kD, c = i % kD;
-    float x = 0.f;
-    if (hoff + gq < a.group) {
-      int t, hq;
-      virtual_head(a, h, hoff + gq, t, hq);
-      const size_t off = q_row(a, b, t, hq) * kD + c;
-      x = a.q_bf16 ? bf2f(reinterpret_cast<const uint16_t*>(a.q)[off]) : reinterpret_cast<const float*>(a.q)[off];
-    }
-    reinterpret_cast<float*>(&qt[c][gq >> 2])[gq & 3] = x;
+struct QueryStage {
+  uint32_t raw[MAXG * kD / 256];  // as stored: bf16 or fp32 bits
+};
+// Queries of virtual heads hoff .. hoff + MAXG - 1 of the slot, on 256
+// threads: query_load reads them (every load issued before any is used),
+// query_store puts them into LDS, coordinate-major: qt[j][gq/4][gq%4] for head
+// hoff + gq.
+template <int MAXG>
+__device__ __forceinline__ QueryStage<MAXG> query_load(const DecodeArgs& a, int b, int h, int hoff, int tid) {
+  QueryStage<MAXG> r;
+#pragma unroll
+  for (int u = 0; u < MAXG * kD / 256; ++u) {
+    const int i = tid + 256 * u, gq = i / kD, c = i % kD;
+    int t, hq;
+    virtual_head(a, h, hoff + gq < a.group ? hoff + gq : 0, t, hq);
+    const size_t off = q_row(a, b, t, hq) * kD + c;
+    r.raw[u] = a.q_bf16 ? (uint32_t)reinterpret_cast<const uint16_t*>(a.q)[off]
+                        : reinterpret_cast<const uint32_t*>(a.q)[off];
+  }
+  return r;
+}
+template <int MAXG>
+__device__ __forceinline__ void query_store(const DecodeArgs& a, const QueryStage<MAXG>& r, int hoff, int tid,
+                                            floatx4 (*qt)[MAXG / 4]) {
+#pragma unroll
+  for (int u = 0; u < MAXG * kD / 256; ++u) {
+    const int i = tid + 256 * u, gq = i / kD, c = i % kD;
+    const float x = a.q_bf16 ? bf2f(r.raw[u]) : __uint_as_float(r.raw[u]);
+    reinterpret_cast<float*>(&qt[c][gq >> 2])[gq & 3] = hoff + gq < a.group ? x : 0.f;
   }
 }
 
@@ -327,11 +355,16 @@ __device__ __forceinline__ void qprep_part(const DecodeArgs& a, int b, int h, in
                                            QprepLds<MAXG>& L, uint32_t* dig, float* cst_base, int pm, int npl) {
   static_assert(MAXG == 4, "one head tile per work-group");
   const int G = a.group, hoff = 4 * ht;
-  if (part == 0 && ht == 0 && a.app_k && a.vbase == 0) append_ring_token(a, b, h, tid);
+  // Loads first, in the order they are needed (ring token, queries, matrix
+  // row), so each wait covers only what its use needs; the ring write and the
+  // per-head constants' and digits' writes come after the last barrier.
+  const bool append = part == 0 && ht == 0 && a.app_k && a.vbase == 0;
+  const RingToken rtok = append ? ring_token_load(a, b, h, tid) : RingToken{0u, nullptr};
+  const QueryStage<MAXG> qs = query_load<MAXG>(a, b, h, hoff, tid);
   const int i = tid & (kD - 1), hj = tid >> 7;
   float m[kD / 2];
   load_row<kD / 2>(a, part, i, hj * (kD / 2), m);  // in flight while the queries are staged
-  stage_queries<MAXG>(a, b, h, hoff, tid, 256, L.qt);
+  query_store<MAXG>(a, qs, hoff, tid, L.qt);
   __syncthreads();
   {
     float acc[MAXG];
@@ -356,6 +389,7 @@ __device__ __forceinline__ void qprep_part(const DecodeArgs& a, int b, int h, in
                          : 2.f * L.qx[hh][k];
       },
       [&](int, int hh) { return L.e_head[hh]; }, dig);
+  if (append) ring_token_store(a, rtok);
 }
 
 // Separate q-prep kernel of the split scan: work-group (b h, part, head tile).

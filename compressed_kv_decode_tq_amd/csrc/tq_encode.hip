@@ -505,6 +505,32 @@ __device__ __forceinline__ float block_sum128(float x, float* red) {
   return red[0] + red[1];
 }
 
+// Column i of a 128 x 128 fp32 matrix M (row-major, M[k][i] at k * kD + i),
+// read into registers with every load issued before any is used (one memory
+// round trip instead of one per group of unrolled loads), and its product with
+// the staged vector xs: sum_k M[k][i] xs[k].
+struct Col128 {
+  float m[kD];
+};
+__device__ __forceinline__ Col128 load_col128(const float* M, int i) {
+  // the matrix does not change inside the token loop, but its column is read
+  // per token: an opaque copy of the pointer keeps the loads where they are
+  // written, so one column at a time is live
+  asm volatile("" : "+s"(M));
+  Col128 c;
+#pragma unroll
+  for (int k = 0; k < kD; ++k) c.m[k] = M[k * kD + i];
+  return c;
+}
+__device__ __forceinline__ float col_dot128(const Col128& c, const float* xs) {
+  asm volatile("" ::: "memory");  // the column's loads are all issued before the products start
+  float acc = 0.f;
+#pragma unroll
+  for (int k = 0; k < kD; ++k) acc = fmaf(c.m[k], xs[k], acc);
+  asm volatile("" ::: "memory");  // and no later column's loads start before they end (one column live)
+  return acc;
+}
+
 // Few-token encode (a decode step's new tokens): one work-group of 128
 // threads per (sequence, head, 32-token block) tile, one thread per
 // coordinate, in fp32 with coalesced column reads of fp32 matrices.  Per
@@ -542,14 +568,12 @@ __device__ __forceinline__ void encode_small_body(EncodeArgs a) {
     const int64_t row = ((int64_t)b * a.n_new + t) * a.h_kv + h;
     const float x = IN_BF16 ? bf2f(reinterpret_cast<const uint16_t*>(src)[row * kD + i])
                             : reinterpret_cast<const float*>(src)[row * kD + i];
+    const Col128 cpi = load_col128(pit, i);  // in flight with the token's own load and norm
     const float n = sqrtf(block_sum128(x * x, red));
     const float inv = n > 0.f ? 1.0f / n : 0.f;
     xs[i] = x;
     __syncthreads();
-    float acc = 0.f;
-#pragma unroll 16
-    for (int k = 0; k < kD; ++k) acc = fmaf(pit[k * kD + i], xs[k], acc);
-    const float y = acc * inv;
+    const float y = col_dot128(cpi, xs) * inv;
     int idx = 0;
     float c;
     if (hi) {
@@ -575,19 +599,16 @@ __device__ __forceinline__ void encode_small_body(EncodeArgs a) {
     bool zbit = false;
     float gam = 0.f;
     if (QJL) {
+      const Col128 cp = load_col128(a.pi, i);  // (Pi^T r)_i = sum_j Pi[j][i] r_j
       gam = sqrtf(block_sum128(r * r, red));  // its barriers also end the reads of xs
       xs[i] = r;
       __syncthreads();
-      float ro = 0.f;  // (Pi^T r)_i = sum_j Pi[j][i] r_j
-#pragma unroll 16
-      for (int j = 0; j < kD; ++j) ro = fmaf(a.pi[j * kD + i], xs[j], ro);
+      const float ro = col_dot128(cp, xs);
+      const Col128 cs = load_col128(stt, i);  // (S ro)_i = sum_j S^T[j][i] ro_j
       __syncthreads();
       xs[i] = ro;
       __syncthreads();
-      float z = 0.f;  // (S ro)_i = sum_j S^T[j][i] ro_j
-#pragma unroll 16
-      for (int j = 0; j < kD; ++j) z = fmaf(stt[j * kD + i], xs[j], z);
-      zbit = z >= 0.f;
+      zbit = col_dot128(cs, xs) >= 0.f;
     }
     // plane words by ballot: wave wv holds coordinates 64 wv .. 64 wv + 63,
     // the words 2 wv and 2 wv + 1 of every plane
