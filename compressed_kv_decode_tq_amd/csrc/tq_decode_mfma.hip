@@ -191,7 +191,7 @@ __device__ __forceinline__ void emit_digits(int tid, int nthreads, int pl0, int 
 // Per-head digit exponent sigma and score constants of one product (part 0:
 // Pi q, part 1: S q) of one head, on one wave.
 __device__ __forceinline__ int head_constants(const DecodeArgs& a, const float* x, int part, int lane, int pm,
-                                              int npl, float* cst) {
+                                              bool qjl, float* cst) {
   // sr: sum over the coordinates of the base table; srh over the half-bit
   // coordinates (i mod 32 < 16) of the fractional layout; for the QJL part,
   // sr is sum(q_s).  s3, s3h: the same sums over the coordinates = 3 mod 4
@@ -238,7 +238,7 @@ __device__ __forceinline__ int head_constants(const DecodeArgs& a, const float* 
       }
       cst[0] = a.key_cst * sr + a.key_cst_hi * srh + 0.5f * (s3 * w + (a.key_half ? s3h * wh : 0.f));
       cst[1] = (float)e;                     // sigma of the MSE planes
-      if (npl == pm) cst[2] = cst[3] = 0.f;  // no QJL plane
+      if (!qjl) cst[2] = cst[3] = 0.f;  // no QJL plane
     } else {
       cst[2] = (float)e;  // sigma of the QJL plane
       // sum(q_s), less the dword-3 offset of the QJL plane (whose x is 2 q_s):
@@ -352,7 +352,8 @@ struct QprepLds {
 // ([group][4]).
 template <int MAXG>
 __device__ __forceinline__ void qprep_part(const DecodeArgs& a, int b, int h, int part, int ht, int tid,
-                                           QprepLds<MAXG>& L, uint32_t* dig, float* cst_base, int pm, int npl) {
+                                           QprepLds<MAXG>& L, uint32_t* dig, float* cst_base, int pm, int pmd,
+                                           int npl) {
   static_assert(MAXG == 4, "one head tile per work-group");
   const int G = a.group, hoff = 4 * ht;
   // Loads first, in the order they are needed (ring token, queries, matrix
@@ -377,28 +378,34 @@ __device__ __forceinline__ void qprep_part(const DecodeArgs& a, int b, int h, in
   __syncthreads();
   const int lane = tid & 63, wv = tid >> 6;
   for (int gq = wv; gq < MAXG; gq += 4) {
-    const int e = head_constants(a, L.qx[gq], part, lane, pm, npl, hoff + gq < G ? cst_base + (hoff + gq) * 4 : nullptr);
+    const int e = head_constants(a, L.qx[gq], part, lane, pm, npl > pmd,
+                                 hoff + gq < G ? cst_base + (hoff + gq) * 4 : nullptr);
     if (lane == 0) L.e_head[gq] = e;
   }
   __syncthreads();
-  const int pl0 = part == 0 ? 0 : pm, pl1 = part == 0 ? pm : pm + 1;
+  const int pl0 = part == 0 ? 0 : pmd, pl1 = part == 0 ? pmd : pmd + 1;
   emit_digits(
       tid, 256, pl0, pl1, npl, ht, G,
       [&](int pl, int hh, int k) {
-        return part == 0 ? (a.key_half && (k & 31) < 16 ? a.key_w_hi[pl] : a.key_w[pl]) * L.qx[hh][k]
-                         : 2.f * L.qx[hh][k];
+        if (part != 0) return 2.f * L.qx[hh][k];
+        // shared word (pmd < pm): bits 0..15 of lane group g's word are the half
+        // plane of coordinates 32g..32g+15, bits 16..31 the parity plane of the
+        // same coordinates
+        if (pmd < pm && pl == 2)
+          return (k & 31) < 16 ? a.key_w_hi[2] * L.qx[hh][k] : a.key_w_hi[3] * L.qx[hh][k - 16];
+        return (a.key_half && (k & 31) < 16 ? a.key_w_hi[pl] : a.key_w[pl]) * L.qx[hh][k];
       },
       [&](int, int hh) { return L.e_head[hh]; }, dig);
   if (append) ring_token_store(a, rtok);
 }
 
 // Separate q-prep kernel of the split scan: work-group (b h, part, head tile).
-__global__ __launch_bounds__(256) void qprep_mfma_kernel(DecodeArgs a, int pm, int npl, int nht) {
+__global__ __launch_bounds__(256) void qprep_mfma_kernel(DecodeArgs a, int pm, int pmd, int npl, int nht) {
   __shared__ QprepLds<4> lds;
   const int b = __builtin_amdgcn_workgroup_id_x() / a.h_kv, h = __builtin_amdgcn_workgroup_id_x() % a.h_kv;
   uint32_t* dig = reinterpret_cast<uint32_t*>(a.qdig) + (size_t)(b * a.h_kv + h) * (nht * npl * 2 * 64 * 4);
   qprep_part<4>(a, b, h, (int)__builtin_amdgcn_workgroup_id_y(), (int)__builtin_amdgcn_workgroup_id_z(),
-                (int)__builtin_amdgcn_workitem_id_x(), lds, dig, a.qconst + ws_row(a, b, h, 0) * 4, pm, npl);
+                (int)__builtin_amdgcn_workitem_id_x(), lds, dig, a.qconst + ws_row(a, b, h, 0) * 4, pm, pmd, npl);
 }
 
 template <int PM, bool QJL, bool VMSE, int PVB, int NHT, bool HALF = false>
@@ -409,7 +416,13 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
   constexpr int KP = KB + (QJL ? 1 : 0);               // stored key planes
   // HALF: index plane KB - 1 is the half plane (16-bit chunk per lane group)
   static_assert(!HALF || (QJL && KB >= 2), "the half-bit layout has QJL and a full plane below the half plane");
-  constexpr int NPL = PM + (QJL ? 1 : 0);              // score planes
+  // Half-bit keys with a 3-bit table: Walsh planes 2 (the half plane) and 3
+  // (the parity plane) weigh only the half-bit coordinates, so one operand word
+  // carries both (the half plane in bits 0..15, the parity of the same
+  // coordinates in bits 16..31) and one MFMA scores them.
+  constexpr bool SHARED = HALF && PM == 4;
+  constexpr int PMD = SHARED ? 3 : PM;                 // index-plane MFMAs
+  constexpr int NPL = PMD + (QJL ? 1 : 0);             // score planes
   constexpr int VB = VMSE ? (PVB == 1 ? 1 : (PVB == 2 ? 2 : 3)) : PVB;  // stored value planes
   constexpr int NG = 4;                                // min/max groups of 32 channels
   constexpr int NHEAD = 4 * NHT;
@@ -676,7 +689,11 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
       uint32_t P[PM];
       P[0] = X[ct][0];
       if (PM >= 2) P[1 % PM] = X[ct][1 % KP];
-      if (PM == 4) {
+      if (SHARED) {
+        // the half plane's word has its 16 bits at the bottom; the parity of
+        // the same coordinates goes above them
+        P[2 % PM] = X[ct][2 % KP] | ((X[ct][0] ^ X[ct][1 % KP] ^ X[ct][2 % KP]) << 16);
+      } else if (PM == 4) {
         P[2 % PM] = X[ct][2 % KP];
         P[3 % PM] = X[ct][0] ^ X[ct][1 % KP] ^ X[ct][2 % KP];
       }
@@ -688,7 +705,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_mfma_kernel(DecodeArgs a) {
         cq[ht] = floatx4{-c3[ht], 0.f, 0.f, 0.f};
       }
 #pragma unroll
-      for (int pl = 0; pl < PM; ++pl) {
+      for (int pl = 0; pl < PMD; ++pl) {
         const i32x8 Bk = fp4_bits(P[pl], k88, k11);
 #pragma unroll
         for (int ht = 0; ht < NHT; ++ht) cm[ht] = mfma_f8f4(qa[ht][pl], Bk, cm[ht], sc_m[ht]);
@@ -1094,9 +1111,12 @@ hipError_t launch_decode_mfma(const DecodeArgs& a_in, int key_mse_bits, int key_
   const int nht = a_in.group > 4 ? 2 : 1;
   const DecodeArgs& a = a_in;
   const int pm = 1 << (key_mse_bits - 1);
-  const int npl = pm + (key_qjl ? 1 : 0);
+  // half-bit keys with a 3-bit table: Walsh planes 2 and 3 share one operand
+  // word (the scan's SHARED layout), so the index product has three digit planes
+  const int pmd = (a.key_half && pm == 4) ? 3 : pm;
+  const int npl = pmd + (key_qjl ? 1 : 0);
   const dim3 qgrid(a.batch * a.h_kv, key_qjl ? 2 : 1, nht);
-  hipLaunchKernelGGL(qprep_mfma_kernel, qgrid, dim3(256), 0, stream, a, pm, npl, nht);
+  hipLaunchKernelGGL(qprep_mfma_kernel, qgrid, dim3(256), 0, stream, a, pm, pmd, npl, nht);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = nht == 1 ? dispatch_mfma<1>(a, key_mse_bits, key_qjl, value_mse, value_bits, stream, tl)
