@@ -470,7 +470,8 @@ def main():
         torch.cuda.empty_cache()
     sha = _source_sha("tq_decode_mfma.hip", "tq_decode.hip", "tq_common.h", "tq_internal.h")
     generic = os.environ.get("TQ_DECODE_PATH") == "generic"
-    traffic = None if generic else _traffic(SCAN_KERNEL, w.name, sha)
+    # the committed counter summaries are single-query runs
+    traffic = None if generic or args.queries != 1 else _traffic(SCAN_KERNEL, w.name, sha)
     scan_kernel_name = ("scan_kernel (VALU split scan over the compressed cache)"
                         if generic
                         else "scan_mfma_kernel (int8-MFMA split scan over the compressed cache)")
