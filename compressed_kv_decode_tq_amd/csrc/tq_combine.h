@@ -65,13 +65,16 @@ __device__ __forceinline__ float unit_sum(float x, float* red) {
 // split s at part0 + s * sstride, with the exact ring tokens; MSE values (VMSE)
 // are rotated back with Pi^T once.  Writes out[.][c].  The loads that need no
 // earlier result (split headers, each quarter's first kPre split words, the
-// ring key rows, each quarter's first kRingPre ring values) are issued before
-// their first use.  a.splits <= MAXS; at most kMaxRing ring tokens.
-template <bool VMSE, int MAXS>
+// ring key rows, each quarter's first kRingPre ring values and, for MSE
+// values, each quarter's rows of Pi) are issued before their first use.
+// a.splits <= MAXS; at most kMaxRing ring tokens.  PRE: split accumulator
+// words per thread loaded up front (each quarter's first PRE splits; the rest
+// come kBatch at a time).
+template <bool VMSE, int MAXS, int PRE>
 __device__ __forceinline__ void combine_unit(const DecodeArgs& a, int b, int h, int gq, CombineLds<MAXS>& L,
                                              const float* part0, size_t sstride) {
   constexpr int Q = kCombineQuarters;
-  constexpr int kPre = 8;      // split accumulator words per thread loaded up front
+  constexpr int kPre = PRE;
   constexpr int kRingPre = 8;  // ring values per thread loaded up front
   constexpr int kBatch = 8;    // loads per later round
   const int tid = threadIdx.x, c = tid & (kD - 1), qq = tid / kD;
@@ -116,6 +119,13 @@ __device__ __forceinline__ void combine_unit(const DecodeArgs& a, int b, int h, 
 #pragma unroll
     for (int u = 0; u < kRingPre; ++u)
       rv[u] = a.ring_v[(ring_row + (size_t)min(qq + Q * u, nr - 1) * a.h_kv) * kD + c];
+  }
+  // MSE values: column c of Pi, rows (kD / Q) qq .. + kD / Q - 1 (the
+  // rotation back of this quarter's part of the merged accumulator)
+  float wpi[VMSE ? kD / Q : 1];
+  if (VMSE) {
+#pragma unroll
+    for (int u = 0; u < kD / Q; ++u) wpi[u] = a.pi[(size_t)((kD / Q) * qq + u) * kD + c];
   }
   if (tid < kD) L.qv[c] = a.q_bf16 ? bf2f(qraw) : __uint_as_float(qraw);
   float M = -INFINITY;
@@ -188,13 +198,7 @@ __device__ __forceinline__ void combine_unit(const DecodeArgs& a, int b, int h, 
     float o = 0.f;
     if (any) {
 #pragma unroll
-      for (int i0 = 0; i0 < kD / Q; i0 += 16) {
-        float w[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) w[u] = a.pi[(size_t)((kD / Q) * qq + i0 + u) * kD + c];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) o = fmaf(w[u], L.arot[(kD / Q) * qq + i0 + u], o);
-      }
+      for (int u = 0; u < kD / Q; ++u) o = fmaf(wpi[u], L.arot[(kD / Q) * qq + u], o);
     }
     A = o;
   }

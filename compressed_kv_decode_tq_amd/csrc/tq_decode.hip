@@ -315,12 +315,17 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(DecodeArgs a) {
 // never splits a slot into more than kSplitTarget parts).
 constexpr int kMaxCombineSplits = (int)kSplitTarget;
 
-template <bool VMSE>
+// Split accumulator words per thread loaded up front: 8 (a quarter of up to
+// 32 splits) or, for slots split more than that, 24 (up to 96 splits, the
+// long-sequence splits, in one round trip).
+constexpr int kCombinePreShort = 8, kCombinePreLong = 24;
+
+template <bool VMSE, int PRE>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeArgs a) {
   __shared__ CombineLds<kMaxCombineSplits> lds;
   const int rows = a.h_kv * a.group;
   const int b = blockIdx.x / rows, h = (blockIdx.x % rows) / a.group, gq = blockIdx.x % a.group;
-  combine_unit<VMSE, kMaxCombineSplits>(a, b, h, gq, lds, a.partial + ws_row(a, b, h, gq) * (kD + 2),
+  combine_unit<VMSE, kMaxCombineSplits, PRE>(a, b, h, gq, lds, a.partial + ws_row(a, b, h, gq) * (kD + 2),
                                         (size_t)a.batch * a.h_kv * a.group * (kD + 2));
 }
 
@@ -385,10 +390,19 @@ hipError_t launch_decode(const DecodeArgs& a, int key_mse_bits, int key_qjl, int
 }
 
 hipError_t launch_combine(const DecodeArgs& a, int value_mse, hipStream_t stream) {
-  if (value_mse)
-    hipLaunchKernelGGL(combine_kernel<true>, dim3(a.batch * a.h_kv * a.group), dim3(kCombineThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(combine_kernel<false>, dim3(a.batch * a.h_kv * a.group), dim3(kCombineThreads), 0, stream, a);
+  const dim3 grid(a.batch * a.h_kv * a.group), block(kCombineThreads);
+  const bool many = a.splits > kCombineQuarters * kCombinePreShort;
+  if (value_mse) {
+    if (many)
+      hipLaunchKernelGGL((combine_kernel<true, kCombinePreLong>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((combine_kernel<true, kCombinePreShort>), grid, block, 0, stream, a);
+  } else {
+    if (many)
+      hipLaunchKernelGGL((combine_kernel<false, kCombinePreLong>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((combine_kernel<false, kCombinePreShort>), grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 

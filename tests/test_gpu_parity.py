@@ -331,6 +331,17 @@ def test_decode_group_sizes():
         _decode_case(w, [300], [1], f"G={g}")
 
 
+@pytest.mark.parametrize("n", [8192, 8448, 32768])
+@pytest.mark.parametrize("name", ["batched_small", "long_small"])
+def test_decode_combine_split_counts(name, n):
+    """One slot of n tokens in 256-token splits: 32 splits (the combine's
+    short prefetch, eight per quarter), 33 (its long prefetch) and 128 (past
+    the long prefetch's 24 per quarter, so the rest come in batches), with
+    min/max and MSE values and five ring tokens."""
+    w = SMALL[name].replace(batch=1, h_kv=1, h_q=4, n_tokens=n)
+    _decode_case(w, [n], [5], f"{name} n={n}")
+
+
 def test_decode_split_invariance_and_determinism():
     """The same slot decoded alone (sixteen 256-token splits) and among 192
     copies (four 1024-token splits) gives the same output to fp32 rounding;
