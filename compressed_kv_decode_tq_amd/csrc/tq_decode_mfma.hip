@@ -143,14 +143,16 @@ __device__ __forceinline__ float col_sum4(float x) {
 // Query digits of the score MFMAs.  For head tile ht, score plane pl and A
 // lane (g, m), m = 4 hh + L: 32 fp8 bytes, byte b of dword v holding digit L of
 // the value x of head 4 ht + hh at the coordinate that element meets in the
-// MFMA (score_coordinate), times 2^sigma / (nibble weight).  Plane pl < PM
-// multiplies w_pl * (Pi q); plane PM (QJL) 2 * (S q).  The four digits are a
+// MFMA (score_coordinate), times 2^sigma / (nibble weight).  The index
+// planes multiply w_pl * (Pi q) (the shared half/parity word of 3.5-bit keys
+// takes w_2 against its low and w_3 against its high 16 bits); the QJL plane,
+// the last, 2 * (S q).  The four digits are a
 // float expansion: d0 = fp8(y), d1 = fp8(16 (y - d0)), ... (each rounded to
 // nearest), so y = d0 + d1/16 + d2/256 + d3/4096 to about 2^-16 relative; the
 // MFMA's row scale 2^(-sigma - 4L) undoes the scaling, so the four digit rows
 // of a head sum to sum_c x_c bit_c - 0.5 sum_{c = 3 mod 4} x_c (the offset of
 // fp4_bits' dword 3, added back through the head constants).  The two products are independent down to
-// their digits: work-group (b h, 0) makes the PM index planes from Pi q (and
+// their digits: work-group (b h, 0) makes the index planes from Pi q (and
 // appends the ring token), (b h, 1) the QJL plane from S q.
 // One work item is (plane, lane group, head of the tile, dword) of head tile
 // ht: it expands the four coordinates of that dword once and writes the dword
