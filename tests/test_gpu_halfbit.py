@@ -31,6 +31,8 @@ CASES = {
                                                            key_mse_bits=1),
     "3.5-bit keys, MSE values": wl.WORKLOADS[4].replace(n_tokens=700, decode_steps=1, key_half=1, key_mse_bits=2),
     "2.5-bit keys, fp32 inputs": wl.WORKLOADS[1].replace(batch=1, n_tokens=500, key_half=1, key_mse_bits=1),
+    # six query heads per KV head: two head tiles on the shared half/parity word
+    "3.5-bit keys, Qwen layer": wl.by_name("qwen2.5-1.5b-layer-n4096-k3.5bit").replace(n_tokens=700),
 }
 
 

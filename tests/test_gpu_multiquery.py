@@ -95,6 +95,13 @@ def test_multi_query_without_ring():
     _multi_case(w, 4, [1000], [0], "long mse, no ring")
 
 
+def test_multi_query_half_bit_keys():
+    # T = 2 over four query heads per KV head: eight virtual heads, two head
+    # tiles on the shared half/parity operand word of 3.5-bit keys
+    w = wl.WORKLOADS[3].replace(batch=2, n_tokens=600, decode_steps=1, key_half=1)
+    _multi_case(w, 2, [600, 411], [3, 0], "batched minmax, 3.5-bit keys")
+
+
 def test_multi_query_qwen_layer():
     w = wl.by_name("qwen2.5-1.5b-layer-n4096").replace(n_tokens=1536)
     _multi_case(w, 2, [1536], [0], "qwen, six heads per KV head")
